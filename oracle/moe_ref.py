@@ -1,0 +1,276 @@
+"""Plain, slow CPU oracle of the sparse MoE FFN layer (float64, NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with the
+HIP path (``sparse_moe_ffn_gemm_amd``) and never imports it; both sides receive
+their inputs from ``synth``.
+
+What the layer computes, and where the pages state it:
+
+* "GPT-OSS on day 0", section "On Hopper" (the layer's feature list): the MLP is
+  a sparse mixture of experts with SwiGLU experts; the expert weights come from
+  a softmax taken *after* top-k; the experts carry biases.  The same page fixes
+  FP8 with 128x128 block scaling as the weight quantisation scheme.
+* same page, section "Kernels -> MoE": routing picks the top-k experts and takes
+  the softmax over the selected logits only (unlike DeepSeek-style routers that
+  softmax over all experts); the bias enters the grouped GEMM as the initial
+  accumulator value, once per output tile.
+* same page, "Kernels -> MoE" on dispatch/combine, and "Hosting Qwen on
+  Blackwell", section "MoE Dispatch - Combine / Expert Parallel": dispatch
+  aggregates routing information and gathers each expert's tokens into the
+  GEMM input buffers; combine is the gate-weighted accumulation of the expert
+  outputs per token.
+
+Readings where the pages are silent (each also listed in the design doc):
+  e4m3 is the OCP "fn" variant (bias 7, max 448, no infinities, 0x7F/0xFF NaN);
+  a scale is fp32(amax / 448) (IEEE fp32 divide), 1.0 for an all-zero block, and
+  a code is the nearest e4m3 value (ties to even) of fp32(v / s) clamped to
+  +-448; blocks tile each [N, K] matrix from (0, 0) with ragged edge blocks;
+  activations are quantised per token in 1x128 groups along K with the same
+  rule; w13 rows [0, I) are the gate projection and rows [I, 2I) the up
+  projection; SwiGLU is silu(gate) * up with silu(z) = z / (1 + e^-z); b13 is
+  added before SwiGLU and b2 to each expert's output (so it is gate-weighted);
+  top-k order is descending logit with ties to the lower expert index; the
+  dispatch order is expert-major and token-ascending inside an expert.
+
+Pins (tests/test_oracle_*.py): the e4m3 codec against its closed-form definition
+and torch's float8_e4m3fn, a brute-force nearest-code encoder and an independent
+scalar quantiser; router logits, top-k and gates against pure-Python loops and
+sorted(); the permutation against bincount / identity; the whole layer against
+a per-token brute-force evaluation written with scalar loops, a dense E=1, k=1
+SwiGLU FFN, the zero-weight (bias-only) case, b2-linearity and the token- and
+expert-relabelling invariances.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+BLOCK = 128
+
+
+# ----------------------------------------------------------------------------------------
+# FP8 e4m3 (OCP "fn") codec
+# ----------------------------------------------------------------------------------------
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each e4m3 code, float64.
+
+    e = bits 6..3, m = bits 2..0:  e >= 1: (-1)^s 2^(e-7) (1 + m/8);  e == 0:
+    (-1)^s 2^-6 (m/8);  magnitude code 0x7F is NaN (no infinities).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest e4m3 code (ties to the even code) of float32 values, after clamping to +-448.
+
+    The spacing of e4m3 values in the binade [2^e, 2^(e+1)) is 2^(e-3); below 2^-6
+    (subnormals) it is 2^-9.  Rounding |v| to a multiple of that spacing with
+    round-half-even gives the nearest representable value; its code is then read
+    off the definition (exponent field e+7, mantissa = fraction * 8).  The sign bit
+    is kept (a negative value that rounds to zero gives 0x80).
+    """
+    v32 = np.asarray(v, dtype=np.float32)
+    if np.isnan(v32).any():
+        raise ValueError("NaN has no defined code here")
+    a = np.minimum(np.abs(v32.astype(np.float64)), E4M3_MAX)
+    _, ex = np.frexp(a)                 # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)          # binade exponent (subnormal range uses -6)
+    step = np.ldexp(1.0, e - 3)
+    q = np.rint(a / step) * step        # a / step is exact (power-of-two step)
+    # code of q
+    qf, qe = np.frexp(q)
+    qe = qe - 1                          # q = (1 + frac) 2^qe for q >= 2^-6
+    normal = q >= 2.0 ** -6
+    mant = np.where(normal, np.rint((np.ldexp(q, -np.where(normal, qe, 0)) - 1.0) * 8.0), 0.0)
+    code_n = ((qe + 7) << 3) + mant.astype(np.int64)
+    code_s = np.rint(q / 2.0 ** -9).astype(np.int64)
+    mag = np.where(normal, code_n, code_s)
+    sign = np.signbit(v32).astype(np.int64) << 7
+    return (mag | sign).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------------------
+# Block quantisation (weights 128x128, activations 1x128)
+# ----------------------------------------------------------------------------------------
+
+def quantize_blocks(w, rows: int = BLOCK, cols: int = BLOCK):
+    """Quantise a float32 matrix [N, K] (or a batch [..., N, K]) in rows x cols blocks.
+
+    Per block: a = max |w| (fp32);  s = fp32(a / 448) if a > 0 else 1;
+    code = e4m3_encode(fp32(w / s)).  Returns (codes uint8 [..., N, K],
+    scales float32 [..., ceil(N/rows), ceil(K/cols)]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    *lead, N, K = w.shape
+    nb, kb = -(-N // rows), -(-K // cols)
+    codes = np.empty(w.shape, np.uint8)
+    scales = np.empty(tuple(lead) + (nb, kb), np.float32)
+    for i in range(nb):
+        r0, r1 = i * rows, min((i + 1) * rows, N)
+        for j in range(kb):
+            c0, c1 = j * cols, min((j + 1) * cols, K)
+            blk = w[..., r0:r1, c0:c1]
+            amax = np.abs(blk).max(axis=(-2, -1))
+            s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+            scales[..., i, j] = s
+            codes[..., r0:r1, c0:c1] = e4m3_encode(blk / s[..., None, None])
+    return codes, scales
+
+
+def dequantize_blocks(codes, scales, rows: int = BLOCK, cols: int = BLOCK) -> np.ndarray:
+    """decode(code) * scale of its block, float64."""
+    codes = np.asarray(codes)
+    N, K = codes.shape[-2:]
+    s = np.asarray(scales, dtype=np.float64)
+    s_full = np.repeat(np.repeat(s, rows, axis=-2)[..., :N, :], cols, axis=-1)[..., :K]
+    return e4m3_decode(codes) * s_full
+
+
+def quantize_activations(a32):
+    """Per-row 1x128 quantisation of a float32 [R, K] matrix: (codes, scales [R, ceil(K/128)])."""
+    return quantize_blocks(np.asarray(a32, dtype=np.float32), rows=1, cols=BLOCK)
+
+
+# ----------------------------------------------------------------------------------------
+# Routing
+# ----------------------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def router_logits(x_bits, router_w, router_b) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] W[e, h] + b[e], float64 (x taken exactly from bf16)."""
+    x = bf16_to_f64(x_bits)
+    return x @ np.asarray(router_w, np.float64).T + np.asarray(router_b, np.float64)
+
+
+def topk_softmax(logits, k: int):
+    """Top-k experts per token (descending logit, ties -> lower index) and the softmax
+    over the k selected logits only: g_j = exp(l_j - l_1) / sum_i exp(l_i - l_1)."""
+    logits = np.asarray(logits, np.float64)
+    order = np.argsort(-logits, axis=1, kind="stable")
+    ids = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(logits, ids.astype(np.int64), axis=1)
+    z = np.exp(sel - sel[:, :1])
+    gates = z / z.sum(axis=1, keepdims=True)
+    return ids, gates
+
+
+def permute(ids, E: int):
+    """Dispatch tables: counts[e], offsets (exclusive prefix sum, E+1 entries), perm[p] =
+    t*k + j for the p-th routed row in expert-major, token-ascending order, and inv =
+    the inverse of perm (inv[t*k + j] = p)."""
+    ids = np.asarray(ids, np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.argsort(flat, kind="stable").astype(np.int32)   # ties keep t*k+j order
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size, dtype=np.int32)
+    return counts, offsets, perm, inv
+
+
+# ----------------------------------------------------------------------------------------
+# Experts and combine
+# ----------------------------------------------------------------------------------------
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(xd_rows, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, I: int):
+    """One expert on its rows (float64).
+
+    C = xd . deq(w13)^T + b13 ;  h = silu(C[:, :I]) * C[:, I:] ;  h is rounded to
+    fp32 and quantised per row in 1x128 groups ;  y = deq(h) . deq(w2)^T + b2.
+    Returns (y, h_codes, h_scales, h64)."""
+    W13 = dequantize_blocks(w13_codes, w13_scales)
+    C = xd_rows @ W13.T + bf16_to_f64(b13)
+    h = silu(C[:, :I]) * C[:, I:]
+    hq, hs = quantize_activations(h.astype(np.float32))
+    hd = dequantize_blocks(hq, hs, rows=1, cols=BLOCK)
+    W2 = dequantize_blocks(w2_codes, w2_scales)
+    y = hd @ W2.T + bf16_to_f64(b2)
+    return y, hq, hs, h
+
+
+def combine(y, gates, inv, T: int, k: int) -> np.ndarray:
+    """out[t] = sum_j gates[t, j] * y[inv[t*k + j]]  (float64)."""
+    yr = y[np.asarray(inv, np.int64).reshape(T, k)]          # [T, k, H]
+    return np.einsum("tk,tkh->th", np.asarray(gates, np.float64), yr)
+
+
+def f64_to_bf16_bits(a) -> np.ndarray:
+    """Round float64 to bfloat16 once (nearest, ties to even) -- the output format."""
+    a = np.asarray(a, np.float64)
+    # exact: split via float32 is not single rounding, so round directly from float64
+    m, e = np.frexp(a)                       # a = m 2^e, |m| in [0.5, 1)
+    q = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # 8 significant bits, half-even
+    return (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def forward(x_bits, router_w, router_b, top_k: int, I: int, w13_codes, w13_scales, b13,
+            w2_codes, w2_scales, b2, token_subset=None):
+    """The layer forward pass.
+
+    ``w13_codes`` etc. are indexable by expert (arrays [E, ...] or dict-like of the
+    experts needed).  With ``token_subset`` only those tokens are evaluated: routing,
+    x quantisation and the combine are per token, so a token's output does not depend
+    on which other tokens are present (the dispatch tables are still built over all
+    tokens).  Returns a dict of every stage's result."""
+    T = x_bits.shape[0]
+    E = router_w.shape[0]
+    logits = router_logits(x_bits, router_w, router_b)
+    ids, gates = topk_softmax(logits, top_k)
+    counts, offsets, perm, inv = permute(ids, E)
+    x32 = bf16_to_f64(x_bits).astype(np.float32)
+    toks = np.arange(T) if token_subset is None else np.asarray(token_subset)
+    xq, sx = quantize_activations(x32[toks])
+    xd = dequantize_blocks(xq, sx, rows=1, cols=BLOCK)
+    H = x_bits.shape[1]
+    y = np.zeros((toks.size, top_k, H))
+    for e in np.unique(ids[toks]):
+        rows_t, rows_j = np.nonzero(ids[toks] == e)
+        ye, _, _, _ = expert_ffn(xd[rows_t], w13_codes[e], w13_scales[e], b13[e],
+                                 w2_codes[e], w2_scales[e], b2[e], I)
+        y[rows_t, rows_j] = ye
+    out = np.einsum("tk,tkh->th", gates[toks], y)
+    return dict(logits=logits, ids=ids, gates=gates, counts=counts, offsets=offsets, perm=perm,
+                inv=inv, xq=xq, sx=sx, out=out, out_bf16=f64_to_bf16_bits(out), tokens=toks)
+
+
+def forward_dispatched(x_bits, router_w, router_b, top_k: int, I: int, w13_codes, w13_scales,
+                       b13, w2_codes, w2_scales, b2):
+    """The same layer evaluated through the dispatch tables (permute -> per-expert
+    contiguous segments -> combine via inv), as the pages' dispatch/combine split
+    describes.  Used to pin ``forward`` and the tables against each other."""
+    T = x_bits.shape[0]
+    E = router_w.shape[0]
+    logits = router_logits(x_bits, router_w, router_b)
+    ids, gates = topk_softmax(logits, top_k)
+    counts, offsets, perm, inv = permute(ids, E)
+    x32 = bf16_to_f64(x_bits).astype(np.float32)
+    xq, sx = quantize_activations(x32)
+    xd = dequantize_blocks(xq, sx, rows=1, cols=BLOCK)
+    tok_of_row = perm // top_k
+    y = np.zeros((T * top_k, x_bits.shape[1]))
+    for e in range(E):
+        p0, p1 = offsets[e], offsets[e + 1]
+        if p1 > p0:
+            y[p0:p1], _, _, _ = expert_ffn(xd[tok_of_row[p0:p1]], w13_codes[e], w13_scales[e],
+                                           b13[e], w2_codes[e], w2_scales[e], b2[e], I)
+    out = combine(y, gates, inv, T, top_k)
+    return dict(ids=ids, gates=gates, counts=counts, offsets=offsets, perm=perm, inv=inv,
+                y=y, out=out, out_bf16=f64_to_bf16_bits(out))
