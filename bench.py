@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one ``moe_forward`` of the whole layer (router GEMM, top-k + softmax,
+dispatch, activation quantisation, GEMM1 + SwiGLU + requantisation, GEMM2, combine)
+over one batch of T synthetic tokens whose inputs are already resident in HBM.  The
+default workload is the gpt-oss-120b-shaped prefill layer (T=8192, H=2880, E=128,
+top-4, I=2880).  Per-stage device times come from HIP events recorded between the
+library's kernels on the same stream (``moe_forward_profiled``) inside the timed
+region.  Rank 0 prints one JSON line.
+
+The CPU baseline is the fp64 oracle (test infrastructure) timed on a bounded sample of
+tokens of the same layer, on one host thread.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MoE layer tokens/s + TFLOP/s & HBM GB/s vs MI355X peak (gpt-oss-120b shape)"
+
+
+def kb(n):
+    return (n + 127) // 128
+
+
+def algorithmic(shape, counts):
+    """Algorithmic flops and compulsory HBM bytes of the layer and of its two GEMMs.
+
+    Weights are counted once per *active* expert (an expert with no routed token is
+    never read).  Intermediates (x codes, h, y) count where a kernel must read or write
+    them at least once."""
+    T, H, E, k, I = shape.T, shape.H, shape.E, shape.top_k, shape.I
+    rows = T * k
+    active = int((counts > 0).sum())
+    w13 = active * (2 * I * H + kb(2 * I) * kb(H) * 4 + (2 * I * 2 if shape.expert_bias else 0))
+    w2 = active * (H * I + kb(H) * kb(I) * 4 + (H * 2 if shape.expert_bias else 0))
+    layer_bytes = T * H * 2 + E * H * 4 + E * 4 + w13 + w2 + T * H * 2
+    xq = T * H + T * kb(H) * 4
+    hq = rows * I + rows * kb(I) * 4
+    g1_flops = 2 * rows * H * 2 * I
+    g2_flops = 2 * rows * I * H
+    return dict(
+        active_experts=active,
+        layer_flops=g1_flops + g2_flops, layer_bytes=layer_bytes,
+        gemm1=dict(flops=g1_flops, bytes=w13 + xq + hq),
+        gemm2=dict(flops=g2_flops, bytes=w2 + hq + rows * H * 4))
+
+
+def traffic_from_profiles(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "sparse_moe_ffn_gemm_amd", "csrc", rec.get("source", "gemm.hip"))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, li, n_tokens):
+    """The oracle's forward on the first ``n_tokens`` tokens (one thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe_ref as R
+    from synth import expert_weights
+    from synth.cases import _base_shape
+
+    base = _base_shape(shape)
+    dev = "cuda" if base.weights_on_device else "cpu"
+    toks = np.arange(min(n_tokens, shape.T))
+    with threadpool_limits(limits=1):
+        ids, _ = R.topk_softmax(R.router_logits(li.x, li.router_w, li.router_b), shape.top_k)
+        need = np.unique(ids[toks])
+        c13, s13, c2, s2 = {}, {}, {}, {}
+        for e in need:   # offline weight conversion: not timed
+            c13[e], s13[e] = R.quantize_blocks(expert_weights(shape, "w13", int(e), dev).cpu().numpy())
+            c2[e], s2[e] = R.quantize_blocks(expert_weights(shape, "w2", int(e), dev).cpu().numpy())
+        t0 = time.perf_counter()
+        R.forward(li.x, li.router_w, li.router_b, shape.top_k, shape.I, c13, s13, li.b13, c2, s2,
+                  li.b2, token_subset=toks)
+        dt = time.perf_counter() - t0
+    return {"value": round(toks.size / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {toks.size} of {shape.T} tokens ({need.size} experts), fp64 NumPy "
+                      f"forward incl. weight dequantisation, {dt:.1f} s"}
+
+
+def copy_calibration(gib=1.0, reps=5):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt-oss-120b-prefill")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this layer runs on one GPU; multi-GPU runs (--gpus > 1) are not part "
+              "of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import sparse_moe_ffn_gemm_amd as moe
+    from sparse_moe_ffn_gemm_amd._lib import PROFILE_STAGES
+    from synth import SHAPES, expert_weights, make_inputs
+
+    if args.workload not in SHAPES:
+        sys.exit(f"unknown workload {args.workload}; one of {list(SHAPES)}")
+    shape = SHAPES[args.workload]
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    li = make_inputs(shape)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    layer = moe.MoELayer.from_expert_weights(
+        torch.from_numpy(li.router_w), torch.from_numpy(li.router_b), shape.top_k,
+        bf(li.b13) if shape.expert_bias else None, bf(li.b2) if shape.expert_bias else None,
+        lambda e: expert_weights(shape, "w13", e, "cuda"),
+        lambda e: expert_weights(shape, "w2", e, "cuda"), device=dev)
+    x = bf(li.x)
+    out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=dev)
+    routing = moe.new_routing(shape.T, shape.E, shape.top_k, dev)
+    ws = layer.workspace(shape.T)
+    fwd_args = (x, layer.router_w, layer.router_b, layer.w13, layer.w13_scales, layer.b13,
+                layer.w2, layer.w2_scales, layer.b2, shape.top_k)
+    torch.cuda.synchronize()
+    print(f"[bench] {shape.name}: setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr,
+          flush=True)
+
+    for _ in range(args.warmup):
+        moe.forward(*fwd_args, out=out, routing=routing, workspace=ws)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PROFILE_STAGES) + 1)]
+              for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for s in range(args.steps):
+        moe.forward_profiled(events[s], *fwd_args, out=out, routing=routing, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    stage_ms = {name: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
+                                     for s in range(args.steps)]))
+                for i, name in enumerate(PROFILE_STAGES)}
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall:.3f} s); stages "
+          + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in stage_ms.items()), file=sys.stderr,
+          flush=True)
+
+    counts = routing["expert_counts"].cpu().numpy()
+    alg = algorithmic(shape, counts)
+    step_s = ms_step / 1e3
+    tflops = alg["layer_flops"] / step_s / 1e12
+    gbs = alg["layer_bytes"] / step_s / 1e9
+
+    # dominant kernel: the one with the most device time
+    dom = max(("gemm1", "gemm2"), key=lambda k: stage_ms[k])
+    k_s = stage_ms[dom] / 1e3
+    k_alg = alg[dom]
+    intensity = k_alg["flops"] / k_alg["bytes"]
+    ridge = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": k_alg["flops"] / k_s / 1e12, "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": k_alg["bytes"] / k_s / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profiles(shape.name, dom)
+    roof["kernel"] = dom
+    roof["achieved"] = round(roof["achieved"], 2)
+    roof["frac"] = round(roof["frac"], 4)
+
+    line = {
+        "metric": METRIC, "value": round(shape.T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "E": shape.E,
+                   "top_k": shape.top_k, "I": shape.I, "parallelism": "single-gpu"},
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+        "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "active_experts": alg["active_experts"],
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(shape, li, args.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

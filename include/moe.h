@@ -1,0 +1,160 @@
+/* moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN layer.
+ *
+ * The layer ("GPT-OSS on day 0", section "On Hopper" feature list and section
+ * "Kernels -> MoE"; "Hosting Qwen on Blackwell", section "MoE Dispatch - Combine"):
+ *
+ *   logits = x . Wr^T + br                      router GEMM, fp32
+ *   ids, gates = top-k(logits), softmax over the k selected logits
+ *   for every expert e and the tokens routed to it (expert-major dispatch):
+ *     C = deq(xq) . deq(w13_e)^T + b13_e        FP8 GEMM, 128x128-block-scaled weights
+ *     h = silu(C[:, :I]) * C[:, I:]             SwiGLU (rows [0,I) of w13 = gate, [I,2I) = up)
+ *     y = deq(hq) . deq(w2_e)^T + b2_e          FP8 GEMM
+ *   out[t] = sum_j gates[t,j] * y(t, j)          gate-weighted combine, rounded once to bf16
+ *
+ * Activations x and h are quantised per token (per routed row for h) in 1x128 groups
+ * along K; weights in 128x128 blocks.  A scale is fp32(amax / 448) (1 for an all-zero
+ * group), a code the nearest OCP e4m3 value (ties to even) of fp32(v / scale) clamped
+ * to +-448.  Blocks tile each matrix from (0,0); edge blocks are partial.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are caller-owned DEVICE pointers, row-major, contiguous,
+ *     16-byte aligned.  bf16 is passed as uint16_t bit patterns, fp8 as uint8_t OCP
+ *     e4m3fn codes.  `stream` is a hipStream_t (NULL = the null stream).
+ *   - Arguments are validated synchronously; on error a negative status is returned
+ *     and NOTHING is enqueued.  On success the work is only ENQUEUED on `stream`:
+ *     no host synchronisation and no device allocation happen inside the library.
+ *   - Inputs are read-only and must not alias outputs or the workspace.
+ *   - Calls are re-entrant; concurrent calls must use distinct workspaces.
+ *   - A launch failure reported by the HIP runtime returns MOE_ERR_HIP.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,         /* null / misaligned pointer, non-positive size */
+    MOE_ERR_UNSUPPORTED_SHAPE = -2,   /* shape outside the supported envelope below */
+    MOE_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes < moe_workspace_bytes(...) */
+    MOE_ERR_HIP = -4                  /* the HIP runtime reported a launch error */
+} moe_status;
+
+/* Supported envelope: 1 <= T, 1 <= E <= 256, 1 <= top_k <= min(E, 8),
+ * H and I positive multiples of 64, T * top_k < 2^31, T * H < 2^31. */
+
+/* Routing tables, all caller-owned device buffers:
+ *   topk_ids       [T, top_k] int32   expert ids per token, descending logit,
+ *                                     exact ties -> lower expert index
+ *   topk_gates     [T, top_k] float   softmax over the selected logits (sum = 1)
+ *   expert_counts  [E]        int32   routed rows per expert
+ *   expert_offsets [E + 1]    int32   exclusive prefix sum of the counts
+ *   perm           [T*top_k]  int32   perm[p] = t*top_k + j of the p-th routed row, in
+ *                                     expert-major, token-ascending order
+ *   inv_perm       [T*top_k]  int32   inverse of perm: inv_perm[t*top_k + j] = p
+ * ("Hosting Qwen on Blackwell", section "Expert Parallel": the dispatch step aggregates
+ * the routing information and gathers each expert's tokens for its GEMM.) */
+typedef struct {
+    int32_t* topk_ids;
+    float* topk_gates;
+    int32_t* expert_counts;
+    int32_t* expert_offsets;
+    int32_t* perm;
+    int32_t* inv_perm;
+} moe_routing;
+
+/* Byte offsets of the intermediates inside a workspace (for diagnostics):
+ *   xq [T, H] u8 + sx [T, ceil(H/128)] f32     quantised activations
+ *   h  [T*top_k, I] u8 + sh [T*top_k, ceil(I/128)] f32   quantised SwiGLU output,
+ *                                               rows in dispatch (perm) order
+ *   y  [T*top_k, H] f32                        expert outputs incl. b2, dispatch order
+ *   routing.*                                  the tables used when routing_out == NULL
+ * Valid after a completed moe_forward on that workspace. */
+typedef struct {
+    size_t xq, sx, h, sh, y;
+    size_t topk_ids, topk_gates, expert_counts, expert_offsets, perm, inv_perm;
+    size_t total;
+} moe_workspace_regions;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(moe_status s);
+
+/* Bytes of device workspace moe_route / moe_forward need for this shape; 0 if the shape
+ * is unsupported. */
+size_t moe_workspace_bytes(int T, int H, int E, int top_k, int I);
+
+/* Fills `out` with the workspace layout for this shape. */
+moe_status moe_workspace_layout(int T, int H, int E, int top_k, int I, moe_workspace_regions* out);
+
+/* 128x128 block quantisation of E stacked fp32 matrices ("GPT-OSS on day 0", section
+ * "On Hopper": FP8 with 128x128 block scaling; weights are converted statically, as in
+ * "Hosting Qwen on Blackwell", section "Quantization").
+ *   w      [E, N, K] float      source weights
+ *   codes  [E, N, K] uint8      e4m3 codes (output)
+ *   scales [E, ceil(N/128), ceil(K/128)] float   block scales (output)
+ * Requires E, N >= 1 and K a positive multiple of 16. */
+moe_status moe_quantize_weights(const float* w, int E, int N, int K, uint8_t* codes,
+                                float* scales, void* stream);
+
+/* Per-token 1x128 activation quantisation (the activation side of the FP8 GEMMs).
+ *   x      [T, H] bf16          input
+ *   codes  [T, H] uint8         e4m3 codes (output)
+ *   scales [T, ceil(H/128)] float (output)
+ * Requires T >= 1 and H a positive multiple of 64. */
+moe_status moe_quantize_activations(const uint16_t* x, int T, int H, uint8_t* codes,
+                                    float* scales, void* stream);
+
+/* Router GEMM + top-k + softmax over the selected logits + dispatch tables ("GPT-OSS on
+ * day 0", section "Kernels -> MoE").
+ *   x        [T, H] bf16        activations
+ *   router_w [E, H] float       router weight (nn.Linear layout)
+ *   router_b [E] float          router bias (NULL = zero)
+ *   out      routing tables (all six pointers required)
+ *   workspace / workspace_bytes  >= moe_workspace_bytes(T, H, E, top_k, 64) */
+moe_status moe_route(const uint16_t* x, const float* router_w, const float* router_b, int T,
+                     int H, int E, int top_k, const moe_routing* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* The whole layer forward.
+ *   x          [T, H] bf16
+ *   router_w   [E, H] float,  router_b [E] float (NULL = zero)
+ *   w13        [E, 2I, H] e4m3 codes, w13_scales [E, ceil(2I/128), ceil(H/128)] float
+ *   b13        [E, 2I] bf16 (NULL = zero)
+ *   w2         [E, H, I] e4m3 codes,  w2_scales [E, ceil(H/128), ceil(I/128)] float
+ *   b2         [E, H] bf16 (NULL = zero)
+ *   out        [T, H] bf16, fully overwritten
+ *   routing_out  optional (NULL allowed): also receive the routing tables
+ *   workspace  >= moe_workspace_bytes(T, H, E, top_k, I) bytes of device memory */
+moe_status moe_forward(const uint16_t* x, const float* router_w, const float* router_b,
+                       const uint8_t* w13, const float* w13_scales, const uint16_t* b13,
+                       const uint8_t* w2, const float* w2_scales, const uint16_t* b2, int T,
+                       int H, int E, int top_k, int I, uint16_t* out,
+                       const moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* moe_forward with per-stage timing: identical work and results, plus
+ * MOE_PROFILE_EVENTS hipEvent_t handles (created by the caller) recorded on `stream`
+ * before each stage and after the last one:
+ *   0 router GEMM  1 top-k + softmax  2 dispatch scan  3 dispatch scatter
+ *   4 activation quantisation  5 GEMM1 (+ bias, SwiGLU, requantisation)
+ *   6 GEMM2 (+ bias)  7 combine  8 end
+ * so hipEventElapsedTime(events[i], events[i+1]) is stage i's device time.
+ * `events` must hold MOE_PROFILE_EVENTS valid hipEvent_t (else MOE_ERR_INVALID_ARG). */
+#define MOE_PROFILE_EVENTS 9
+moe_status moe_forward_profiled(const uint16_t* x, const float* router_w, const float* router_b,
+                                const uint8_t* w13, const float* w13_scales, const uint16_t* b13,
+                                const uint8_t* w2, const float* w2_scales, const uint16_t* b2,
+                                int T, int H, int E, int top_k, int I, uint16_t* out,
+                                const moe_routing* routing_out, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

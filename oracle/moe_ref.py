@@ -53,40 +53,36 @@ BLOCK = 128
 # FP8 e4m3 (OCP "fn") codec
 # ----------------------------------------------------------------------------------------
 
-def e4m3_decode(codes) -> np.ndarray:
-    """Value of each e4m3 code, float64.
-
-    e = bits 6..3, m = bits 2..0:  e >= 1: (-1)^s 2^(e-7) (1 + m/8);  e == 0:
-    (-1)^s 2^-6 (m/8);  magnitude code 0x7F is NaN (no infinities).
-    """
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
+    """The OCP e4m3fn definition, for an array of codes (int64)."""
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = (c & 0x7).astype(np.float64)
     mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
-    val = sign * mag
-    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
 
 
-def e4m3_encode(v) -> np.ndarray:
-    """Nearest e4m3 code (ties to the even code) of float32 values, after clamping to +-448.
+_E4M3_TABLE = _e4m3_value(np.arange(256, dtype=np.int64))
 
-    The spacing of e4m3 values in the binade [2^e, 2^(e+1)) is 2^(e-3); below 2^-6
-    (subnormals) it is 2^-9.  Rounding |v| to a multiple of that spacing with
-    round-half-even gives the nearest representable value; its code is then read
-    off the definition (exponent field e+7, mantissa = fraction * 8).  The sign bit
-    is kept (a negative value that rounds to zero gives 0x80).
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each e4m3 code, float64.
+
+    e = bits 6..3, m = bits 2..0:  e >= 1: (-1)^s 2^(e-7) (1 + m/8);  e == 0:
+    (-1)^s 2^-6 (m/8);  magnitude code 0x7F is NaN (no infinities).  The definition
+    is evaluated once for all 256 codes and then looked up.
     """
-    v32 = np.asarray(v, dtype=np.float32)
-    if np.isnan(v32).any():
-        raise ValueError("NaN has no defined code here")
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def _encode_flat(v32: np.ndarray) -> np.ndarray:
     a = np.minimum(np.abs(v32.astype(np.float64)), E4M3_MAX)
     _, ex = np.frexp(a)                 # a = f * 2^ex, f in [0.5, 1)
     e = np.maximum(ex - 1, -6)          # binade exponent (subnormal range uses -6)
     step = np.ldexp(1.0, e - 3)
     q = np.rint(a / step) * step        # a / step is exact (power-of-two step)
     # code of q
-    qf, qe = np.frexp(q)
+    _, qe = np.frexp(q)
     qe = qe - 1                          # q = (1 + frac) 2^qe for q >= 2^-6
     normal = q >= 2.0 ** -6
     mant = np.where(normal, np.rint((np.ldexp(q, -np.where(normal, qe, 0)) - 1.0) * 8.0), 0.0)
@@ -97,6 +93,27 @@ def e4m3_encode(v) -> np.ndarray:
     return (mag | sign).astype(np.uint8)
 
 
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest e4m3 code (ties to the even code) of float32 values, after clamping to +-448.
+
+    The spacing of e4m3 values in the binade [2^e, 2^(e+1)) is 2^(e-3); below 2^-6
+    (subnormals) it is 2^-9.  Rounding |v| to a multiple of that spacing with
+    round-half-even gives the nearest representable value; its code is then read
+    off the definition (exponent field e+7, mantissa = fraction * 8).  The sign bit
+    is kept (a negative value that rounds to zero gives 0x80).  Evaluated in slices
+    of the flattened input only to bound the temporaries.
+    """
+    v32 = np.asarray(v, dtype=np.float32)
+    if np.isnan(v32).any():
+        raise ValueError("NaN has no defined code here")
+    flat = v32.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+    step = 1 << 18
+    for i in range(0, flat.size, step):
+        out[i:i + step] = _encode_flat(flat[i:i + step])
+    return out.reshape(v32.shape)
+
+
 # ----------------------------------------------------------------------------------------
 # Block quantisation (weights 128x128, activations 1x128)
 # ----------------------------------------------------------------------------------------
@@ -105,33 +122,32 @@ def quantize_blocks(w, rows: int = BLOCK, cols: int = BLOCK):
     """Quantise a float32 matrix [N, K] (or a batch [..., N, K]) in rows x cols blocks.
 
     Per block: a = max |w| (fp32);  s = fp32(a / 448) if a > 0 else 1;
-    code = e4m3_encode(fp32(w / s)).  Returns (codes uint8 [..., N, K],
-    scales float32 [..., ceil(N/rows), ceil(K/cols)]).
-    """
+    code = e4m3_encode(fp32(w / s)).  Edge blocks are partial: the matrix is padded
+    with zeros to whole blocks (zeros change no block maximum) and the padding is
+    dropped afterwards.  Returns (codes uint8 [..., N, K], scales float32
+    [..., ceil(N/rows), ceil(K/cols)])."""
     w = np.asarray(w, dtype=np.float32)
     *lead, N, K = w.shape
     nb, kb = -(-N // rows), -(-K // cols)
-    codes = np.empty(w.shape, np.uint8)
-    scales = np.empty(tuple(lead) + (nb, kb), np.float32)
-    for i in range(nb):
-        r0, r1 = i * rows, min((i + 1) * rows, N)
-        for j in range(kb):
-            c0, c1 = j * cols, min((j + 1) * cols, K)
-            blk = w[..., r0:r1, c0:c1]
-            amax = np.abs(blk).max(axis=(-2, -1))
-            s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-            scales[..., i, j] = s
-            codes[..., r0:r1, c0:c1] = e4m3_encode(blk / s[..., None, None])
-    return codes, scales
+    pad = np.zeros(tuple(lead) + (nb * rows, kb * cols), np.float32)
+    pad[..., :N, :K] = w
+    blocks = pad.reshape(tuple(lead) + (nb, rows, kb, cols))
+    amax = np.abs(blocks).max(axis=(-3, -1))                       # [..., nb, kb]
+    scales = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = blocks / scales[..., :, None, :, None]                      # fp32 / fp32 -> fp32
+    codes = e4m3_encode(q).reshape(pad.shape)[..., :N, :K]
+    return np.ascontiguousarray(codes), scales
 
 
 def dequantize_blocks(codes, scales, rows: int = BLOCK, cols: int = BLOCK) -> np.ndarray:
     """decode(code) * scale of its block, float64."""
-    codes = np.asarray(codes)
-    N, K = codes.shape[-2:]
+    vals = e4m3_decode(codes)
     s = np.asarray(scales, dtype=np.float64)
-    s_full = np.repeat(np.repeat(s, rows, axis=-2)[..., :N, :], cols, axis=-1)[..., :K]
-    return e4m3_decode(codes) * s_full
+    N, K = vals.shape[-2:]
+    for i in range(s.shape[-2]):
+        for j in range(s.shape[-1]):
+            vals[..., i * rows:(i + 1) * rows, j * cols:(j + 1) * cols] *= s[..., i, j, None, None]
+    return vals
 
 
 def quantize_activations(a32):
@@ -266,11 +282,14 @@ def forward_dispatched(x_bits, router_w, router_b, top_k: int, I: int, w13_codes
     xd = dequantize_blocks(xq, sx, rows=1, cols=BLOCK)
     tok_of_row = perm // top_k
     y = np.zeros((T * top_k, x_bits.shape[1]))
+    hq = np.zeros((T * top_k, I), np.uint8)
+    hs = np.ones((T * top_k, -(-I // BLOCK)), np.float32)
     for e in range(E):
         p0, p1 = offsets[e], offsets[e + 1]
         if p1 > p0:
-            y[p0:p1], _, _, _ = expert_ffn(xd[tok_of_row[p0:p1]], w13_codes[e], w13_scales[e],
-                                           b13[e], w2_codes[e], w2_scales[e], b2[e], I)
+            y[p0:p1], hq[p0:p1], hs[p0:p1], _ = expert_ffn(
+                xd[tok_of_row[p0:p1]], w13_codes[e], w13_scales[e], b13[e], w2_codes[e],
+                w2_scales[e], b2[e], I)
     out = combine(y, gates, inv, T, top_k)
-    return dict(ids=ids, gates=gates, counts=counts, offsets=offsets, perm=perm, inv=inv,
-                y=y, out=out, out_bf16=f64_to_bf16_bits(out))
+    return dict(logits=logits, ids=ids, gates=gates, counts=counts, offsets=offsets, perm=perm,
+                inv=inv, xq=xq, sx=sx, hq=hq, hs=hs, y=y, out=out, out_bf16=f64_to_bf16_bits(out))

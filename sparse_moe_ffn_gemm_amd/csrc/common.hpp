@@ -1,0 +1,60 @@
+// Device helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kBlock = 128;          // quantisation block / group edge
+constexpr float kFp8Max = 448.0f;    // largest finite OCP e4m3 value
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; inputs are finite.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Scale of a group with absolute maximum `amax`: fp32(amax / 448) with an IEEE
+// (correctly rounded) division, 1 for an all-zero group.
+__device__ __forceinline__ float group_scale(float amax) {
+  return amax > 0.0f ? amax / kFp8Max : 1.0f;
+}
+
+// Two e4m3 codes (OCP fn, round to nearest even) of v0/s and v1/s, clamped to +-448,
+// packed into the low 16 bits.  The quotient is an IEEE division so that the code is
+// the one the fp32 quantisation rule defines.
+__device__ __forceinline__ uint32_t encode2(float v0, float v1, float s) {
+  float q0 = fminf(fmaxf(v0 / s, -kFp8Max), kFp8Max);
+  float q1 = fminf(fmaxf(v1 / s, -kFp8Max), kFp8Max);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false)) & 0xFFFFu;
+}
+
+// Four codes packed little-endian into one dword.
+__device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float v3, float s) {
+  return encode2(v0, v1, s) | (encode2(v2, v3, s) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Max over each aligned group of `W` lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = W / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,66 @@
+// Internal launchers of the gfx950 kernels (one translation unit per kernel family).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace moe {
+
+// One M-tile of the grouped GEMMs: rows [row_begin, row_end) of expert `expert` in
+// dispatch order.
+struct MTile {
+  int expert, row_begin, row_end, pad;
+};
+
+// ---- quantisers ----
+void launch_quantize_weights(const float* w, int E, int N, int K, uint8_t* codes, float* scales,
+                             hipStream_t st);
+void launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* codes, float* scales,
+                         hipStream_t st);
+
+// ---- routing ----
+constexpr int kRouterTile = 64;     // tokens / experts per router GEMM workgroup
+constexpr int kChunk = 64;          // tokens per dispatch chunk
+
+// partial[s][t][e] = sum over the s-th slice of H of x[t,h] * W[e,h]
+void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
+                          int kslice, float* partial, hipStream_t st);
+// ids/gates + per-chunk expert histogram hist[chunk][E]
+void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
+                 int32_t* ids, float* gates, int32_t* hist, hipStream_t st);
+// counts, offsets, per-chunk bases and the M-tile list for tiles of `bm` rows
+void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32_t* counts,
+                          int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
+                          hipStream_t st);
+void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,
+                             int top_k, int32_t* perm, int32_t* inv, hipStream_t st);
+
+// ---- grouped FP8 GEMMs ----
+struct GemmArgs {
+  const uint8_t* A;          // gemm1: xq [T, K] (rows gathered through perm); gemm2: h [rows, K]
+  const float* A_scale;      // [*, ceil(K/128)]
+  const int32_t* perm;       // gemm1 only
+  int top_k;
+  const uint8_t* B;          // [E, N, K]
+  const float* B_scale;      // [E, ceil(N/128), ceil(K/128)]
+  const uint16_t* bias;      // [E, N] or NULL
+  const MTile* tiles;
+  const int32_t* num_tiles;
+  int K, N, I;
+  uint8_t* h_out;            // gemm1: [rows, I]
+  float* h_scale;            // gemm1: [rows, ceil(I/128)]
+  float* y_out;              // gemm2: [rows, N]
+};
+
+// Rows per M-tile chosen for a layer with `rows` routed rows over E experts.
+int gemm_tile_rows(long rows, int E);
+void launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
+void launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
+
+// ---- combine ----
+void launch_combine(const float* y, const float* gates, const int32_t* inv, int T, int H,
+                    int top_k, uint16_t* out, hipStream_t st);
+
+}  // namespace moe

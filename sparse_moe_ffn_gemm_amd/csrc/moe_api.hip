@@ -1,0 +1,291 @@
+// C ABI of the MoE layer: argument validation, workspace layout and the launch
+// sequence.  Everything is enqueued on the caller's stream; nothing here waits for
+// the device or allocates device memory.
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+using moe::ceil_div;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int T, H, E, k, I;
+  long rows;
+  int ksplit, kslice, nchunks, bm, max_tiles;
+  size_t partial, hist, chunk_base, tiles, num_tiles;
+  size_t ids, gates, counts, offsets, perm, inv;
+  size_t xq, sx, h, sh, y;
+  size_t total;
+};
+
+bool shape_ok(int T, int H, int E, int k, int I) {
+  if (T < 1 || E < 1 || E > 256 || k < 1 || k > 8 || k > E) return false;
+  if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return false;
+  const long rows = static_cast<long>(T) * k;
+  if (rows >= (1L << 31) || static_cast<long>(T) * H >= (1L << 31)) return false;
+  if (rows * H >= (1L << 40) || rows * I >= (1L << 40)) return false;
+  return true;
+}
+
+void make_plan(int T, int H, int E, int k, int I, Plan* p) {
+  p->T = T; p->H = H; p->E = E; p->k = k; p->I = I;
+  p->rows = static_cast<long>(T) * k;
+  // split H across workgroups when there are few token x expert tiles (decode)
+  const int tiles2d = ceil_div(T, moe::kRouterTile) * ceil_div(E, moe::kRouterTile);
+  int ks = ceil_div(1024, tiles2d);
+  ks = std::max(1, std::min(ks, H / 128 > 0 ? H / 128 : 1));
+  p->kslice = ceil_div(ceil_div(H, ks), 32) * 32;
+  p->ksplit = ceil_div(H, p->kslice);
+  p->nchunks = ceil_div(T, moe::kChunk);
+  p->bm = moe::gemm_tile_rows(p->rows, E);
+  p->max_tiles = static_cast<int>(p->rows / p->bm + std::min<long>(E, p->rows));
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  p->partial = take(sizeof(float) * p->ksplit * static_cast<size_t>(T) * E);
+  p->hist = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
+  p->chunk_base = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
+  p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->max_tiles));
+  p->num_tiles = take(sizeof(int32_t));
+  p->ids = take(sizeof(int32_t) * p->rows);
+  p->gates = take(sizeof(float) * p->rows);
+  p->counts = take(sizeof(int32_t) * E);
+  p->offsets = take(sizeof(int32_t) * (E + 1));
+  p->perm = take(sizeof(int32_t) * p->rows);
+  p->inv = take(sizeof(int32_t) * p->rows);
+  p->xq = take(static_cast<size_t>(T) * H);
+  p->sx = take(sizeof(float) * static_cast<size_t>(T) * ceil_div(H, moe::kBlock));
+  p->h = take(static_cast<size_t>(p->rows) * I);
+  p->sh = take(sizeof(float) * static_cast<size_t>(p->rows) * ceil_div(I, moe::kBlock));
+  p->y = take(sizeof(float) * static_cast<size_t>(p->rows) * H);
+  p->total = off;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
+}
+
+moe_status finish() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// routing tables of one call: the caller's or the workspace's
+struct Tables {
+  int32_t* ids;
+  float* gates;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+};
+
+// Records profiling event i on the stream (no-op without events).
+void mark(hipEvent_t* ev, int i, hipStream_t st) {
+  if (ev) (void)hipEventRecord(ev[i], st);
+}
+
+void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const float* rb,
+                     const Tables& tb, void* ws, hipStream_t st, hipEvent_t* ev = nullptr) {
+  mark(ev, 0, st);
+  moe::launch_router_logits(x, rw, p.T, p.H, p.E, p.ksplit, p.kslice, at<float>(ws, p.partial), st);
+  mark(ev, 1, st);
+  moe::launch_topk(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, tb.ids, tb.gates,
+                   at<int32_t>(ws, p.hist), st);
+  mark(ev, 2, st);
+  moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, tb.counts, tb.offsets,
+                            at<int32_t>(ws, p.chunk_base), at<moe::MTile>(ws, p.tiles),
+                            at<int32_t>(ws, p.num_tiles), st);
+  mark(ev, 3, st);
+  moe::launch_dispatch_scatter(tb.ids, at<int32_t>(ws, p.chunk_base), p.T, p.E, p.k, tb.perm,
+                               tb.inv, st);
+}
+
+bool routing_ok(const moe_routing* r) {
+  return r && r->topk_ids && r->topk_gates && r->expert_counts && r->expert_offsets && r->perm &&
+         r->inv_perm && aligned16(r->topk_ids) && aligned16(r->topk_gates) &&
+         aligned16(r->perm) && aligned16(r->inv_perm);
+}
+
+}  // namespace
+
+static moe_status forward_impl(const uint16_t* x, const float* router_w, const float* router_b,
+                       const uint8_t* w13, const float* w13_scales, const uint16_t* b13,
+                       const uint8_t* w2, const float* w2_scales, const uint16_t* b2, int T,
+                       int H, int E, int top_k, int I, uint16_t* out,
+                       const moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                       void* stream, hipEvent_t* ev) {
+  if (!x || !router_w || !w13 || !w13_scales || !w2 || !w2_scales || !out || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(w13) || !aligned16(w2) ||
+      !aligned16(out) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if (routing_out && !routing_ok(routing_out)) return MOE_ERR_INVALID_ARG;
+  if (!shape_ok(T, H, E, top_k, I)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  Plan p;
+  make_plan(T, H, E, top_k, I, &p);
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  (void)hipGetLastError();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  const Tables tb = routing_out
+                        ? Tables{routing_out->topk_ids, routing_out->topk_gates,
+                                 routing_out->expert_counts, routing_out->expert_offsets,
+                                 routing_out->perm, routing_out->inv_perm}
+                        : Tables{at<int32_t>(ws, p.ids), at<float>(ws, p.gates),
+                                 at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
+                                 at<int32_t>(ws, p.perm), at<int32_t>(ws, p.inv)};
+  enqueue_routing(p, x, router_w, router_b, tb, ws, st, ev);
+  mark(ev, 4, st);
+  moe::launch_quantize_act(x, T, H, at<uint8_t>(ws, p.xq), at<float>(ws, p.sx), st);
+  mark(ev, 5, st);
+
+  moe::GemmArgs g1{};
+  g1.A = at<uint8_t>(ws, p.xq);
+  g1.A_scale = at<float>(ws, p.sx);
+  g1.perm = tb.perm;
+  g1.top_k = top_k;
+  g1.B = w13;
+  g1.B_scale = w13_scales;
+  g1.bias = b13;
+  g1.tiles = at<moe::MTile>(ws, p.tiles);
+  g1.num_tiles = at<int32_t>(ws, p.num_tiles);
+  g1.K = H;
+  g1.N = 2 * I;
+  g1.I = I;
+  g1.h_out = at<uint8_t>(ws, p.h);
+  g1.h_scale = at<float>(ws, p.sh);
+  moe::launch_gemm1(g1, p.bm, p.max_tiles, st);
+  mark(ev, 6, st);
+
+  moe::GemmArgs g2{};
+  g2.A = at<uint8_t>(ws, p.h);
+  g2.A_scale = at<float>(ws, p.sh);
+  g2.perm = nullptr;
+  g2.top_k = top_k;
+  g2.B = w2;
+  g2.B_scale = w2_scales;
+  g2.bias = b2;
+  g2.tiles = g1.tiles;
+  g2.num_tiles = g1.num_tiles;
+  g2.K = I;
+  g2.N = H;
+  g2.I = I;
+  g2.y_out = at<float>(ws, p.y);
+  moe::launch_gemm2(g2, p.bm, p.max_tiles, st);
+  mark(ev, 7, st);
+  moe::launch_combine(at<float>(ws, p.y), tb.gates, tb.inv, T, H, top_k, out, st);
+  mark(ev, 8, st);
+  return finish();
+}
+
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_bytes(int T, int H, int E, int top_k, int I) {
+  if (!shape_ok(T, H, E, top_k, I)) return 0;
+  Plan p;
+  make_plan(T, H, E, top_k, I, &p);
+  return p.total;
+}
+
+moe_status moe_workspace_layout(int T, int H, int E, int top_k, int I, moe_workspace_regions* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  if (!shape_ok(T, H, E, top_k, I)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  Plan p;
+  make_plan(T, H, E, top_k, I, &p);
+  out->xq = p.xq; out->sx = p.sx; out->h = p.h; out->sh = p.sh; out->y = p.y;
+  out->topk_ids = p.ids; out->topk_gates = p.gates; out->expert_counts = p.counts;
+  out->expert_offsets = p.offsets; out->perm = p.perm; out->inv_perm = p.inv;
+  out->total = p.total;
+  return MOE_OK;
+}
+
+moe_status moe_quantize_weights(const float* w, int E, int N, int K, uint8_t* codes,
+                                float* scales, void* stream) {
+  if (!w || !codes || !scales || !aligned16(w) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARG;
+  if (K % 16 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (static_cast<long>(E) * ceil_div(N, 128) * ceil_div(K, 128) >= (1L << 31))
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  (void)hipGetLastError();
+  moe::launch_quantize_weights(w, E, N, K, codes, scales, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+moe_status moe_quantize_activations(const uint16_t* x, int T, int H, uint8_t* codes,
+                                    float* scales, void* stream) {
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+  if (H % 64 != 0 || static_cast<long>(T) * H >= (1L << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  (void)hipGetLastError();
+  moe::launch_quantize_act(x, T, H, codes, scales, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+moe_status moe_route(const uint16_t* x, const float* router_w, const float* router_b, int T,
+                     int H, int E, int top_k, const moe_routing* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!x || !router_w || !workspace || !routing_ok(out) || !aligned16(x) ||
+      !aligned16(router_w) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if (!shape_ok(T, H, E, top_k, 64)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  Plan p;
+  make_plan(T, H, E, top_k, 64, &p);
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  (void)hipGetLastError();
+  const Tables tb{out->topk_ids, out->topk_gates, out->expert_counts, out->expert_offsets,
+                  out->perm, out->inv_perm};
+  enqueue_routing(p, x, router_w, router_b, tb, workspace, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+moe_status moe_forward(const uint16_t* x, const float* router_w, const float* router_b,
+                       const uint8_t* w13, const float* w13_scales, const uint16_t* b13,
+                       const uint8_t* w2, const float* w2_scales, const uint16_t* b2, int T,
+                       int H, int E, int top_k, int I, uint16_t* out,
+                       const moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
+                      top_k, I, out, routing_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_profiled(const uint16_t* x, const float* router_w, const float* router_b,
+                                const uint8_t* w13, const float* w13_scales, const uint16_t* b13,
+                                const uint8_t* w2, const float* w2_scales, const uint16_t* b2,
+                                int T, int H, int E, int top_k, int I, uint16_t* out,
+                                const moe_routing* routing_out, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < MOE_PROFILE_EVENTS; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
+                      top_k, I, out, routing_out, workspace, workspace_bytes, stream,
+                      reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
+}
+
+}  // extern "C"

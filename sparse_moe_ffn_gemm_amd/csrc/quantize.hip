@@ -1,0 +1,105 @@
+// FP8 e4m3 quantisers: 128x128 weight blocks and 1x128 activation groups.
+//
+// "GPT-OSS on day 0", section "On Hopper": FP8 with 128x128 block scaling is the
+// weight scheme; "Hosting Qwen on Blackwell", section "Quantization": the weights
+// are converted once, statically.  The activation side uses per-token 1x128 groups
+// (a design choice of this implementation) with the same rounding rule.
+#include "kernels.hpp"
+
+namespace moe {
+
+// One workgroup (256 lanes) per 128x128 block.  Lane (r, c4) owns column quad c4 of
+// rows r, r+8, ..., r+120: 16 float4 loads, kept in registers between the amax pass
+// and the encode pass, so the source is read exactly once.
+__global__ __launch_bounds__(256) void quantize_weights_kernel(const float* __restrict__ w, int N,
+                                                               int K, uint8_t* __restrict__ codes,
+                                                               float* __restrict__ scales) {
+  const int KB = ceil_div(K, kBlock), NB = ceil_div(N, kBlock);
+  const long blk = blockIdx.x;
+  const int kb = static_cast<int>(blk % KB);
+  const int nb = static_cast<int>((blk / KB) % NB);
+  const long e = blk / (static_cast<long>(KB) * NB);
+  const int c4 = threadIdx.x & 31, r = threadIdx.x >> 5;
+  const int col = kb * kBlock + c4 * 4;
+  const size_t mat = static_cast<size_t>(N) * K;
+  const float* src = w + e * mat;
+  float4 v[16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = nb * kBlock + r + 8 * i;
+    if (row < N && col < K) {
+      v[i] = *reinterpret_cast<const float4*>(src + static_cast<size_t>(row) * K + col);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    } else {
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __shared__ float red[4];
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = group_scale(amax);
+  uint8_t* dst = codes + e * mat;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = nb * kBlock + r + 8 * i;
+    if (row < N && col < K)
+      *reinterpret_cast<uint32_t*>(dst + static_cast<size_t>(row) * K + col) =
+          encode4(v[i].x, v[i].y, v[i].z, v[i].w, s);
+  }
+  if (threadIdx.x == 0) scales[blk] = s;
+}
+
+// 16 lanes per 1x128 group, 8 bf16 per lane; a workgroup covers 16 groups.
+__global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __restrict__ x, int T,
+                                                           int H, uint8_t* __restrict__ codes,
+                                                           float* __restrict__ scales) {
+  const int KB = ceil_div(H, kBlock);
+  const long g = static_cast<long>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool live = g < static_cast<long>(T) * KB;
+  const long t = live ? g / KB : 0;
+  const int kb = live ? static_cast<int>(g % KB) : 0;
+  const int col = kb * kBlock + sub * 8;
+  const bool in = live && col < H;
+  float f[8];
+  float amax = 0.0f;
+  if (in) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(x + t * H + col);
+    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_to_f32(static_cast<uint16_t>(wds[i] & 0xFFFFu));
+      f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(wds[i] >> 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+  amax = group_max<16>(amax);
+  const float s = group_scale(amax);
+  if (in) {
+    uint2 q;
+    q.x = encode4(f[0], f[1], f[2], f[3], s);
+    q.y = encode4(f[4], f[5], f[6], f[7], s);
+    *reinterpret_cast<uint2*>(codes + t * H + col) = q;
+  }
+  if (live && sub == 0) scales[g] = s;
+}
+
+void launch_quantize_weights(const float* w, int E, int N, int K, uint8_t* codes, float* scales,
+                             hipStream_t st) {
+  const long blocks = static_cast<long>(E) * ceil_div(N, kBlock) * ceil_div(K, kBlock);
+  quantize_weights_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st>>>(w, N, K, codes,
+                                                                                    scales);
+}
+
+void launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* codes, float* scales,
+                         hipStream_t st) {
+  const long groups = static_cast<long>(T) * ceil_div(H, kBlock);
+  quantize_act_kernel<<<dim3(static_cast<unsigned>((groups + 15) / 16)), dim3(256), 0, st>>>(
+      x, T, H, codes, scales);
+}
+
+}  // namespace moe

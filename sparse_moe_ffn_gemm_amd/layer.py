@@ -1,0 +1,62 @@
+"""A sparse MoE FFN layer object on one GPU: weights quantised once, workspace kept.
+
+Weights are converted statically to e4m3 codes with 128x128 block scales ("Hosting
+Qwen on Blackwell", section "Quantization") by the library's quantisation kernel;
+``forward`` runs the whole layer through ``moe_forward``.
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional
+
+import torch
+
+from . import _lib
+
+
+class MoELayer:
+    def __init__(self, router_w: torch.Tensor, router_b: Optional[torch.Tensor], top_k: int,
+                 w13: torch.Tensor, w13_scales: torch.Tensor, b13: Optional[torch.Tensor],
+                 w2: torch.Tensor, w2_scales: torch.Tensor, b2: Optional[torch.Tensor]):
+        self.router_w, self.router_b, self.top_k = router_w, router_b, top_k
+        self.w13, self.w13_scales, self.b13 = w13, w13_scales, b13
+        self.w2, self.w2_scales, self.b2 = w2, w2_scales, b2
+        self.E, self.H = router_w.shape
+        self.I = w2.shape[2]
+        self._ws = {}
+
+    @classmethod
+    def from_expert_weights(cls, router_w, router_b, top_k: int, b13, b2,
+                            w13_of: Callable[[int], torch.Tensor],
+                            w2_of: Callable[[int], torch.Tensor], device="cuda") -> "MoELayer":
+        """Quantise expert by expert: ``w13_of(e)`` -> [2I, H] fp32, ``w2_of(e)`` -> [H, I] fp32
+        (on any device; moved to ``device`` one expert at a time)."""
+        E, H = router_w.shape
+        first = w2_of(0)
+        I = first.shape[1]
+        kb = _lib.kb
+        w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
+        s13 = torch.empty((E, kb(2 * I), kb(H)), dtype=torch.float32, device=device)
+        w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
+        s2 = torch.empty((E, kb(H), kb(I)), dtype=torch.float32, device=device)
+        for e in range(E):
+            a = w13_of(e).to(device=device, dtype=torch.float32).contiguous()
+            _lib.quantize_weights(a, w13[e:e + 1], s13[e:e + 1])
+            b = (first if e == 0 else w2_of(e)).to(device=device, dtype=torch.float32).contiguous()
+            _lib.quantize_weights(b, w2[e:e + 1], s2[e:e + 1])
+        return cls(router_w.to(device), None if router_b is None else router_b.to(device), top_k,
+                   w13, s13, None if b13 is None else b13.to(device), w2, s2,
+                   None if b2 is None else b2.to(device))
+
+    def workspace(self, T: int) -> torch.Tensor:
+        ws = self._ws.get(T)
+        if ws is None:
+            ws = _lib.new_workspace(T, self.H, self.E, self.top_k, self.I, self.w13.device)
+            self._ws[T] = ws
+        return ws
+
+    def forward(self, x: torch.Tensor, out: torch.Tensor = None, routing: dict = None) -> torch.Tensor:
+        return _lib.forward(x, self.router_w, self.router_b, self.w13, self.w13_scales, self.b13,
+                            self.w2, self.w2_scales, self.b2, self.top_k, out=out, routing=routing,
+                            workspace=self.workspace(x.shape[0]))
+
+    __call__ = forward

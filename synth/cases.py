@@ -54,7 +54,7 @@ class LayerShape:
     I: int
     seed: int
     expert_bias: bool = True
-    router: str = "random"          # "random" | "zipf"
+    router: str = "random"          # "random" | "zipf" | "hot" (expert 0 always chosen)
     weights_on_device: bool = False  # draw expert weights with torch on the GPU
     token_slice_of: Optional[str] = None  # decode layer reusing a prefill layer's draw
 
@@ -173,6 +173,8 @@ def make_inputs(shape: LayerShape) -> LayerInputs:
         b = _zipf_bias(shape)
     else:
         b = _normal(_rng(s, _TAG_RB), (E,), 0.01)
+    if shape.router == "hot":          # edge case: expert 0 is every token's first choice
+        b[0] += np.float32(1000.0)
     if shape.expert_bias:
         b13 = f32_to_bf16_bits(_normal(_rng(s, _TAG_B13), (E, 2 * I), 0.01))
         b2 = f32_to_bf16_bits(_normal(_rng(s, _TAG_B2), (E, H), 0.01))

@@ -1,0 +1,64 @@
+"""GPU parity of routing: expert ids, counts, offsets, permutation and its inverse are
+bit-exact against the oracle; gates within 1e-6.  Inputs satisfy the 1e-3 top-k logit
+margin, so the routing decision has exactly one correct answer."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_moe_ffn_gemm_amd as moe
+from oracle import moe_ref as R
+from synth import SHAPES, custom_shape, make_inputs
+from gpu_helpers import bf16_dev, routing_exact, say
+
+pytestmark = pytest.mark.gpu
+
+EDGE = [
+    custom_shape(T=1, H=256, E=8, top_k=2, I=128, seed=21),
+    custom_shape(T=5, H=64, E=1, top_k=1, I=64, seed=22),
+    custom_shape(T=100, H=512, E=8, top_k=8, I=64, seed=23),       # k = E
+    custom_shape(T=130, H=384, E=64, top_k=2, I=64, seed=24),       # ragged chunks
+    custom_shape(T=300, H=256, E=256, top_k=8, I=64, seed=25),      # E = 256, idle experts
+    custom_shape(T=200, H=256, E=16, top_k=3, I=64, seed=26, router="hot"),
+]
+
+
+def _run(shape, li):
+    x = bf16_dev(li.x)
+    W = torch.from_numpy(li.router_w).cuda()
+    b = torch.from_numpy(li.router_b).cuda()
+    say(f"route {shape.name}: T={shape.T} H={shape.H} E={shape.E} k={shape.top_k}")
+    r = moe.route(x, W, b, shape.top_k)
+    torch.cuda.synchronize()
+    lg = R.router_logits(li.x, li.router_w, li.router_b)
+    ids, gates = R.topk_softmax(lg, shape.top_k)
+    counts, offsets, perm, inv = R.permute(ids, shape.E)
+    ref = dict(logits=lg, ids=ids, gates=gates, counts=counts, offsets=offsets, perm=perm, inv=inv)
+    routing_exact(r, ref, shape.T, shape.top_k, shape.name)
+    return r
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_route_configs(name):
+    shape = SHAPES[name]
+    _run(shape, make_inputs(shape))
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=[s.name for s in EDGE])
+def test_route_edge_cases(shape):
+    r = _run(shape, make_inputs(shape))
+    if shape.router == "hot":
+        assert np.all(r["topk_ids"].cpu().numpy()[:, 0] == 0)
+        assert r["expert_counts"].cpu().numpy()[0] == shape.T
+
+
+def test_route_deterministic():
+    shape = SHAPES["deepseek-v3-skewed"]
+    li = make_inputs(shape)
+    x = bf16_dev(li.x)
+    W = torch.from_numpy(li.router_w).cuda()
+    b = torch.from_numpy(li.router_b).cuda()
+    a = moe.route(x, W, b, shape.top_k)
+    c = moe.route(x, W, b, shape.top_k)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], c[k]), k
