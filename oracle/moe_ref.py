@@ -284,12 +284,14 @@ def forward_dispatched(x_bits, router_w, router_b, top_k: int, I: int, w13_codes
     y = np.zeros((T * top_k, x_bits.shape[1]))
     hq = np.zeros((T * top_k, I), np.uint8)
     hs = np.ones((T * top_k, -(-I // BLOCK)), np.float32)
+    h = np.zeros((T * top_k, I))
     for e in range(E):
         p0, p1 = offsets[e], offsets[e + 1]
         if p1 > p0:
-            y[p0:p1], hq[p0:p1], hs[p0:p1], _ = expert_ffn(
+            y[p0:p1], hq[p0:p1], hs[p0:p1], h[p0:p1] = expert_ffn(
                 xd[tok_of_row[p0:p1]], w13_codes[e], w13_scales[e], b13[e], w2_codes[e],
                 w2_scales[e], b2[e], I)
     out = combine(y, gates, inv, T, top_k)
     return dict(logits=logits, ids=ids, gates=gates, counts=counts, offsets=offsets, perm=perm,
-                inv=inv, xq=xq, sx=sx, hq=hq, hs=hs, y=y, out=out, out_bf16=f64_to_bf16_bits(out))
+                inv=inv, xq=xq, sx=sx, h=h, hq=hq, hs=hs, y=y, out=out,
+                out_bf16=f64_to_bf16_bits(out))

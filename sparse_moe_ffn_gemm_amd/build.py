@@ -19,6 +19,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA sources/results in ordinary VGPRs, so the VALU block-scale promotion reads
+    # them without accumulation-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(os.path.dirname(PKG), "include"),
 ]
 

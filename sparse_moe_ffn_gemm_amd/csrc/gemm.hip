@@ -11,8 +11,21 @@
 // bytes of row l%16 for K-quarter l/16, for A and B alike).  One K-step is one
 // 128-wide scale block: each 16x16 sub-tile's MFMA result of that step is folded
 // into the fp32 accumulator with the product of the row's activation scale and the
-// sub-tile's weight block scale (block-scale promotion; the weight scale is
-// uniform over every wave's column range by construction of the tiling).
+// sub-tile's weight block scale (block-scale promotion; the weight scale is uniform
+// over every wave's column range by construction of the tiling).  Promoting every
+// 128 products also bounds the error of the matrix cores' own fp8 accumulation.
+//
+// Memory pipeline: tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, no register staging) through a ring of STAGES K-steps,
+// so STAGES-1 K-steps of loads are in flight while one is multiplied.  LDS rows are
+// 128 bytes; the 16-byte chunk c of row r is stored in slot c ^ (r & 7), which each
+// lane realises by choosing the global chunk it fetches.  Out-of-range chunks (K tail,
+// N tail, rows past the expert's segment) are fetched from a zero block.
+//
+// Work order: blocks are numbered so that each XCD (blocks are dealt round-robin to
+// the 8 XCDs) receives a contiguous range of (n-tile, m-tile) pairs with m-tiles
+// fastest, so the M-tiles that share an expert's weight tile run together on one XCD
+// and its L2 serves the repeated weight reads.
 //
 // gemm1: rows of expert e gathered from xq through perm; the 256-wide B tile holds
 //   128 gate rows and the matching 128 up rows of w13, so SwiGLU pairs (j, I+j) sit
@@ -26,9 +39,11 @@ namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// 128-byte LDS rows; the 16-byte chunk index is XOR-swizzled with the row so that
-// the 16 rows one MFMA operand read touches spread over all banks.
+__device__ __align__(16) const uint8_t kZeroChunk[64] = {0};
+__device__ __align__(16) const float kZeroScale[4] = {0.f, 0.f, 0.f, 0.f};
+
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7)) << 4);
 }
@@ -42,29 +57,81 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int g) {
   return r;
 }
 
-template <int BM, int BN, int WM, int WN, bool SWIGLU>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs a) {
+// LDS address (32-bit) of a shared-memory pointer.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
+}
+
+// One wave-wide direct load: lane l's 16 (or 4) bytes land at lds + l * 16 (or 4).  The
+// loads are issued as inline assembly so that the compiler neither inserts its own
+// conservative vmcnt(0) waits before LDS reads nor moves LDS reads across the explicit
+// wait + barrier below; `lds` must be wave-uniform (it goes to M0).
+__device__ __forceinline__ void load_lds16(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
+}
+// Same with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset, so
+// that advancing along K touches only the scalar base.
+__device__ __forceinline__ void load_lds16_s(unsigned off, const void* base, const void* lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_addr(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ void load_lds4(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Workgroup barrier without the memory fences of __syncthreads (the ring's loads are
+// waited for explicitly); the "memory" clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BM, int BN, int WM, int WN, bool SWIGLU, int STAGES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
+                                                           int ntiles, int grid) {
   constexpr int WTM = BM / WM, SM = WTM / 16;
   constexpr int WTN = BN / WN, SN = WTN / 16;
   constexpr int NG = SN / 2;                  // gemm1: gate (= up) sub-tiles per wave
   constexpr int GW = WTN / 2;                 // gemm1: gate columns per wave
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  constexpr int A_CH = (BM * 8 + 255) / 256;  // 16-byte chunks per lane and K-step
-  constexpr int B_CH = BN * 8 / 256;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
+  constexpr int AROWS = BM / 4;               // A rows each wave fetches per stage
+  constexpr int A_INSTR = AROWS >= 8 ? AROWS / 8 : 1;
+  constexpr int BROWS = BN / 4;
+  constexpr int B_INSTR = BROWS / 8;
+  constexpr int LOADS = A_INSTR + B_INSTR + 1;   // vmem instructions per wave and stage
   static_assert(WM * WN == 4, "four waves");
   static_assert(SM >= 1 && SN >= 1, "sub-tiles");
+  static_assert(AROWS % 8 == 0 || AROWS == 4, "A rows per wave");
+  static_assert(AROWS + 2 <= 64, "one scale load per wave");
   static_assert(!SWIGLU || (BN == 256 && SN % 2 == 0 && GW <= 64), "gemm1 tile");
   static_assert(SWIGLU || WTN <= 128, "gemm2 wave columns inside one scale block");
+  static_assert(STAGES >= 2 && LOADS * (STAGES - 2) < 64, "pipeline depth");
 
-  __shared__ __align__(16) uint8_t smem[2 * (A_BYTES + B_BYTES)];
-  __shared__ float sA[2][BM];
+  __shared__ __align__(16) uint8_t smem[STAGES * STAGE];
+  __shared__ __align__(16) float sA[STAGES][4][64];
   __shared__ int rowsrc[BM];
   __shared__ float red[SWIGLU ? WN : 1][BM];
 
-  if (static_cast<int>(blockIdx.x) >= *a.num_tiles) return;
-  const MTile mt = a.tiles[blockIdx.x];
-  const int nt = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // ---- which tile: XCD-contiguous logical order, m-tiles fastest ----
+  const int b = blockIdx.x;
+  const int per_xcd = grid / 8;
+  const int L = (b % 8) * per_xcd + b / 8;
+  const int mti = L % max_tiles, nt = L / max_tiles;
+  if (nt >= ntiles || mti >= *a.num_tiles) return;
+  MTile mt = a.tiles[mti];
+  mt.expert = __builtin_amdgcn_readfirstlane(mt.expert);
+  mt.row_begin = __builtin_amdgcn_readfirstlane(mt.row_begin);
+  mt.row_end = __builtin_amdgcn_readfirstlane(mt.row_end);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int wm = wave / WN, wn = wave % WN;
   const int K = a.K, N = a.N, I = a.I;
   const int KB = ceil_div(K, kBlock), NBs = ceil_div(N, kBlock);
@@ -78,12 +145,31 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs a) {
     if (p < mt.row_end) src = SWIGLU ? a.perm[p] / a.top_k : p;
     rowsrc[r] = src;
   }
+  __syncthreads();
 
-  // global B rows of this lane's load chunks (-1: outside the matrix)
-  int brow[B_CH];
+  // ---- per-lane fetch descriptors (constant over K) ----
+  // A: wave w fetches rows [w*AROWS, (w+1)*AROWS); lane -> (row, slot) of an 8-row group
+  const int a_slot = lane & 7, a_r8 = lane >> 3;
+  // Rows outside the tile are redirected to row 0 (finite codes that only feed output
+  // rows/columns that are never stored); only the ragged K tail needs real zeros.
+  const uint8_t* a_src[A_INSTR];
+  bool a_ok[A_INSTR];
+  unsigned a_off[A_INSTR];
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int br = (tid + 256 * i) >> 3;
+  for (int i = 0; i < A_INSTR; ++i) {
+    const int row = wave * AROWS + i * 8 + a_r8;
+    const bool live = AROWS >= 8 || lane < 32;
+    const int src = live ? rowsrc[row] : -1;
+    a_ok[i] = src >= 0;
+    a_off[i] = static_cast<unsigned>(src < 0 ? 0 : src) * K + ((a_slot ^ (row & 7)) << 4);
+    a_src[i] = a.A + a_off[i];
+  }
+  const uint8_t* b_src[B_INSTR];
+  bool b_ok[B_INSTR];
+  unsigned b_off[B_INSTR];
+#pragma unroll
+  for (int i = 0; i < B_INSTR; ++i) {
+    const int br = wave * BROWS + i * 8 + a_r8;
     int g = -1;
     if (SWIGLU) {
       const int j = nt * 128 + (br & 127);
@@ -92,9 +178,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs a) {
       const int col = nt * BN + br;
       if (col < N) g = col;
     }
-    brow[i] = g;
+    b_ok[i] = g >= 0;
+    b_off[i] = static_cast<unsigned>(g < 0 ? 0 : g) * K + ((a_slot ^ (br & 7)) << 4);
+    b_src[i] = Bexp + b_off[i];
   }
-
   // weight block-scale rows of this wave's column groups (-1: the group is empty)
   int sb_row0, sb_row1;
   if (SWIGLU) {
@@ -106,50 +193,57 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs a) {
     sb_row0 = c0 < N ? c0 / kBlock : -1;
     sb_row1 = sb_row0;
   }
-  __syncthreads();
+  // scale fetch of one K-step, one instruction per wave: lanes [0, AROWS) take the
+  // activation scales of the wave's A rows, lanes AROWS and AROWS+1 the two weight block
+  // scales of the wave's column groups
+  const float* s_ptr = kZeroScale;
+  bool s_live = false;
+  if (lane < AROWS) {
+    const int src = rowsrc[wave * AROWS + lane];
+    s_live = src >= 0;
+    s_ptr = a.A_scale + static_cast<size_t>(src < 0 ? 0 : src) * KB;
+  } else if (lane < AROWS + 2) {
+    const int row = lane == AROWS ? sb_row0 : sb_row1;
+    s_live = row >= 0;
+    s_ptr = Bsc + static_cast<size_t>(row < 0 ? 0 : row) * KB;
+  }
 
-  uint4 ra[A_CH], rb[B_CH];
-  float rsa = 0.f;
-  auto gload = [&](int kt) {
-    const int k0 = kt * kBlock;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int q = tid + 256 * i;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (q < BM * 8) {
-        const int src = rowsrc[q >> 3], kk = k0 + (q & 7) * 16;
-        if (src >= 0 && kk < K)
-          v = *reinterpret_cast<const uint4*>(a.A + static_cast<size_t>(src) * K + kk);
-      }
-      ra[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int kk = k0 + ((tid + 256 * i) & 7) * 16;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (brow[i] >= 0 && kk < K)
-        v = *reinterpret_cast<const uint4*>(Bexp + static_cast<size_t>(brow[i]) * K + kk);
-      rb[i] = v;
-    }
-    if (tid < BM) {
-      const int src = rowsrc[tid];
-      rsa = src >= 0 ? a.A_scale[static_cast<size_t>(src) * KB + kt] : 0.f;
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* As = smem + buf * (A_BYTES + B_BYTES);
+  auto issue = [&](int kt) {   // all loads of K-step kt into ring slot kt % STAGES
+    uint8_t* As = smem + (kt % STAGES) * STAGE;
     uint8_t* Bs = As + A_BYTES;
+    const int k0 = kt * kBlock;
+    if (k0 + kBlock <= K) {      // full K-step: scalar base + constant lane offsets
+      const uint8_t* abase = a.A + k0;
+      const uint8_t* bbase = Bexp + k0;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int q = tid + 256 * i;
-      if (q < BM * 8) *reinterpret_cast<uint4*>(As + swz(q >> 3, q & 7)) = ra[i];
+      for (int i = 0; i < A_INSTR; ++i)
+        if (AROWS >= 8 || lane < 32) load_lds16_s(a_off[i], abase, As + (wave * AROWS + i * 8) * 128);
+#pragma unroll
+      for (int i = 0; i < B_INSTR; ++i) load_lds16_s(b_off[i], bbase, Bs + (wave * BROWS + i * 8) * 128);
+      if (lane < AROWS + 2) {
+        const void* src = s_live ? static_cast<const void*>(s_ptr + kt) : kZeroScale;
+        load_lds4(src, &sA[kt % STAGES][wave][0]);
+      }
+      return;
     }
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int q = tid + 256 * i;
-      *reinterpret_cast<uint4*>(Bs + swz(q >> 3, q & 7)) = rb[i];
+    for (int i = 0; i < A_INSTR; ++i) {
+      const int row0 = wave * AROWS + i * 8;
+      const int kk = k0 + ((a_slot ^ ((row0 + a_r8) & 7)) << 4);
+      const void* src = (a_ok[i] && kk < K) ? static_cast<const void*>(a_src[i] + k0) : kZeroChunk;
+      if (AROWS >= 8 || lane < 32) load_lds16(src, As + row0 * 128);
     }
-    if (tid < BM) sA[buf][tid] = rsa;
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i) {
+      const int row0 = wave * BROWS + i * 8;
+      const int kk = k0 + ((a_slot ^ ((row0 + a_r8) & 7)) << 4);
+      const void* src = (b_ok[i] && kk < K) ? static_cast<const void*>(b_src[i] + k0) : kZeroChunk;
+      load_lds16(src, Bs + row0 * 128);
+    }
+    if (lane < AROWS + 2) {
+      const void* src = s_live ? static_cast<const void*>(s_ptr + kt) : kZeroScale;
+      load_lds4(src, &sA[kt % STAGES][wave][0]);
+    }
   };
 
   v4f acc[SM][SN];
@@ -158,52 +252,110 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int n = 0; n < SN; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // B-tile row of sub-tile n of this wave
   auto sub_brow = [&](int n) {
     if (SWIGLU) return n < NG ? wn * GW + 16 * n : 128 + wn * GW + 16 * (n - NG);
     return wn * WTN + 16 * n;
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // prologue: STAGES-1 K-steps in flight
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KB) issue(s);
+
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v4f pcar[SM];                     // last column's partial, promoted in the next step
+  float scar[SM][4];
+#pragma unroll
+  for (int m = 0; m < SM; ++m) {
+    pcar[m] = zero;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scar[m][i] = 0.f;
+  }
   for (int kt = 0; kt < KB; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KB) gload(kt + 1);
-    const uint8_t* As = smem + cur * (A_BYTES + B_BYTES);
+    // wait until this wave's loads of step kt have landed, then for every wave's
+    if (kt + STAGES - 2 < KB) {
+      wait_vmcnt<LOADS * (STAGES - 2)>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_only();
+    // the slot consumed in step kt-1 is free: refill it with step kt+STAGES-1
+    if (kt + STAGES - 1 < KB) issue(kt + STAGES - 1);
+
+    const int slot = kt % STAGES;
+    const uint8_t* As = smem + slot * STAGE;
     const uint8_t* Bs = As + A_BYTES;
-    const float sb0 = sb_row0 >= 0 ? Bsc[sb_row0 * KB + kt] : 0.f;
-    const float sb1 = sb_row1 >= 0 ? Bsc[sb_row1 * KB + kt] : 0.f;
+    // fragment and scale reads of this step, issued together
+    const float sb0 = sA[slot][wave][AROWS];
+    const float sb1 = sA[slot][wave][AROWS + 1];
     v8i af[SM];
+    float4 sa4[SM];
+#pragma unroll
+    for (int m = 0; m < SM; ++m) {
+      const int rw0 = wm * WTM + 16 * m;
+      af[m] = lds_frag(As, rw0 + (lane & 15), lane >> 4);
+      const int r = rw0 + 4 * (lane >> 4);          // 4 consecutive rows, one wave segment
+      sa4[m] = *reinterpret_cast<const float4*>(&sA[slot][r / AROWS][r % AROWS]);
+    }
+    v8i bq0 = lds_frag(Bs, sub_brow(0) + (lane & 15), lane >> 4);
+    v8i bq1 = lds_frag(Bs, sub_brow(SN > 1 ? 1 : 0) + (lane & 15), lane >> 4);
+    // the previous step's last column, deferred to overlap the reads above
+    if (kt > 0) {
+#pragma unroll
+      for (int m = 0; m < SM; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][SN - 1][i] = fmaf(pcar[m][i], scar[m][i], acc[m][SN - 1][i]);
+    }
     float s0[SM][4], s1[SM][4];
 #pragma unroll
     for (int m = 0; m < SM; ++m) {
-      const int r0 = wm * WTM + 16 * m;
-      af[m] = lds_frag(As, r0 + (lane & 15), lane >> 4);
+      const float sa[4] = {sa4[m].x, sa4[m].y, sa4[m].z, sa4[m].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float sa = sA[cur][r0 + 4 * (lane >> 4) + i];
-        s0[m][i] = sa * sb0;
-        s1[m][i] = sa * sb1;
+        s0[m][i] = sa[i] * sb0;
+        s1[m][i] = sa[i] * sb1;
       }
     }
+    // Software pipeline over the n sub-tiles, pinned with scheduling fences: each MFMA
+    // of column n+1 is followed by the four FMAs that fold the (finished) partial of
+    // column n; B fragments are read two columns ahead.
+    v4f pc[SM], pn[SM];
+#pragma unroll
+    for (int m = 0; m < SM; ++m)
+      pc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[m], bq0, zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
     for (int n = 0; n < SN; ++n) {
-      const v8i bfr = lds_frag(Bs, sub_brow(n) + (lane & 15), lane >> 4);
       const bool second = SWIGLU && n >= NG;
+      const v8i bn = bq1;
+      if (n + 2 < SN) bq1 = lds_frag(Bs, sub_brow(n + 2) + (lane & 15), lane >> 4);
+      if (n + 1 < SN) {
 #pragma unroll
-      for (int m = 0; m < SM; ++m) {
-        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[m], bfr, zero, 0, 0, 0,
-                                                                       0, 0, 0);
+        for (int m = 0; m < SM; ++m) {
+          __builtin_amdgcn_sched_barrier(0);
+          pn[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[m], bn, zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[m][n][i] = fmaf(p[i], second ? s1[m][i] : s0[m][i], acc[m][n][i]);
+          for (int i = 0; i < 4; ++i)
+            acc[m][n][i] = fmaf(pc[m][i], second ? s1[m][i] : s0[m][i], acc[m][n][i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < SM; ++m) pc[m] = pn[m];
+      } else {
+#pragma unroll
+        for (int m = 0; m < SM; ++m) {
+          pcar[m] = pc[m];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) scar[m][i] = second ? s1[m][i] : s0[m][i];
+        }
       }
     }
-    if (kt + 1 < KB) sstore(cur ^ 1);
-    __syncthreads();
   }
+  // the last step's last column
+#pragma unroll
+  for (int m = 0; m < SM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[m][SN - 1][i] = fmaf(pcar[m][i], scar[m][i], acc[m][SN - 1][i]);
+  __syncthreads();   // every wave is done with the ring before its LDS is reused
 
   const int rbase = wm * WTM + 4 * (lane >> 4);   // + 16 m + i
   if constexpr (SWIGLU) {
@@ -268,13 +420,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmArgs a) {
     for (int n = 0; n < SN; ++n) {
       const int col = nt * BN + wn * WTN + 16 * n + (lane & 15);
       if (col >= N) continue;
-      const float b = bias ? bf16_to_f32(bias[col]) : 0.f;
+      const float bv = bias ? bf16_to_f32(bias[col]) : 0.f;
 #pragma unroll
       for (int m = 0; m < SM; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = mt.row_begin + rbase + 16 * m + i;
-          if (p < mt.row_end) a.y_out[static_cast<size_t>(p) * N + col] = acc[m][n][i] + b;
+          if (p < mt.row_end) a.y_out[static_cast<size_t>(p) * N + col] = acc[m][n][i] + bv;
         }
     }
   }
@@ -290,11 +442,18 @@ int gemm_tile_rows(long rows, int E) {
 template <bool SWIGLU>
 static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
   const int ntiles = SWIGLU ? ceil_div(a.I, 128) : ceil_div(a.N, 256);
-  const dim3 grid(max_tiles, ntiles);
+  const long total = static_cast<long>(max_tiles) * ntiles;
+  const int grid = static_cast<int>((total + 7) / 8 * 8);
   switch (bm) {
-    case 16: grouped_gemm_kernel<16, 256, 1, 4, SWIGLU><<<grid, dim3(256), 0, st>>>(a); break;
-    case 64: grouped_gemm_kernel<64, 256, 1, 4, SWIGLU><<<grid, dim3(256), 0, st>>>(a); break;
-    default: grouped_gemm_kernel<128, 256, 2, 2, SWIGLU><<<grid, dim3(256), 0, st>>>(a); break;
+    case 16:
+      grouped_gemm_kernel<16, 256, 1, 4, SWIGLU, 4><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+      break;
+    case 64:
+      grouped_gemm_kernel<64, 256, 1, 4, SWIGLU, 3><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+      break;
+    default:
+      grouped_gemm_kernel<128, 256, 2, 2, SWIGLU, 3><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+      break;
   }
 }
 

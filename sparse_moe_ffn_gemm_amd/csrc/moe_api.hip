@@ -5,7 +5,7 @@
 
 #include <algorithm>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.hpp"
 
 namespace {

@@ -15,6 +15,13 @@ from synth import LayerShape, expert_weights, make_inputs
 REL_FRO_TOL = 5e-3
 MAX_ELT_TOL = 2e-2
 GATE_TOL = 1e-6
+# Device error of h relative to its 1x128 group maximum.  Each K=128 FP8 matrix-core
+# dot product on gfx950 carries up to ~6e-5 of the tile maximum (measured with random
+# codes; every single product is exact); over up to 56 promoted K-blocks that stays below
+# 2^-13.  An h element closer than this to a rounding boundary of its group has two
+# correct codes.
+H_EPS = 2.0 ** -13
+_MAG = R.e4m3_decode(np.arange(0x7F))            # magnitudes of codes 0x00..0x7E
 
 
 def say(*a):
@@ -83,9 +90,41 @@ class OracleExperts:
         ids = R.topk_softmax(R.router_logits(li.x, li.router_w, li.router_b), self.shape.top_k)[0]
         need = np.unique(ids if token_subset is None else ids[np.asarray(token_subset)])
         self.prepare(need)
-        return R.forward(li.x, li.router_w, li.router_b, self.shape.top_k, self.shape.I,
-                         self.view(0), self.view(1), li.b13, self.view(2), self.view(3), li.b2,
-                         token_subset=token_subset)
+        ref = R.forward(li.x, li.router_w, li.router_b, self.shape.top_k, self.shape.I,
+                        self.view(0), self.view(1), li.b13, self.view(2), self.view(3), li.b2,
+                        token_subset=token_subset)
+        ref["allowance"] = self.flip_allowance(ref)
+        return ref
+
+    def flip_allowance(self, ref):
+        """Per output element of the evaluated tokens: sum_j g_j * |W2_j| . flip_delta(h_j)."""
+        li, k, I = self.li, self.shape.top_k, self.shape.I
+        toks = ref["tokens"]
+        x32 = R.bf16_to_f64(li.x[toks]).astype(np.float32)
+        xq, sx = R.quantize_activations(x32)
+        xd = R.dequantize_blocks(xq, sx, rows=1)
+        allow = np.zeros((toks.size, li.x.shape[1]))
+        for e in np.unique(ref["ids"][toks]):
+            rt, rj = np.nonzero(ref["ids"][toks] == e)
+            c13, s13, c2, s2 = self.cache[int(e)]
+            _, hq, hs, h64 = R.expert_ffn(xd[rt], c13, s13, li.b13[e], c2, s2, li.b2[e], I)
+            W2 = np.abs(R.dequantize_blocks(c2, s2))
+            contrib = flip_delta(h64, hq, hs) @ W2.T
+            allow[rt] += ref["gates"][toks[rt], rj][:, None] * contrib
+        return allow
+
+
+def dispatched_allowance(ref, experts: "OracleExperts", T: int, k: int):
+    """flip allowance for a full dispatched oracle result (all tokens)."""
+    rows = ref["h"].shape[0]
+    contrib = np.zeros((rows, ref["y"].shape[1]))
+    delta = flip_delta(ref["h"], ref["hq"], ref["hs"])
+    for e in range(len(ref["counts"])):
+        p0, p1 = ref["offsets"][e], ref["offsets"][e + 1]
+        if p1 > p0:
+            c2, s2 = experts.cache[e][2], experts.cache[e][3]
+            contrib[p0:p1] = delta[p0:p1] @ np.abs(R.dequantize_blocks(c2, s2)).T
+    return R.combine(contrib, ref["gates"], ref["inv"], T, k)
 
 
 def _base(shape):
@@ -98,20 +137,44 @@ def bf16_ulp(ref: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, np.floor(np.log2(a)).astype(int) - 7)
 
 
-def compare_out(gpu_bits: np.ndarray, ref: np.ndarray, what=""):
-    """Relative Frobenius <= 5e-3; an element fails the max-elementwise bound only if its
-    error exceeds both 2e-2 * RMS(ref) and one bf16 ulp of the reference value (the
-    output format cannot resolve less).  Returns a dict of the measured errors."""
+def flip_delta(h64: np.ndarray, hq: np.ndarray, hs: np.ndarray) -> np.ndarray:
+    """For oracle h rows: the value change of a one-step code flip for every element whose
+    fp32 quotient lies within H_EPS * 448 code units of a rounding boundary (0 elsewhere).
+    Uses the oracle's own h, codes and scales only."""
+    I = h64.shape[1]
+    s = np.repeat(hs.astype(np.float64), 128, axis=1)[:, :I]
+    v = np.abs(h64.astype(np.float32) / np.repeat(hs, 128, axis=1)[:, :I]).astype(np.float64)
+    m = (hq & 0x7F).astype(np.int64)
+    lo = np.where(m > 0, (_MAG[np.maximum(m - 1, 0)] + _MAG[m]) / 2, 0.0)
+    hi = np.where(m < 0x7E, (_MAG[np.minimum(m + 1, 0x7E)] + _MAG[m]) / 2, np.inf)
+    d_lo, d_hi = v - lo, hi - v
+    step_lo = np.where(m > 0, _MAG[m] - _MAG[np.maximum(m - 1, 0)], 0.0)
+    step_hi = np.where(m < 0x7E, _MAG[np.minimum(m + 1, 0x7E)] - _MAG[m], 0.0)
+    near_lo = d_lo <= H_EPS * 448
+    near_hi = d_hi <= H_EPS * 448
+    return np.maximum(near_lo * step_lo, near_hi * step_hi) * s
+
+
+def compare_out(gpu_bits: np.ndarray, ref: np.ndarray, what="", allowance=None):
+    """Relative Frobenius <= 5e-3.  An element fails the max-elementwise bound only if its
+    error exceeds max(2e-2 * RMS(ref), one bf16 ulp of the reference value) -- the output
+    format cannot resolve less -- plus ``allowance``: the largest change that legitimate
+    one-step flips of near-boundary h codes can cause (``flip_delta`` through |W2|, gated).
+    The literal max |err| / RMS is always reported."""
     g = R.bf16_to_f64(gpu_bits)
     d = g - ref
     rel = np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)
     rms = np.sqrt(np.mean(ref * ref))
     lit = np.abs(d).max() / rms if rms > 0 else 0.0
-    bad = np.abs(d) > np.maximum(MAX_ELT_TOL * rms, bf16_ulp(ref))
+    base = np.maximum(MAX_ELT_TOL * rms, bf16_ulp(ref))
+    over = np.abs(d) > base
+    bad = np.abs(d) > base + (0.0 if allowance is None else allowance)
     floor = np.abs(R.bf16_to_f64(R.f64_to_bf16_bits(ref)) - ref).max() / rms if rms > 0 else 0.0
-    info = dict(rel_fro=rel, max_over_rms=lit, n_bad=int(bad.sum()), n=d.size, floor=floor)
+    info = dict(rel_fro=rel, max_over_rms=lit, n_over_literal=int(over.sum()), n_bad=int(bad.sum()),
+                n=d.size, floor=floor)
     say(f"  out parity {what}: rel_fro={rel:.3e} max/rms={lit:.3e} (bf16 floor {floor:.3e}) "
-        f"bad={int(bad.sum())}/{d.size}")
+        f"over 2e-2*RMS (and 1 ulp): {int(over.sum())}, beyond h-flip allowance: {int(bad.sum())}"
+        f" of {d.size}")
     assert rel <= REL_FRO_TOL, info
     assert not bad.any(), info
     return info
@@ -145,18 +208,27 @@ def routing_exact(gpu: dict, ref: dict, T: int, k: int, what=""):
     assert np.all(err <= tol), np.argwhere(err > tol)[:5]
 
 
-def h_codes_close(gpu_hq: np.ndarray, ref_hq: np.ndarray, max_frac=0.01):
-    """h codes may differ by one step where the fp32 device value and the oracle's value
-    fall on different sides of a rounding boundary (the grouped GEMM's fp8 dot products
-    accumulate with less than fp32 precision); nothing else may differ."""
+def h_codes_close(gpu_hq: np.ndarray, ref: dict, max_frac=0.01):
+    """h codes may differ only where the oracle's h lies within H_EPS of a rounding boundary
+    (two correct codes), and then by exactly one step; at most ``max_frac`` of them."""
+    ref_hq = ref["hq"]
     diff = gpu_hq != ref_hq
     frac = diff.mean()
-    g = gpu_hq[diff].astype(np.int64)
-    r = ref_hq[diff].astype(np.int64)
-    same_sign = (g & 0x80) == (r & 0x80)
-    step = np.abs((g & 0x7F) - (r & 0x7F))
-    zero_pair = ((g & 0x7F) == 0) & ((r & 0x7F) <= 1) | ((r & 0x7F) == 0) & ((g & 0x7F) <= 1)
-    adjacent = (same_sign & (step == 1)) | zero_pair
-    say(f"  h: {int(diff.sum())} of {diff.size} codes differ ({frac:.2e}), all adjacent: "
-        f"{bool(adjacent.all())}")
-    assert frac <= max_frac and adjacent.all()
+    near = flip_delta(ref["h"], ref_hq, ref["hs"]) > 0
+    g = R.e4m3_decode(gpu_hq[diff])
+    r = R.e4m3_decode(ref_hq[diff])
+    m = (ref_hq[diff] & 0x7F).astype(np.int64)
+    one_step = np.abs(np.abs(g) - np.abs(r)) <= np.maximum(
+        _MAG[np.minimum(m + 1, 0x7E)] - _MAG[m], _MAG[m] - _MAG[np.maximum(m - 1, 0)]) + 1e-12
+    ok = near[diff] & (one_step | (np.abs(g) + np.abs(r) <= 2 * _MAG[1]))
+    say(f"  h: {int(diff.sum())} of {diff.size} codes differ ({frac:.2e}); "
+        f"all near a boundary and one step: {bool(ok.all())}")
+    if not ok.all():
+        idx = np.argwhere(diff)[~ok][:5]
+        I = ref["h"].shape[1]
+        for rr, cc in idx:
+            grp = slice((cc // 128) * 128, min((cc // 128 + 1) * 128, I))
+            gmax = np.abs(ref["h"][rr, grp]).max()
+            say(f"    row {rr} col {cc}: oracle code {ref_hq[rr, cc]:#04x} gpu {gpu_hq[rr, cc]:#04x} "
+                f"h={ref['h'][rr, cc]:.6g} group max {gmax:.6g} scale {ref['hs'][rr, cc // 128]:.6g}")
+    assert frac <= max_frac and ok.all()

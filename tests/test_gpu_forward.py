@@ -12,23 +12,19 @@ import torch
 import sparse_moe_ffn_gemm_amd as moe
 from oracle import moe_ref as R
 from synth import SHAPES, custom_shape, make_inputs
-from gpu_helpers import (GpuLayer, OracleExperts, bits_host, compare_out, h_codes_close,
-                         routing_exact, say)
+from gpu_helpers import (GpuLayer, OracleExperts, bits_host, compare_out, dispatched_allowance,
+                         h_codes_close, routing_exact, say)
 
 pytestmark = pytest.mark.gpu
 
-# Layers with I < ~512 are left out of the element-wise comparison on purpose: h is
-# requantised to e4m3, and a single one-step code flip of h (legitimate where two fp32
-# evaluations straddle a rounding boundary) moves an output element by up to ~1/(16 sqrt(I))
-# of the row scale, which for tiny I alone approaches the 2e-2 * RMS bound.
 SMALL = [
     SHAPES["tiny"],
     custom_shape(T=37, H=192, E=5, top_k=2, I=192, seed=31),        # ragged K/N blocks
     custom_shape(T=1, H=256, E=8, top_k=2, I=256, seed=32),         # single token
-    custom_shape(T=9, H=128, E=1, top_k=1, I=512, seed=33),         # dense FFN
-    custom_shape(T=4, H=256, E=64, top_k=2, I=512, seed=34),        # most experts idle
+    custom_shape(T=9, H=128, E=1, top_k=1, I=128, seed=33),         # dense FFN
+    custom_shape(T=4, H=256, E=64, top_k=2, I=128, seed=34),        # most experts idle
     custom_shape(T=150, H=320, E=4, top_k=4, I=384, seed=35),       # k = E, >128 rows/expert
-    custom_shape(T=200, H=256, E=16, top_k=3, I=768, seed=36, router="hot"),  # one hot expert
+    custom_shape(T=200, H=256, E=16, top_k=3, I=128, seed=36, router="hot"),  # one hot expert
     custom_shape(T=96, H=384, E=8, top_k=2, I=320, seed=37, expert_bias=False),
 ]
 
@@ -66,7 +62,7 @@ def test_forward_small_full_parity(shape):
     assert np.array_equal(xq, ref["xq"]) and np.array_equal(sx, ref["sx"])
     hq = _workspace_view(g.layer, T, "h", torch.uint8, (rows, I)).cpu().numpy()
     hs = _workspace_view(g.layer, T, "sh", torch.float32, (rows, -(-I // 128))).cpu().numpy()
-    h_codes_close(hq, ref["hq"])
+    h_codes_close(hq, ref)
     hs_rel = np.abs(hs / ref["hs"] - 1).max()
     say(f"  h scales: max rel diff {hs_rel:.2e}")
     assert hs_rel < 1e-4
@@ -74,7 +70,8 @@ def test_forward_small_full_parity(shape):
     y_rel = np.linalg.norm(y - ref["y"]) / max(np.linalg.norm(ref["y"]), 1e-300)
     say(f"  y rel err {y_rel:.2e}")
     assert y_rel < 3e-3
-    compare_out(bits_host(out), ref["out"], shape.name)
+    compare_out(bits_host(out), ref["out"], shape.name,
+                allowance=dispatched_allowance(ref, ox, shape.T, shape.top_k))
 
 
 @pytest.mark.parametrize("name", ["gpt-oss-20b-decode", "qwen3-235b-decode"])
@@ -85,7 +82,7 @@ def test_forward_decode_layers_all_tokens(name):
     out, routing = _run(g)
     ref = OracleExperts(shape, g.li).forward()
     routing_exact(routing, ref, shape.T, shape.top_k, name)
-    compare_out(bits_host(out), ref["out"], name)
+    compare_out(bits_host(out), ref["out"], name, allowance=ref["allowance"])
 
 
 @pytest.mark.parametrize("name,n_sample", [("gpt-oss-120b-prefill", 12), ("qwen3-235b-prefill", 8),
@@ -101,7 +98,8 @@ def test_forward_prefill_layers_sampled(name, n_sample):
     toks[-1] = shape.T - 1                                   # include the last (ragged) tile
     ref = ox.forward(token_subset=toks)
     routing_exact(routing, ref, shape.T, shape.top_k, name)
-    compare_out(bits_host(out)[toks], ref["out"], f"{name} tokens {toks.tolist()}")
+    compare_out(bits_host(out)[toks], ref["out"], f"{name} tokens {toks.tolist()}",
+                allowance=ref["allowance"])
 
 
 def test_forward_deterministic_and_reentrant():
