@@ -21,7 +21,7 @@ What the layer computes, and where the pages state it:
   GEMM input buffers; combine is the gate-weighted accumulation of the expert
   outputs per token.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   e4m3 is the OCP "fn" variant (bias 7, max 448, no infinities, 0x7F/0xFF NaN);
   a scale is fp32(amax / 448) (IEEE fp32 divide), 1.0 for an all-zero block, and
   a code is the nearest e4m3 value (ties to even) of fp32(v / s) clamped to

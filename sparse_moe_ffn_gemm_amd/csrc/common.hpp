@@ -49,11 +49,26 @@ __device__ __forceinline__ T wave_max(T v) {
   return v;
 }
 
-// Max over each aligned group of `W` lanes (W a power of two <= 64).
+// v from the lane `CTRL` names inside this lane's row of 16 (a DPP row rotation).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over each aligned group of `W` lanes (W a power of two <= 64).  Groups of 16 are
+// DPP rows: four rotations (by 8, 4, 2, 1 lanes) leave the row maximum in every lane
+// without a round trip through LDS.
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
+  if constexpr (W == 16) {
+    v = fmaxf(v, dpp_row<0x128>(v));
+    v = fmaxf(v, dpp_row<0x124>(v));
+    v = fmaxf(v, dpp_row<0x122>(v));
+    v = fmaxf(v, dpp_row<0x121>(v));
+  } else {
 #pragma unroll
-  for (int off = W / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    for (int off = W / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  }
   return v;
 }
 

@@ -18,8 +18,12 @@
 // Memory pipeline: tiles go from global memory straight into LDS
 // (global_load_lds_dwordx4, no register staging) through a ring of STAGES K-steps,
 // so STAGES-1 K-steps of loads are in flight while one is multiplied.  LDS rows are
-// 128 bytes; the 16-byte chunk c of row r is stored in slot c ^ (r & 7), which each
-// lane realises by choosing the global chunk it fetches.  Out-of-range chunks (K tail,
+// 128 bytes; the 16-byte chunk c of row r is stored in slot c ^ ((r >> 1) & 7), which
+// each lane realises by choosing the global chunk it fetches.  The LDS serves a 128-bit
+// read 16 lanes at a time, and a fragment read has its 16 lanes on 16 consecutive rows at
+// one chunk: the two rows of each 256-byte line take the two halves of the banks and the
+// key (r >> 1) & 7 spreads the 8 lines over distinct slots, so those reads are
+// conflict-free.  Out-of-range chunks (K tail,
 // N tail, rows past the expert's segment) are fetched from a zero block.
 //
 // Work order: blocks are numbered so that each XCD (blocks are dealt round-robin to
@@ -44,8 +48,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __align__(16) const uint8_t kZeroChunk[64] = {0};
 __device__ __align__(16) const float kZeroScale[4] = {0.f, 0.f, 0.f, 0.f};
 
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ swz_key(row)) << 4);
 }
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int g) {
@@ -161,7 +167,7 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
     const bool live = AROWS >= 8 || lane < 32;
     const int src = live ? rowsrc[row] : -1;
     a_ok[i] = src >= 0;
-    a_off[i] = static_cast<unsigned>(src < 0 ? 0 : src) * K + ((a_slot ^ (row & 7)) << 4);
+    a_off[i] = static_cast<unsigned>(src < 0 ? 0 : src) * K + ((a_slot ^ swz_key(row)) << 4);
     a_src[i] = a.A + a_off[i];
   }
   const uint8_t* b_src[B_INSTR];
@@ -179,7 +185,7 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
       if (col < N) g = col;
     }
     b_ok[i] = g >= 0;
-    b_off[i] = static_cast<unsigned>(g < 0 ? 0 : g) * K + ((a_slot ^ (br & 7)) << 4);
+    b_off[i] = static_cast<unsigned>(g < 0 ? 0 : g) * K + ((a_slot ^ swz_key(br)) << 4);
     b_src[i] = Bexp + b_off[i];
   }
   // weight block-scale rows of this wave's column groups (-1: the group is empty)
@@ -229,14 +235,14 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
       const int row0 = wave * AROWS + i * 8;
-      const int kk = k0 + ((a_slot ^ ((row0 + a_r8) & 7)) << 4);
+      const int kk = k0 + ((a_slot ^ swz_key(row0 + a_r8)) << 4);
       const void* src = (a_ok[i] && kk < K) ? static_cast<const void*>(a_src[i] + k0) : kZeroChunk;
       if (AROWS >= 8 || lane < 32) load_lds16(src, As + row0 * 128);
     }
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
       const int row0 = wave * BROWS + i * 8;
-      const int kk = k0 + ((a_slot ^ ((row0 + a_r8) & 7)) << 4);
+      const int kk = k0 + ((a_slot ^ swz_key(row0 + a_r8)) << 4);
       const void* src = (b_ok[i] && kk < K) ? static_cast<const void*>(b_src[i] + k0) : kZeroChunk;
       load_lds16(src, Bs + row0 * 128);
     }

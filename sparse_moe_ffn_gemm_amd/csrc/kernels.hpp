@@ -33,7 +33,7 @@ void launch_topk(const float* partial, int ksplit, const float* bias, int T, int
 // counts, offsets, per-chunk bases and the M-tile list for tiles of `bm` rows
 void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32_t* counts,
                           int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
-                          hipStream_t st);
+                          int32_t* expert_tile_off, hipStream_t st);
 void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,
                              int top_k, int32_t* perm, int32_t* inv, hipStream_t st);
 
@@ -48,6 +48,8 @@ struct GemmArgs {
   const uint16_t* bias;      // [E, N] or NULL
   const MTile* tiles;
   const int32_t* num_tiles;
+  const int32_t* expert_tile_off;   // [E+1] first M-tile of each expert, [E] = num_tiles
+  int E;
   int K, N, I;
   uint8_t* h_out;            // gemm1: [rows, I]
   float* h_scale;            // gemm1: [rows, ceil(I/128)]

@@ -20,7 +20,7 @@ struct Plan {
   int T, H, E, k, I;
   long rows;
   int ksplit, kslice, nchunks, bm, max_tiles;
-  size_t partial, hist, chunk_base, tiles, num_tiles;
+  size_t partial, hist, chunk_base, tiles, num_tiles, expert_tile_off;
   size_t ids, gates, counts, offsets, perm, inv;
   size_t xq, sx, h, sh, y;
   size_t total;
@@ -58,6 +58,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   p->chunk_base = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
   p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->max_tiles));
   p->num_tiles = take(sizeof(int32_t));
+  p->expert_tile_off = take(sizeof(int32_t) * (E + 1));
   p->ids = take(sizeof(int32_t) * p->rows);
   p->gates = take(sizeof(float) * p->rows);
   p->counts = take(sizeof(int32_t) * E);
@@ -108,7 +109,7 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
   mark(ev, 2, st);
   moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, tb.counts, tb.offsets,
                             at<int32_t>(ws, p.chunk_base), at<moe::MTile>(ws, p.tiles),
-                            at<int32_t>(ws, p.num_tiles), st);
+                            at<int32_t>(ws, p.num_tiles), at<int32_t>(ws, p.expert_tile_off), st);
   mark(ev, 3, st);
   moe::launch_dispatch_scatter(tb.ids, at<int32_t>(ws, p.chunk_base), p.T, p.E, p.k, tb.perm,
                                tb.inv, st);
@@ -163,6 +164,8 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g1.bias = b13;
   g1.tiles = at<moe::MTile>(ws, p.tiles);
   g1.num_tiles = at<int32_t>(ws, p.num_tiles);
+  g1.expert_tile_off = at<int32_t>(ws, p.expert_tile_off);
+  g1.E = E;
   g1.K = H;
   g1.N = 2 * I;
   g1.I = I;
@@ -181,6 +184,8 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.bias = b2;
   g2.tiles = g1.tiles;
   g2.num_tiles = g1.num_tiles;
+  g2.expert_tile_off = g1.expert_tile_off;
+  g2.E = E;
   g2.K = I;
   g2.N = H;
   g2.I = I;

@@ -221,7 +221,8 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __res
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ chunk_base,
                                                             MTile* __restrict__ tiles,
-                                                            int32_t* __restrict__ num_tiles) {
+                                                            int32_t* __restrict__ num_tiles,
+                                                            int32_t* __restrict__ expert_tile_off) {
   __shared__ int tmp[256];
   const int e = threadIdx.x;
   int cnt = 0;
@@ -248,7 +249,11 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __res
     m.pad = 0;
     tiles[toff + i] = m;
   }
-  if (e == 255) num_tiles[0] = toff + nt;
+  if (e < E) expert_tile_off[e] = toff;
+  if (e == 255) {
+    num_tiles[0] = toff + nt;
+    expert_tile_off[E] = toff + nt;
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -294,9 +299,10 @@ void launch_topk(const float* partial, int ksplit, const float* bias, int T, int
 
 void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32_t* counts,
                           int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
-                          hipStream_t st) {
+                          int32_t* expert_tile_off, hipStream_t st) {
   dispatch_scan_kernel<<<dim3(1), dim3(256), 0, st>>>(hist, nchunks, E, bm, counts, offsets,
-                                                       chunk_base, tiles, num_tiles);
+                                                       chunk_base, tiles, num_tiles,
+                                                       expert_tile_off);
 }
 
 void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,
