@@ -26,6 +26,9 @@ SMALL = [
     custom_shape(T=150, H=320, E=4, top_k=4, I=384, seed=35),       # k = E, >128 rows/expert
     custom_shape(T=200, H=256, E=16, top_k=3, I=128, seed=36, router="hot"),  # one hot expert
     custom_shape(T=96, H=384, E=8, top_k=2, I=320, seed=37, expert_bias=False),
+    # > 160 rows per expert: 256-row tiles, a short last tile per expert, ragged K and N
+    custom_shape(T=600, H=320, E=4, top_k=2, I=320, seed=38),
+    custom_shape(T=700, H=448, E=2, top_k=1, I=192, seed=39, expert_bias=False),
 ]
 
 
