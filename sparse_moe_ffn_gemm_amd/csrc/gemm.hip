@@ -439,39 +439,64 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
 }
 
 // ------------------------------------------------------------------------------------
-// Large-group variant: 256 x 256 workgroup tile, eight waves in a 4 (M) x 2 (N) grid,
-// each wave 64 x 128 (4 x 8 sub-tiles of 16 x 16), two waves per SIMD so that one wave's
-// promotion FMAs and LDS reads overlap the other's MFMAs.  The LDS ring holds two K-steps
-// (2 x 64 KB): the loads of step k+1 are in flight while step k is multiplied.  Wave rows
-// that lie entirely past the M-tile's rows skip their MFMAs (a short last tile of an
-// expert costs only its live rows).  Two K-steps of lookahead do not cover the latency of
-// a weight tile that comes from HBM, so each step also touches, PF K-steps ahead, the
-// cache lines of the A and B rows it will load then (a one-dword direct-to-LDS load per
-// line into a scratch area), which brings them into L2 early.
+// Large-group variant: 256 x BN workgroup tile, eight waves in a 4 (M) x 2 (N) grid,
+// each wave 64 x BN/2 (4 x BN/32 sub-tiles of 16 x 16), two waves per SIMD so that one
+// wave's promotion FMAs and LDS reads overlap the other's MFMAs.  A (activation) and B
+// (weight) tiles have rings of their own: A slots are filled SA-1 K-steps ahead, B slots
+// SB-1 K-steps ahead, so the weights, which mostly come from HBM, get the longer lead.
+// Wave rows that lie entirely past the M-tile's rows skip their MFMAs.
+//
+// gemm1 (SWIGLU): the B tile holds BN/2 gate rows of w13 and the matching BN/2 up rows;
+// wave wn takes gate and up columns [wn BN/4, (wn+1) BN/4) of them, so SwiGLU pairs sit
+// in the same lane.  The weight scale is taken per 16-column sub-tile (a sub-tile never
+// straddles a 128-row scale block since I is a multiple of 64).
 // ------------------------------------------------------------------------------------
-template <bool SWIGLU, int PF>
-__global__ __launch_bounds__(512) void grouped_gemm256_kernel(const GemmArgs a, int max_tiles,
-                                                              int ntiles, int grid) {
-  constexpr int BM = 256, BN = 256, WN = 2;
-  constexpr int SM = 4, SN = 8, NG = 4, GW = 64;     // gemm1: 64 gate + 64 up columns/wave
-  constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
-  constexpr int ROWS_PER_WAVE = 32;                  // A and B rows each wave fetches
-  constexpr int LOADS = 4 + 4 + 1;                   // vmem instructions per wave and step
+template <bool SWIGLU, int BN, int SA, int SB>
+__global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int max_tiles,
+                                                               int ntiles, int grid) {
+  constexpr int BM = 256, WN = 2;
+  constexpr int SM = 4, SN = BN / 32;                // sub-tiles per wave
+  constexpr int NG = SN / 2, GW = BN / 4;            // gemm1: gate sub-tiles / columns per wave
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  constexpr int A_ROWS = BM / 8, B_ROWS = BN / 8;    // rows each wave fetches per step
+  constexpr int A_INSTR = A_ROWS / 8, B_INSTR = B_ROWS / 8;
+  static_assert(BN % 64 == 0 && (!SWIGLU || SN % 2 == 0), "tile");
+  static_assert(SA >= 2 && SB >= SA, "rings");
+  static_assert(2 * SN <= 32, "scale lanes");
 
-  __shared__ __align__(16) uint8_t smem[2 * STAGE];
-  __shared__ __align__(16) float sS[2][8][64];      // per wave: 32 A-row scales, 4 B scales
+  __shared__ __align__(16) uint8_t ringA[SA * A_BYTES];
+  __shared__ __align__(16) uint8_t ringB[SB * B_BYTES];
+  // per A slot and wave: lanes [0, 32) the activation scales of the wave's A rows,
+  // [32, 32 + 2 SN) the weight block scales of sub-tile n of column wave wn (wn SN + n)
+  __shared__ __align__(16) float sS[SA][8][64];
   __shared__ int rowsrc[BM];
   __shared__ float red[WN][BM];
-  __shared__ __align__(16) float pf_sink[8][64];    // destination of the L2 touches
 
+  // ---- which tile: expert-major order (an expert's M-tiles fastest, then its n-tiles),
+  // cut into eight contiguous ranges, one per XCD (blocks are dealt to the XCDs round-
+  // robin): the concurrent workgroups of an XCD share the expert's activation rows
+  // across n-tiles and each weight tile across the expert's M-tiles in their L2 ----
+  const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
+  const int per_xcd = (total + 7) / 8;
   const int b = blockIdx.x;
-  const int L = (b % 8) * (grid / 8) + b / 8;
-  const int mti = L % max_tiles, nt = L / max_tiles;
-  if (nt >= ntiles || mti >= *a.num_tiles) return;
-  MTile mt = a.tiles[mti];
+  if (b / 8 >= per_xcd) return;
+  const int L = (b % 8) * per_xcd + b / 8;
+  if (L >= total) return;
+  int lo = 0, hi = a.E;                      // the expert e with off[e] * ntiles <= L < off[e+1] * ntiles
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.expert_tile_off[mid] * ntiles <= L) lo = mid; else hi = mid;
+  }
+  const int t0 = a.expert_tile_off[lo];
+  const int mcount = a.expert_tile_off[lo + 1] - t0;
+  const int local = L - t0 * ntiles;
+  const int nt = local / mcount;
+  MTile mt = a.tiles[t0 + local % mcount];
   mt.expert = __builtin_amdgcn_readfirstlane(mt.expert);
   mt.row_begin = __builtin_amdgcn_readfirstlane(mt.row_begin);
   mt.row_end = __builtin_amdgcn_readfirstlane(mt.row_end);
+  (void)max_tiles;
+  (void)grid;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -479,8 +504,7 @@ __global__ __launch_bounds__(512) void grouped_gemm256_kernel(const GemmArgs a, 
   const int K = a.K, N = a.N, I = a.I;
   const int KB = ceil_div(K, kBlock), NBs = ceil_div(N, kBlock);
   const int e = mt.expert;
-  const int live_rows = mt.row_end - mt.row_begin;
-  const bool wave_live = wm * 64 < live_rows;
+  const bool wave_live = wm * 64 < mt.row_end - mt.row_begin;
   const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * K;
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
 
@@ -492,111 +516,94 @@ __global__ __launch_bounds__(512) void grouped_gemm256_kernel(const GemmArgs a, 
   }
   __syncthreads();
 
-  // ---- fetch descriptors: wave w fetches A rows and B rows [32 w, 32 w + 32) ----
+  // global row of w13 / w2 behind B-tile row br (-1: past the matrix)
+  auto b_global_row = [&](int br) {
+    if (SWIGLU) {
+      const int j = nt * (BN / 2) + (br % (BN / 2));
+      return j < I ? (br >= BN / 2 ? I : 0) + j : -1;
+    }
+    const int col = nt * BN + br;
+    return col < N ? col : -1;
+  };
+
+  // ---- fetch descriptors ----
   const int a_slot = lane & 7, a_r8 = lane >> 3;
-  unsigned a_off[4], b_off[4];
-  bool a_ok[4], b_ok[4];
+  unsigned a_off[A_INSTR], b_off[B_INSTR];
+  bool a_ok[A_INSTR], b_ok[B_INSTR];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wave * ROWS_PER_WAVE + i * 8 + a_r8;
+  for (int i = 0; i < A_INSTR; ++i) {
+    const int row = wave * A_ROWS + i * 8 + a_r8;
     const int src = rowsrc[row];
     a_ok[i] = src >= 0;
     a_off[i] = static_cast<unsigned>(src < 0 ? 0 : src) * K + ((a_slot ^ swz_key(row)) << 4);
-    int g = -1;
-    if (SWIGLU) {
-      const int j = nt * 128 + (row & 127);
-      if (j < I) g = (row >> 7) * I + j;
-    } else {
-      const int col = nt * BN + row;
-      if (col < N) g = col;
-    }
+  }
+#pragma unroll
+  for (int i = 0; i < B_INSTR; ++i) {
+    const int row = wave * B_ROWS + i * 8 + a_r8;
+    const int g = b_global_row(row);
     b_ok[i] = g >= 0;
     b_off[i] = static_cast<unsigned>(g < 0 ? 0 : g) * K + ((a_slot ^ swz_key(row)) << 4);
   }
-  // scale lanes: [0, 32) the activation scales of the wave's A rows; 32 + q the weight
-  // block scale of column group q (gemm1: q = 2 wn' + {gate, up}; gemm2: q = wn')
   const float* s_ptr = kZeroScale;
   bool s_live = false;
   if (lane < 32) {
-    const int src = rowsrc[wave * ROWS_PER_WAVE + lane];
+    const int src = rowsrc[wave * A_ROWS + lane];
     s_live = src >= 0;
     s_ptr = a.A_scale + static_cast<size_t>(src < 0 ? 0 : src) * KB;
-  } else if (lane < 36) {
-    const int q = lane - 32;
-    int row = -1;
+  } else if (lane < 32 + 2 * SN) {
+    const int q = lane - 32, qw = q / SN, n = q % SN;   // column wave qw, sub-tile n
+    int row;
     if (SWIGLU) {
-      const int j0 = nt * 128 + (q >> 1) * GW;
-      if (j0 < I) row = ((q & 1) ? I + j0 : j0) / kBlock;
-    } else if (q < 2) {
-      const int c0 = nt * BN + q * 128;
-      if (c0 < N) row = c0 / kBlock;
+      const int j0 = nt * (BN / 2) + qw * GW + 16 * (n % NG);
+      row = j0 < I ? ((n >= NG ? I : 0) + j0) / kBlock : -1;
+    } else {
+      const int c0 = nt * BN + qw * (BN / 2) + 16 * n;
+      row = c0 < N ? c0 / kBlock : -1;
     }
     s_live = row >= 0;
     s_ptr = Bsc + static_cast<size_t>(row < 0 ? 0 : row) * KB;
   }
 
-  auto issue = [&](int kt) {   // all loads of K-step kt into ring slot kt & 1
-    uint8_t* As = smem + (kt & 1) * STAGE;
-    uint8_t* Bs = As + A_BYTES;
+  auto issue_a = [&](int kt) {   // A rows and all scales of K-step kt
+    uint8_t* As = ringA + (kt % SA) * A_BYTES;
     const int k0 = kt * kBlock;
     if (k0 + kBlock <= K) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) load_lds16_s(a_off[i], a.A + k0, As + (wave * ROWS_PER_WAVE + i * 8) * 128);
+      for (int i = 0; i < A_INSTR; ++i) load_lds16_s(a_off[i], a.A + k0, As + (wave * A_ROWS + i * 8) * 128);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) load_lds16_s(b_off[i], Bexp + k0, Bs + (wave * ROWS_PER_WAVE + i * 8) * 128);
-    } else {                     // ragged K tail: chunks past K come from zeros
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wave * ROWS_PER_WAVE + i * 8 + a_r8;
+      for (int i = 0; i < A_INSTR; ++i) {
+        const int row = wave * A_ROWS + i * 8 + a_r8;
         const int kk = k0 + ((a_slot ^ swz_key(row)) << 4);
         const void* src = (a_ok[i] && kk < K) ? static_cast<const void*>(a.A + a_off[i] + k0) : kZeroChunk;
-        load_lds16(src, As + (wave * ROWS_PER_WAVE + i * 8) * 128);
+        load_lds16(src, As + (wave * A_ROWS + i * 8) * 128);
       }
+    }
+    if (lane < 32 + 2 * SN) {
+      const void* src = s_live ? static_cast<const void*>(s_ptr + kt) : kZeroScale;
+      load_lds4(src, &sS[kt % SA][wave][0]);
+    }
+  };
+  auto issue_b = [&](int kt) {
+    uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
+    const int k0 = kt * kBlock;
+    if (k0 + kBlock <= K) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wave * ROWS_PER_WAVE + i * 8 + a_r8;
+      for (int i = 0; i < B_INSTR; ++i) load_lds16_s(b_off[i], Bexp + k0, Bs + (wave * B_ROWS + i * 8) * 128);
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_INSTR; ++i) {
+        const int row = wave * B_ROWS + i * 8 + a_r8;
         const int kk = k0 + ((a_slot ^ swz_key(row)) << 4);
         const void* src = (b_ok[i] && kk < K) ? static_cast<const void*>(Bexp + b_off[i] + k0) : kZeroChunk;
-        load_lds16(src, Bs + (wave * ROWS_PER_WAVE + i * 8) * 128);
+        load_lds16(src, Bs + (wave * B_ROWS + i * 8) * 128);
       }
-    }
-    if (lane < 36) {
-      const void* src = s_live ? static_cast<const void*>(s_ptr + kt) : kZeroScale;
-      load_lds4(src, &sS[kt & 1][wave][0]);
     }
   };
 
-  // L2 touch of K-step kt: lanes [0, 32) the A rows, lanes [32, 64) the B rows of this
-  // wave's fetch range; the first and the last dword of each row's 128-byte chunk (the
-  // chunk may straddle two cache lines)
-  const uint8_t* pf_row;
-  {
-    const int row = wave * ROWS_PER_WAVE + (lane & 31);
-    if (lane < 32) {
-      const int src = rowsrc[row];
-      pf_row = a.A + static_cast<size_t>(src < 0 ? 0 : src) * K;
-    } else {
-      int g = 0;
-      if (SWIGLU) {
-        const int j = nt * 128 + (row & 127);
-        if (j < I) g = (row >> 7) * I + j;
-      } else {
-        const int col = nt * BN + row;
-        if (col < N) g = col;
-      }
-      pf_row = Bexp + static_cast<size_t>(g) * K;
-    }
-  }
-  auto touch = [&](int kt) {
-    const int k0 = kt * kBlock;
-    const int k1 = min(k0 + kBlock, K) - 4;
-    load_lds4(pf_row + k0, &pf_sink[wave][0]);
-    load_lds4(pf_row + k1, &pf_sink[wave][0]);
-  };
-
-  auto sub_brow = [&](int n) {
-    if (SWIGLU) return n < NG ? wn * GW + 16 * n : 128 + wn * GW + 16 * (n - NG);
-    return wn * 128 + 16 * n;
+  auto sub_brow = [&](int n) {   // B-tile row of sub-tile n of this wave
+    if (SWIGLU) return n < NG ? wn * GW + 16 * n : BN / 2 + wn * GW + 16 * (n - NG);
+    return wn * (BN / 2) + 16 * n;
   };
 
   v4f acc[SM][SN];
@@ -606,50 +613,47 @@ __global__ __launch_bounds__(512) void grouped_gemm256_kernel(const GemmArgs a, 
     for (int n = 0; n < SN; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (PF > 1) {
-    for (int d = 1; d < PF && d < KB; ++d) touch(d);
+  // prologue: B runs SB-1 steps ahead, A SA-1; within a step the A loads are issued
+  // before the B loads of the later step, so "A(k) and B(k) landed" is "at most the B
+  // loads issued after A(k) are outstanding"
+  for (int s = 0; s < SB - SA && s < KB; ++s) issue_b(s);
+  for (int s = 0; s < SA - 1; ++s) {
+    if (s < KB) issue_a(s);
+    if (s + SB - SA < KB) issue_b(s + SB - SA);
   }
-  issue(0);
   for (int kt = 0; kt < KB; ++kt) {
-    // this wave's loads of step kt have landed (the two L2 touches issued after them in
-    // the previous step may still be in flight) ...
-    if (PF > 1 && kt > 0 && kt - 1 + PF < KB) {
-      wait_vmcnt<2>();
+    // the loads issued after A(kt) are those of B(kt + SB - SA): a later step (which may
+    // stay in flight) when SB > SA, step kt itself when SB == SA
+    if (SB > SA && kt + SB - SA < KB) {
+      wait_vmcnt<B_INSTR>();
     } else {
       wait_vmcnt<0>();
     }
-    barrier_only();           // ... and every wave's; step kt-1's slot is free
-    if (kt + 1 < KB) issue(kt + 1);
-    if (PF > 1 && kt + PF < KB) touch(kt + PF);
+    barrier_only();            // every wave's loads of step kt landed; step kt-1's slots free
+    if (kt + SA - 1 < KB) issue_a(kt + SA - 1);
+    if (kt + SB - 1 < KB) issue_b(kt + SB - 1);
     if (!wave_live) continue;
 
-    const int slot = kt & 1;
-    const uint8_t* As = smem + slot * STAGE;
-    const uint8_t* Bs = As + A_BYTES;
-    float sb0, sb1;
-    if (SWIGLU) {
-      sb0 = sS[slot][0][32 + 2 * wn];
-      sb1 = sS[slot][0][33 + 2 * wn];
-    } else {
-      sb0 = sS[slot][0][32 + wn];
-      sb1 = sb0;
-    }
+    const int sa_slot = kt % SA;
+    const uint8_t* As = ringA + sa_slot * A_BYTES;
+    const uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
+    // The weight fragment is the MFMA's first operand and the activation fragment its
+    // second, so a lane's four results are four adjacent columns of one row: the block
+    // scale is one value per (m, n) and the epilogue stores are 4 or 16 bytes wide.
+    float sbv[SN];
+#pragma unroll
+    for (int n = 0; n < SN; ++n) sbv[n] = sS[sa_slot][0][32 + wn * SN + n];
     v8i af[SM];
-    float s0[SM][4], s1[SM][4];
+    float sav[SM];
 #pragma unroll
     for (int m = 0; m < SM; ++m) {
-      const int rw0 = wm * 64 + 16 * m;
-      af[m] = lds_frag(As, rw0 + (lane & 15), lane >> 4);
-      const int r = rw0 + 4 * (lane >> 4);
-      const float4 sa = *reinterpret_cast<const float4*>(&sS[slot][r >> 5][r & 31]);
-      s0[m][0] = sa.x * sb0; s0[m][1] = sa.y * sb0; s0[m][2] = sa.z * sb0; s0[m][3] = sa.w * sb0;
-      if (SWIGLU) {
-        s1[m][0] = sa.x * sb1; s1[m][1] = sa.y * sb1; s1[m][2] = sa.z * sb1; s1[m][3] = sa.w * sb1;
-      }
+      const int r = wm * 64 + 16 * m + (lane & 15);
+      af[m] = lds_frag(As, r, lane >> 4);
+      sav[m] = sS[sa_slot][r / A_ROWS][r % A_ROWS];
     }
-    // Software pipeline over the 32 products (column-major): product j goes to partial
-    // j % 3 and is folded into its accumulator two products later, so the FMAs never wait
-    // for the MFMA just issued; B fragments are read one column ahead.
+    // Software pipeline over the SM x SN products (column-major): product j goes to
+    // partial j % 3 and is folded into its accumulator two products later, so the FMAs
+    // never wait for the MFMA just issued; B fragments are read one column ahead.
     v8i bq[2];
     bq[0] = lds_frag(Bs, sub_brow(0) + (lane & 15), lane >> 4);
     v4f pp[3];
@@ -658,94 +662,118 @@ __global__ __launch_bounds__(512) void grouped_gemm256_kernel(const GemmArgs a, 
       if (j < SM * SN) {
         const int n = j / SM, m = j % SM;
         if (m == 0 && n + 1 < SN) bq[(n + 1) & 1] = lds_frag(Bs, sub_brow(n + 1) + (lane & 15), lane >> 4);
-        pp[j % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[m], bq[n & 1], zero, 0, 0, 0, 0, 0, 0);
+        pp[j % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n & 1], af[m], zero, 0, 0, 0, 0, 0, 0);
       }
       if (j >= 2) {
         const int q = j - 2, n = q / SM, m = q % SM;
-        const bool second = SWIGLU && n >= NG;
+        const float sc = sav[m] * sbv[n];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(pp[q % 3][i], second ? s1[m][i] : s0[m][i], acc[m][n][i]);
+        for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(pp[q % 3][i], sc, acc[m][n][i]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   wait_vmcnt<0>();
-  __syncthreads();   // every wave is done with the ring before its LDS is reused
 
-  const int rbase = wm * 64 + 4 * (lane >> 4);   // + 16 m + i
+  // ---- epilogue: lane holds rows r(m) = wm*64 + 16m + (lane & 15) and, per sub-tile n,
+  // the four adjacent columns 16n + 4 (lane >> 4) + i of its column range ----
+  const int cq = 4 * (lane >> 4);
   if constexpr (SWIGLU) {
     const int KBI = ceil_div(I, kBlock);
     const uint16_t* bias = a.bias ? a.bias + static_cast<size_t>(e) * N : nullptr;
     float hv[SM][NG][4];
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
-      const int j = nt * 128 + wn * GW + 16 * n + (lane & 15);
-      const bool ok = j < I;
-      const float bg = (bias && ok) ? bf16_to_f32(bias[j]) : 0.f;
-      const float bu = (bias && ok) ? bf16_to_f32(bias[I + j]) : 0.f;
+      const int j0 = nt * (BN / 2) + wn * GW + 16 * n + cq;
+      const bool ok = j0 < I;                 // I is a multiple of 64: all four or none
+      float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias && ok) {
+        const uint2 g2 = *reinterpret_cast<const uint2*>(bias + j0);
+        const uint2 u2 = *reinterpret_cast<const uint2*>(bias + I + j0);
+        bg[0] = __uint_as_float(g2.x << 16); bg[1] = __uint_as_float(g2.x & 0xFFFF0000u);
+        bg[2] = __uint_as_float(g2.y << 16); bg[3] = __uint_as_float(g2.y & 0xFFFF0000u);
+        bu[0] = __uint_as_float(u2.x << 16); bu[1] = __uint_as_float(u2.x & 0xFFFF0000u);
+        bu[2] = __uint_as_float(u2.y << 16); bu[3] = __uint_as_float(u2.y & 0xFFFF0000u);
+      }
 #pragma unroll
       for (int m = 0; m < SM; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float g = acc[m][n][i] + bg;
-          const float u = acc[m][n + NG][i] + bu;
+          const float g = acc[m][n][i] + bg[i];
+          const float u = acc[m][n + NG][i] + bu[i];
           const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
           hv[m][n][i] = ok ? h : 0.f;
         }
     }
+    // Each 1x128 group of h is a row's 128 columns [128 c, 128 c + 128); a tile holds
+    // BN/2 of them starting at nt * BN/2.  The scale of a group is only complete when
+    // every tile that covers part of it has contributed, so tiles whose column range is
+    // not a whole number of groups (BN/2 != 128) reduce per group across the tile.
+    static_assert(!SWIGLU || BN == 256, "gemm1 groups are whole tiles");
 #pragma unroll
-    for (int m = 0; m < SM; ++m)
+    for (int m = 0; m < SM; ++m) {
+      float mx = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = 0.f;
+      for (int n = 0; n < NG; ++n)
 #pragma unroll
-        for (int n = 0; n < NG; ++n) mx = fmaxf(mx, fabsf(hv[m][n][i]));
-        mx = group_max<16>(mx);
-        if ((lane & 15) == 0) red[wn][rbase + 16 * m + i] = mx;
-      }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(hv[m][n][i]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (lane < 16) red[wn][wm * 64 + 16 * m + lane] = mx;
+    }
     __syncthreads();
-    uint8_t* hs = smem;   // h codes of the tile, [256][128], staged for 16-byte stores
 #pragma unroll
-    for (int m = 0; m < SM; ++m)
+    for (int m = 0; m < SM; ++m) {
+      const int r = wm * 64 + 16 * m + (lane & 15);
+      const int p = mt.row_begin + r;
+      const float sc = group_scale(fmaxf(red[0][r], red[1][r]));   // exact fp32(amax / 448)
+      // quotient h / sc: reciprocal estimate plus one residual correction
+      const float rs = __builtin_amdgcn_rcpf(sc);
+      if (p < mt.row_end) {
+        uint8_t* hrow = a.h_out + static_cast<size_t>(p) * I;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rbase + 16 * m + i;
-        const float s = group_scale(fmaxf(red[0][r], red[1][r]));
+        for (int n = 0; n < NG; ++n) {
+          const int j0 = nt * (BN / 2) + wn * GW + 16 * n + cq;
+          float q[4];
 #pragma unroll
-        for (int n = 0; n < NG; ++n)
-          hs[r * 128 + wn * GW + 16 * n + (lane & 15)] =
-              static_cast<uint8_t>(encode2(hv[m][n][i], 0.f, s) & 0xFFu);
-        const int p = mt.row_begin + r;
-        if (wn == 0 && (lane & 15) == 0 && p < mt.row_end)
-          a.h_scale[static_cast<size_t>(p) * KBI + nt] = s;
+          for (int i = 0; i < 4; ++i) {
+            const float q0 = hv[m][n][i] * rs;
+            const float q1 = fmaf(fmaf(-q0, sc, hv[m][n][i]), rs, q0);
+            q[i] = fminf(fmaxf(q1, -kFp8Max), kFp8Max);
+          }
+          const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false)) & 0xFFFFu;
+          const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], 0, false)) & 0xFFFFu;
+          if (j0 < I) *reinterpret_cast<uint32_t*>(hrow + j0) = lo | (hi << 16);
+        }
+        if (wn == 0 && lane < 16) a.h_scale[static_cast<size_t>(p) * KBI + nt] = sc;
       }
-    __syncthreads();
-    for (int q = tid; q < BM * 8; q += 512) {
-      const int r = q >> 3, c = q & 7;
-      const int p = mt.row_begin + r, col = nt * 128 + c * 16;
-      if (p < mt.row_end && col < I)
-        *reinterpret_cast<uint4*>(a.h_out + static_cast<size_t>(p) * I + col) =
-            *reinterpret_cast<const uint4*>(hs + r * 128 + c * 16);
     }
   } else {
     const uint16_t* bias = a.bias ? a.bias + static_cast<size_t>(e) * N : nullptr;
 #pragma unroll
     for (int n = 0; n < SN; ++n) {
-      const int col = nt * BN + wn * 128 + 16 * n + (lane & 15);
-      if (col >= N) continue;
-      const float bv = bias ? bf16_to_f32(bias[col]) : 0.f;
+      const int c0 = nt * BN + wn * (BN / 2) + 16 * n + cq;
+      if (c0 >= N) continue;                  // N is a multiple of 64: all four or none
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+        const uint2 b2 = *reinterpret_cast<const uint2*>(bias + c0);
+        bv[0] = __uint_as_float(b2.x << 16); bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+        bv[2] = __uint_as_float(b2.y << 16); bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+      }
 #pragma unroll
-      for (int m = 0; m < SM; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = mt.row_begin + rbase + 16 * m + i;
-          if (p < mt.row_end) a.y_out[static_cast<size_t>(p) * N + col] = acc[m][n][i] + bv;
-        }
+      for (int m = 0; m < SM; ++m) {
+        const int p = mt.row_begin + wm * 64 + 16 * m + (lane & 15);
+        if (p < mt.row_end)
+          *reinterpret_cast<float4*>(a.y_out + static_cast<size_t>(p) * N + c0) =
+              make_float4(acc[m][n][0] + bv[0], acc[m][n][1] + bv[1], acc[m][n][2] + bv[2], acc[m][n][3] + bv[3]);
+      }
     }
   }
 }
 
-constexpr int kGemmPrefetch = 0;   // K-steps between the L2 touch and the use of a chunk
+// Large-group launch shapes (workgroup tile 256 x BN, A / B ring depths).
+constexpr int kG1BN = 256, kG1SA = 2, kG1SB = 2;
+constexpr int kG2BN = 192, kG2SA = 2, kG2SB = 3;
 
 int gemm_tile_rows(long rows, int E) {
   const long avg = rows / (E > 0 ? E : 1);
@@ -761,7 +789,14 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
   const long total = static_cast<long>(max_tiles) * ntiles;
   const int grid = static_cast<int>((total + 7) / 8 * 8);
   if (bm == 256) {
-    grouped_gemm256_kernel<SWIGLU, kGemmPrefetch><<<grid, 512, 0, st>>>(a, max_tiles, ntiles, grid);
+    constexpr int BN = SWIGLU ? kG1BN : kG2BN;
+    const int nt_big = SWIGLU ? ceil_div(a.I, BN / 2) : ceil_div(a.N, BN);
+    const long tot = static_cast<long>(max_tiles) * nt_big;
+    const int g = static_cast<int>((tot + 7) / 8 * 8);
+    if constexpr (SWIGLU)
+      grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
+    else
+      grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
     return;
   }
   switch (bm) {
