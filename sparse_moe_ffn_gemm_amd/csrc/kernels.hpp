@@ -22,12 +22,13 @@ void launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* codes, float*
 
 // ---- routing ----
 constexpr int kRouterTile = 64;     // tokens / experts per router GEMM workgroup
-constexpr int kChunk = 64;          // tokens per dispatch chunk
+constexpr int kChunk = 256;         // tokens per dispatch chunk
 
-// partial[s][t][e] = sum over the s-th slice of H of x[t,h] * W[e,h]
+// partial[s][t][e] = sum over the s-th slice of H of x[t,h] * W[e,h]; also clears
+// hist[0, hist_n) for the top-k step
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
-                          int kslice, float* partial, hipStream_t st);
-// ids/gates + per-chunk expert histogram hist[chunk][E]
+                          int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st);
+// ids/gates, counted into the per-chunk expert histogram hist[chunk][E] (cleared before)
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
                  int32_t* ids, float* gates, int32_t* hist, hipStream_t st);
 // counts, offsets, per-chunk bases and the M-tile list for tiles of `bm` rows

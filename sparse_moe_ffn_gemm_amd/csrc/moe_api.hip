@@ -102,7 +102,8 @@ void mark(hipEvent_t* ev, int i, hipStream_t st) {
 void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const float* rb,
                      const Tables& tb, void* ws, hipStream_t st, hipEvent_t* ev = nullptr) {
   mark(ev, 0, st);
-  moe::launch_router_logits(x, rw, p.T, p.H, p.E, p.ksplit, p.kslice, at<float>(ws, p.partial), st);
+  moe::launch_router_logits(x, rw, p.T, p.H, p.E, p.ksplit, p.kslice, at<float>(ws, p.partial),
+                            at<int32_t>(ws, p.hist), p.nchunks * p.E, st);
   mark(ev, 1, st);
   moe::launch_topk(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, tb.ids, tb.gates,
                    at<int32_t>(ws, p.hist), st);
