@@ -471,6 +471,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
   __shared__ __align__(16) float sS[SA][8][64];
   __shared__ int rowsrc[BM];
   __shared__ float red[WN][BM];
+  __shared__ __align__(16) uint16_t sbias[BN];      // bias of the tile's B rows (bf16)
 
   // ---- which tile: expert-major order (an expert's M-tiles fastest, then its n-tiles),
   // cut into eight contiguous ranges, one per XCD (blocks are dealt to the XCDs round-
@@ -613,6 +614,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
     for (int n = 0; n < SN; ++n) acc[m][n] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
+  {  // the tile's bias, staged with the first loads: wave w fetches B rows [w BN/8, (w+1) BN/8)
+    const int br = wave * (BN / 8) + 2 * lane;
+    const int g = b_global_row(br);
+    const void* src = (a.bias != nullptr && g >= 0)
+                          ? static_cast<const void*>(a.bias + static_cast<size_t>(e) * N + g)
+                          : static_cast<const void*>(kZeroChunk);
+    if (lane < BN / 16) load_lds4(src, &sbias[wave * (BN / 8)]);
+  }
   // prologue: B runs SB-1 steps ahead, A SA-1; within a step the A loads are issued
   // before the B loads of the later step, so "A(k) and B(k) landed" is "at most the B
   // loads issued after A(k) are outstanding"
@@ -621,56 +630,89 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
     if (s < KB) issue_a(s);
     if (s + SB - SA < KB) issue_b(s + SB - SA);
   }
-  for (int kt = 0; kt < KB; ++kt) {
-    // the loads issued after A(kt) are those of B(kt + SB - SA): a later step (which may
-    // stay in flight) when SB > SA, step kt itself when SB == SA
+  // "this wave's loads of step kt landed": the loads issued after A(kt) are those of
+  // B(kt + SB - SA), a later step (which may stay in flight) when SB > SA, step kt
+  // itself when SB == SA
+  auto wait_step = [&](int kt) {
     if (SB > SA && kt + SB - SA < KB) {
       wait_vmcnt<B_INSTR>();
     } else {
       wait_vmcnt<0>();
     }
-    barrier_only();            // every wave's loads of step kt landed; step kt-1's slots free
-    if (kt + SA - 1 < KB) issue_a(kt + SA - 1);
-    if (kt + SB - 1 < KB) issue_b(kt + SB - 1);
-    if (!wave_live) continue;
-
-    const int sa_slot = kt % SA;
-    const uint8_t* As = ringA + sa_slot * A_BYTES;
-    const uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
-    // The weight fragment is the MFMA's first operand and the activation fragment its
-    // second, so a lane's four results are four adjacent columns of one row: the block
-    // scale is one value per (m, n) and the epilogue stores are 4 or 16 bytes wide.
-    float sbv[SN];
+  };
+  // The weight fragment is the MFMA's first operand and the activation fragment its
+  // second, so a lane's four results are four adjacent columns of one row: the block
+  // scale is one value per (m, n) and the epilogue stores are 4 or 16 bytes wide.
+  v8i af[SM], bq[3];
+  float sav[SM], sbv[SN];
+  auto read_step = [&](int kt) {   // scales, A fragments and the first B fragment
+    const int sl = kt % SA;
+    const uint8_t* As = ringA + sl * A_BYTES;
 #pragma unroll
-    for (int n = 0; n < SN; ++n) sbv[n] = sS[sa_slot][0][32 + wn * SN + n];
-    v8i af[SM];
-    float sav[SM];
+    for (int n = 0; n < SN; ++n) sbv[n] = sS[sl][0][32 + wn * SN + n];
 #pragma unroll
     for (int m = 0; m < SM; ++m) {
       const int r = wm * 64 + 16 * m + (lane & 15);
       af[m] = lds_frag(As, r, lane >> 4);
-      sav[m] = sS[sa_slot][r / A_ROWS][r % A_ROWS];
+      sav[m] = sS[sl][r / A_ROWS][r % A_ROWS];
     }
-    // Software pipeline over the SM x SN products (column-major): product j goes to
-    // partial j % 3 and is folded into its accumulator two products later, so the FMAs
-    // never wait for the MFMA just issued; B fragments are read one column ahead.
-    v8i bq[2];
-    bq[0] = lds_frag(Bs, sub_brow(0) + (lane & 15), lane >> 4);
-    v4f pp[3];
+    bq[0] = lds_frag(ringB + (kt % SB) * B_BYTES, sub_brow(0) + (lane & 15), lane >> 4);
+    bq[1] = lds_frag(ringB + (kt % SB) * B_BYTES, sub_brow(1) + (lane & 15), lane >> 4);
+  };
+
+  // Software pipeline over the NP = SM x SN products of a step (column-major): product j
+  // goes to partial j % 4 and is folded into its accumulator LAG products later (an MFMA
+  // result is ready only a few MFMA issue slots after the MFMA), so the FMAs never wait
+  // for the matrix pipe; B fragments are read two columns ahead.  The last LAG products of
+  // a step are folded during the first MFMAs of the next one, after the barrier and the
+  // next step's fragment reads have been issued, so the matrix pipe keeps running across
+  // the step boundary.
+  constexpr int NP = SM * SN, LAG = 2;
+  static_assert(NP % 4 == 0 && LAG < 4, "partials rotate across steps");
+  v4f pp[4];
+  float sc_tail[LAG] = {};
+  wait_step(0);
+  barrier_only();
+  if (wave_live) read_step(0);
+  for (int kt = 0; kt < KB; ++kt) {
+    // the slots of step kt-1 are free (every wave passed the barrier after reading them)
+    if (kt + SA - 1 < KB) issue_a(kt + SA - 1);
+    if (kt + SB - 1 < KB) issue_b(kt + SB - 1);
+    if (wave_live) {
+      const uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
 #pragma unroll
-    for (int j = 0; j < SM * SN + 2; ++j) {
-      if (j < SM * SN) {
+      for (int j = 0; j < NP; ++j) {
         const int n = j / SM, m = j % SM;
-        if (m == 0 && n + 1 < SN) bq[(n + 1) & 1] = lds_frag(Bs, sub_brow(n + 1) + (lane & 15), lane >> 4);
-        pp[j % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n & 1], af[m], zero, 0, 0, 0, 0, 0, 0);
-      }
-      if (j >= 2) {
-        const int q = j - 2, n = q / SM, m = q % SM;
-        const float sc = sav[m] * sbv[n];
+        if (m == 0 && n + 2 < SN) bq[(n + 2) % 3] = lds_frag(Bs, sub_brow(n + 2) + (lane & 15), lane >> 4);
+        pp[j % 4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n % 3], af[m], zero, 0, 0, 0, 0, 0, 0);
+        if (j >= LAG) {
+          const int q = j - LAG;
+          const float sc = sav[q % SM] * sbv[q / SM];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[m][n][i] = fmaf(pp[q % 3][i], sc, acc[m][n][i]);
+          for (int i = 0; i < 4; ++i) acc[q % SM][q / SM][i] = fmaf(pp[q % 4][i], sc, acc[q % SM][q / SM][i]);
+        } else if (kt > 0) {   // the previous step's product NP - LAG + j
+          const int q = NP - LAG + j;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[q % SM][q / SM][i] = fmaf(pp[q % 4][i], sc_tail[j], acc[q % SM][q / SM][i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < LAG; ++j) sc_tail[j] = sav[(NP - LAG + j) % SM] * sbv[(NP - LAG + j) / SM];
+    }
+    if (kt + 1 < KB) {
+      wait_step(kt + 1);
+      barrier_only();   // every wave is done with step kt's slots; step kt+1 has landed
+      if (wave_live) read_step(kt + 1);
+    }
+  }
+  if (wave_live) {      // the last step's last LAG products
+#pragma unroll
+    for (int j = 0; j < LAG; ++j) {
+      const int q = NP - LAG + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[q % SM][q / SM][i] = fmaf(pp[q % 4][i], sc_tail[j], acc[q % SM][q / SM][i]);
     }
   }
   wait_vmcnt<0>();
@@ -680,21 +722,18 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
   const int cq = 4 * (lane >> 4);
   if constexpr (SWIGLU) {
     const int KBI = ceil_div(I, kBlock);
-    const uint16_t* bias = a.bias ? a.bias + static_cast<size_t>(e) * N : nullptr;
     float hv[SM][NG][4];
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
       const int j0 = nt * (BN / 2) + wn * GW + 16 * n + cq;
       const bool ok = j0 < I;                 // I is a multiple of 64: all four or none
-      float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias && ok) {
-        const uint2 g2 = *reinterpret_cast<const uint2*>(bias + j0);
-        const uint2 u2 = *reinterpret_cast<const uint2*>(bias + I + j0);
-        bg[0] = __uint_as_float(g2.x << 16); bg[1] = __uint_as_float(g2.x & 0xFFFF0000u);
-        bg[2] = __uint_as_float(g2.y << 16); bg[3] = __uint_as_float(g2.y & 0xFFFF0000u);
-        bu[0] = __uint_as_float(u2.x << 16); bu[1] = __uint_as_float(u2.x & 0xFFFF0000u);
-        bu[2] = __uint_as_float(u2.y << 16); bu[3] = __uint_as_float(u2.y & 0xFFFF0000u);
-      }
+      const uint2 g2 = *reinterpret_cast<const uint2*>(&sbias[sub_brow(n) + cq]);
+      const uint2 u2 = *reinterpret_cast<const uint2*>(&sbias[sub_brow(n + NG) + cq]);
+      float bg[4], bu[4];
+      bg[0] = __uint_as_float(g2.x << 16); bg[1] = __uint_as_float(g2.x & 0xFFFF0000u);
+      bg[2] = __uint_as_float(g2.y << 16); bg[3] = __uint_as_float(g2.y & 0xFFFF0000u);
+      bu[0] = __uint_as_float(u2.x << 16); bu[1] = __uint_as_float(u2.x & 0xFFFF0000u);
+      bu[2] = __uint_as_float(u2.y << 16); bu[3] = __uint_as_float(u2.y & 0xFFFF0000u);
 #pragma unroll
       for (int m = 0; m < SM; ++m)
 #pragma unroll
@@ -749,17 +788,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
       }
     }
   } else {
-    const uint16_t* bias = a.bias ? a.bias + static_cast<size_t>(e) * N : nullptr;
 #pragma unroll
     for (int n = 0; n < SN; ++n) {
       const int c0 = nt * BN + wn * (BN / 2) + 16 * n + cq;
       if (c0 >= N) continue;                  // N is a multiple of 64: all four or none
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
-        const uint2 b2 = *reinterpret_cast<const uint2*>(bias + c0);
-        bv[0] = __uint_as_float(b2.x << 16); bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
-        bv[2] = __uint_as_float(b2.y << 16); bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
-      }
+      const uint2 b2 = *reinterpret_cast<const uint2*>(&sbias[sub_brow(n) + cq]);
+      float bv[4];
+      bv[0] = __uint_as_float(b2.x << 16); bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+      bv[2] = __uint_as_float(b2.y << 16); bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
 #pragma unroll
       for (int m = 0; m < SM; ++m) {
         const int p = mt.row_begin + wm * 64 + 16 * m + (lane & 15);
