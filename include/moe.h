@@ -72,7 +72,8 @@ typedef struct {
  *   xq [T, H] u8 + sx [T, ceil(H/128)] f32     quantised activations
  *   h  [T*top_k, I] u8 + sh [T*top_k, ceil(I/128)] f32   quantised SwiGLU output,
  *                                               rows in dispatch (perm) order
- *   y  [T*top_k, H] f32                        expert outputs incl. b2, dispatch order
+ *   y  [T*top_k, H] f16                        expert outputs incl. b2, dispatch order
+ *                                               (IEEE half, saturated to +-65504)
  *   routing.*                                  the tables used when routing_out == NULL
  * Valid after a completed moe_forward on that workspace. */
 typedef struct {

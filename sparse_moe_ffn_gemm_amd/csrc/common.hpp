@@ -22,6 +22,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// fp32 -> IEEE half bits, round to nearest even, saturated to +-65504 (the expert-output
+// buffer: 11 significant bits, a quarter of a bf16 output ulp after the gate sum).
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
+  f = fminf(fmaxf(f, -65504.0f), 65504.0f);
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
 // Scale of a group with absolute maximum `amax`: fp32(amax / 448) with an IEEE
 // (correctly rounded) division, 1 for an all-zero group.
 __device__ __forceinline__ float group_scale(float amax) {
@@ -70,6 +80,35 @@ __device__ __forceinline__ float group_max(float v) {
     for (int off = W / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   }
   return v;
+}
+
+// Quantises columns [col, col + 8) of one 1x128 group of a bf16 row (16 lanes of a DPP row
+// cover the group; `in` is false for lanes past the row's end) and returns the group's
+// scale, the same in all 16 lanes.  Codes go to codes_row + col.
+__device__ __forceinline__ float quantize_group16(const uint16_t* row, int col, bool in,
+                                                  uint8_t* codes_row) {
+  float f[8];
+  float amax = 0.0f;
+  if (in) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(row + col);
+    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_to_f32(static_cast<uint16_t>(wds[i] & 0xFFFFu));
+      f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(wds[i] >> 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+  amax = group_max<16>(amax);
+  const float s = group_scale(amax);
+  if (in) {
+    uint2 q;
+    q.x = encode4(f[0], f[1], f[2], f[3], s);
+    q.y = encode4(f[4], f[5], f[6], f[7], s);
+    *reinterpret_cast<uint2*>(codes_row + col) = q;
+  }
+  return s;
 }
 
 }  // namespace moe

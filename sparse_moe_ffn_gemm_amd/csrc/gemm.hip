@@ -149,6 +149,7 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
     const int p = mt.row_begin + r;
     int src = -1;
     if (p < mt.row_end) src = SWIGLU ? a.perm[p] / a.top_k : p;
+    if (static_cast<unsigned>(src) >= static_cast<unsigned>(a.A_rows)) src = -1;   // never read past A
     rowsrc[r] = src;
   }
   __syncthreads();
@@ -185,7 +186,10 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
       if (col < N) g = col;
     }
     b_ok[i] = g >= 0;
-    b_off[i] = static_cast<unsigned>(g < 0 ? 0 : g) * K + ((a_slot ^ swz_key(br)) << 4);
+    // a row past the matrix re-reads the tile's first row (already in flight, so it costs no
+    // HBM traffic); it only feeds output columns that are never stored
+    const int g_first = SWIGLU ? nt * 128 : nt * BN;
+    b_off[i] = static_cast<unsigned>(g < 0 ? g_first : g) * K + ((a_slot ^ swz_key(br)) << 4);
     b_src[i] = Bexp + b_off[i];
   }
   // weight block-scale rows of this wave's column groups (-1: the group is empty)
@@ -432,7 +436,7 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = mt.row_begin + rbase + 16 * m + i;
-          if (p < mt.row_end) a.y_out[static_cast<size_t>(p) * N + col] = acc[m][n][i] + bv;
+          if (p < mt.row_end) a.y_out[static_cast<size_t>(p) * N + col] = f32_to_f16_sat(acc[m][n][i] + bv);
         }
     }
   }
@@ -513,6 +517,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
     const int p = mt.row_begin + r;
     int src = -1;
     if (p < mt.row_end) src = SWIGLU ? a.perm[p] / a.top_k : p;
+    if (static_cast<unsigned>(src) >= static_cast<unsigned>(a.A_rows)) src = -1;   // never read past A
     rowsrc[r] = src;
   }
   __syncthreads();
@@ -543,7 +548,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
     const int row = wave * B_ROWS + i * 8 + a_r8;
     const int g = b_global_row(row);
     b_ok[i] = g >= 0;
-    b_off[i] = static_cast<unsigned>(g < 0 ? 0 : g) * K + ((a_slot ^ swz_key(row)) << 4);
+    // a row past the matrix re-reads the tile's first row (already in flight: no HBM
+    // traffic); it only feeds output columns that are never stored
+    b_off[i] = static_cast<unsigned>(g < 0 ? b_global_row(0) : g) * K + ((a_slot ^ swz_key(row)) << 4);
   }
   const float* s_ptr = kZeroScale;
   bool s_live = false;
@@ -800,8 +807,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
       for (int m = 0; m < SM; ++m) {
         const int p = mt.row_begin + wm * 64 + 16 * m + (lane & 15);
         if (p < mt.row_end)
-          *reinterpret_cast<float4*>(a.y_out + static_cast<size_t>(p) * N + c0) =
-              make_float4(acc[m][n][0] + bv[0], acc[m][n][1] + bv[1], acc[m][n][2] + bv[2], acc[m][n][3] + bv[3]);
+          *reinterpret_cast<uint2*>(a.y_out + static_cast<size_t>(p) * N + c0) = make_uint2(
+              f32_to_f16_sat(acc[m][n][0] + bv[0]) | (static_cast<uint32_t>(f32_to_f16_sat(acc[m][n][1] + bv[1])) << 16),
+              f32_to_f16_sat(acc[m][n][2] + bv[2]) | (static_cast<uint32_t>(f32_to_f16_sat(acc[m][n][3] + bv[3])) << 16));
       }
     }
   }
@@ -821,7 +829,10 @@ int gemm_tile_rows(long rows, int E) {
 
 template <bool SWIGLU>
 static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
-  const int ntiles = SWIGLU ? ceil_div(a.I, 128) : ceil_div(a.N, 256);
+  // decode-sized groups stream weights: gemm2 takes 128-column tiles there, twice as many
+  // workgroups over the same bytes, so the last round of tiles is not half empty
+  const int bn = (!SWIGLU && bm == 16) ? 128 : 256;
+  const int ntiles = SWIGLU ? ceil_div(a.I, 128) : ceil_div(a.N, bn);
   const long total = static_cast<long>(max_tiles) * ntiles;
   const int grid = static_cast<int>((total + 7) / 8 * 8);
   if (bm == 256) {
@@ -837,7 +848,10 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
   }
   switch (bm) {
     case 16:
-      grouped_gemm_kernel<16, 256, 1, 4, SWIGLU, 4><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+      if constexpr (SWIGLU)
+        grouped_gemm_kernel<16, 256, 1, 4, true, 4><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+      else
+        grouped_gemm_kernel<16, 128, 1, 4, false, 4><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
       break;
     case 64:
       grouped_gemm_kernel<64, 256, 1, 4, SWIGLU, 3><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);

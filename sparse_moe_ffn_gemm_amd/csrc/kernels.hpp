@@ -41,6 +41,7 @@ void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int 
 // ---- grouped FP8 GEMMs ----
 struct GemmArgs {
   const uint8_t* A;          // gemm1: xq [T, K] (rows gathered through perm); gemm2: h [rows, K]
+  int A_rows;                // rows of A (T for gemm1, T * top_k for gemm2)
   const float* A_scale;      // [*, ceil(K/128)]
   const int32_t* perm;       // gemm1 only
   int top_k;
@@ -54,7 +55,7 @@ struct GemmArgs {
   int K, N, I;
   uint8_t* h_out;            // gemm1: [rows, I]
   float* h_scale;            // gemm1: [rows, ceil(I/128)]
-  float* y_out;              // gemm2: [rows, N]
+  uint16_t* y_out;           // gemm2: [rows, N] fp16
 };
 
 // Rows per M-tile chosen for a layer with `rows` routed rows over E experts.
@@ -63,7 +64,7 @@ void launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
 void launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
 
 // ---- combine ----
-void launch_combine(const float* y, const float* gates, const int32_t* inv, int T, int H,
+void launch_combine(const uint16_t* y, const float* gates, const int32_t* inv, int T, int H,
                     int top_k, uint16_t* out, hipStream_t st);
 
 }  // namespace moe

@@ -42,7 +42,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   const int tiles2d = ceil_div(T, moe::kRouterTile) * ceil_div(E, moe::kRouterTile);
   int ks = ceil_div(1024, tiles2d);
   ks = std::max(1, std::min(ks, H / 128 > 0 ? H / 128 : 1));
-  p->kslice = ceil_div(ceil_div(H, ks), 32) * 32;
+  p->kslice = ceil_div(ceil_div(H, ks), 64) * 64;
   p->ksplit = ceil_div(H, p->kslice);
   p->nchunks = ceil_div(T, moe::kChunk);
   p->bm = moe::gemm_tile_rows(p->rows, E);
@@ -69,7 +69,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   p->sx = take(sizeof(float) * static_cast<size_t>(T) * ceil_div(H, moe::kBlock));
   p->h = take(static_cast<size_t>(p->rows) * I);
   p->sh = take(sizeof(float) * static_cast<size_t>(p->rows) * ceil_div(I, moe::kBlock));
-  p->y = take(sizeof(float) * static_cast<size_t>(p->rows) * H);
+  p->y = take(sizeof(uint16_t) * static_cast<size_t>(p->rows) * H);
   p->total = off;
 }
 
@@ -157,6 +157,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
 
   moe::GemmArgs g1{};
   g1.A = at<uint8_t>(ws, p.xq);
+  g1.A_rows = T;
   g1.A_scale = at<float>(ws, p.sx);
   g1.perm = tb.perm;
   g1.top_k = top_k;
@@ -177,6 +178,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
 
   moe::GemmArgs g2{};
   g2.A = at<uint8_t>(ws, p.h);
+  g2.A_rows = static_cast<int>(p.rows);
   g2.A_scale = at<float>(ws, p.sh);
   g2.perm = nullptr;
   g2.top_k = top_k;
@@ -190,10 +192,10 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.K = I;
   g2.N = H;
   g2.I = I;
-  g2.y_out = at<float>(ws, p.y);
+  g2.y_out = at<uint16_t>(ws, p.y);
   moe::launch_gemm2(g2, p.bm, p.max_tiles, st);
   mark(ev, 7, st);
-  moe::launch_combine(at<float>(ws, p.y), tb.gates, tb.inv, T, H, top_k, out, st);
+  moe::launch_combine(at<uint16_t>(ws, p.y), tb.gates, tb.inv, T, H, top_k, out, st);
   mark(ev, 8, st);
   return finish();
 }

@@ -64,27 +64,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __res
   const int kb = live ? static_cast<int>(g % KB) : 0;
   const int col = kb * kBlock + sub * 8;
   const bool in = live && col < H;
-  float f[8];
-  float amax = 0.0f;
-  if (in) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + t * H + col);
-    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_to_f32(static_cast<uint16_t>(wds[i] & 0xFFFFu));
-      f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(wds[i] >> 16));
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  }
-  amax = group_max<16>(amax);
-  const float s = group_scale(amax);
-  if (in) {
-    uint2 q;
-    q.x = encode4(f[0], f[1], f[2], f[3], s);
-    q.y = encode4(f[4], f[5], f[6], f[7], s);
-    *reinterpret_cast<uint2*>(codes + t * H + col) = q;
-  }
+  const float s = quantize_group16(x + t * H, col, in, codes + t * H);
   if (live && sub == 0) scales[g] = s;
 }
 

@@ -18,12 +18,24 @@ namespace moe {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------------------------
-// logits partials on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): products and
-// sums in fp32.  Workgroup tile 64 tokens x 64 experts, 4 waves of 32x32; grid.z
-// splits H so that small-T (decode) layers still spread over many CUs.
+// logits partials on the bf16 matrix cores with fp32 accumulation, exactly as in fp32:
+// x is bf16 already, and every fp32 weight w is split by truncation into three bf16
+// parts w = hi + mid + lo (8 + 8 + 8 significant bits, no rounding anywhere), so each
+// product x * part is exact in fp32 and x . w = x . hi + x . mid + x . lo is summed in
+// fp32 by v_mfma_f32_16x16x32_bf16 (three times the products of an fp32 GEMM at eight
+// times the fp32 matrix rate).  Workgroup tile 64 tokens x 64 experts, 4 waves of
+// 32 x 32; grid.z splits H so that small-T (decode) layers still spread over many CUs.
+// The matrix cores accumulate 128 columns at a time into `acc`, folded into `tot`, so no
+// long running sum absorbs small terms.
 // ------------------------------------------------------------------------------------
-constexpr int kRC = 32;           // H columns staged per step
-constexpr int kRS = kRC + 4;      // padded LDS row (floats)
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+constexpr int kRC = 64;           // H columns staged per step
+constexpr int kRS = kRC + 8;      // padded LDS row (bf16): 144-byte rows spread the banks
+
+__device__ __forceinline__ v8bf lds_bf8(const uint16_t* p) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(v8bf, u);
+}
 
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ W, int T,
@@ -31,8 +43,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             float* __restrict__ partial,
                                                             int32_t* __restrict__ hist,
                                                             int hist_n) {
-  __shared__ __align__(16) float xs[kRouterTile * kRS];
-  __shared__ __align__(16) float ws[kRouterTile * kRS];
+  __shared__ __align__(16) uint16_t xs[kRouterTile * kRS];
+  __shared__ __align__(16) uint16_t wp[3][kRouterTile * kRS];   // hi, mid, lo parts of W
   {  // clear the dispatch histograms that the top-k step accumulates (a slice per block)
     const int nb = gridDim.x * gridDim.y * gridDim.z;
     const int bid = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
@@ -45,8 +57,6 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   const int h_end = min(H, h_begin + kslice);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  // Two-level fp32 sum: the matrix cores accumulate 128 columns at a time into `acc`,
-  // which is then folded into `tot`, so no long running sum absorbs small terms.
   v4f acc[2][2], tot[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -54,50 +64,60 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     for (int j = 0; j < 2; ++j) acc[i][j] = tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int h0 = h_begin; h0 < h_end; h0 += kRC) {
-    {  // x: 64 rows x 32 bf16 = 4 chunks of 8 per row, one chunk per lane
-      const int row = tid >> 2, c = tid & 3;
-      const int t = t0 + row, h = h0 + c * 8;
-      float f[8];
-      if (t < T && h < h_end) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + h);
-        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[2 * i] = bf16_to_f32(static_cast<uint16_t>(wd[i] & 0xFFFFu));
-          f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(wd[i] >> 16));
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = 0.f;
-      }
-      float4* d = reinterpret_cast<float4*>(xs + row * kRS + c * 8);
-      d[0] = make_float4(f[0], f[1], f[2], f[3]);
-      d[1] = make_float4(f[4], f[5], f[6], f[7]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {  // W: 64 rows x 32 floats = 8 float4 per row
+    for (int i = 0; i < 2; ++i) {   // x: 64 rows x 64 bf16 = 8 chunks of 8 per row
       const int q = tid + 256 * i;
       const int row = q >> 3, c = q & 7;
+      const int t = t0 + row, h = h0 + c * 8;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (t < T && h < h_end) v = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + h);
+      *reinterpret_cast<uint4*>(xs + row * kRS + c * 8) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // W: 64 rows x 64 floats = 16 float4 per row, split in 3
+      const int q = tid + 256 * i;
+      const int row = q >> 4, c = q & 15;
       const int e = e0 + row, h = h0 + c * 4;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e < E && h < h_end) v = *reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + h);
-      *reinterpret_cast<float4*>(ws + row * kRS + c * 4) = v;
+      const float w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t ph[2] = {0u, 0u}, pm[2] = {0u, 0u}, pl[2] = {0u, 0u};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t u = __float_as_uint(w[k]);
+        const float hi = __uint_as_float(u & 0xFFFF0000u);
+        const float r1 = w[k] - hi;                                  // exact
+        const uint32_t um = __float_as_uint(r1);
+        const float mid = __uint_as_float(um & 0xFFFF0000u);
+        const float lo = r1 - mid;                                   // exact, <= 8 bits
+        ph[k >> 1] |= (u >> 16) << (16 * (k & 1));
+        pm[k >> 1] |= (um >> 16) << (16 * (k & 1));
+        pl[k >> 1] |= (__float_as_uint(lo) >> 16) << (16 * (k & 1));
+      }
+      *reinterpret_cast<uint2*>(&wp[0][row * kRS + c * 4]) = make_uint2(ph[0], ph[1]);
+      *reinterpret_cast<uint2*>(&wp[1][row * kRS + c * 4]) = make_uint2(pm[0], pm[1]);
+      *reinterpret_cast<uint2*>(&wp[2][row * kRS + c * 4]) = make_uint2(pl[0], pl[1]);
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < kRC; kk += 4) {
-      float a[2], b[2];
+    for (int kk = 0; kk < kRC; kk += 32) {
+      const int kofs = kk + 8 * (lane >> 4);
+      v8bf a[2], b[3][2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = xs[(wm * 32 + 16 * i + (lane & 15)) * kRS + kk + (lane >> 4)];
+      for (int i = 0; i < 2; ++i) a[i] = lds_bf8(xs + (wm * 32 + 16 * i + (lane & 15)) * kRS + kofs);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = ws[(wn * 32 + 16 * j + (lane & 15)) * kRS + kk + (lane >> 4)];
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[p][j] = lds_bf8(&wp[p][(wn * 32 + 16 * j + (lane & 15)) * kRS + kofs]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[p][j], acc[i][j], 0, 0, 0);
     }
-    if (((h0 - h_begin) / kRC) % 4 == 3 || h0 + kRC >= h_end) {
+    if (((h0 - h_begin) / kRC) % 2 == 1 || h0 + kRC >= h_end) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -135,22 +155,28 @@ __device__ __forceinline__ void argmax_step(float& v, int& idx, int off) {
   }
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int ksplit,
-                                                   const float* __restrict__ bias, int T, int E,
-                                                   int top_k, int32_t* __restrict__ ids,
-                                                   float* __restrict__ gates,
-                                                   int32_t* __restrict__ hist) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+// Top-k of token t for the calling wave: the k selected experts (descending logit, ties
+// to the lower index) and their softmax gates, valid in lanes [0, top_k) as (id, gate) of
+// rank j = lane.  Logits are the router partial sums over H slices plus the bias.
+__device__ __forceinline__ void topk_token(const float* __restrict__ partial, int ksplit,
+                                           const float* __restrict__ bias, int T, int E, int top_k,
+                                           int t, int lane, int* id_out, float* gate_out) {
   const size_t TE = static_cast<size_t>(T) * E;
   float v[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
     if (e < E) {
-      float s = 0.f;
-      for (int sp = 0; sp < ksplit; ++sp) s += partial[sp * TE + static_cast<size_t>(t) * E + e];
+      // four independent partial sums so that the slice loads are in flight together
+      const float* src = partial + static_cast<size_t>(t) * E + e;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      int sp = 0;
+      for (; sp + 4 <= ksplit; sp += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s4[u] += src[(sp + u) * TE];
+      }
+      for (; sp < ksplit; ++sp) s4[0] += src[sp * TE];
+      float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       s += bias ? bias[e] : 0.f;
       v[q] = s == s ? s : -INFINITY;   // a NaN logit never wins
     } else {
@@ -190,14 +216,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     z[j] = j < top_k ? expf(sel_v[j] - sel_v[0]) : 0.f;
     sum += z[j];
   }
-  int32_t* h = hist + static_cast<size_t>(t / kChunk) * E;
+  *id_out = 0;
+  *gate_out = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    if (j < top_k && lane == j) {
-      ids[static_cast<size_t>(t) * top_k + j] = sel_i[j];
-      gates[static_cast<size_t>(t) * top_k + j] = z[j] / sum;
-      atomicAdd(&h[sel_i[j]], 1);
+    if (lane == j) {
+      *id_out = sel_i[j];
+      *gate_out = z[j] / sum;
     }
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int ksplit,
+                                                   const float* __restrict__ bias, int T, int E,
+                                                   int top_k, int32_t* __restrict__ ids,
+                                                   float* __restrict__ gates,
+                                                   int32_t* __restrict__ hist) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int id;
+  float g;
+  topk_token(partial, ksplit, bias, T, E, top_k, t, lane, &id, &g);
+  if (lane < top_k) {
+    ids[static_cast<size_t>(t) * top_k + lane] = id;
+    gates[static_cast<size_t>(t) * top_k + lane] = g;
+    atomicAdd(&hist[static_cast<size_t>(t / kChunk) * E + id], 1);
+  }
 }
 
 // ------------------------------------------------------------------------------------
