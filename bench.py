@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt-oss-120b-prefill")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
