@@ -55,7 +55,7 @@ def algorithmic(shape, counts):
         active_experts=active,
         layer_flops=g1_flops + g2_flops, layer_bytes=layer_bytes,
         gemm1=dict(flops=g1_flops, bytes=w13 + xq + hq),
-        gemm2=dict(flops=g2_flops, bytes=w2 + hq + rows * H * 4))
+        gemm2=dict(flops=g2_flops, bytes=w2 + hq + rows * H * 2))
 
 
 def traffic_from_profiles(workload, kernel):

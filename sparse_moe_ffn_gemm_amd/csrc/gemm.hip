@@ -455,24 +455,25 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
 // in the same lane.  The weight scale is taken per 16-column sub-tile (a sub-tile never
 // straddles a 128-row scale block since I is a multiple of 64).
 // ------------------------------------------------------------------------------------
-template <bool SWIGLU, int BN, int SA, int SB>
-__global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int max_tiles,
-                                                               int ntiles, int grid) {
-  constexpr int BM = 256, WN = 2;
+template <bool SWIGLU, int BN, int SA, int SB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const GemmArgs a, int max_tiles,
+                                                                      int ntiles, int grid) {
+  constexpr int NT = WAVES * 64, BM = 64 * (WAVES / 2), WN = 2;
   constexpr int SM = 4, SN = BN / 32;                // sub-tiles per wave
   constexpr int NG = SN / 2, GW = BN / 4;            // gemm1: gate sub-tiles / columns per wave
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  constexpr int A_ROWS = BM / 8, B_ROWS = BN / 8;    // rows each wave fetches per step
+  constexpr int A_ROWS = BM / WAVES, B_ROWS = BN / WAVES;   // rows each wave fetches per step
   constexpr int A_INSTR = A_ROWS / 8, B_INSTR = B_ROWS / 8;
   static_assert(BN % 64 == 0 && (!SWIGLU || SN % 2 == 0), "tile");
   static_assert(SA >= 2 && SB >= SA, "rings");
-  static_assert(2 * SN <= 32, "scale lanes");
+  static_assert(2 * SN <= 32 && A_ROWS == 32, "scale lanes");
+  static_assert(WAVES == 4 || WAVES == 8, "waves");
 
   __shared__ __align__(16) uint8_t ringA[SA * A_BYTES];
   __shared__ __align__(16) uint8_t ringB[SB * B_BYTES];
   // per A slot and wave: lanes [0, 32) the activation scales of the wave's A rows,
   // [32, 32 + 2 SN) the weight block scales of sub-tile n of column wave wn (wn SN + n)
-  __shared__ __align__(16) float sS[SA][8][64];
+  __shared__ __align__(16) float sS[SA][WAVES][64];
   __shared__ int rowsrc[BM];
   __shared__ float red[WN][BM];
   __shared__ __align__(16) uint16_t sbias[BN];      // bias of the tile's B rows (bf16)
@@ -513,7 +514,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
   const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * K;
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
 
-  for (int r = tid; r < BM; r += 512) {
+  for (int r = tid; r < BM; r += NT) {
     const int p = mt.row_begin + r;
     int src = -1;
     if (p < mt.row_end) src = SWIGLU ? a.perm[p] / a.top_k : p;
@@ -622,12 +623,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
   {  // the tile's bias, staged with the first loads: wave w fetches B rows [w BN/8, (w+1) BN/8)
-    const int br = wave * (BN / 8) + 2 * lane;
+    const int br = wave * (BN / WAVES) + 2 * lane;
     const int g = b_global_row(br);
     const void* src = (a.bias != nullptr && g >= 0)
                           ? static_cast<const void*>(a.bias + static_cast<size_t>(e) * N + g)
                           : static_cast<const void*>(kZeroChunk);
-    if (lane < BN / 16) load_lds4(src, &sbias[wave * (BN / 8)]);
+    if (lane < BN / (2 * WAVES)) load_lds4(src, &sbias[wave * (BN / WAVES)]);
   }
   // prologue: B runs SB-1 steps ahead, A SA-1; within a step the A loads are issued
   // before the B loads of the later step, so "A(k) and B(k) landed" is "at most the B
@@ -841,9 +842,9 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
     const long tot = static_cast<long>(max_tiles) * nt_big;
     const int g = static_cast<int>((tot + 7) / 8 * 8);
     if constexpr (SWIGLU)
-      grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
+      grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, 8><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
     else
-      grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
+      grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, 8><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
     return;
   }
   switch (bm) {
