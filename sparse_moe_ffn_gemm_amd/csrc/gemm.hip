@@ -36,7 +36,13 @@
 //   in the same lane; the epilogue adds b13, applies silu(gate)*up and requantises
 //   each 1x128 group of h (row amax across lanes and waves) to e4m3.
 // gemm2: rows of h in dispatch order, B = w2 [H, I]; the epilogue adds b2 and stores
-//   y in fp32.
+//   y in fp16 (saturated).
+//
+// Kernels by group size (rows per expert): 256-row tiles over eight waves for prefill
+// (grouped_gemm_big_kernel), 16/64/128-row tiles over four waves through one LDS ring
+// (grouped_gemm_kernel), and for decode-sized groups whose weight rows are not whole
+// cache lines, a barrier-free register stream in long per-row runs
+// (grouped_gemm_rowrun_kernel).
 #include "kernels.hpp"
 
 namespace moe {
@@ -92,6 +98,43 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Which (n-tile, M-tile) this workgroup computes: expert-major order (an expert's M-tiles
+// fastest, then its n-tiles), cut into eight contiguous ranges, one per XCD (blocks are
+// dealt to the XCDs round-robin), so the concurrent workgroups of an XCD share the
+// expert's activation rows across n-tiles and each weight tile across the expert's
+// M-tiles in their L2.  False for blocks past the device-side tile count.
+__device__ __forceinline__ bool pick_tile(const GemmArgs& a, int ntiles, int& nt, MTile& mt) {
+  const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
+  const int per_xcd = (total + 7) / 8;
+  const int b = blockIdx.x;
+  if (b / 8 >= per_xcd) return false;
+  const int L = (b % 8) * per_xcd + b / 8;
+  if (L >= total) return false;
+  // the expert e with off[e] * ntiles <= L < off[e+1] * ntiles: off is non-decreasing, so
+  // e + 1 is the number of experts with off[e] * ntiles <= L, counted by ballots over one
+  // round of independent loads (E <= 256)
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+#pragma unroll
+  for (int base = 0; base < 256; base += 64) {
+    if (base < a.E) {
+      const int idx = base + lane;
+      const bool le = idx < a.E && a.expert_tile_off[idx] * ntiles <= L;
+      cnt += __builtin_popcountll(__ballot(le));
+    }
+  }
+  const int lo = __builtin_amdgcn_readfirstlane(cnt - 1);
+  const int t0 = a.expert_tile_off[lo];
+  const int mcount = a.expert_tile_off[lo + 1] - t0;
+  const int local = L - t0 * ntiles;
+  nt = local / mcount;
+  mt = a.tiles[t0 + local % mcount];
+  mt.expert = __builtin_amdgcn_readfirstlane(mt.expert);
+  mt.row_begin = __builtin_amdgcn_readfirstlane(mt.row_begin);
+  mt.row_end = __builtin_amdgcn_readfirstlane(mt.row_end);
+  return true;
 }
 
 // Workgroup barrier without the memory fences of __syncthreads (the ring's loads are
@@ -478,29 +521,9 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
   __shared__ float red[WN][BM];
   __shared__ __align__(16) uint16_t sbias[BN];      // bias of the tile's B rows (bf16)
 
-  // ---- which tile: expert-major order (an expert's M-tiles fastest, then its n-tiles),
-  // cut into eight contiguous ranges, one per XCD (blocks are dealt to the XCDs round-
-  // robin): the concurrent workgroups of an XCD share the expert's activation rows
-  // across n-tiles and each weight tile across the expert's M-tiles in their L2 ----
-  const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
-  const int per_xcd = (total + 7) / 8;
-  const int b = blockIdx.x;
-  if (b / 8 >= per_xcd) return;
-  const int L = (b % 8) * per_xcd + b / 8;
-  if (L >= total) return;
-  int lo = 0, hi = a.E;                      // the expert e with off[e] * ntiles <= L < off[e+1] * ntiles
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.expert_tile_off[mid] * ntiles <= L) lo = mid; else hi = mid;
-  }
-  const int t0 = a.expert_tile_off[lo];
-  const int mcount = a.expert_tile_off[lo + 1] - t0;
-  const int local = L - t0 * ntiles;
-  const int nt = local / mcount;
-  MTile mt = a.tiles[t0 + local % mcount];
-  mt.expert = __builtin_amdgcn_readfirstlane(mt.expert);
-  mt.row_begin = __builtin_amdgcn_readfirstlane(mt.row_begin);
-  mt.row_end = __builtin_amdgcn_readfirstlane(mt.row_end);
+  int nt;
+  MTile mt;
+  if (!pick_tile(a, ntiles, nt, mt)) return;
   (void)max_tiles;
   (void)grid;
 
@@ -816,9 +839,234 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Row-run streaming variant for decode-sized groups (M-tiles of at most 16 rows), the
+// HBM-bound case: every weight byte feeds only the tile's 16 rows.  The weight stream
+// is laid out for DRAM locality: HBM throughput of a read stream grows with the
+// contiguous run fetched from each weight row at a time (measured with register loads
+// over rows of 2880 bytes: about 4.1 TB/s for 128-byte runs, 5.4 TB/s for 512 and
+// 6.4 TB/s for about 1 KB).  So each wave owns ONE 16-row weight sub-tile and walks its
+// rows in bursts of KS K-blocks (KS x 128 contiguous bytes per row), two bursts in
+// flight in registers, with no barrier in the K loop.  The tile's 16 activation rows
+// (all of K) and their scales are staged in LDS once, fetched while the first weight
+// bursts are in flight.
+//
+// A workgroup is eight waves over 16 rows x 128 output columns, wave w taking columns
+// [16w, 16w+16).  gemm1: the wave streams the 16 gate rows and then the 16 matching up
+// rows of w13, so each lane ends with the gate and up sums of the same four columns
+// and the workgroup's 128 columns are exactly one 1x128 group of h.  gemm2: the wave
+// streams 16 rows of w2.  All sixteen rows of a sub-tile share one 128-row scale block.
+//
+// K tail (K a multiple of 64): the staged activation tile holds zeros past K, and the
+// weight fragment's upper half re-reads its lower half in a half-filled last block, so
+// the extra products vanish.  Bursts padded past the last K-block re-read that block
+// (L2 hits) and are scaled by zero.  Rows past the tile's end are staged from its first
+// row; their outputs are never stored.
+// ------------------------------------------------------------------------------------
+template <bool SWIGLU, int KS>
+__global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs a, int ntiles) {
+  constexpr int WAVES = 8;
+  constexpr int NSUB = SWIGLU ? 2 : 1;       // weight sub-tiles per wave (gate, up)
+  extern __shared__ __align__(16) uint8_t dyn_lds[];
+
+  int nt;
+  MTile mt;
+  if (!pick_tile(a, ntiles, nt, mt)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = a.K, N = a.N, I = a.I;
+  const int KB = ceil_div(K, kBlock), NBs = ceil_div(N, kBlock);
+  const int e = mt.expert;
+  const int r = lane & 15, g = lane >> 4;
+  // LDS: activation tile [KB][16][128] (chunk-swizzled rows), its scales [KB4][16]
+  // (KB rounded up to the 4 blocks one scale fetch covers), and the gemm1 row-amax
+  // exchange [8][16]
+  uint8_t* sA = dyn_lds;
+  float* sSa = reinterpret_cast<float*>(dyn_lds + KB * 2048);
+  float* red = sSa + ceil_div(KB, 4) * 64;
+
+  const int c0 = nt * 128 + 16 * wave;       // the wave's first output column
+  const bool live = c0 < (SWIGLU ? I : N);   // I, N multiples of 64: all 16 or none
+
+  // ---- the wave's weight stream: sub-tile s, K-block j, in bursts of KS blocks ----
+  const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * K;
+  const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
+  const int bps = ceil_div(KB, KS);          // bursts per sub-tile
+  const int nb = NSUB * bps;                 // bursts of the wave
+  const int nbp = (nb + 1) & ~1;             // padded to the two-slot ring
+  unsigned b_off[NSUB];
+  float sbg[NSUB];                           // lane j: weight block scale of K-block j
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int row = (SWIGLU && s == 1 ? I : 0) + c0 + r;
+    b_off[s] = static_cast<unsigned>(row) * K + 16 * g;
+    const int brow = ((SWIGLU && s == 1 ? I : 0) + c0) / kBlock;
+    sbg[s] = (live && lane < KB) ? Bsc[static_cast<size_t>(brow) * KB + lane] : 0.f;
+  }
+
+  v8i ring[2][KS];
+  auto issue = [&](int b, v8i (&bq)[KS]) {
+    const int bb = b < nb ? b : nb - 1;
+    const int s = bb / bps, j0 = (bb % bps) * KS;
+    const unsigned bo = (NSUB == 2 && s == 1) ? b_off[NSUB - 1] : b_off[0];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int jj = j0 + t < KB ? j0 + t : KB - 1;
+      const unsigned hoff = (jj + 1) * kBlock <= K ? 64u : 0u;   // half block: re-read chunks 0-3
+      const uint8_t* base = Bexp + jj * kBlock;
+      const uint4 lo = *reinterpret_cast<const uint4*>(base + bo);
+      const uint4 hi = *reinterpret_cast<const uint4*>(base + hoff + bo);
+      bq[t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  };
+  v4f acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int b, const v8i (&bq)[KS]) {
+    const bool bl = b < nb;
+    const int bb = bl ? b : nb - 1;
+    const int s = bb / bps, j0 = (bb % bps) * KS;
+    const float sbs = (NSUB == 2 && s == 1) ? sbg[NSUB - 1] : sbg[0];
+    v4f pr[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int jj = j0 + t < KB ? j0 + t : KB - 1;
+      const v8i af = lds_frag(sA + jj * 2048, r, g);
+      pr[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[t], af, zero, 0, 0, 0, 0, 0, 0);
+    }
+    v4f part = zero;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int j = j0 + t;
+      const int jj = j < KB ? j : KB - 1;
+      const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbs), jj));
+      const float sc = (bl && j < KB) ? sSa[jj * 16 + r] * sb : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[i] = fmaf(pr[t][i], sc, part[i]);
+    }
+    if (NSUB == 2 && s == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[NSUB - 1][i] += part[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[0][i] += part[i];
+    }
+  };
+
+  // the first two weight bursts go out before the activation rows are even located
+  if (live) {
+    issue(0, ring[0]);
+    issue(1, ring[1]);
+  }
+  // ---- stage the activation tile and its scales (all waves share the fetches) ----
+  auto src_row = [&](int rr) {
+    const int q = mt.row_begin + rr < mt.row_end ? mt.row_begin + rr : mt.row_begin;
+    const int s = SWIGLU ? a.perm[q] / a.top_k : q;
+    return static_cast<unsigned>(s) < static_cast<unsigned>(a.A_rows) ? s : 0;   // never read past A
+  };
+  {
+    // fetch q: block q >> 1, rows 8 (q & 1) .. +8; lane -> row 8 (q & 1) + (lane >> 3),
+    // LDS slot lane & 7 holding global chunk slot ^ (row & 7)
+    const int rq = lane >> 3, slot = lane & 7;
+    const unsigned off0 = static_cast<unsigned>(src_row(rq)) * K;
+    const unsigned off1 = static_cast<unsigned>(src_row(8 + rq)) * K;
+    for (int q = wave; q < 2 * KB; q += WAVES) {
+      const int j = q >> 1, row = 8 * (q & 1) + rq;
+      const int kk = j * kBlock + ((slot ^ swz_key(row)) << 4);
+      const void* src = kk < K ? static_cast<const void*>(a.A + ((q & 1) ? off1 : off0) + kk)
+                               : static_cast<const void*>(kZeroChunk);
+      load_lds16(src, sA + j * 2048 + 8 * (q & 1) * 128);
+    }
+    // scales: fetch q covers blocks 4q .. 4q+3, lane -> block 4q + (lane >> 4), row lane & 15
+    const unsigned so = static_cast<unsigned>(src_row(r)) * KB;
+    for (int q = wave; q < ceil_div(KB, 4); q += WAVES) {
+      const int j = 4 * q + g;
+      const void* src = j < KB ? static_cast<const void*>(a.A_scale + so + j) : static_cast<const void*>(kZeroScale);
+      load_lds4(src, sSa + 64 * q);
+    }
+  }
+
+  wait_vmcnt<0>();   // this wave's staging fetches (and its first bursts) have landed ...
+  __syncthreads();   // ... and so have every wave's
+
+  if (live) {
+    for (int b0 = 0; b0 < nbp - 2; b0 += 2) {
+      compute(b0, ring[0]);
+      issue(b0 + 2, ring[0]);
+      compute(b0 + 1, ring[1]);
+      issue(b0 + 3, ring[1]);
+    }
+    compute(nbp - 2, ring[0]);
+    compute(nbp - 1, ring[1]);
+  }
+
+  // ---- epilogue: lane holds row r and the four columns c0 + 4g + i ----
+  const int p = mt.row_begin + r;
+  const int cq = c0 + 4 * g;
+  const uint16_t* bias = a.bias ? a.bias + static_cast<size_t>(e) * N : nullptr;
+  if constexpr (SWIGLU) {
+    const int KBI = ceil_div(I, kBlock);
+    float hv[4];
+    float mx = 0.f;
+    float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live && bias) {
+      const uint2 g2 = *reinterpret_cast<const uint2*>(bias + cq);
+      const uint2 u2 = *reinterpret_cast<const uint2*>(bias + I + cq);
+      bg[0] = __uint_as_float(g2.x << 16); bg[1] = __uint_as_float(g2.x & 0xFFFF0000u);
+      bg[2] = __uint_as_float(g2.y << 16); bg[3] = __uint_as_float(g2.y & 0xFFFF0000u);
+      bu[0] = __uint_as_float(u2.x << 16); bu[1] = __uint_as_float(u2.x & 0xFFFF0000u);
+      bu[2] = __uint_as_float(u2.y << 16); bu[3] = __uint_as_float(u2.y & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gv = acc[0][i] + bg[i];
+      const float uv = acc[NSUB - 1][i] + bu[i];
+      const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+      hv[i] = live ? h : 0.f;
+      mx = fmaxf(mx, fabsf(hv[i]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (lane < 16) red[wave * 16 + lane] = mx;
+    __syncthreads();
+    if (!live || p >= mt.row_end) return;
+    float amax = red[r];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) amax = fmaxf(amax, red[w * 16 + r]);
+    const float sc = group_scale(amax);
+    const float rs = __builtin_amdgcn_rcpf(sc);   // quotient: reciprocal plus one correction
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q0 = hv[i] * rs;
+      const float q1 = fmaf(fmaf(-q0, sc, hv[i]), rs, q0);
+      q[i] = fminf(fmaxf(q1, -kFp8Max), kFp8Max);
+    }
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false)) & 0xFFFFu;
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], 0, false)) & 0xFFFFu;
+    *reinterpret_cast<uint32_t*>(a.h_out + static_cast<size_t>(p) * I + cq) = lo | (hi << 16);
+    if (wave == 0 && lane < 16) a.h_scale[static_cast<size_t>(p) * KBI + nt] = sc;
+  } else {
+    if (!live || p >= mt.row_end) return;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      const uint2 b2 = *reinterpret_cast<const uint2*>(bias + cq);
+      bv[0] = __uint_as_float(b2.x << 16); bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+      bv[2] = __uint_as_float(b2.y << 16); bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+    }
+    *reinterpret_cast<uint2*>(a.y_out + static_cast<size_t>(p) * N + cq) = make_uint2(
+        f32_to_f16_sat(acc[0][0] + bv[0]) | (static_cast<uint32_t>(f32_to_f16_sat(acc[0][1] + bv[1])) << 16),
+        f32_to_f16_sat(acc[0][2] + bv[2]) | (static_cast<uint32_t>(f32_to_f16_sat(acc[0][3] + bv[3])) << 16));
+  }
+}
+
 // Large-group launch shapes (workgroup tile 256 x BN, A / B ring depths).
 constexpr int kG1BN = 256, kG1SA = 2, kG1SB = 2;
 constexpr int kG2BN = 192, kG2SA = 2, kG2SB = 3;
+// Dynamic LDS of the row-run kernel at its largest K (64 blocks).
+constexpr int kRowrunMaxLds = 64 * 2048 + 16 * 256 + 8 * 16 * 4;
 
 int gemm_tile_rows(long rows, int E) {
   const long avg = rows / (E > 0 ? E : 1);
@@ -846,6 +1094,25 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
     else
       grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, 8><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
     return;
+  }
+  // Decode-sized groups whose weight rows are not whole 128-byte lines (K = 64 mod 128,
+  // so every other row starts mid-line and each 128-byte block of it spans two lines):
+  // the row-run kernel, which fetches 64-byte pieces (always within one line) in long
+  // per-row runs.  Rows that are whole lines stream faster through the LDS ring below.
+  const int KB = ceil_div(a.K, kBlock);
+  if (bm == 16 && a.K % kBlock != 0 && KB <= 64) {
+    constexpr int KS = 4;
+    const int nts = ceil_div(SWIGLU ? a.I : a.N, 128);
+    const int g = static_cast<int>((static_cast<long>(max_tiles) * nts + 7) / 8 * 8);
+    const size_t lds = static_cast<size_t>(KB) * 2048 + ceil_div(KB, 4) * 256 + 8 * 16 * 4;
+    // above 64 KB of dynamic LDS a kernel must opt in (once per process)
+    static const bool lds_ok =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, KS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
+    if (lds <= 64 * 1024 || lds_ok) {
+      grouped_gemm_rowrun_kernel<SWIGLU, KS><<<g, 512, lds, st>>>(a, nts);
+      return;
+    }
   }
   switch (bm) {
     case 16:

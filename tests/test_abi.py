@@ -47,7 +47,7 @@ def test_workspace_bytes_envelope(shape, ok):
         r = moe.workspace_layout(*shape)
         assert r.total == n
         T, H, E, k, I = shape
-        assert r.y + 4 * T * k * H <= n and r.xq % 256 == 0 and r.y % 256 == 0
+        assert r.y + 2 * T * k * H <= n and r.xq % 256 == 0 and r.y % 256 == 0
 
 
 def _fwd(L, **kw):
