@@ -43,6 +43,8 @@
 // (grouped_gemm_kernel), and for decode-sized groups whose weight rows are not whole
 // cache lines, a barrier-free register stream in long per-row runs
 // (grouped_gemm_rowrun_kernel).
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace moe {
@@ -100,21 +102,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// Which (n-tile, M-tile) this workgroup computes: expert-major order (an expert's M-tiles
-// fastest, then its n-tiles), cut into eight contiguous ranges, one per XCD (blocks are
-// dealt to the XCDs round-robin), so the concurrent workgroups of an XCD share the
-// expert's activation rows across n-tiles and each weight tile across the expert's
-// M-tiles in their L2.  False for blocks past the device-side tile count.
-__device__ __forceinline__ bool pick_tile(const GemmArgs& a, int ntiles, int& nt, MTile& mt) {
-  const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
-  const int per_xcd = (total + 7) / 8;
-  const int b = blockIdx.x;
-  if (b / 8 >= per_xcd) return false;
-  const int L = (b % 8) * per_xcd + b / 8;
-  if (L >= total) return false;
-  // the expert e with off[e] * ntiles <= L < off[e+1] * ntiles: off is non-decreasing, so
-  // e + 1 is the number of experts with off[e] * ntiles <= L, counted by ballots over one
-  // round of independent loads (E <= 256)
+// Tile L of the expert-major order (an expert's M-tiles fastest, then its n-tiles) of
+// `ntiles` n-tiles per M-tile.  The expert e with off[e] * ntiles <= L < off[e+1] * ntiles:
+// off is non-decreasing, so e + 1 is the number of experts with off[e] * ntiles <= L,
+// counted by ballots over one round of independent loads (E <= 256).
+__device__ __forceinline__ void tile_of(const GemmArgs& a, int ntiles, int L, int& nt, MTile& mt) {
   const int lane = threadIdx.x & 63;
   int cnt = 0;
 #pragma unroll
@@ -134,6 +126,21 @@ __device__ __forceinline__ bool pick_tile(const GemmArgs& a, int ntiles, int& nt
   mt.expert = __builtin_amdgcn_readfirstlane(mt.expert);
   mt.row_begin = __builtin_amdgcn_readfirstlane(mt.row_begin);
   mt.row_end = __builtin_amdgcn_readfirstlane(mt.row_end);
+}
+
+// Which tile this workgroup of a one-tile-per-workgroup launch computes: the expert-major
+// order cut into eight contiguous ranges, one per XCD (blocks are dealt to the XCDs round-
+// robin), so the concurrent workgroups of an XCD share the expert's activation rows
+// across n-tiles and each weight tile across the expert's M-tiles in their L2.  False
+// for blocks past the device-side tile count.
+__device__ __forceinline__ bool pick_tile(const GemmArgs& a, int ntiles, int& nt, MTile& mt) {
+  const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
+  const int per_xcd = (total + 7) / 8;
+  const int b = blockIdx.x;
+  if (b / 8 >= per_xcd) return false;
+  const int L = (b % 8) * per_xcd + b / 8;
+  if (L >= total) return false;
+  tile_of(a, ntiles, L, nt, mt);
   return true;
 }
 
@@ -486,54 +493,64 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
 }
 
 // ------------------------------------------------------------------------------------
-// Large-group variant: 256 x BN workgroup tile, eight waves in a 4 (M) x 2 (N) grid,
-// each wave 64 x BN/2 (4 x BN/32 sub-tiles of 16 x 16), two waves per SIMD so that one
-// wave's promotion FMAs and LDS reads overlap the other's MFMAs.  A (activation) and B
-// (weight) tiles have rings of their own: A slots are filled SA-1 K-steps ahead, B slots
-// SB-1 K-steps ahead, so the weights, which mostly come from HBM, get the longer lead.
-// Wave rows that lie entirely past the M-tile's rows skip their MFMAs.
+// Large-group variant: eight waves, two per SIMD so that one wave's promotion FMAs and
+// LDS reads overlap the other's MFMAs.  A full M-tile is 256 x BN, the waves in a
+// 4 (M) x 2 (N) grid, each 64 x BN/2 (4 x BN/32 sub-tiles of 16 x 16).  A (activation)
+// and B (weight) tiles have rings of their own: A slots are filled SA-1 K-steps ahead, B
+// slots SB-1 K-steps ahead, so the weights, which mostly come from HBM, get the longer
+// lead.  Wave rows that lie entirely past the M-tile's rows skip their MFMAs.
+//
+// An expert's last M-tile often holds only a few rows (groups are about 256 +- 16 rows
+// long).  Such a tile does a quarter of the work but, with one K-step of prefetch, waits
+// a full load latency per K-step.  Tiles of at most 64 rows therefore take a narrow body
+// in the same launch: 64 x BN, waves in a 2 x 4 grid of 32 x BN/4, and rings one step
+// deeper (an A slot is a quarter the size), so they still run beside the expert's full
+// tile on the same XCD and share its weight tile through L2.
 //
 // gemm1 (SWIGLU): the B tile holds BN/2 gate rows of w13 and the matching BN/2 up rows;
 // wave wn takes gate and up columns [wn BN/4, (wn+1) BN/4) of them, so SwiGLU pairs sit
 // in the same lane.  The weight scale is taken per 16-column sub-tile (a sub-tile never
 // straddles a 128-row scale block since I is a multiple of 64).
 // ------------------------------------------------------------------------------------
-template <bool SWIGLU, int BN, int SA, int SB, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const GemmArgs a, int max_tiles,
-                                                                      int ntiles, int grid) {
-  constexpr int NT = WAVES * 64, BM = 64 * (WAVES / 2), WN = 2;
-  constexpr int SM = 4, SN = BN / 32;                // sub-tiles per wave
-  constexpr int NG = SN / 2, GW = BN / 4;            // gemm1: gate sub-tiles / columns per wave
+// LDS bytes of one tile body: A and B rings, scale slots, row sources, row-amax exchange,
+// bias
+template <int BN, int WM, int SM, int SA, int SB>
+constexpr int big_tile_lds() {
+  return SA * (16 * SM * WM) * 128 + SB * BN * 128 + SA * 8 * 64 * 4 + (16 * SM * WM) * 4 +
+         (8 / WM) * (16 * SM * WM) * 4 + BN * 2;
+}
+
+// One M-tile x n-tile: WM x (8 / WM) waves, each SM 16-row sub-tiles by BN / (8 / WM)
+// columns; SA / SB ring slots.
+template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB>
+__device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile mt, uint8_t* lds) {
+  constexpr int WAVES = 8, NT = WAVES * 64, WN = WAVES / WM, BM = 16 * SM * WM;
+  constexpr int WR = 16 * SM, WC = BN / WN;          // rows / columns of a wave
+  constexpr int SN = WC / 16;                        // sub-tiles per wave along N
+  constexpr int NG = SN / 2, GW = BN / (2 * WN);     // gemm1: gate sub-tiles / columns per wave
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   constexpr int A_ROWS = BM / WAVES, B_ROWS = BN / WAVES;   // rows each wave fetches per step
   constexpr int A_INSTR = A_ROWS / 8, B_INSTR = B_ROWS / 8;
-  static_assert(BN % 64 == 0 && (!SWIGLU || SN % 2 == 0), "tile");
+  static_assert(WC % 16 == 0 && BN % 64 == 0 && (!SWIGLU || SN % 2 == 0), "tile");
   static_assert(SA >= 2 && SB >= SA, "rings");
-  static_assert(2 * SN <= 32 && A_ROWS == 32, "scale lanes");
-  static_assert(WAVES == 4 || WAVES == 8, "waves");
+  static_assert(A_ROWS % 8 == 0 && A_ROWS <= 32 && WN * SN <= 32 && B_ROWS % 8 == 0, "scale lanes");
 
-  __shared__ __align__(16) uint8_t ringA[SA * A_BYTES];
-  __shared__ __align__(16) uint8_t ringB[SB * B_BYTES];
-  // per A slot and wave: lanes [0, 32) the activation scales of the wave's A rows,
-  // [32, 32 + 2 SN) the weight block scales of sub-tile n of column wave wn (wn SN + n)
-  __shared__ __align__(16) float sS[SA][WAVES][64];
-  __shared__ int rowsrc[BM];
-  __shared__ float red[WN][BM];
-  __shared__ __align__(16) uint16_t sbias[BN];      // bias of the tile's B rows (bf16)
-
-  int nt;
-  MTile mt;
-  if (!pick_tile(a, ntiles, nt, mt)) return;
-  (void)max_tiles;
-  (void)grid;
+  uint8_t* ringA = lds;
+  uint8_t* ringB = ringA + SA * A_BYTES;
+  // per A slot and wave: lanes [0, A_ROWS) the activation scales of the wave's A rows,
+  // [32, 32 + WN SN) the weight block scales of sub-tile n of column wave wn (wn SN + n)
+  float (*sS)[WAVES][64] = reinterpret_cast<float (*)[WAVES][64]>(ringB + SB * B_BYTES);
+  int* rowsrc = reinterpret_cast<int*>(sS + SA);                   // [BM]
+  float (*red)[BM] = reinterpret_cast<float (*)[BM]>(rowsrc + BM);  // [WN][BM]
+  uint16_t* sbias = reinterpret_cast<uint16_t*>(red + WN);          // [BN] bias of the B rows (bf16)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int K = a.K, N = a.N, I = a.I;
   const int KB = ceil_div(K, kBlock), NBs = ceil_div(N, kBlock);
   const int e = mt.expert;
-  const bool wave_live = wm * 64 < mt.row_end - mt.row_begin;
+  const bool wave_live = wm * WR < mt.row_end - mt.row_begin;
   const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * K;
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
 
@@ -578,18 +595,18 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
   }
   const float* s_ptr = kZeroScale;
   bool s_live = false;
-  if (lane < 32) {
+  if (lane < A_ROWS) {
     const int src = rowsrc[wave * A_ROWS + lane];
     s_live = src >= 0;
     s_ptr = a.A_scale + static_cast<size_t>(src < 0 ? 0 : src) * KB;
-  } else if (lane < 32 + 2 * SN) {
+  } else if (lane >= 32 && lane < 32 + WN * SN) {
     const int q = lane - 32, qw = q / SN, n = q % SN;   // column wave qw, sub-tile n
     int row;
     if (SWIGLU) {
       const int j0 = nt * (BN / 2) + qw * GW + 16 * (n % NG);
       row = j0 < I ? ((n >= NG ? I : 0) + j0) / kBlock : -1;
     } else {
-      const int c0 = nt * BN + qw * (BN / 2) + 16 * n;
+      const int c0 = nt * BN + qw * WC + 16 * n;
       row = c0 < N ? c0 / kBlock : -1;
     }
     s_live = row >= 0;
@@ -611,7 +628,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
         load_lds16(src, As + (wave * A_ROWS + i * 8) * 128);
       }
     }
-    if (lane < 32 + 2 * SN) {
+    if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN)) {   // lanes 0.. always: one instruction
       const void* src = s_live ? static_cast<const void*>(s_ptr + kt) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
     }
@@ -635,7 +652,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
 
   auto sub_brow = [&](int n) {   // B-tile row of sub-tile n of this wave
     if (SWIGLU) return n < NG ? wn * GW + 16 * n : BN / 2 + wn * GW + 16 * (n - NG);
-    return wn * (BN / 2) + 16 * n;
+    return wn * WC + 16 * n;
   };
 
   v4f acc[SM][SN];
@@ -661,12 +678,16 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
     if (s < KB) issue_a(s);
     if (s + SB - SA < KB) issue_b(s + SB - SA);
   }
-  // "this wave's loads of step kt landed": the loads issued after A(kt) are those of
-  // B(kt + SB - SA), a later step (which may stay in flight) when SB > SA, step kt
-  // itself when SB == SA
+  // "this wave's loads of step kt landed": A(j) is always followed by B(j + SB - SA), and
+  // by the time step kt is waited for, A(kt + SA - 2) and B(kt + SB - 2) are the last
+  // loads issued.  So with SB > SA the loads after A(kt) are B(kt + SB - SA) and the
+  // SA - 2 later (A, B) step pairs; with SB == SA (B(kt) right after A(kt)) just those
+  // pairs.  Near the end of K, where some of them were never issued, wait for all.
   auto wait_step = [&](int kt) {
-    if (SB > SA && kt + SB - SA < KB) {
-      wait_vmcnt<B_INSTR>();
+    constexpr int PAIR = A_INSTR + 1 + B_INSTR;
+    constexpr int AFTER = (SB > SA ? B_INSTR : 0) + (SA - 2) * PAIR;
+    if (kt + SB - 2 < KB) {
+      wait_vmcnt<AFTER>();
     } else {
       wait_vmcnt<0>();
     }
@@ -683,7 +704,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
     for (int n = 0; n < SN; ++n) sbv[n] = sS[sl][0][32 + wn * SN + n];
 #pragma unroll
     for (int m = 0; m < SM; ++m) {
-      const int r = wm * 64 + 16 * m + (lane & 15);
+      const int r = wm * WR + 16 * m + (lane & 15);
       af[m] = lds_frag(As, r, lane >> 4);
       sav[m] = sS[sl][r / A_ROWS][r % A_ROWS];
     }
@@ -699,8 +720,11 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
   // next step's fragment reads have been issued, so the matrix pipe keeps running across
   // the step boundary.
   constexpr int NP = SM * SN, LAG = 2;
-  static_assert(NP % 4 == 0 && LAG < 4, "partials rotate across steps");
-  v4f pp[4];
+  // partials rotate through P registers; P divides NP so that a step's first products
+  // never overwrite the previous step's last LAG, still unfolded
+  constexpr int P = NP % 4 == 0 ? 4 : 3;
+  static_assert(NP % P == 0 && LAG < P, "partials rotate across steps");
+  v4f pp[P];
   float sc_tail[LAG] = {};
   wait_step(0);
   barrier_only();
@@ -715,17 +739,17 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
       for (int j = 0; j < NP; ++j) {
         const int n = j / SM, m = j % SM;
         if (m == 0 && n + 2 < SN) bq[(n + 2) % 3] = lds_frag(Bs, sub_brow(n + 2) + (lane & 15), lane >> 4);
-        pp[j % 4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n % 3], af[m], zero, 0, 0, 0, 0, 0, 0);
+        pp[j % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n % 3], af[m], zero, 0, 0, 0, 0, 0, 0);
         if (j >= LAG) {
           const int q = j - LAG;
           const float sc = sav[q % SM] * sbv[q / SM];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[q % SM][q / SM][i] = fmaf(pp[q % 4][i], sc, acc[q % SM][q / SM][i]);
+          for (int i = 0; i < 4; ++i) acc[q % SM][q / SM][i] = fmaf(pp[q % P][i], sc, acc[q % SM][q / SM][i]);
         } else if (kt > 0) {   // the previous step's product NP - LAG + j
           const int q = NP - LAG + j;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[q % SM][q / SM][i] = fmaf(pp[q % 4][i], sc_tail[j], acc[q % SM][q / SM][i]);
+            acc[q % SM][q / SM][i] = fmaf(pp[q % P][i], sc_tail[j], acc[q % SM][q / SM][i]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -743,12 +767,12 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
     for (int j = 0; j < LAG; ++j) {
       const int q = NP - LAG + j;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[q % SM][q / SM][i] = fmaf(pp[q % 4][i], sc_tail[j], acc[q % SM][q / SM][i]);
+      for (int i = 0; i < 4; ++i) acc[q % SM][q / SM][i] = fmaf(pp[q % P][i], sc_tail[j], acc[q % SM][q / SM][i]);
     }
   }
   wait_vmcnt<0>();
 
-  // ---- epilogue: lane holds rows r(m) = wm*64 + 16m + (lane & 15) and, per sub-tile n,
+  // ---- epilogue: lane holds rows r(m) = wm*WR + 16m + (lane & 15) and, per sub-tile n,
   // the four adjacent columns 16n + 4 (lane >> 4) + i of its column range ----
   const int cq = 4 * (lane >> 4);
   if constexpr (SWIGLU) {
@@ -789,14 +813,17 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(hv[m][n][i]));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (lane < 16) red[wn][wm * 64 + 16 * m + lane] = mx;
+      if (lane < 16) red[wn][wm * WR + 16 * m + lane] = mx;
     }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < SM; ++m) {
-      const int r = wm * 64 + 16 * m + (lane & 15);
+      const int r = wm * WR + 16 * m + (lane & 15);
       const int p = mt.row_begin + r;
-      const float sc = group_scale(fmaxf(red[0][r], red[1][r]));   // exact fp32(amax / 448)
+      float amax = red[0][r];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) amax = fmaxf(amax, red[w][r]);
+      const float sc = group_scale(amax);   // exact fp32(amax / 448)
       // quotient h / sc: reciprocal estimate plus one residual correction
       const float rs = __builtin_amdgcn_rcpf(sc);
       if (p < mt.row_end) {
@@ -821,7 +848,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
   } else {
 #pragma unroll
     for (int n = 0; n < SN; ++n) {
-      const int c0 = nt * BN + wn * (BN / 2) + 16 * n + cq;
+      const int c0 = nt * BN + wn * WC + 16 * n + cq;
       if (c0 >= N) continue;                  // N is a multiple of 64: all four or none
       const uint2 b2 = *reinterpret_cast<const uint2*>(&sbias[sub_brow(n) + cq]);
       float bv[4];
@@ -829,11 +856,53 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_big_kernel(const Gemm
       bv[2] = __uint_as_float(b2.y << 16); bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
 #pragma unroll
       for (int m = 0; m < SM; ++m) {
-        const int p = mt.row_begin + wm * 64 + 16 * m + (lane & 15);
+        const int p = mt.row_begin + wm * WR + 16 * m + (lane & 15);
         if (p < mt.row_end)
           *reinterpret_cast<uint2*>(a.y_out + static_cast<size_t>(p) * N + c0) = make_uint2(
               f32_to_f16_sat(acc[m][n][0] + bv[0]) | (static_cast<uint32_t>(f32_to_f16_sat(acc[m][n][1] + bv[1])) << 16),
               f32_to_f16_sat(acc[m][n][2] + bv[2]) | (static_cast<uint32_t>(f32_to_f16_sat(acc[m][n][3] + bv[3])) << 16));
+      }
+    }
+  }
+}
+
+// Large-group GEMM launch: full M-tiles (256 rows, rings SA / SB) and narrow ones (at
+// most 64 rows, rings SAN / SBN) share the launch and the work order.
+//
+// Persistent: one workgroup per CU (the LDS of a tile body is most of a CU's), each
+// taking tiles from work queues until they run dry.  Tiles take from about 25 to 65 us,
+// and with one workgroup per block the in-order dealing of blocks to XCDs left CUs idle
+// between tiles (measured: busy about 77% of the launch).  The expert-major tile order is
+// cut into eight contiguous ranges, one queue per XCD (block b runs on XCD b mod 8), so
+// the workgroups of an XCD run neighbouring tiles together and share the expert's
+// activation rows and weight tiles in their L2; a workgroup whose XCD's queue is empty
+// takes from the other XCDs' queues.  Every queue head only grows, so every workgroup
+// leaves after at most total + 8 of its fetches.
+template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN>
+__global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int ntiles) {
+  constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN>();
+  __shared__ __align__(16) uint8_t lds[kFull > kNarrow ? kFull : kNarrow];
+  __shared__ int s_next;
+  const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
+  const int per_xcd = (total + kGemmQueues - 1) / kGemmQueues;
+  const int x0 = blockIdx.x % kGemmQueues;
+  for (int d = 0; d < kGemmQueues; ++d) {
+    const int x = (x0 + d) % kGemmQueues;
+    const int lo = x * per_xcd;
+    const int n = total - lo < per_xcd ? total - lo : per_xcd;   // may be <= 0
+    for (;;) {
+      __syncthreads();   // the previous tile is done with LDS and with s_next
+      if (threadIdx.x == 0) s_next = n > 0 ? atomicAdd(&a.queue[x], 1) : n;
+      __syncthreads();
+      const int t = __builtin_amdgcn_readfirstlane(s_next);
+      if (t >= n) break;
+      int nt;
+      MTile mt;
+      tile_of(a, ntiles, lo + t, nt, mt);
+      if (mt.row_end - mt.row_begin <= 64) {
+        big_tile<SWIGLU, BN, 2, 2, SAN, SBN>(a, nt, mt, lds);
+      } else {
+        big_tile<SWIGLU, BN, 4, 4, SA, SB>(a, nt, mt, lds);
       }
     }
   }
@@ -1065,8 +1134,23 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 // Large-group launch shapes (workgroup tile 256 x BN, A / B ring depths).
 constexpr int kG1BN = 256, kG1SA = 2, kG1SB = 2;
 constexpr int kG2BN = 192, kG2SA = 2, kG2SB = 3;
+// Ring depth of narrow (at most 64-row) tiles in the large-group launch.
+constexpr int kNarrowS = 3;
 // Dynamic LDS of the row-run kernel at its largest K (64 blocks).
 constexpr int kRowrunMaxLds = 64 * 2048 + 16 * 256 + 8 * 16 * 4;
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 int gemm_tile_rows(long rows, int E) {
   const long avg = rows / (E > 0 ? E : 1);
@@ -1088,11 +1172,13 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
     constexpr int BN = SWIGLU ? kG1BN : kG2BN;
     const int nt_big = SWIGLU ? ceil_div(a.I, BN / 2) : ceil_div(a.N, BN);
     const long tot = static_cast<long>(max_tiles) * nt_big;
-    const int g = static_cast<int>((tot + 7) / 8 * 8);
+    // persistent: one workgroup per CU (a multiple of the queue count), at most one per tile
+    const long cus = device_cus();
+    const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
     if constexpr (SWIGLU)
-      grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, 8><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
+      grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS><<<g, 512, 0, st>>>(a, nt_big);
     else
-      grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, 8><<<g, 512, 0, st>>>(a, max_tiles, nt_big, g);
+      grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS><<<g, 512, 0, st>>>(a, nt_big);
     return;
   }
   // Decode-sized groups whose weight rows are not whole 128-byte lines (K = 64 mod 128,

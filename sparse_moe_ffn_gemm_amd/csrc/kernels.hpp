@@ -23,6 +23,7 @@ void launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* codes, float*
 // ---- routing ----
 constexpr int kRouterTile = 64;     // tokens / experts per router GEMM workgroup
 constexpr int kChunk = 256;         // tokens per dispatch chunk
+constexpr int kGemmQueues = 8;      // per-XCD work queues of one large-group GEMM launch
 
 // partial[s][t][e] = sum over the s-th slice of H of x[t,h] * W[e,h]; also clears
 // hist[0, hist_n) for the top-k step
@@ -31,7 +32,9 @@ void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E
 // ids/gates, counted into the per-chunk expert histogram hist[chunk][E] (cleared before)
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
                  int32_t* ids, float* gates, int32_t* hist, hipStream_t st);
-// counts, offsets, per-chunk bases and the M-tile list for tiles of `bm` rows
+// counts, offsets, per-chunk bases and the M-tile list for tiles of `bm` rows;
+// num_tiles[0] = number of M-tiles, num_tiles[1 .. 2 kGemmQueues] (the two GEMMs' work
+// queues) are cleared
 void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32_t* counts,
                           int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
                           int32_t* expert_tile_off, hipStream_t st);
@@ -51,6 +54,7 @@ struct GemmArgs {
   const MTile* tiles;
   const int32_t* num_tiles;
   const int32_t* expert_tile_off;   // [E+1] first M-tile of each expert, [E] = num_tiles
+  int32_t* queue;            // [kGemmQueues] work-queue heads, zero at launch
   int E;
   int K, N, I;
   uint8_t* h_out;            // gemm1: [rows, I]

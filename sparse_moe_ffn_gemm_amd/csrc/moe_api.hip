@@ -57,7 +57,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   p->hist = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
   p->chunk_base = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
   p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->max_tiles));
-  p->num_tiles = take(sizeof(int32_t));
+  p->num_tiles = take(sizeof(int32_t) * (1 + 2 * moe::kGemmQueues));   // + the GEMMs' queues
   p->expert_tile_off = take(sizeof(int32_t) * (E + 1));
   p->ids = take(sizeof(int32_t) * p->rows);
   p->gates = take(sizeof(float) * p->rows);
@@ -173,6 +173,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g1.I = I;
   g1.h_out = at<uint8_t>(ws, p.h);
   g1.h_scale = at<float>(ws, p.sh);
+  g1.queue = at<int32_t>(ws, p.num_tiles) + 1;
   moe::launch_gemm1(g1, p.bm, p.max_tiles, st);
   mark(ev, 6, st);
 
@@ -193,6 +194,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.N = H;
   g2.I = I;
   g2.y_out = at<uint16_t>(ws, p.y);
+  g2.queue = at<int32_t>(ws, p.num_tiles) + 1 + moe::kGemmQueues;
   moe::launch_gemm2(g2, p.bm, p.max_tiles, st);
   mark(ev, 7, st);
   moe::launch_combine(at<uint16_t>(ws, p.y), tb.gates, tb.inv, T, H, top_k, out, st);

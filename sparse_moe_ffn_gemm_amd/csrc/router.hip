@@ -318,6 +318,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
       expert_tile_off[E] = toff + ntl;
     }
   }
+  if (tid >= 1 && tid <= 2 * kGemmQueues) num_tiles[tid] = 0;   // the GEMMs' work queues
 }
 
 // ------------------------------------------------------------------------------------
