@@ -145,7 +145,9 @@ moe_status moe_forward(const uint16_t* x, const float* router_w, const float* ro
  *   4 activation quantisation  5 GEMM1 (+ bias, SwiGLU, requantisation)
  *   6 GEMM2 (+ bias)  7 combine  8 end
  * so hipEventElapsedTime(events[i], events[i+1]) is stage i's device time.
- * `events` must hold MOE_PROFILE_EVENTS valid hipEvent_t (else MOE_ERR_INVALID_ARG). */
+ * `events` must point to MOE_PROFILE_EVENTS entries (NULL array: MOE_ERR_INVALID_ARG);
+ * a NULL entry is not recorded, so a caller can time some stages only (each recorded
+ * event adds a small gap between kernels). */
 #define MOE_PROFILE_EVENTS 9
 moe_status moe_forward_profiled(const uint16_t* x, const float* router_w, const float* router_b,
                                 const uint8_t* w13, const float* w13_scales, const uint16_t* b13,

@@ -4,10 +4,10 @@ The compute runs in hand-written HIP kernels inside ``libmoe_mi355x.so`` (C ABI 
 include/moe.h); this package is its Python binding.  Build with
 ``python -m sparse_moe_ffn_gemm_amd.build``.
 """
-from ._lib import (MoEError, Routing, WorkspaceRegions, forward, forward_profiled, lib, new_routing, new_workspace,
+from ._lib import (PROFILE_STAGES, MoEError, Routing, WorkspaceRegions, forward, forward_profiled, lib, new_routing, new_workspace,
                    quantize_activations, quantize_weights, route, workspace_bytes, workspace_layout)
 from .layer import MoELayer
 
-__all__ = ["MoEError", "Routing", "WorkspaceRegions", "forward", "forward_profiled", "lib", "new_routing",
+__all__ = ["PROFILE_STAGES", "MoEError", "Routing", "WorkspaceRegions", "forward", "forward_profiled", "lib", "new_routing",
            "new_workspace", "quantize_activations", "quantize_weights", "route",
            "workspace_bytes", "workspace_layout", "MoELayer"]

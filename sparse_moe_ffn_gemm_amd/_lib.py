@@ -226,14 +226,15 @@ def forward(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, top_
 def forward_profiled(events, x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2,
                      top_k: int, out=None, routing: dict = None, workspace=None) -> torch.Tensor:
     """``forward`` that also records ``events`` (9 torch.cuda.Event(enable_timing=True),
-    recorded on the current stream) before each stage and after the last."""
+    recorded on the current stream) before each stage and after the last; a ``None``
+    entry leaves that boundary unrecorded."""
     if len(events) != len(PROFILE_STAGES) + 1:
         raise ValueError("need one event per stage plus one")
     out, args, _keep = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales,
                                      b2, top_k, out, routing, workspace)
     for ev in events:          # materialise the underlying hipEvent_t
-        if ev.cuda_event == 0:
+        if ev is not None and ev.cuda_event == 0:
             ev.record()
-    arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+    arr = (ctypes.c_void_p * len(events))(*[0 if ev is None else ev.cuda_event for ev in events])
     _check(lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
     return out

@@ -719,6 +719,11 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // a step are folded during the first MFMAs of the next one, after the barrier and the
   // next step's fragment reads have been issued, so the matrix pipe keeps running across
   // the step boundary.
+  // gemm1: a wave's gate columns (GW of them, 32-aligned) lie in one 128-row scale block
+  // of w13, and so do its up columns (I is a multiple of 64), so sub-tiles share two
+  // weight scales and a step needs 2 SM scale products instead of SM SN
+  auto scale_col = [&](int n) { return SWIGLU ? (n < NG ? 0 : NG) : n; };
+  static_assert(!SWIGLU || (GW % 32 == 0 && 128 % GW == 0), "gate columns of a wave in one block");
   constexpr int NP = SM * SN, LAG = 2;
   // partials rotate through P registers; P divides NP so that a step's first products
   // never overwrite the previous step's last LAG, still unfolded
@@ -742,7 +747,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
         pp[j % P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n % 3], af[m], zero, 0, 0, 0, 0, 0, 0);
         if (j >= LAG) {
           const int q = j - LAG;
-          const float sc = sav[q % SM] * sbv[q / SM];
+          const float sc = sav[q % SM] * sbv[scale_col(q / SM)];
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[q % SM][q / SM][i] = fmaf(pp[q % P][i], sc, acc[q % SM][q / SM][i]);
         } else if (kt > 0) {   // the previous step's product NP - LAG + j
@@ -754,7 +759,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int j = 0; j < LAG; ++j) sc_tail[j] = sav[(NP - LAG + j) % SM] * sbv[(NP - LAG + j) / SM];
+      for (int j = 0; j < LAG; ++j) sc_tail[j] = sav[(NP - LAG + j) % SM] * sbv[scale_col((NP - LAG + j) / SM)];
     }
     if (kt + 1 < KB) {
       wait_step(kt + 1);

@@ -118,6 +118,26 @@ def test_forward_deterministic_and_reentrant():
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
+def test_forward_profiled_matches_forward_with_partial_events():
+    """The per-stage timing entry point does the same work: bit-identical output with all
+    stage events, and with only the GEMM1 boundaries recorded (NULL entries elsewhere)."""
+    shape = SHAPES["gpt-oss-20b-decode"]
+    g = GpuLayer(shape)
+    args = (g.x, g.layer.router_w, g.layer.router_b, g.layer.w13, g.layer.w13_scales,
+            g.layer.b13, g.layer.w2, g.layer.w2_scales, g.layer.b2, shape.top_k)
+    ref = moe.forward(*args).clone()
+    full = [torch.cuda.Event(enable_timing=True) for _ in range(len(moe.PROFILE_STAGES) + 1)]
+    a = moe.forward_profiled(full, *args).clone()
+    part = [None] * (len(moe.PROFILE_STAGES) + 1)
+    i1 = moe.PROFILE_STAGES.index("gemm1")
+    part[i1], part[i1 + 1] = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b = moe.forward_profiled(part, *args).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, ref) and torch.equal(b, ref)
+    assert all(full[i].elapsed_time(full[i + 1]) >= 0 for i in range(len(full) - 1))
+    assert part[i1].elapsed_time(part[i1 + 1]) > 0
+
+
 def test_forward_smaller_call_after_larger_reuses_workspace():
     shape = SHAPES["tiny"]
     g = GpuLayer(shape)
