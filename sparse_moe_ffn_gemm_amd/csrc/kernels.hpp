@@ -34,10 +34,12 @@ void launch_topk(const float* partial, int ksplit, const float* bias, int T, int
                  int32_t* ids, float* gates, int32_t* hist, hipStream_t st);
 // counts, offsets, per-chunk bases and the M-tile list for tiles of `bm` rows;
 // num_tiles[0] = number of M-tiles, num_tiles[1 .. 2 kGemmQueues] (the two GEMMs' work
-// queues) are cleared
+// queues) are cleared.  With ids != NULL (only when nchunks == 1) the same workgroup also
+// does the scatter (perm, inv), replacing launch_dispatch_scatter.
 void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32_t* counts,
                           int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
-                          int32_t* expert_tile_off, hipStream_t st);
+                          int32_t* expert_tile_off, hipStream_t st, const int32_t* ids = nullptr,
+                          int T = 0, int top_k = 0, int32_t* perm = nullptr, int32_t* inv = nullptr);
 void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,
                              int top_k, int32_t* perm, int32_t* inv, hipStream_t st);
 

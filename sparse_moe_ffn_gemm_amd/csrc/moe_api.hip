@@ -108,12 +108,16 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
   moe::launch_topk(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, tb.ids, tb.gates,
                    at<int32_t>(ws, p.hist), st);
   mark(ev, 2, st);
+  // a single chunk of tokens (decode-sized T): the scan's workgroup also scatters
+  const bool one_chunk = p.nchunks == 1;
   moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, tb.counts, tb.offsets,
                             at<int32_t>(ws, p.chunk_base), at<moe::MTile>(ws, p.tiles),
-                            at<int32_t>(ws, p.num_tiles), at<int32_t>(ws, p.expert_tile_off), st);
+                            at<int32_t>(ws, p.num_tiles), at<int32_t>(ws, p.expert_tile_off), st,
+                            one_chunk ? tb.ids : nullptr, p.T, p.k, tb.perm, tb.inv);
   mark(ev, 3, st);
-  moe::launch_dispatch_scatter(tb.ids, at<int32_t>(ws, p.chunk_base), p.T, p.E, p.k, tb.perm,
-                               tb.inv, st);
+  if (!one_chunk)
+    moe::launch_dispatch_scatter(tb.ids, at<int32_t>(ws, p.chunk_base), p.T, p.E, p.k, tb.perm,
+                                 tb.inv, st);
 }
 
 bool routing_ok(const moe_routing* r) {

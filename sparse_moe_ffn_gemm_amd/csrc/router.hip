@@ -245,9 +245,58 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
 }
 
 // ------------------------------------------------------------------------------------
+// scatter of one chunk of kChunk tokens.  The chunk's (token, j) entries are taken 256 at a
+// time in token order; inside a wave, the lanes whose expert matches a lane's expert bit
+// for bit (eight ballots) give its rank; waves before it in the same round and earlier
+// rounds (a running per-expert count) give the rest of its slot.  run[e] holds the
+// chunk's first slot of expert e on entry.  Every thread of the workgroup passes the
+// barriers; threads [0, 256) do the work.
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ ids, int chunk, int T,
+                                              int E, int top_k, int32_t* __restrict__ perm,
+                                              int32_t* __restrict__ inv, int* run, int (*wc)[256]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool act = tid < 256;
+  const int t0 = chunk * kChunk;
+  const int n = min(kChunk, T - t0) * top_k;
+  const size_t flat0 = static_cast<size_t>(t0) * top_k;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int r = 0; r < n; r += 256) {
+    if (act) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) wc[ww][tid] = 0;
+    }
+    __syncthreads();
+    const int i = r + tid;
+    const int ex = (act && i < n) ? ids[flat0 + i] : -1;
+    unsigned long long peer = __ballot(ex >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = (ex >> bit) & 1;
+      const unsigned long long m = __ballot(set);
+      peer &= set ? m : ~m;
+    }
+    const int rank = __popcll(peer & below);
+    if (ex >= 0 && rank == 0) wc[w][ex] = __popcll(peer);
+    __syncthreads();
+    if (ex >= 0) {
+      int pos = run[ex] + rank;
+      for (int ww = 0; ww < w; ++ww) pos += wc[ww][ex];
+      const int flat = static_cast<int>(flat0) + i;   // = t * top_k + j
+      perm[pos] = flat;
+      inv[flat] = pos;
+    }
+    __syncthreads();
+    if (tid < E) run[tid] += wc[0][tid] + wc[1][tid] + wc[2][tid] + wc[3][tid];
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // scan: one workgroup of 1024 lanes; lane (q, e) owns expert e over the q-th quarter of
 // the chunks.  counts -> offsets (LDS exclusive scan over experts) -> per-chunk bases,
 // then the M-tile list (tiles of bm rows, expert-major) and each expert's first tile.
+// With a single chunk (decode-sized T) the same workgroup then scatters it, which saves
+// a launch on the latency-bound decode path.
 // ------------------------------------------------------------------------------------
 __device__ int exclusive_scan256(int v, int* tmp) {   // lanes [0, 256) hold the values
   const int tid = threadIdx.x;
@@ -271,7 +320,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
                                                              int32_t* __restrict__ chunk_base,
                                                              MTile* __restrict__ tiles,
                                                              int32_t* __restrict__ num_tiles,
-                                                             int32_t* __restrict__ expert_tile_off) {
+                                                             int32_t* __restrict__ expert_tile_off,
+                                                             const int32_t* __restrict__ ids, int T,
+                                                             int top_k, int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ inv) {
   __shared__ int part[4][256];
   __shared__ int tmp[256];
   const int tid = threadIdx.x, e = tid & 255, q = tid >> 8;
@@ -319,14 +371,14 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
     }
   }
   if (tid >= 1 && tid <= 2 * kGemmQueues) num_tiles[tid] = 0;   // the GEMMs' work queues
+  if (ids != nullptr) {   // a single chunk (T <= kChunk): its scatter follows in this workgroup
+    __syncthreads();      // every thread is past the tile scan's use of tmp and part
+    if (tid < E) tmp[tid] = off;   // the chunk's first slot of each expert = its offset
+    scatter_chunk(ids, 0, T, E, top_k, perm, inv, tmp, part);
+  }
 }
 
-// ------------------------------------------------------------------------------------
-// scatter: one workgroup per chunk of kChunk tokens.  The chunk's (token, j) entries are
-// taken 256 at a time in token order; inside a wave, the lanes whose expert matches a
-// lane's expert bit for bit (eight ballots) give its rank; waves before it in the same
-// round and earlier rounds (a running per-expert count) give the rest of its slot.
-// ------------------------------------------------------------------------------------
+// One workgroup per chunk.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
                                                                const int32_t* __restrict__ chunk_base,
                                                                int T, int E, int top_k,
@@ -334,38 +386,9 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
                                                                int32_t* __restrict__ inv) {
   __shared__ int run[256];
   __shared__ int wc[4][256];
-  const int chunk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t0 = chunk * kChunk;
-  const int n = min(kChunk, T - t0) * top_k;
-  const size_t flat0 = static_cast<size_t>(t0) * top_k;
+  const int chunk = blockIdx.x, tid = threadIdx.x;
   if (tid < E) run[tid] = chunk_base[static_cast<size_t>(chunk) * E + tid];
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int r = 0; r < n; r += 256) {
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) wc[ww][tid] = 0;
-    __syncthreads();
-    const int i = r + tid;
-    const int ex = i < n ? ids[flat0 + i] : -1;
-    unsigned long long peer = __ballot(ex >= 0);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool set = (ex >> bit) & 1;
-      const unsigned long long m = __ballot(set);
-      peer &= set ? m : ~m;
-    }
-    const int rank = __popcll(peer & below);
-    if (ex >= 0 && rank == 0) wc[w][ex] = __popcll(peer);
-    __syncthreads();
-    if (ex >= 0) {
-      int pos = run[ex] + rank;
-      for (int ww = 0; ww < w; ++ww) pos += wc[ww][ex];
-      const int flat = static_cast<int>(flat0) + i;   // = t * top_k + j
-      perm[pos] = flat;
-      inv[flat] = pos;
-    }
-    __syncthreads();
-    if (tid < E) run[tid] += wc[0][tid] + wc[1][tid] + wc[2][tid] + wc[3][tid];
-  }
+  scatter_chunk(ids, chunk, T, E, top_k, perm, inv, run, wc);
 }
 
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
@@ -382,10 +405,11 @@ void launch_topk(const float* partial, int ksplit, const float* bias, int T, int
 
 void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32_t* counts,
                           int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
-                          int32_t* expert_tile_off, hipStream_t st) {
+                          int32_t* expert_tile_off, hipStream_t st, const int32_t* ids, int T,
+                          int top_k, int32_t* perm, int32_t* inv) {
   dispatch_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(hist, nchunks, E, bm, counts, offsets,
                                                        chunk_base, tiles, num_tiles,
-                                                       expert_tile_off);
+                                                       expert_tile_off, ids, T, top_k, perm, inv);
 }
 
 void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,
