@@ -25,10 +25,13 @@ constexpr int kRouterTile = 64;     // tokens / experts per router GEMM workgrou
 constexpr int kChunk = 256;         // tokens per dispatch chunk
 constexpr int kGemmQueues = 8;      // per-XCD work queues of one large-group GEMM launch
 
-// partial[s][t][e] = sum over the s-th slice of H of x[t,h] * W[e,h]; also clears
-// hist[0, hist_n) for the top-k step
+// partial[s][t][e] = sum over the s-th slice of H (kslice a multiple of 128) of
+// x[t,h] * W[e,h]; also clears hist[0, hist_n) for the top-k step, and with xq != NULL
+// writes the 1x128 quantisation of x (codes xq [T,H], scales sx [T, ceil(H/128)]), the
+// same as launch_quantize_act
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
-                          int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st);
+                          int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
+                          uint8_t* xq = nullptr, float* sx = nullptr);
 // ids/gates, counted into the per-chunk expert histogram hist[chunk][E] (cleared before)
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
                  int32_t* ids, float* gates, int32_t* hist, hipStream_t st);

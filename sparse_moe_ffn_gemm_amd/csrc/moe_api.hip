@@ -42,7 +42,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   const int tiles2d = ceil_div(T, moe::kRouterTile) * ceil_div(E, moe::kRouterTile);
   int ks = ceil_div(1024, tiles2d);
   ks = std::max(1, std::min(ks, H / 128 > 0 ? H / 128 : 1));
-  p->kslice = ceil_div(ceil_div(H, ks), 64) * 64;
+  p->kslice = ceil_div(ceil_div(H, ks), moe::kBlock) * moe::kBlock;   // whole quantisation groups
   p->ksplit = ceil_div(H, p->kslice);
   p->nchunks = ceil_div(T, moe::kChunk);
   p->bm = moe::gemm_tile_rows(p->rows, E);
@@ -99,11 +99,15 @@ void mark(hipEvent_t* ev, int i, hipStream_t st) {
   if (ev && ev[i]) (void)hipEventRecord(ev[i], st);
 }
 
+// Router (which also quantises x when `quant_x`), top-k and the dispatch tables.
 void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const float* rb,
-                     const Tables& tb, void* ws, hipStream_t st, hipEvent_t* ev = nullptr) {
+                     const Tables& tb, void* ws, hipStream_t st, hipEvent_t* ev = nullptr,
+                     bool quant_x = false) {
   mark(ev, 0, st);
   moe::launch_router_logits(x, rw, p.T, p.H, p.E, p.ksplit, p.kslice, at<float>(ws, p.partial),
-                            at<int32_t>(ws, p.hist), p.nchunks * p.E, st);
+                            at<int32_t>(ws, p.hist), p.nchunks * p.E, st,
+                            quant_x ? at<uint8_t>(ws, p.xq) : nullptr,
+                            quant_x ? at<float>(ws, p.sx) : nullptr);
   mark(ev, 1, st);
   moe::launch_topk(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, tb.ids, tb.gates,
                    at<int32_t>(ws, p.hist), st);
@@ -154,9 +158,8 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
                         : Tables{at<int32_t>(ws, p.ids), at<float>(ws, p.gates),
                                  at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
                                  at<int32_t>(ws, p.perm), at<int32_t>(ws, p.inv)};
-  enqueue_routing(p, x, router_w, router_b, tb, ws, st, ev);
-  mark(ev, 4, st);
-  moe::launch_quantize_act(x, T, H, at<uint8_t>(ws, p.xq), at<float>(ws, p.sx), st);
+  enqueue_routing(p, x, router_w, router_b, tb, ws, st, ev, /*quant_x=*/true);
+  mark(ev, 4, st);   // (the activation quantisation ran inside the router kernel)
   mark(ev, 5, st);
 
   moe::GemmArgs g1{};

@@ -24,13 +24,18 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // product x * part is exact in fp32 and x . w = x . hi + x . mid + x . lo is summed in
 // fp32 by v_mfma_f32_16x16x32_bf16 (three times the products of an fp32 GEMM at eight
 // times the fp32 matrix rate).  Workgroup tile 64 tokens x 64 experts, 4 waves of
-// 32 x 32; grid.z splits H so that small-T (decode) layers still spread over many CUs.
-// The matrix cores accumulate 128 columns at a time into `acc`, folded into `tot`, so no
-// long running sum absorbs small terms.
+// 32 x 32; grid.z splits H (in whole 128-column groups) so that small-T (decode) layers
+// still spread over many CUs.  A step stages 128 columns of x and W in LDS while the
+// next step's are loaded into registers; the matrix cores accumulate one step into
+// `acc`, folded into `tot`, so no long running sum absorbs small terms.
+//
+// The workgroups of the first expert tile also quantise the x tile they staged (one
+// 1x128 group per token and step, the same rule and code as the activation quantiser),
+// so x is read from HBM once for both uses.
 // ------------------------------------------------------------------------------------
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-constexpr int kRC = 64;           // H columns staged per step
-constexpr int kRS = kRC + 8;      // padded LDS row (bf16): 144-byte rows spread the banks
+constexpr int kRC = 128;          // H columns staged per step (one quantisation group)
+constexpr int kRS = kRC + 8;      // padded LDS row (bf16): 272-byte rows spread the banks
 
 __device__ __forceinline__ v8bf lds_bf8(const uint16_t* p) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
@@ -42,7 +47,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             int H, int E, int kslice,
                                                             float* __restrict__ partial,
                                                             int32_t* __restrict__ hist,
-                                                            int hist_n) {
+                                                            int hist_n, uint8_t* __restrict__ xq,
+                                                            float* __restrict__ sx) {
   __shared__ __align__(16) uint16_t xs[kRouterTile * kRS];
   __shared__ __align__(16) uint16_t wp[3][kRouterTile * kRS];   // hi, mid, lo parts of W
   {  // clear the dispatch histograms that the top-k step accumulates (a slice per block)
@@ -57,30 +63,45 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   const int h_end = min(H, h_begin + kslice);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
+  const bool quant = xq != nullptr && blockIdx.y == 0;
+  const int KBH = ceil_div(H, kBlock);
   v4f acc[2][2], tot[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int h0 = h_begin; h0 < h_end; h0 += kRC) {
+  // one step's global loads: x 64 rows x 16 chunks of 8 bf16, W 64 rows x 32 float4
+  uint4 xr[4];
+  float4 wr[8];
+  auto load = [&](int h0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {   // x: 64 rows x 64 bf16 = 8 chunks of 8 per row
+    for (int i = 0; i < 4; ++i) {
       const int q = tid + 256 * i;
-      const int row = q >> 3, c = q & 7;
-      const int t = t0 + row, h = h0 + c * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (t < T && h < h_end) v = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + h);
-      *reinterpret_cast<uint4*>(xs + row * kRS + c * 8) = v;
+      const int t = t0 + (q >> 4), h = h0 + (q & 15) * 8;
+      xr[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (t < T && h < h_end) xr[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + h);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {   // W: 64 rows x 64 floats = 16 float4 per row, split in 3
+    for (int i = 0; i < 8; ++i) {
       const int q = tid + 256 * i;
-      const int row = q >> 4, c = q & 15;
-      const int e = e0 + row, h = h0 + c * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < E && h < h_end) v = *reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + h);
-      const float w[4] = {v.x, v.y, v.z, v.w};
+      const int e = e0 + (q >> 5), h = h0 + (q & 31) * 4;
+      wr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < E && h < h_end) wr[i] = *reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + h);
+    }
+  };
+  if (h_begin < h_end) load(h_begin);
+  for (int h0 = h_begin; h0 < h_end; h0 += kRC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      *reinterpret_cast<uint4*>(xs + (q >> 4) * kRS + (q & 15) * 8) = xr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {   // split in 3 exact bf16 parts
+      const int q = tid + 256 * i;
+      const int row = q >> 5, c = q & 31;
+      const float w[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
       uint32_t ph[2] = {0u, 0u}, pm[2] = {0u, 0u}, pl[2] = {0u, 0u};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -99,6 +120,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       *reinterpret_cast<uint2*>(&wp[2][row * kRS + c * 4]) = make_uint2(pl[0], pl[1]);
     }
     __syncthreads();
+    if (h0 + kRC < h_end) load(h0 + kRC);   // next step's loads fly during this step
+    if (quant) {   // 16 lanes per token group, 16 tokens per pass
+      const int g = h0 / kBlock;
+#pragma unroll
+      for (int pass = 0; pass < kRouterTile / 16; ++pass) {
+        const int row = pass * 16 + (tid >> 4), col = 8 * (tid & 15);
+        const int t = t0 + row;
+        const bool in = t < T && h0 + col < h_end;
+        const float sc = quantize_group16(xs + row * kRS, col, in,
+                                          xq + static_cast<size_t>(t < T ? t : 0) * H + h0);
+        if ((tid & 15) == 0 && t < T) sx[static_cast<size_t>(t) * KBH + g] = sc;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < kRC; kk += 32) {
       const int kofs = kk + 8 * (lane >> 4);
@@ -117,15 +155,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
           for (int p = 0; p < 3; ++p)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[p][j], acc[i][j], 0, 0, 0);
     }
-    if (((h0 - h_begin) / kRC) % 2 == 1 || h0 + kRC >= h_end) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          tot[i][j] += acc[i][j];
-          acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
-    }
+      for (int j = 0; j < 2; ++j) tot[i][j] += acc[i][j];
     __syncthreads();
   }
   float* out = partial + static_cast<size_t>(blockIdx.z) * T * E;
@@ -392,9 +425,11 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
 }
 
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
-                          int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st) {
+                          int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
+                          uint8_t* xq, float* sx) {
   dim3 grid(ceil_div(T, kRouterTile), ceil_div(E, kRouterTile), ksplit);
-  router_logits_kernel<<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist, hist_n);
+  router_logits_kernel<<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist, hist_n,
+                                                   xq, sx);
 }
 
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,

@@ -118,6 +118,25 @@ def test_forward_deterministic_and_reentrant():
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
+@pytest.mark.parametrize("shape", [SHAPES["gpt-oss-20b-decode"],
+                                   custom_shape(T=150, H=448, E=70, top_k=2, I=128, seed=40),
+                                   custom_shape(T=300, H=2880, E=8, top_k=2, I=128, seed=41)],
+                         ids=["gpt-oss-20b-decode", "T150-H448-E70", "T300-H2880-E8"])
+def test_forward_activation_codes_match_quantiser(shape):
+    """The router kernel quantises x for GEMM1 (1x128 groups): its codes and scales in the
+    workspace are bit-identical to moe_quantize_activations' (ragged last group, several
+    token tiles, H slices and expert tiles)."""
+    g = GpuLayer(shape)
+    g.layer(g.x)
+    codes, scales = moe.quantize_activations(g.x)
+    torch.cuda.synchronize()
+    kb = (shape.H + 127) // 128
+    xq = _workspace_view(g.layer, shape.T, "xq", torch.uint8, (shape.T, shape.H))
+    sx = _workspace_view(g.layer, shape.T, "sx", torch.float32, (shape.T, kb))
+    assert torch.equal(xq, codes)
+    assert torch.equal(sx.view(torch.int32), scales.view(torch.int32))
+
+
 def test_forward_profiled_matches_forward_with_partial_events():
     """The per-stage timing entry point does the same work: bit-identical output with all
     stage events, and with only the GEMM1 boundaries recorded (NULL entries elsewhere)."""
