@@ -28,10 +28,12 @@ constexpr int kGemmQueues = 8;      // per-XCD work queues of one large-group GE
 // partial[s][t][e] = sum over the s-th slice of H (kslice a multiple of 128) of
 // x[t,h] * W[e,h]; also clears hist[0, hist_n) for the top-k step, and with xq != NULL
 // writes the 1x128 quantisation of x (codes xq [T,H], scales sx [T, ceil(H/128)]), the
-// same as launch_quantize_act
+// same as launch_quantize_act.  With parts != NULL (space for 3 E H bf16) W is first
+// split once into its three bf16 planes there (worth it when many token tiles would each
+// split their weight tile again).
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
                           int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
-                          uint8_t* xq = nullptr, float* sx = nullptr);
+                          uint8_t* xq = nullptr, float* sx = nullptr, uint16_t* parts = nullptr);
 // ids/gates, counted into the per-chunk expert histogram hist[chunk][E] (cleared before)
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
                  int32_t* ids, float* gates, int32_t* hist, hipStream_t st);

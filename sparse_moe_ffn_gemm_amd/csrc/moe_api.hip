@@ -20,7 +20,8 @@ struct Plan {
   int T, H, E, k, I;
   long rows;
   int ksplit, kslice, nchunks, bm, max_tiles;
-  size_t partial, hist, chunk_base, tiles, num_tiles, expert_tile_off;
+  bool presplit;   // router weights split once per call (many token tiles)
+  size_t partial, hist, wparts, chunk_base, tiles, num_tiles, expert_tile_off;
   size_t ids, gates, counts, offsets, perm, inv;
   size_t xq, sx, h, sh, y;
   size_t total;
@@ -55,6 +56,8 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   };
   p->partial = take(sizeof(float) * p->ksplit * static_cast<size_t>(T) * E);
   p->hist = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
+  p->presplit = ceil_div(T, moe::kRouterTile) >= 8;
+  p->wparts = take(p->presplit ? sizeof(uint16_t) * 3 * static_cast<size_t>(E) * H : 0);
   p->chunk_base = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
   p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->max_tiles));
   p->num_tiles = take(sizeof(int32_t) * (1 + 2 * moe::kGemmQueues));   // + the GEMMs' queues
@@ -107,7 +110,8 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
   moe::launch_router_logits(x, rw, p.T, p.H, p.E, p.ksplit, p.kslice, at<float>(ws, p.partial),
                             at<int32_t>(ws, p.hist), p.nchunks * p.E, st,
                             quant_x ? at<uint8_t>(ws, p.xq) : nullptr,
-                            quant_x ? at<float>(ws, p.sx) : nullptr);
+                            quant_x ? at<float>(ws, p.sx) : nullptr,
+                            p.presplit ? at<uint16_t>(ws, p.wparts) : nullptr);
   mark(ev, 1, st);
   moe::launch_topk(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, tb.ids, tb.gates,
                    at<int32_t>(ws, p.hist), st);

@@ -42,13 +42,51 @@ __device__ __forceinline__ v8bf lds_bf8(const uint16_t* p) {
   return __builtin_bit_cast(v8bf, u);
 }
 
+// Exact three-way split of four fp32 weights into bf16 parts (hi, mid, lo), packed two
+// per dword: w = hi + mid + lo by truncation, no rounding anywhere.
+__device__ __forceinline__ void split3(const float4 v, uint2& ph, uint2& pm, uint2& pl) {
+  const float w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[2] = {0u, 0u}, m[2] = {0u, 0u}, l[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t u = __float_as_uint(w[k]);
+    const float hi = __uint_as_float(u & 0xFFFF0000u);
+    const float r1 = w[k] - hi;                                  // exact
+    const uint32_t um = __float_as_uint(r1);
+    const float mid = __uint_as_float(um & 0xFFFF0000u);
+    const float lo = r1 - mid;                                   // exact, <= 8 bits
+    h[k >> 1] |= (u >> 16) << (16 * (k & 1));
+    m[k >> 1] |= (um >> 16) << (16 * (k & 1));
+    l[k >> 1] |= (__float_as_uint(lo) >> 16) << (16 * (k & 1));
+  }
+  ph = make_uint2(h[0], h[1]);
+  pm = make_uint2(m[0], m[1]);
+  pl = make_uint2(l[0], l[1]);
+}
+
+// W [E, H] fp32 -> planes [3][E, H] bf16 (hi, mid, lo), once per call for layers with
+// many token tiles, so the router workgroups load the parts instead of each splitting
+// its weight tile again.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ W, long n4,
+                                                           long plane, uint16_t* __restrict__ parts) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  uint2 ph, pm, pl;
+  split3(reinterpret_cast<const float4*>(W)[i], ph, pm, pl);
+  reinterpret_cast<uint2*>(parts)[i] = ph;
+  reinterpret_cast<uint2*>(parts + plane)[i] = pm;
+  reinterpret_cast<uint2*>(parts + 2 * plane)[i] = pl;
+}
+
+template <bool PRESPLIT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ W, int T,
                                                             int H, int E, int kslice,
                                                             float* __restrict__ partial,
                                                             int32_t* __restrict__ hist,
                                                             int hist_n, uint8_t* __restrict__ xq,
-                                                            float* __restrict__ sx) {
+                                                            float* __restrict__ sx,
+                                                            const uint16_t* __restrict__ parts) {
   __shared__ __align__(16) uint16_t xs[kRouterTile * kRS];
   __shared__ __align__(16) uint16_t wp[3][kRouterTile * kRS];   // hi, mid, lo parts of W
   {  // clear the dispatch histograms that the top-k step accumulates (a slice per block)
@@ -71,9 +109,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < 2; ++j) tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // one step's global loads: x 64 rows x 16 chunks of 8 bf16, W 64 rows x 32 float4
+  // one step's global loads: x 64 rows x 16 chunks of 8 bf16; W 64 rows x 32 float4, or
+  // (pre-split) three planes of 64 rows x 16 chunks of 8 bf16
   uint4 xr[4];
-  float4 wr[8];
+  float4 wr[PRESPLIT ? 1 : 8];
+  uint4 pr[PRESPLIT ? 12 : 1];
+  const long plane = static_cast<long>(E) * H;
   auto load = [&](int h0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -82,12 +123,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       xr[i] = make_uint4(0u, 0u, 0u, 0u);
       if (t < T && h < h_end) xr[i] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * H + h);
     }
+    if constexpr (PRESPLIT) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = tid + 256 * i;
-      const int e = e0 + (q >> 5), h = h0 + (q & 31) * 4;
-      wr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < E && h < h_end) wr[i] = *reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + h);
+      for (int i = 0; i < 12; ++i) {
+        const int q = tid + 256 * (i & 3), pl = i >> 2;
+        const int e = e0 + (q >> 4), h = h0 + (q & 15) * 8;
+        pr[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (e < E && h < h_end)
+          pr[i] = *reinterpret_cast<const uint4*>(parts + pl * plane + static_cast<size_t>(e) * H + h);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = tid + 256 * i;
+        const int e = e0 + (q >> 5), h = h0 + (q & 31) * 4;
+        wr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e < E && h < h_end) wr[i] = *reinterpret_cast<const float4*>(W + static_cast<size_t>(e) * H + h);
+      }
     }
   };
   if (h_begin < h_end) load(h_begin);
@@ -97,27 +149,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       const int q = tid + 256 * i;
       *reinterpret_cast<uint4*>(xs + (q >> 4) * kRS + (q & 15) * 8) = xr[i];
     }
+    if constexpr (PRESPLIT) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {   // split in 3 exact bf16 parts
-      const int q = tid + 256 * i;
-      const int row = q >> 5, c = q & 31;
-      const float w[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
-      uint32_t ph[2] = {0u, 0u}, pm[2] = {0u, 0u}, pl[2] = {0u, 0u};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t u = __float_as_uint(w[k]);
-        const float hi = __uint_as_float(u & 0xFFFF0000u);
-        const float r1 = w[k] - hi;                                  // exact
-        const uint32_t um = __float_as_uint(r1);
-        const float mid = __uint_as_float(um & 0xFFFF0000u);
-        const float lo = r1 - mid;                                   // exact, <= 8 bits
-        ph[k >> 1] |= (u >> 16) << (16 * (k & 1));
-        pm[k >> 1] |= (um >> 16) << (16 * (k & 1));
-        pl[k >> 1] |= (__float_as_uint(lo) >> 16) << (16 * (k & 1));
+      for (int i = 0; i < 12; ++i) {
+        const int q = tid + 256 * (i & 3);
+        *reinterpret_cast<uint4*>(&wp[i >> 2][(q >> 4) * kRS + (q & 15) * 8]) = pr[i];
       }
-      *reinterpret_cast<uint2*>(&wp[0][row * kRS + c * 4]) = make_uint2(ph[0], ph[1]);
-      *reinterpret_cast<uint2*>(&wp[1][row * kRS + c * 4]) = make_uint2(pm[0], pm[1]);
-      *reinterpret_cast<uint2*>(&wp[2][row * kRS + c * 4]) = make_uint2(pl[0], pl[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {   // split in 3 exact bf16 parts
+        const int q = tid + 256 * i;
+        const int row = q >> 5, c = q & 31;
+        uint2 ph, pm, pl;
+        split3(wr[i], ph, pm, pl);
+        *reinterpret_cast<uint2*>(&wp[0][row * kRS + c * 4]) = ph;
+        *reinterpret_cast<uint2*>(&wp[1][row * kRS + c * 4]) = pm;
+        *reinterpret_cast<uint2*>(&wp[2][row * kRS + c * 4]) = pl;
+      }
     }
     __syncthreads();
     if (h0 + kRC < h_end) load(h0 + kRC);   // next step's loads fly during this step
@@ -426,10 +474,18 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
 
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
                           int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
-                          uint8_t* xq, float* sx) {
+                          uint8_t* xq, float* sx, uint16_t* parts) {
   dim3 grid(ceil_div(T, kRouterTile), ceil_div(E, kRouterTile), ksplit);
-  router_logits_kernel<<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist, hist_n,
-                                                   xq, sx);
+  if (parts != nullptr) {
+    const long n4 = static_cast<long>(E) * H / 4;   // H is a multiple of 64
+    router_split_kernel<<<dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st>>>(
+        W, n4, static_cast<long>(E) * H, parts);
+    router_logits_kernel<true><<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist,
+                                                           hist_n, xq, sx, parts);
+  } else {
+    router_logits_kernel<false><<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist,
+                                                            hist_n, xq, sx, nullptr);
+  }
 }
 
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
