@@ -207,6 +207,31 @@ def main():
           + ", ".join(f"{k} {v * 1e3:.1f} us" for k, v in stage_ms.items()), file=sys.stderr,
           flush=True)
 
+    # Per-step distribution (after the timed region): each step bracketed by its own events;
+    # for weight-streaming (HBM-bound) layers also with the caches evicted before every step
+    # by reading a 1 GiB buffer (outside the events; a read sweep leaves no dirty lines to
+    # write back during the step), so no weight bytes come from L2 or the 256 MB
+    # last-level cache.
+    def per_step(n, flush=None):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        sink = torch.empty(1, dtype=torch.float32, device=dev)
+        for a, b in ev:
+            if flush is not None:
+                torch.sum(flush, dim=0, out=sink)
+            a.record()
+            moe.forward(*fwd_args, out=out, routing=routing, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev])
+        return {"p10": round(float(np.percentile(t, 10)), 4), "p50": round(float(np.median(t)), 4),
+                "p90": round(float(np.percentile(t, 90)), 4)}
+    step_dist = {"warm_ms": per_step(max(args.steps, 20))}
+    if shape.T * shape.top_k <= 4096:            # decode-sized: weight streaming
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        step_dist["cold_ms"] = per_step(max(args.steps, 20), flush=scratch)
+        del scratch
+
     counts = routing["expert_counts"].cpu().numpy()
     alg = algorithmic(shape, counts)
     step_s = ms_step / 1e3
@@ -241,6 +266,7 @@ def main():
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "active_experts": alg["active_experts"],
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "step_ms_dist": step_dist,
         "roofline": roof,
         "cpu_baseline": None,
     }
