@@ -19,6 +19,9 @@ EDGE = [
     custom_shape(T=130, H=384, E=64, top_k=2, I=64, seed=24),       # ragged chunks
     custom_shape(T=300, H=256, E=256, top_k=8, I=64, seed=25),      # E = 256, idle experts
     custom_shape(T=200, H=256, E=16, top_k=3, I=64, seed=26, router="hot"),
+    # the last single-chunk batch (scan and scatter in one workgroup) and the first two-chunk one
+    custom_shape(T=256, H=192, E=32, top_k=4, I=64, seed=27),
+    custom_shape(T=257, H=192, E=32, top_k=4, I=64, seed=28),
 ]
 
 
