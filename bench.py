@@ -19,9 +19,11 @@ tokens of the same layer, on one host thread.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -60,9 +62,9 @@ def algorithmic(shape, counts):
         gemm2=dict(flops=g2_flops, bytes=w2 + hq + rows * H * 2))
 
 
-def traffic_from_profiles(workload, kernel):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken
-    on the current kernel source (else None)."""
+def pmc_record(workload, kernel):
+    """The committed rocprofv3 counter summary of one GEMM launch on this workload, if it
+    was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -70,9 +72,52 @@ def traffic_from_profiles(workload, kernel):
         rec = json.load(f)
     src = os.path.join(ROOT, "sparse_moe_ffn_gemm_amd", "csrc", rec.get("source", "gemm.hip"))
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if sha != rec.get("source_sha256"):
+    return rec if sha == rec.get("source_sha256") else None
+
+
+def gpu_sysfs(torch, index=0):
+    """sysfs directory of the torch device, matched by PCI address (None if not found)."""
+    p = torch.cuda.get_device_properties(index)
+    try:
+        addr = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}."
+    except AttributeError:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    for d in glob.glob("/sys/class/drm/card*/device"):
+        if (os.path.basename(os.path.realpath(d)).startswith(addr)
+                and os.path.exists(os.path.join(d, "pp_dpm_sclk"))):
+            return d
+    return None
+
+
+def current_mhz(sysdir, name):
+    """The level a pp_dpm_* file marks as current ('*'), in MHz (None if unreadable)."""
+    if sysdir is None:
+        return None
+    try:
+        with open(os.path.join(sysdir, name)) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*mhz", line, re.I)
+                    return int(m.group(1)) if m else None
+    except OSError:
+        pass
+    return None
+
+
+def device_copy_gbs(torch, dev, mib=1024, reps=5):
+    """Bytes read + written per second by a plain 1 GiB device-to-device copy (context for
+    the vendor HBM peak)."""
+    a = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * a.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def cpu_baseline(shape, li, n_tokens):
@@ -163,6 +208,9 @@ def main():
     fwd_args = (x, layer.router_w, layer.router_b, layer.w13, layer.w13_scales, layer.b13,
                 layer.w2, layer.w2_scales, layer.b2, shape.top_k)
     torch.cuda.synchronize()
+    sysdir = gpu_sysfs(torch)
+    clocks = {"sclk_mhz_before": current_mhz(sysdir, "pp_dpm_sclk"),
+              "mclk_mhz_before": current_mhz(sysdir, "pp_dpm_mclk")}
     print(f"[bench] {shape.name}: setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr,
           flush=True)
 
@@ -232,6 +280,30 @@ def main():
         step_dist["cold_ms"] = per_step(max(args.steps, 20), flush=scratch)
         del scratch
 
+    # Engine clock while the layer runs (clocks are not locked): enqueue about 0.3 s of
+    # steps, then read the current sysfs level until they finish.
+    n_busy = int(min(4000, max(20, 300.0 / ms_step)))
+    done = torch.cuda.Event()
+    for _ in range(n_busy):
+        moe.forward(*fwd_args, out=out, routing=routing, workspace=ws)
+    done.record()
+    busy = []
+    while not done.query():
+        v = current_mhz(sysdir, "pp_dpm_sclk")
+        if v is None:
+            break
+        busy.append(v)
+        time.sleep(0.002)
+    torch.cuda.synchronize()
+    if busy:
+        clocks["sclk_mhz_busy"] = {"p10": float(np.percentile(busy, 10)),
+                                   "p50": float(np.median(busy)),
+                                   "p90": float(np.percentile(busy, 90)), "samples": len(busy)}
+    clocks["sclk_mhz_after"] = current_mhz(sysdir, "pp_dpm_sclk")
+    clocks["mclk_mhz_after"] = current_mhz(sysdir, "pp_dpm_mclk")
+    clocks["locked"] = False
+    copy_gbs = device_copy_gbs(torch, dev)
+
     counts = routing["expert_counts"].cpu().numpy()
     alg = algorithmic(shape, counts)
     step_s = ms_step / 1e3
@@ -249,7 +321,11 @@ def main():
         roof = {"bound": "hbm", "achieved": k_alg["bytes"] / k_s / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_from_profiles(shape.name, dom)
+    rec = pmc_record(shape.name, dom)
+    roof["traffic"] = rec.get("hbm_bytes_per_launch") if rec else None
+    if rec and "mfma_busy_frac" in rec:
+        # matrix-core busy cycles / (active cycles x SIMDs), from the same counter run
+        roof["mfma_busy_frac_counter"] = rec["mfma_busy_frac"]
     roof["kernel"] = dom
     roof["kernel_us"] = round(dom_ms * 1e3, 2)
     roof["achieved"] = round(roof["achieved"], 2)
@@ -265,6 +341,11 @@ def main():
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_FP8_TFLOPS, 4),
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "active_experts": alg["active_experts"],
+        "expert_rows": {"min": int(counts.min()), "max": int(counts.max()),
+                        "mean": round(float(counts.mean()), 2), "idle": int((counts == 0).sum())},
+        "margin_redraws": int(li.redraws),
+        "device_copy_gbs": round(copy_gbs, 1),
+        "clocks": clocks,
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "step_ms_dist": step_dist,
         "roofline": roof,
