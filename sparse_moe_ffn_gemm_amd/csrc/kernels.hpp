@@ -47,6 +47,16 @@ void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32
                           int T = 0, int top_k = 0, int32_t* perm = nullptr, int32_t* inv = nullptr);
 void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,
                              int top_k, int32_t* perm, int32_t* inv, hipStream_t st);
+constexpr int kTailLogits = 16384;  // largest T x E of the one-workgroup routing tail
+constexpr int kTailSplit = 64;      // and its largest number of router H slices
+constexpr int kTailTopK = 4;        // and its largest top_k
+// T <= kChunk, T E <= kTailLogits, ksplit <= kTailSplit, top_k <= kTailTopK: top-k + softmax, scan, M-tile list and scatter in one
+// workgroup (replaces
+// launch_topk + launch_dispatch_scan; the router need not clear any histogram).
+void launch_route_tail(const float* partial, int ksplit, const float* bias, int T, int E,
+                       int top_k, int bm, int32_t* ids, float* gates, int32_t* counts,
+                       int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
+                       int32_t* expert_tile_off, int32_t* perm, int32_t* inv, hipStream_t st);
 
 // ---- grouped FP8 GEMMs ----
 struct GemmArgs {

@@ -36,6 +36,12 @@ bool shape_ok(int T, int H, int E, int k, int I) {
   return true;
 }
 
+// Decode-sized layers whose routing tail (top-k, scan, scatter) runs in one workgroup.
+bool uses_route_tail(int T, int E, int k, int ksplit) {
+  return T <= moe::kChunk && static_cast<long>(T) * E <= moe::kTailLogits &&
+         k <= moe::kTailTopK && ksplit <= moe::kTailSplit;
+}
+
 void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   p->T = T; p->H = H; p->E = E; p->k = k; p->I = I;
   p->rows = static_cast<long>(T) * k;
@@ -43,6 +49,8 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   const int tiles2d = ceil_div(T, moe::kRouterTile) * ceil_div(E, moe::kRouterTile);
   int ks = ceil_div(1024, tiles2d);
   ks = std::max(1, std::min(ks, H / 128 > 0 ? H / 128 : 1));
+  // the one-workgroup routing tail reads every slice of every logit: keep them few
+  if (uses_route_tail(T, E, k, 0)) ks = std::min(ks, 16);
   p->kslice = ceil_div(ceil_div(H, ks), moe::kBlock) * moe::kBlock;   // whole quantisation groups
   p->ksplit = ceil_div(H, p->kslice);
   p->nchunks = ceil_div(T, moe::kChunk);
@@ -107,17 +115,28 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
                      const Tables& tb, void* ws, hipStream_t st, hipEvent_t* ev = nullptr,
                      bool quant_x = false) {
   mark(ev, 0, st);
+  // a single chunk of tokens (decode-sized T): one workgroup does the scan and the
+  // scatter; with few logits the same workgroup also does top-k + softmax
+  const bool one_chunk = p.nchunks == 1;
+  const bool tail = uses_route_tail(p.T, p.E, p.k, p.ksplit);
   moe::launch_router_logits(x, rw, p.T, p.H, p.E, p.ksplit, p.kslice, at<float>(ws, p.partial),
-                            at<int32_t>(ws, p.hist), p.nchunks * p.E, st,
+                            at<int32_t>(ws, p.hist), tail ? 0 : p.nchunks * p.E, st,
                             quant_x ? at<uint8_t>(ws, p.xq) : nullptr,
                             quant_x ? at<float>(ws, p.sx) : nullptr,
                             p.presplit ? at<uint16_t>(ws, p.wparts) : nullptr);
   mark(ev, 1, st);
+  if (tail) {
+    moe::launch_route_tail(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, p.bm, tb.ids,
+                           tb.gates, tb.counts, tb.offsets, at<int32_t>(ws, p.chunk_base),
+                           at<moe::MTile>(ws, p.tiles), at<int32_t>(ws, p.num_tiles),
+                           at<int32_t>(ws, p.expert_tile_off), tb.perm, tb.inv, st);
+    mark(ev, 2, st);
+    mark(ev, 3, st);
+    return;
+  }
   moe::launch_topk(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, tb.ids, tb.gates,
                    at<int32_t>(ws, p.hist), st);
   mark(ev, 2, st);
-  // a single chunk of tokens (decode-sized T): the scan's workgroup also scatters
-  const bool one_chunk = p.nchunks == 1;
   moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, tb.counts, tb.offsets,
                             at<int32_t>(ws, p.chunk_base), at<moe::MTile>(ws, p.tiles),
                             at<int32_t>(ws, p.num_tiles), at<int32_t>(ws, p.expert_tile_off), st,

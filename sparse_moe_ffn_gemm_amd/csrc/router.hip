@@ -227,84 +227,123 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 // l, l+64, l+128, l+192.  Each round takes the wave-wide (largest value, lowest index)
 // and removes it.  The chosen experts are counted into the token's chunk histogram.
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ void argmax_step(float& v, int& idx, int off) {
-  const float ov = __shfl_xor(v, off, 64);
-  const int oi = __shfl_xor(idx, off, 64);
+// (v, idx) := the larger of (v, idx) and (ov, oi): larger value, ties to the lower index
+// (a total order, so any reduction tree gives the same winner).
+__device__ __forceinline__ void argmax_take(float& v, int& idx, float ov, int oi) {
   if (ov > v || (ov == v && oi < idx)) {
     v = ov;
     idx = oi;
   }
 }
 
-// Top-k of token t for the calling wave: the k selected experts (descending logit, ties
-// to the lower index) and their softmax gates, valid in lanes [0, top_k) as (id, gate) of
-// rank j = lane.  Logits are the router partial sums over H slices plus the bias.
-__device__ __forceinline__ void topk_token(const float* __restrict__ partial, int ksplit,
-                                           const float* __restrict__ bias, int T, int E, int top_k,
-                                           int t, int lane, int* id_out, float* gate_out) {
-  const size_t TE = static_cast<size_t>(T) * E;
-  float v[4];
+template <int CTRL>
+__device__ __forceinline__ int dpp_row_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave-wide argmax, left in every lane, on the vector ALU only: DPP row rotations by 8, 4,
+// 2 and 1 give every lane its row of 16's winner, then the four rows' winners are read
+// from lanes 0, 16, 32 and 48 (no LDS permutes, which serialise on the CU's LDS when many
+// waves select at once).
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+  argmax_take(v, idx, dpp_row<0x128>(v), dpp_row_i<0x128>(idx));
+  argmax_take(v, idx, dpp_row<0x124>(v), dpp_row_i<0x124>(idx));
+  argmax_take(v, idx, dpp_row<0x122>(v), dpp_row_i<0x122>(idx));
+  argmax_take(v, idx, dpp_row<0x121>(v), dpp_row_i<0x121>(idx));
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(idx, 0);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    if (e < E) {
-      // four independent partial sums so that the slice loads are in flight together
-      const float* src = partial + static_cast<size_t>(t) * E + e;
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
-      int sp = 0;
-      for (; sp + 4 <= ksplit; sp += 4) {
+  for (int r = 16; r < 64; r += 16)
+    argmax_take(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), r)),
+                __builtin_amdgcn_readlane(idx, r));
+  v = bv;
+  idx = bi;
+}
+
+// Top-k of NT tokens for the calling wave (their dependent cross-lane steps
+// interleaved), from their logits v[n][q] = logit of expert lane + 64 q (-inf past E; a
+// NaN logit never wins): the k selected experts (descending logit, ties to the lower
+// index) and their softmax gates, valid in lanes [0, top_k) as (id, gate) of rank
+// j = lane.
+template <int NT>
+__device__ __forceinline__ void topk_select(float (&v)[NT][4], int E, int top_k, int lane,
+                                            int (&id_out)[NT], float (&gate_out)[NT]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s4[u] += src[(sp + u) * TE];
-      }
-      for (; sp < ksplit; ++sp) s4[0] += src[sp * TE];
-      float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      s += bias ? bias[e] : 0.f;
-      v[q] = s == s ? s : -INFINITY;   // a NaN logit never wins
-    } else {
-      v[q] = -INFINITY;
-    }
-  }
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[n][q] = v[n][q] == v[n][q] ? v[n][q] : -INFINITY;
   // k <= 8 rounds, fully unrolled so that every array stays in registers
-  float sel_v[8];
-  int sel_i[8];
+  float sel_v[NT][8];
+  int sel_i[NT][8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    sel_v[j] = -INFINITY;
-    sel_i[j] = 0;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      sel_v[n][j] = -INFINITY;
+      sel_i[n][j] = 0;
+    }
     if (j < top_k) {
-      float bv = v[0];
-      int bi = lane;
+      float bv[NT];
+      int bi[NT];
 #pragma unroll
-      for (int q = 1; q < 4; ++q)
-        if (v[q] > bv) {  // strict: ties keep the lower expert index
-          bv = v[q];
-          bi = lane + 64 * q;
-        }
-      if (bi >= E) bi = 0x7FFFFFFF;
+      for (int n = 0; n < NT; ++n) {
+        bv[n] = v[n][0];
+        bi[n] = lane;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) argmax_step(bv, bi, off);
-      if (bi >= E) bi = 0;             // unreachable for finite inputs; keeps ids in range
-      sel_v[j] = bv;
-      sel_i[j] = bi;
+        for (int q = 1; q < 4; ++q)
+          if (v[n][q] > bv[n]) {  // strict: ties keep the lower expert index
+            bv[n] = v[n][q];
+            bi[n] = lane + 64 * q;
+          }
+        if (bi[n] >= E) bi[n] = 0x7FFFFFFF;
+      }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (bi == lane + 64 * q) v[q] = -INFINITY;
+      for (int n = 0; n < NT; ++n) wave_argmax(bv[n], bi[n]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        if (bi[n] >= E) bi[n] = 0;     // unreachable for finite inputs; keeps ids in range
+        sel_v[n][j] = bv[n];
+        sel_i[n][j] = bi[n];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (bi[n] == lane + 64 * q) v[n][q] = -INFINITY;
+      }
     }
   }
-  float z[8], sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    z[j] = j < top_k ? expf(sel_v[j] - sel_v[0]) : 0.f;
-    sum += z[j];
-  }
-  *id_out = 0;
-  *gate_out = 0.f;
+  for (int n = 0; n < NT; ++n) {
+    float z[8], sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (lane == j) {
-      *id_out = sel_i[j];
-      *gate_out = z[j] / sum;
+    for (int j = 0; j < 8; ++j) {
+      z[j] = j < top_k ? expf(sel_v[n][j] - sel_v[n][0]) : 0.f;
+      sum += z[j];
     }
+    id_out[n] = 0;
+    gate_out[n] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (lane == j) {
+        id_out[n] = sel_i[n][j];
+        gate_out[n] = z[j] / sum;
+      }
+  }
+}
+
+// Logit of token t, expert e: the router partial sums over the H slices plus the bias
+// (four independent partial sums so that the slice loads are in flight together).
+__device__ __forceinline__ float logit_of(const float* __restrict__ partial, int ksplit,
+                                          const float* __restrict__ bias, size_t TE, size_t idx,
+                                          int e) {
+  const float* src = partial + idx;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  int sp = 0;
+  for (; sp + 4 <= ksplit; sp += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s4[u] += src[(sp + u) * TE];
+  }
+  for (; sp < ksplit; ++sp) s4[0] += src[sp * TE];
+  float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  return s + (bias ? bias[e] : 0.f);
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int ksplit,
@@ -315,13 +354,21 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  int id;
-  float g;
-  topk_token(partial, ksplit, bias, T, E, top_k, t, lane, &id, &g);
+  const size_t TE = static_cast<size_t>(T) * E;
+  float v[1][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    v[0][q] = e < E ? logit_of(partial, ksplit, bias, TE, static_cast<size_t>(t) * E + e, e)
+                    : -INFINITY;
+  }
+  int id[1];
+  float g[1];
+  topk_select<1>(v, E, top_k, lane, id, g);
   if (lane < top_k) {
-    ids[static_cast<size_t>(t) * top_k + lane] = id;
-    gates[static_cast<size_t>(t) * top_k + lane] = g;
-    atomicAdd(&hist[static_cast<size_t>(t / kChunk) * E + id], 1);
+    ids[static_cast<size_t>(t) * top_k + lane] = id[0];
+    gates[static_cast<size_t>(t) * top_k + lane] = g[0];
+    atomicAdd(&hist[static_cast<size_t>(t / kChunk) * E + id[0]], 1);
   }
 }
 
@@ -379,34 +426,46 @@ __device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ ids, i
 // With a single chunk (decode-sized T) the same workgroup then scatters it, which saves
 // a launch on the latency-bound decode path.
 // ------------------------------------------------------------------------------------
-__device__ int exclusive_scan256(int v, int* tmp) {   // lanes [0, 256) hold the values
-  const int tid = threadIdx.x;
-  if (tid < 256) tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = (tid < 256 && tid >= off) ? tmp[tid - off] : 0;
-    __syncthreads();
-    if (tid < 256) tmp[tid] += add;
-    __syncthreads();
-  }
-  const int incl = tid < 256 ? tmp[tid] : 0;
-  __syncthreads();
-  return incl - v;
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
 }
 
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ hist,
-                                                             int nchunks, int E, int bm,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ chunk_base,
-                                                             MTile* __restrict__ tiles,
-                                                             int32_t* __restrict__ num_tiles,
-                                                             int32_t* __restrict__ expert_tile_off,
-                                                             const int32_t* __restrict__ ids, int T,
-                                                             int top_k, int32_t* __restrict__ perm,
-                                                             int32_t* __restrict__ inv) {
-  __shared__ int part[4][256];
-  __shared__ int tmp[256];
+// Exclusive prefix sum over lanes [0, 256) of the workgroup (4 waves): an inclusive scan
+// inside each wave on DPP (row shifts by 1, 2, 4, 8 within rows of 16, then the row
+// broadcasts of lanes 15 and 31), the wave totals through LDS, one barrier each way.
+// Every thread of the workgroup must call it; lanes >= 256 get 0.
+__device__ int exclusive_scan256(int v, int* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int x = v;
+  x += dpp_i<0x111, 0xF>(x);     // row_shr:1
+  x += dpp_i<0x112, 0xF>(x);     // row_shr:2
+  x += dpp_i<0x114, 0xF>(x);     // row_shr:4
+  x += dpp_i<0x118, 0xF>(x);     // row_shr:8
+  x += dpp_i<0x142, 0xA>(x);     // row_bcast:15 into rows 1 and 3
+  x += dpp_i<0x143, 0xC>(x);     // row_bcast:31 into rows 2 and 3
+  if (tid < 256 && lane == 63) tmp[w] = x;
+  __syncthreads();
+  int base = 0;
+  if (tid < 256)
+    for (int ww = 0; ww < w; ++ww) base += tmp[ww];
+  __syncthreads();
+  return tid < 256 ? base + x - v : 0;
+}
+
+// The scan's body for a workgroup of 1024 lanes; `hist` and `ids` may point to global
+// memory or to this workgroup's LDS.
+__device__ __forceinline__ void dispatch_scan_body(const int32_t* hist, int nchunks, int E, int bm,
+                                                   int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ chunk_base,
+                                                   MTile* __restrict__ tiles,
+                                                   int32_t* __restrict__ num_tiles,
+                                                   int32_t* __restrict__ expert_tile_off,
+                                                   const int32_t* ids, int T, int top_k,
+                                                   int32_t* __restrict__ perm,
+                                                   int32_t* __restrict__ inv, int (*part)[256],
+                                                   int* tmp) {
   const int tid = threadIdx.x, e = tid & 255, q = tid >> 8;
   const int per = (nchunks + 3) / 4;
   const int c0 = min(nchunks, q * per), c1 = min(nchunks, c0 + per);
@@ -459,6 +518,198 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   }
 }
 
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ hist,
+                                                             int nchunks, int E, int bm,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ chunk_base,
+                                                             MTile* __restrict__ tiles,
+                                                             int32_t* __restrict__ num_tiles,
+                                                             int32_t* __restrict__ expert_tile_off,
+                                                             const int32_t* __restrict__ ids, int T,
+                                                             int top_k, int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ inv) {
+  __shared__ int part[4][256];
+  __shared__ int tmp[256];
+  dispatch_scan_body(hist, nchunks, E, bm, counts, offsets, chunk_base, tiles, num_tiles,
+                     expert_tile_off, ids, T, top_k, perm, inv, part, tmp);
+}
+
+// ------------------------------------------------------------------------------------
+// The same logit with every slice load issued at once (MAXS >= ksplit registers; the
+// indices past ksplit are clamped to the last slice, so every load stays inside the
+// partials, and their values are dropped), summed pairwise: one memory round trip.
+template <int MAXS>
+__device__ __forceinline__ float logit_wide(const float* __restrict__ partial, int ksplit,
+                                            const float* __restrict__ bias, size_t TE, size_t idx,
+                                            int e) {
+  float r[MAXS];
+#pragma unroll
+  for (int u = 0; u < MAXS; ++u) r[u] = partial[static_cast<size_t>(min(u, ksplit - 1)) * TE + idx];
+#pragma unroll
+  for (int u = 0; u < MAXS; ++u) r[u] = u < ksplit ? r[u] : 0.f;
+#pragma unroll
+  for (int w = MAXS / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int u = 0; u < w; ++u) r[u] += r[u + w];
+  return r[0] + (bias ? bias[e] : 0.f);
+}
+
+// logits[t * SE + e] for every (t, e), a NaN logit stored as -inf (it never wins).
+template <int MAXS>
+__device__ __forceinline__ void tail_logits(const float* __restrict__ partial, int ksplit,
+                                            const float* __restrict__ bias, int T, int E, int SE,
+                                            float* logits) {
+  const int TE = T * E;
+  for (int i = threadIdx.x; i < TE; i += blockDim.x) {
+    const float v = logit_wide<MAXS>(partial, ksplit, bias, TE, i, i % E);
+    logits[(i / E) * SE + i % E] = v == v ? v : -INFINITY;
+  }
+}
+
+// Inserts candidate (v, i) (v not NaN) into the list (lv, li) of K candidates kept in
+// descending order of value; empty slots hold NaN, at the end, and take any candidate.
+// Candidates must arrive in ascending expert order (of equal values the earlier stays
+// ahead, so ties go to the lower index).  The K compares are independent of each other
+// (the list is sorted, so they switch once from false to true at the insertion point)
+// and each slot then takes the candidate, its predecessor or itself: no serial chain.
+template <int K>
+__device__ __forceinline__ void list_insert(float (&lv)[K], int (&li)[K], float v, int i) {
+  bool tk[K];
+#pragma unroll
+  for (int s = 0; s < K; ++s) tk[s] = !(v <= lv[s]);
+#pragma unroll
+  for (int s = K - 1; s >= 1; --s) {
+    lv[s] = tk[s] ? (tk[s - 1] ? lv[s - 1] : v) : lv[s];
+    li[s] = tk[s] ? (tk[s - 1] ? li[s - 1] : i) : li[s];
+  }
+  lv[0] = tk[0] ? v : lv[0];
+  li[0] = tk[0] ? i : li[0];
+}
+
+// Top-k + softmax of every token with a lane per token, from logits in LDS (no NaN):
+// wave (g, p), p < P, keeps the best K of experts [p E / P, (p + 1) E / P) for tokens
+// 64 g + lane in registers (P = min(4, E / K) parts, so with P > 1 every list is full);
+// then wave g merges each token's P lists (parts in order, so the insertions stay in
+// ascending expert order), takes the softmax over the first top_k and writes ids, gates,
+// the LDS copy of the ids and the LDS histogram.  The partial lists are kept as
+// cv/ci[(p K + s) kChunk + t].
+template <int K>
+__device__ __forceinline__ void tail_topk(const float* logits, int SE, int T, int E, int top_k,
+                                          float* cv, int* ci, int32_t* __restrict__ ids,
+                                          float* __restrict__ gates, int* sids, int* hist) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = (T + 63) / 64;
+  const int P = max(1, min(4, E / K));
+  float lv[K];
+  int li[K];
+  if (wave < 4 * G && (wave & 3) < P) {
+    const int g = wave >> 2, p = wave & 3;
+    const int t = 64 * g + lane;
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      lv[s] = __int_as_float(0x7FC00000);   // empty (NaN)
+      li[s] = 0;
+    }
+    if (t < T) {
+      const int e1 = (p + 1) * E / P;
+#pragma unroll 4
+      for (int e = p * E / P; e < e1; ++e) list_insert<K>(lv, li, logits[t * SE + e], e);
+      if (P > 1) {
+#pragma unroll
+        for (int s = 0; s < K; ++s) {
+          cv[(p * K + s) * kChunk + t] = lv[s];
+          ci[(p * K + s) * kChunk + t] = li[s];
+        }
+      }
+    }
+  }
+  if (P > 1) {
+    __syncthreads();
+    if (wave < G) {
+      const int t = 64 * wave + lane;
+#pragma unroll
+      for (int s = 0; s < K; ++s) {
+        lv[s] = __int_as_float(0x7FC00000);
+        li[s] = 0;
+      }
+      if (t < T)
+        for (int c = 0; c < P * K; ++c) list_insert<K>(lv, li, cv[c * kChunk + t], ci[c * kChunk + t]);
+    }
+  }
+  // the finished list of token 64 g + lane is in wave 4 g (P == 1) or wave g (P > 1)
+  const int g = P > 1 ? wave : wave >> 2;
+  const bool owner = P > 1 ? wave < G : (wave < 4 * G && (wave & 3) == 0);
+  const int t = 64 * g + lane;
+  if (owner && t < T) {
+    float z[K], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      z[j] = j < top_k ? expf(lv[j] - lv[0]) : 0.f;
+      sum += z[j];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (j < top_k) {
+        ids[static_cast<size_t>(t) * top_k + j] = li[j];
+        gates[static_cast<size_t>(t) * top_k + j] = z[j] / sum;
+        sids[t * top_k + j] = li[j];
+        atomicAdd(&hist[li[j]], 1);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Routing tail of a decode-sized layer (T <= kChunk, one dispatch chunk, T E <=
+// kTailLogits, at most kTailSplit H slices) in one workgroup of 16 waves: the router
+// partials summed into LDS logits (all slice loads of a logit in flight together), top-k
+// + softmax with a lane per token (tail_topk), then the scan, the M-tile list and the
+// scatter.  Replaces three launches on the latency-bound path.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void route_tail_kernel(const float* __restrict__ partial,
+                                                          int ksplit,
+                                                          const float* __restrict__ bias, int T,
+                                                          int E, int top_k, int bm,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ gates,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ chunk_base,
+                                                          MTile* __restrict__ tiles,
+                                                          int32_t* __restrict__ num_tiles,
+                                                          int32_t* __restrict__ expert_tile_off,
+                                                          int32_t* __restrict__ perm,
+                                                          int32_t* __restrict__ inv) {
+  __shared__ int part[4][256];
+  __shared__ int tmp[256];
+  __shared__ int hist[256];
+  __shared__ int sids[kChunk * 8];
+  __shared__ float logits[kTailLogits + kChunk];   // rows of SE = E | 1 (odd: no bank conflicts)
+  __shared__ float cv[kChunk * 4 * 8];
+  __shared__ int ci[kChunk * 4 * 8];
+  const int tid = threadIdx.x;
+  const int SE = E | 1;
+  if (tid < 256) hist[tid] = 0;
+  if (ksplit <= 8)
+    tail_logits<8>(partial, ksplit, bias, T, E, SE, logits);
+  else if (ksplit <= 16)
+    tail_logits<16>(partial, ksplit, bias, T, E, SE, logits);
+  else if (ksplit <= 32)
+    tail_logits<32>(partial, ksplit, bias, T, E, SE, logits);
+  else
+    tail_logits<64>(partial, ksplit, bias, T, E, SE, logits);
+  __syncthreads();
+  if (top_k <= 2)
+    tail_topk<2>(logits, SE, T, E, top_k, cv, ci, ids, gates, sids, hist);
+  else if (top_k <= 4)
+    tail_topk<4>(logits, SE, T, E, top_k, cv, ci, ids, gates, sids, hist);
+  else
+    tail_topk<8>(logits, SE, T, E, top_k, cv, ci, ids, gates, sids, hist);
+  __syncthreads();
+  dispatch_scan_body(hist, 1, E, bm, counts, offsets, chunk_base, tiles, num_tiles,
+                     expert_tile_off, sids, T, top_k, perm, inv, part, tmp);
+}
+
 // One workgroup per chunk.
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
                                                                const int32_t* __restrict__ chunk_base,
@@ -501,6 +752,15 @@ void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32
   dispatch_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(hist, nchunks, E, bm, counts, offsets,
                                                        chunk_base, tiles, num_tiles,
                                                        expert_tile_off, ids, T, top_k, perm, inv);
+}
+
+void launch_route_tail(const float* partial, int ksplit, const float* bias, int T, int E,
+                       int top_k, int bm, int32_t* ids, float* gates, int32_t* counts,
+                       int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
+                       int32_t* expert_tile_off, int32_t* perm, int32_t* inv, hipStream_t st) {
+  route_tail_kernel<<<dim3(1), dim3(1024), 0, st>>>(partial, ksplit, bias, T, E, top_k, bm, ids,
+                                                    gates, counts, offsets, chunk_base, tiles,
+                                                    num_tiles, expert_tile_off, perm, inv);
 }
 
 void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,

@@ -22,6 +22,9 @@ EDGE = [
     # the last single-chunk batch (scan and scatter in one workgroup) and the first two-chunk one
     custom_shape(T=256, H=192, E=32, top_k=4, I=64, seed=27),
     custom_shape(T=257, H=192, E=32, top_k=4, I=64, seed=28),
+    # one-workgroup routing tail: fewer experts than list slots, uneven expert parts
+    custom_shape(T=40, H=128, E=3, top_k=3, I=64, seed=29),
+    custom_shape(T=64, H=128, E=70, top_k=4, I=64, seed=30),
 ]
 
 
@@ -65,3 +68,26 @@ def test_route_deterministic():
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k], c[k]), k
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 32, 4), (64, 32, 8), (300, 32, 4), (7, 5, 3)])
+def test_route_exact_ties(T, E, k):
+    """A zero router gives every logit exactly 0: each token takes experts 0 .. k-1 (ties
+    to the lower index) with gates 1/k, on the one-workgroup tail (k <= 4, one chunk), the
+    single-chunk kernels (k = 8) and the multi-chunk path (T = 300)."""
+    g = torch.Generator().manual_seed(T * 1000 + E * 10 + k)
+    x = torch.randn(T, 128, generator=g).to(torch.bfloat16).cuda()
+    W = torch.zeros(E, 128, dtype=torch.float32, device="cuda")
+    b = torch.zeros(E, dtype=torch.float32, device="cuda")
+    say(f"route ties T={T} E={E} k={k}")
+    r = moe.route(x, W, b, k)
+    torch.cuda.synchronize()
+    ids = r["topk_ids"].cpu().numpy()
+    assert np.array_equal(ids, np.tile(np.arange(k, dtype=ids.dtype), (T, 1)))
+    np.testing.assert_allclose(r["topk_gates"].cpu().numpy(), 1.0 / k, rtol=0, atol=1e-6)
+    counts = r["expert_counts"].cpu().numpy()
+    assert np.array_equal(counts, np.array([T] * k + [0] * (E - k)))
+    # expert-major, token-ascending: slot e T + t holds (t, j = e)
+    perm = r["perm"].cpu().numpy()
+    want = np.array([t * k + e for e in range(k) for t in range(T)])
+    assert np.array_equal(perm, want)
