@@ -146,8 +146,9 @@ moe_status moe_forward(const uint16_t* x, const float* router_w, const float* ro
  *   6 GEMM2 (+ bias)  7 combine  8 end
  * so hipEventElapsedTime(events[i], events[i+1]) is stage i's device time (the
  * activation quantisation runs inside stage 0's kernel, so stage 4 is empty; for
- * T <= 256 one kernel does top-k, scan and scatter in stage 1, and stages 2 and 3
- * are empty).
+ * T <= 256 the scatter runs inside stage 2's kernel and stage 3 is empty, and when also
+ * top_k <= 4 and T * E <= 16384 one kernel does top-k, scan and scatter in stage 1 and
+ * stages 2 and 3 are both empty).
  * `events` must point to MOE_PROFILE_EVENTS entries (NULL array: MOE_ERR_INVALID_ARG);
  * a NULL entry is not recorded, so a caller can time some stages only (each recorded
  * event adds a small gap between kernels). */
