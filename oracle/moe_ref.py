@@ -33,6 +33,13 @@ Readings where the pages are silent:
   top-k order is descending logit with ties to the lower expert index; the
   dispatch order is expert-major and token-ascending inside an expert.
 
+MXFP8 variant ("Hosting Qwen on Blackwell", section "Quantization": weights
+converted statically to MXFP8): the OCP Microscaling format -- blocks of 32
+consecutive elements along K share a power-of-two scale, stored as an E8M0 code
+(exponent + 127), exponent floor(log2(amax)) - 8 so that the block maximum lands in
+[256, 512) before the e4m3 rounding (clamped to +-448); an all-zero block gets
+exponent 0; the activations (x, h) use the same 1x32 blocks along K.
+
 Pins (tests/test_oracle_*.py): the e4m3 codec against its closed-form definition
 and torch's float8_e4m3fn, a brute-force nearest-code encoder and an independent
 scalar quantiser; router logits, top-k and gates against pure-Python loops and
@@ -156,6 +163,45 @@ def quantize_activations(a32):
 
 
 # ----------------------------------------------------------------------------------------
+# MXFP8 (microscaling): "Hosting Qwen on Blackwell", section "Quantization" -- the
+# weights converted statically to MXFP8.  The format is the OCP Microscaling one: a
+# block of 32 consecutive elements along K shares one E8M0 scale (a power of two, code
+# = exponent + 127); the elements are e4m3.
+# ----------------------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E4M3_EMAX = 8          # exponent of the largest normal e4m3 value (448 = 1.75 * 2^8)
+
+
+def quantize_mx(a):
+    """MXFP8 quantisation of a float32 array [..., K] along its last axis (K a multiple
+    of 32).  Per block of 32: amax = max |v|; shared exponent X = floor(log2(amax)) - 8,
+    clamped to [-127, 127] (X = 0 for an all-zero block); element code =
+    e4m3_encode(v * 2^-X) (an exact power-of-two scaling, then clamped to +-448).
+    Returns (codes uint8 [..., K], scale codes uint8 [..., K/32] = X + 127)."""
+    a = np.asarray(a, dtype=np.float32)
+    K = a.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = a.reshape(a.shape[:-1] + (K // MX_BLOCK, MX_BLOCK)).astype(np.float64)
+    amax = np.abs(blocks).max(axis=-1)
+    _, ex = np.frexp(amax)                       # amax = m 2^ex, m in [0.5, 1)
+    X = np.where(amax > 0, np.clip(ex - 1 - E4M3_EMAX, -127, 127), 0).astype(np.int64)
+    scaled = blocks * np.ldexp(1.0, -X)[..., None]          # exact in float64
+    codes = e4m3_encode(scaled.astype(np.float32)).reshape(a.shape)
+    return codes, (X + 127).astype(np.uint8)
+
+
+def dequantize_mx(codes, scales) -> np.ndarray:
+    """decode(code) * 2^(scale code - 127) of its 32-block, float64."""
+    vals = e4m3_decode(codes)
+    K = vals.shape[-1]
+    X = np.asarray(scales, np.int64) - 127
+    v = vals.reshape(vals.shape[:-1] + (K // MX_BLOCK, MX_BLOCK)) * np.ldexp(1.0, X)[..., None]
+    return v.reshape(vals.shape)
+
+
+# ----------------------------------------------------------------------------------------
 # Routing
 # ----------------------------------------------------------------------------------------
 
@@ -206,18 +252,32 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(xd_rows, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, I: int):
+def _quantizer(fmt: str):
+    """(quantise a float32 activation matrix, dequantise it, dequantise an expert matrix)
+    of the block-scaled ("block": 1x128 activations, 128x128 weights) or the MXFP8
+    ("mxfp8": 1x32 blocks along K for both) format."""
+    if fmt == "block":
+        return (quantize_activations, lambda q, s: dequantize_blocks(q, s, rows=1, cols=BLOCK),
+                dequantize_blocks)
+    if fmt == "mxfp8":
+        return quantize_mx, dequantize_mx, dequantize_mx
+    raise ValueError(f"unknown format {fmt}")
+
+
+def expert_ffn(xd_rows, w13_codes, w13_scales, b13, w2_codes, w2_scales, b2, I: int,
+               fmt: str = "block"):
     """One expert on its rows (float64).
 
     C = xd . deq(w13)^T + b13 ;  h = silu(C[:, :I]) * C[:, I:] ;  h is rounded to
-    fp32 and quantised per row in 1x128 groups ;  y = deq(h) . deq(w2)^T + b2.
-    Returns (y, h_codes, h_scales, h64)."""
-    W13 = dequantize_blocks(w13_codes, w13_scales)
+    fp32 and quantised per row (1x128 groups, or 1x32 MX blocks) ;
+    y = deq(h) . deq(w2)^T + b2.  Returns (y, h_codes, h_scales, h64)."""
+    q_act, dq_act, dq_w = _quantizer(fmt)
+    W13 = dq_w(w13_codes, w13_scales)
     C = xd_rows @ W13.T + bf16_to_f64(b13)
     h = silu(C[:, :I]) * C[:, I:]
-    hq, hs = quantize_activations(h.astype(np.float32))
-    hd = dequantize_blocks(hq, hs, rows=1, cols=BLOCK)
-    W2 = dequantize_blocks(w2_codes, w2_scales)
+    hq, hs = q_act(h.astype(np.float32))
+    hd = dq_act(hq, hs)
+    W2 = dq_w(w2_codes, w2_scales)
     y = hd @ W2.T + bf16_to_f64(b2)
     return y, hq, hs, h
 
@@ -238,14 +298,16 @@ def f64_to_bf16_bits(a) -> np.ndarray:
 
 
 def forward(x_bits, router_w, router_b, top_k: int, I: int, w13_codes, w13_scales, b13,
-            w2_codes, w2_scales, b2, token_subset=None):
+            w2_codes, w2_scales, b2, token_subset=None, fmt: str = "block"):
     """The layer forward pass.
 
     ``w13_codes`` etc. are indexable by expert (arrays [E, ...] or dict-like of the
     experts needed).  With ``token_subset`` only those tokens are evaluated: routing,
     x quantisation and the combine are per token, so a token's output does not depend
     on which other tokens are present (the dispatch tables are still built over all
-    tokens).  Returns a dict of every stage's result."""
+    tokens).  ``fmt`` = "mxfp8" takes MXFP8 weights (scales [E, N, K/32] E8M0 codes) and
+    quantises x and h in 1x32 MX blocks.  Returns a dict of every stage's result."""
+    q_act, dq_act, _ = _quantizer(fmt)
     T = x_bits.shape[0]
     E = router_w.shape[0]
     logits = router_logits(x_bits, router_w, router_b)
@@ -253,14 +315,14 @@ def forward(x_bits, router_w, router_b, top_k: int, I: int, w13_codes, w13_scale
     counts, offsets, perm, inv = permute(ids, E)
     x32 = bf16_to_f64(x_bits).astype(np.float32)
     toks = np.arange(T) if token_subset is None else np.asarray(token_subset)
-    xq, sx = quantize_activations(x32[toks])
-    xd = dequantize_blocks(xq, sx, rows=1, cols=BLOCK)
+    xq, sx = q_act(x32[toks])
+    xd = dq_act(xq, sx)
     H = x_bits.shape[1]
     y = np.zeros((toks.size, top_k, H))
     for e in np.unique(ids[toks]):
         rows_t, rows_j = np.nonzero(ids[toks] == e)
         ye, _, _, _ = expert_ffn(xd[rows_t], w13_codes[e], w13_scales[e], b13[e],
-                                 w2_codes[e], w2_scales[e], b2[e], I)
+                                 w2_codes[e], w2_scales[e], b2[e], I, fmt)
         y[rows_t, rows_j] = ye
     out = np.einsum("tk,tkh->th", gates[toks], y)
     return dict(logits=logits, ids=ids, gates=gates, counts=counts, offsets=offsets, perm=perm,
