@@ -160,6 +160,55 @@ moe_status moe_forward_profiled(const uint16_t* x, const float* router_w, const 
                                 const moe_routing* routing_out, void* workspace,
                                 size_t workspace_bytes, void* stream, void* const* events);
 
+/* ---- MXFP8 variant ("Hosting Qwen on Blackwell", section "Quantization": the weights
+ * are converted statically to MXFP8, the microscaling format, instead of 128x128 block
+ * scaling).  OCP Microscaling rule: every 32 consecutive elements along K share one
+ * E8M0 scale code c (scale 2^(c - 127)), c - 127 = floor(log2(amax)) - 8 clamped to
+ * [-127, 127] (0 for an all-zero block); an element code is the nearest e4m3 value
+ * (ties to even) of v * 2^-(c - 127), clamped to +-448.  Weights, x and h all use 1x32
+ * blocks along K.
+ *
+ * Scale layout: a row of K elements has K/32 codes, stored in a row of
+ * 4 * ceil(K/128) bytes (whole 4-byte words per 128-wide K-step, as the GEMMs stage
+ * them); the bytes past K/32 hold 127.  Scale arrays of moe_forward_mx must be 4-byte
+ * aligned. */
+
+/* MXFP8 quantisation of E stacked fp32 matrices.
+ *   w      [E, N, K] float      source weights
+ *   codes  [E, N, K] uint8      e4m3 codes (output)
+ *   scales [E, N, 4 ceil(K/128)] uint8   E8M0 codes, padded rows (output)
+ * Requires E, N >= 1 and K a positive multiple of 32. */
+moe_status moe_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t* codes,
+                                   uint8_t* scales, void* stream);
+
+/* Per-token 1x32 MXFP8 activation quantisation (the rule the MXFP8 forward applies to x).
+ *   x      [T, H] bf16          input
+ *   codes  [T, H] uint8         e4m3 codes (output)
+ *   scales [T, 4 ceil(H/128)] uint8   E8M0 codes, padded rows (output)
+ * Requires T >= 1 and H a positive multiple of 64. */
+moe_status moe_quantize_activations_mx(const uint16_t* x, int T, int H, uint8_t* codes,
+                                       uint8_t* scales, void* stream);
+
+/* The whole layer forward with MXFP8 experts: moe_forward's arguments and semantics, with
+ *   w13_scales [E, 2I, 4 ceil(H/128)] uint8 and w2_scales [E, H, 4 ceil(I/128)] uint8
+ * (moe_quantize_weights_mx), and x and h quantised in 1x32 MX blocks.  The workspace is
+ * the same (moe_workspace_bytes). */
+moe_status moe_forward_mx(const uint16_t* x, const float* router_w, const float* router_b,
+                          const uint8_t* w13, const uint8_t* w13_scales, const uint16_t* b13,
+                          const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2, int T,
+                          int H, int E, int top_k, int I, uint16_t* out,
+                          const moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* moe_forward_mx with the per-stage events of moe_forward_profiled. */
+moe_status moe_forward_mx_profiled(const uint16_t* x, const float* router_w,
+                                   const float* router_b, const uint8_t* w13,
+                                   const uint8_t* w13_scales, const uint16_t* b13,
+                                   const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2,
+                                   int T, int H, int E, int top_k, int I, uint16_t* out,
+                                   const moe_routing* routing_out, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED_SHAPE
 
 EXPORTS = ["moe_status_str", "moe_workspace_bytes", "moe_workspace_layout",
            "moe_quantize_weights", "moe_quantize_activations", "moe_route", "moe_forward",
-           "moe_forward_profiled"]
+           "moe_forward_profiled", "moe_quantize_weights_mx", "moe_quantize_activations_mx",
+           "moe_forward_mx", "moe_forward_mx_profiled"]
 
 PROFILE_STAGES = ["router_gemm", "topk_softmax", "dispatch_scan", "dispatch_scatter",
                   "act_quant", "gemm1", "gemm2", "combine"]
@@ -73,6 +74,14 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.restype = i
         L.moe_forward_profiled.argtypes = L.moe_forward.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
         L.moe_forward_profiled.restype = i
+        L.moe_quantize_weights_mx.argtypes = [vp, i, i, i, vp, vp, vp]
+        L.moe_quantize_weights_mx.restype = i
+        L.moe_quantize_activations_mx.argtypes = [vp, i, i, vp, vp, vp]
+        L.moe_quantize_activations_mx.restype = i
+        L.moe_forward_mx.argtypes = L.moe_forward.argtypes
+        L.moe_forward_mx.restype = i
+        L.moe_forward_mx_profiled.argtypes = L.moe_forward_profiled.argtypes
+        L.moe_forward_mx_profiled.restype = i
         _lib = L
     return _lib
 
@@ -157,6 +166,43 @@ def quantize_activations(x: torch.Tensor):
     return codes, scales
 
 
+def mx_row(K: int) -> int:
+    """Bytes of one row of MXFP8 scale codes for K elements (4 per 128-wide K-step)."""
+    return 4 * kb(K)
+
+
+def quantize_weights_mx(w: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
+    """MXFP8 quantisation of w [E, N, K] (or [N, K]) fp32 -> (codes uint8, E8M0 scale codes
+    uint8 [E, N, 4 ceil(K/128)], pads 127)."""
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    E, N, K = w3.shape
+    if codes is None:
+        codes = torch.empty((E, N, K), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((E, N, mx_row(K)), dtype=torch.uint8, device=w.device)
+    st = lib().moe_quantize_weights_mx(_dev(w3, torch.float32, "w"), E, N, K,
+                                       _fp8(codes.view(E, N, K), "codes"),
+                                       _dev(scales.view(E, N, mx_row(K)), torch.uint8, "scales"),
+                                       _stream(w.device))
+    _check(st, "moe_quantize_weights_mx")
+    if squeeze:
+        return codes.view(N, K), scales.view(N, mx_row(K))
+    return codes, scales
+
+
+def quantize_activations_mx(x: torch.Tensor):
+    """Per-token 1x32 MXFP8 quantisation of x [T, H] bf16 -> (codes uint8 [T, H], E8M0 scale
+    codes uint8 [T, 4 ceil(H/128)])."""
+    T, H = x.shape
+    codes = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((T, mx_row(H)), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quantize_activations_mx(_dev(x, torch.bfloat16, "x"), T, H, _fp8(codes, "codes"),
+                                             _dev(scales, torch.uint8, "scales"), _stream(x.device)),
+           "moe_quantize_activations_mx")
+    return codes, scales
+
+
 def new_routing(T: int, E: int, top_k: int, device="cuda") -> dict:
     i32 = dict(dtype=torch.int32, device=device)
     return dict(topk_ids=torch.empty((T, top_k), **i32),
@@ -201,25 +247,36 @@ def _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2
     if workspace is None:
         workspace = new_workspace(T, H, E, top_k, I, x.device)
     rs = _routing_struct(routing, T, E, top_k) if routing is not None else None
+    mx = w13_scales.dtype == torch.uint8          # MXFP8 E8M0 codes, else fp32 block scales
+    if mx:
+        s13 = _dev(w13_scales, torch.uint8, "w13_scales", (E, 2 * I, mx_row(H)))
+        s2 = _dev(w2_scales, torch.uint8, "w2_scales", (E, H, mx_row(I)))
+    else:
+        s13 = _dev(w13_scales, torch.float32, "w13_scales", (E, kb(2 * I), kb(H)))
+        s2 = _dev(w2_scales, torch.float32, "w2_scales", (E, kb(H), kb(I)))
     args = [
         _dev(x, torch.bfloat16, "x"), _dev(router_w, torch.float32, "router_w", (E, H)),
         _dev(router_b, torch.float32, "router_b", (E,)),
-        _fp8(w13, "w13", (E, 2 * I, H)), _dev(w13_scales, torch.float32, "w13_scales", (E, kb(2 * I), kb(H))),
+        _fp8(w13, "w13", (E, 2 * I, H)), s13,
         _dev(b13, torch.bfloat16, "b13", (E, 2 * I)),
-        _fp8(w2, "w2", (E, H, I)), _dev(w2_scales, torch.float32, "w2_scales", (E, kb(H), kb(I))),
+        _fp8(w2, "w2", (E, H, I)), s2,
         _dev(b2, torch.bfloat16, "b2", (E, H)),
         T, H, E, top_k, I, _dev(out, torch.bfloat16, "out", (T, H)),
         ctypes.byref(rs) if rs is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(x.device)]
-    return out, args, (rs, workspace)
+    return out, args, (rs, workspace), mx
 
 
 def forward(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, top_k: int,
             out=None, routing: dict = None, workspace=None) -> torch.Tensor:
-    """The layer forward: out [T, H] bf16."""
-    out, args, _keep = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales,
-                                     b2, top_k, out, routing, workspace)
-    _check(lib().moe_forward(*args), "moe_forward")
+    """The layer forward: out [T, H] bf16.  uint8 weight scales (E8M0 codes from
+    ``quantize_weights_mx``) select the MXFP8 layer, fp32 ones the block-scaled layer."""
+    out, args, _keep, mx = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2,
+                                         w2_scales, b2, top_k, out, routing, workspace)
+    if mx:
+        _check(lib().moe_forward_mx(*args), "moe_forward_mx")
+    else:
+        _check(lib().moe_forward(*args), "moe_forward")
     return out
 
 
@@ -230,11 +287,14 @@ def forward_profiled(events, x, router_w, router_b, w13, w13_scales, b13, w2, w2
     entry leaves that boundary unrecorded."""
     if len(events) != len(PROFILE_STAGES) + 1:
         raise ValueError("need one event per stage plus one")
-    out, args, _keep = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales,
-                                     b2, top_k, out, routing, workspace)
+    out, args, _keep, mx = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2,
+                                         w2_scales, b2, top_k, out, routing, workspace)
     for ev in events:          # materialise the underlying hipEvent_t
         if ev is not None and ev.cuda_event == 0:
             ev.record()
     arr = (ctypes.c_void_p * len(events))(*[0 if ev is None else ev.cuda_event for ev in events])
-    _check(lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
+    if mx:
+        _check(lib().moe_forward_mx_profiled(*args, arr), "moe_forward_mx_profiled")
+    else:
+        _check(lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
     return out

@@ -111,4 +111,65 @@ __device__ __forceinline__ float quantize_group16(const uint16_t* row, int col, 
   return s;
 }
 
+// ---- MXFP8 (OCP microscaling): 1x32 blocks along K, E8M0 scale = exponent + 127 ----
+constexpr int kMxBlock = 32;
+
+// E8M0 code of a 32-block with absolute maximum `amax`: exponent floor(log2(amax)) - 8
+// (the block maximum lands in [256, 512) before the e4m3 rounding), clamped below at
+// -127 (a subnormal amax has exponent field 0 and lands there), 0 for an all-zero block.
+// floor(log2) of a normal fp32 value is its exponent field - 127; the largest (127)
+// gives 119, so no upper clamp is needed.
+__device__ __forceinline__ int mx_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 127;
+  const int ex = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu) - 127;
+  return max(ex - 8, -127) + 127;
+}
+
+// 2^-(code - 127), a normal fp32 power of two for every code in [0, 246].
+__device__ __forceinline__ float mx_inv_scale(int code) {
+  return __uint_as_float(static_cast<uint32_t>(254 - code) << 23);
+}
+
+// Four e4m3 codes of v * m (m a power of two: the product is exact), clamped to +-448,
+// round to nearest even, packed little-endian.
+__device__ __forceinline__ uint32_t encode4_mul(float v0, float v1, float v2, float v3, float m) {
+  const float q0 = fminf(fmaxf(v0 * m, -kFp8Max), kFp8Max);
+  const float q1 = fminf(fmaxf(v1 * m, -kFp8Max), kFp8Max);
+  const float q2 = fminf(fmaxf(v2 * m, -kFp8Max), kFp8Max);
+  const float q3 = fminf(fmaxf(v3 * m, -kFp8Max), kFp8Max);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false)) & 0xFFFFu;
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, 0, false)) & 0xFFFFu;
+  return lo | (hi << 16);
+}
+
+// MX-quantises columns [col, col + 8) of one 32-block of a bf16 row (4 aligned lanes cover
+// the block; `in` is false for lanes past the row's end, whose codes are not written) and
+// returns the block's E8M0 code, the same in all 4 lanes.  Codes go to codes_row + col.
+__device__ __forceinline__ int quantize_mx8(const uint16_t* row, int col, bool in,
+                                            uint8_t* codes_row) {
+  float f[8];
+  float amax = 0.0f;
+  if (in) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(row + col);
+    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_to_f32(static_cast<uint16_t>(wds[i] & 0xFFFFu));
+      f[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(wds[i] >> 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+  amax = group_max<4>(amax);
+  const int code = mx_scale_code(amax);
+  if (in) {
+    const float m = mx_inv_scale(code);
+    uint2 q;
+    q.x = encode4_mul(f[0], f[1], f[2], f[3], m);
+    q.y = encode4_mul(f[4], f[5], f[6], f[7], m);
+    *reinterpret_cast<uint2*>(codes_row + col) = q;
+  }
+  return code;
+}
+
 }  // namespace moe

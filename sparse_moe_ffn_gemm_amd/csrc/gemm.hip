@@ -522,7 +522,7 @@ constexpr int big_tile_lds() {
 
 // One M-tile x n-tile: WM x (8 / WM) waves, each SM 16-row sub-tiles by BN / (8 / WM)
 // columns; SA / SB ring slots.
-template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB>
+template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile mt, uint8_t* lds) {
   constexpr int WAVES = 8, NT = WAVES * 64, WN = WAVES / WM, BM = 16 * SM * WM;
   constexpr int WR = 16 * SM, WC = BN / WN;          // rows / columns of a wave
@@ -613,6 +613,24 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     s_ptr = Bsc + static_cast<size_t>(row < 0 ? 0 : row) * KB;
   }
 
+  // MXFP8: every thread stages one 4-byte E8M0 row of K-step kt (the four 32-blocks of
+  // its 128 columns): thread t < BM the A row t, BM <= t < BM + BN the B row t - BM; one
+  // load per wave and step, like the block scales above
+  const uint8_t* x_ptr = reinterpret_cast<const uint8_t*>(kZeroScale);
+  bool x_live = false;
+  if constexpr (MX) {
+    const int RS = 4 * KB;
+    if (tid < BM) {
+      const int src = rowsrc[tid];
+      x_live = src >= 0;
+      x_ptr = a.A_mx + static_cast<size_t>(src < 0 ? 0 : src) * RS;
+    } else if (tid < BM + BN) {
+      const int g = b_global_row(tid - BM);
+      x_live = g >= 0;
+      x_ptr = a.B_mx + (static_cast<size_t>(e) * N + (g < 0 ? 0 : g)) * RS;
+    }
+  }
+
   auto issue_a = [&](int kt) {   // A rows and all scales of K-step kt
     uint8_t* As = ringA + (kt % SA) * A_BYTES;
     const int k0 = kt * kBlock;
@@ -628,7 +646,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
         load_lds16(src, As + (wave * A_ROWS + i * 8) * 128);
       }
     }
-    if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN)) {   // lanes 0.. always: one instruction
+    if constexpr (MX) {
+      const void* src = x_live ? static_cast<const void*>(x_ptr + 4 * kt) : kZeroScale;
+      load_lds4(src, &sS[kt % SA][wave][0]);
+    } else if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN)) {   // lanes 0.. always: one instruction
       const void* src = s_live ? static_cast<const void*>(s_ptr + kt) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
     }
@@ -697,16 +718,29 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // scale is one value per (m, n) and the epilogue stores are 4 or 16 bytes wide.
   v8i af[SM], bq[3];
   float sav[SM], sbv[SN];
+  int xa[SM], xb[SN];   // MXFP8: the lane's E8M0 codes (row lane & 15, 32-block lane >> 4)
   auto read_step = [&](int kt) {   // scales, A fragments and the first B fragment
     const int sl = kt % SA;
     const uint8_t* As = ringA + sl * A_BYTES;
+    if constexpr (MX) {
+      const uint8_t* xs = reinterpret_cast<const uint8_t*>(&sS[sl][0][0]);
 #pragma unroll
-    for (int n = 0; n < SN; ++n) sbv[n] = sS[sl][0][32 + wn * SN + n];
+      for (int n = 0; n < SN; ++n) xb[n] = xs[4 * (BM + sub_brow(n) + (lane & 15)) + (lane >> 4)];
 #pragma unroll
-    for (int m = 0; m < SM; ++m) {
-      const int r = wm * WR + 16 * m + (lane & 15);
-      af[m] = lds_frag(As, r, lane >> 4);
-      sav[m] = sS[sl][r / A_ROWS][r % A_ROWS];
+      for (int m = 0; m < SM; ++m) {
+        const int r = wm * WR + 16 * m + (lane & 15);
+        af[m] = lds_frag(As, r, lane >> 4);
+        xa[m] = xs[4 * r + (lane >> 4)];
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < SN; ++n) sbv[n] = sS[sl][0][32 + wn * SN + n];
+#pragma unroll
+      for (int m = 0; m < SM; ++m) {
+        const int r = wm * WR + 16 * m + (lane & 15);
+        af[m] = lds_frag(As, r, lane >> 4);
+        sav[m] = sS[sl][r / A_ROWS][r % A_ROWS];
+      }
     }
     bq[0] = lds_frag(ringB + (kt % SB) * B_BYTES, sub_brow(0) + (lane & 15), lane >> 4);
     bq[1] = lds_frag(ringB + (kt % SB) * B_BYTES, sub_brow(1) + (lane & 15), lane >> 4);
@@ -738,7 +772,16 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     // the slots of step kt-1 are free (every wave passed the barrier after reading them)
     if (kt + SA - 1 < KB) issue_a(kt + SA - 1);
     if (kt + SB - 1 < KB) issue_b(kt + SB - 1);
-    if (wave_live) {
+    if (MX && wave_live) {   // the matrix cores apply the E8M0 scales: no promotion
+      const uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int n = j / SM, m = j % SM;
+        if (m == 0 && n + 2 < SN) bq[(n + 2) % 3] = lds_frag(Bs, sub_brow(n + 2) + (lane & 15), lane >> 4);
+        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n % 3], af[m], acc[m][n], 0, 0,
+                                                                     0, xb[n], 0, xa[m]);
+      }
+    } else if (wave_live) {
       const uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
@@ -767,7 +810,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       if (wave_live) read_step(kt + 1);
     }
   }
-  if (wave_live) {      // the last step's last LAG products
+  if (!MX && wave_live) {      // the last step's last LAG products
 #pragma unroll
     for (int j = 0; j < LAG; ++j) {
       const int q = NP - LAG + j;
@@ -803,6 +846,42 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
           const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
           hv[m][n][i] = ok ? h : 0.f;
         }
+    }
+    if constexpr (MX) {
+      // 1x32 MX blocks of h: the wave's gate sub-tiles 2q and 2q+1 are 32 aligned
+      // columns; the block maximum of a row is the lane's 8 values and those of the row's
+      // other 3 lanes (lane >> 4).  Blocks past I (h = 0 there) get the pad code 127.
+      static_assert(NG % 2 == 0, "whole MX blocks per wave");
+      const int RSI = 4 * KBI;
+#pragma unroll
+      for (int m = 0; m < SM; ++m) {
+        const int p = mt.row_begin + wm * WR + 16 * m + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < NG / 2; ++q) {
+          float mx = 0.f;
+#pragma unroll
+          for (int n = 2 * q; n < 2 * q + 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(hv[m][n][i]));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const int code = mx_scale_code(mx);
+          const float mul = mx_inv_scale(code);
+          const int jb = nt * (BN / 2) + wn * GW + 32 * q;
+          if (p < mt.row_end) {
+            uint8_t* hrow = a.h_out + static_cast<size_t>(p) * I;
+#pragma unroll
+            for (int n = 2 * q; n < 2 * q + 2; ++n) {
+              const int j0 = jb + 16 * (n - 2 * q) + cq;
+              if (j0 < I)
+                *reinterpret_cast<uint32_t*>(hrow + j0) =
+                    encode4_mul(hv[m][n][0], hv[m][n][1], hv[m][n][2], hv[m][n][3], mul);
+            }
+            if ((lane >> 4) == 0) a.h_mx[static_cast<size_t>(p) * RSI + jb / kMxBlock] = static_cast<uint8_t>(code);
+          }
+        }
+      }
+      return;
     }
     // Each 1x128 group of h is a row's 128 columns [128 c, 128 c + 128); a tile holds
     // BN/2 of them starting at nt * BN/2.  The scale of a group is only complete when
@@ -883,7 +962,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
 // activation rows and weight tiles in their L2; a workgroup whose XCD's queue is empty
 // takes from the other XCDs' queues.  Every queue head only grows, so every workgroup
 // leaves after at most total + 8 of its fetches.
-template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN>
+template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN, bool MX = false>
 __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int ntiles) {
   constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN>();
   __shared__ __align__(16) uint8_t lds[kFull > kNarrow ? kFull : kNarrow];
@@ -905,9 +984,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
       MTile mt;
       tile_of(a, ntiles, lo + t, nt, mt);
       if (mt.row_end - mt.row_begin <= 64) {
-        big_tile<SWIGLU, BN, 2, 2, SAN, SBN>(a, nt, mt, lds);
+        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX>(a, nt, mt, lds);
       } else {
-        big_tile<SWIGLU, BN, 4, 4, SA, SB>(a, nt, mt, lds);
+        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX>(a, nt, mt, lds);
       }
     }
   }
@@ -1173,17 +1252,25 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
   const int ntiles = SWIGLU ? ceil_div(a.I, 128) : ceil_div(a.N, bn);
   const long total = static_cast<long>(max_tiles) * ntiles;
   const int grid = static_cast<int>((total + 7) / 8 * 8);
-  if (bm == 256) {
+  // MXFP8 layers take the large-group kernel at every group size (their tile list is
+  // built with 256-row tiles); so do block-scaled layers with large groups
+  if (bm == 256 || a.mx) {
     constexpr int BN = SWIGLU ? kG1BN : kG2BN;
     const int nt_big = SWIGLU ? ceil_div(a.I, BN / 2) : ceil_div(a.N, BN);
     const long tot = static_cast<long>(max_tiles) * nt_big;
     // persistent: one workgroup per CU (a multiple of the queue count), at most one per tile
     const long cus = device_cus();
     const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
-    if constexpr (SWIGLU)
+    if (a.mx) {
+      if constexpr (SWIGLU)
+        grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, true><<<g, 512, 0, st>>>(a, nt_big);
+      else
+        grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS, true><<<g, 512, 0, st>>>(a, nt_big);
+    } else if constexpr (SWIGLU) {
       grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS><<<g, 512, 0, st>>>(a, nt_big);
-    else
+    } else {
       grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS><<<g, 512, 0, st>>>(a, nt_big);
+    }
     return;
   }
   // Decode-sized groups whose weight rows are not whole 128-byte lines (K = 64 mod 128,

@@ -19,6 +19,11 @@ void launch_quantize_weights(const float* w, int E, int N, int K, uint8_t* codes
                              hipStream_t st);
 void launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* codes, float* scales,
                          hipStream_t st);
+// MXFP8: codes as above; E8M0 scales in rows of 4 ceil(K/128) bytes (pads hold 127)
+void launch_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t* codes,
+                                uint8_t* scales, hipStream_t st);
+void launch_quantize_act_mx(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales,
+                            hipStream_t st);
 
 // ---- routing ----
 constexpr int kRouterTile = 64;     // tokens / experts per router GEMM workgroup
@@ -31,9 +36,12 @@ constexpr int kGemmQueues = 8;      // per-XCD work queues of one large-group GE
 // same as launch_quantize_act.  With parts != NULL (space for 3 E H bf16) W is first
 // split once into its three bf16 planes there (worth it when many token tiles would each
 // split their weight tile again).
+// With sx_mx != NULL the x quantisation is MXFP8 instead (E8M0 codes into sx_mx, rows of
+// 4 ceil(H/128) bytes).
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
                           int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
-                          uint8_t* xq = nullptr, float* sx = nullptr, uint16_t* parts = nullptr);
+                          uint8_t* xq = nullptr, float* sx = nullptr, uint16_t* parts = nullptr,
+                          uint8_t* sx_mx = nullptr);
 // ids/gates, counted into the per-chunk expert histogram hist[chunk][E] (cleared before)
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
                  int32_t* ids, float* gates, int32_t* hist, hipStream_t st);
@@ -77,6 +85,12 @@ struct GemmArgs {
   uint8_t* h_out;            // gemm1: [rows, I]
   float* h_scale;            // gemm1: [rows, ceil(I/128)]
   uint16_t* y_out;           // gemm2: [rows, N] fp16
+  // MXFP8 instead of the block scales (A_scale, B_scale, h_scale unused): E8M0 codes in
+  // rows of 4 ceil(K/128) bytes -- A_mx [*, ...], B_mx [E, N, ...], h_mx [rows, 4 ceil(I/128)]
+  bool mx;
+  const uint8_t* A_mx;
+  const uint8_t* B_mx;
+  uint8_t* h_mx;
 };
 
 // Rows per M-tile chosen for a layer with `rows` routed rows over E experts.

@@ -42,7 +42,8 @@ bool uses_route_tail(int T, int E, int k, int ksplit) {
          k <= moe::kTailTopK && ksplit <= moe::kTailSplit;
 }
 
-void make_plan(int T, int H, int E, int k, int I, Plan* p) {
+// `mx`: MXFP8 layers take 256-row M-tiles at every group size (one GEMM kernel family).
+void make_plan(int T, int H, int E, int k, int I, Plan* p, bool mx = false) {
   p->T = T; p->H = H; p->E = E; p->k = k; p->I = I;
   p->rows = static_cast<long>(T) * k;
   // split H across workgroups when there are few token x expert tiles (decode)
@@ -54,8 +55,11 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p) {
   p->kslice = ceil_div(ceil_div(H, ks), moe::kBlock) * moe::kBlock;   // whole quantisation groups
   p->ksplit = ceil_div(H, p->kslice);
   p->nchunks = ceil_div(T, moe::kChunk);
-  p->bm = moe::gemm_tile_rows(p->rows, E);
-  p->max_tiles = static_cast<int>(p->rows / p->bm + std::min<long>(E, p->rows));
+  // the tile list is sized for the block-scaled tile height, an upper bound for the
+  // 256-row tiles of MXFP8 too, so both formats share one workspace layout
+  const int bm_block = moe::gemm_tile_rows(p->rows, E);
+  p->bm = mx ? 256 : bm_block;
+  p->max_tiles = static_cast<int>(p->rows / bm_block + std::min<long>(E, p->rows));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -113,7 +117,7 @@ void mark(hipEvent_t* ev, int i, hipStream_t st) {
 // Router (which also quantises x when `quant_x`), top-k and the dispatch tables.
 void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const float* rb,
                      const Tables& tb, void* ws, hipStream_t st, hipEvent_t* ev = nullptr,
-                     bool quant_x = false) {
+                     bool quant_x = false, bool mx = false) {
   mark(ev, 0, st);
   // a single chunk of tokens (decode-sized T): one workgroup does the scan and the
   // scatter; with few logits the same workgroup also does top-k + softmax
@@ -122,8 +126,9 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
   moe::launch_router_logits(x, rw, p.T, p.H, p.E, p.ksplit, p.kslice, at<float>(ws, p.partial),
                             at<int32_t>(ws, p.hist), tail ? 0 : p.nchunks * p.E, st,
                             quant_x ? at<uint8_t>(ws, p.xq) : nullptr,
-                            quant_x ? at<float>(ws, p.sx) : nullptr,
-                            p.presplit ? at<uint16_t>(ws, p.wparts) : nullptr);
+                            quant_x && !mx ? at<float>(ws, p.sx) : nullptr,
+                            p.presplit ? at<uint16_t>(ws, p.wparts) : nullptr,
+                            quant_x && mx ? at<uint8_t>(ws, p.sx) : nullptr);
   mark(ev, 1, st);
   if (tail) {
     moe::launch_route_tail(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, p.bm, tb.ids,
@@ -147,6 +152,8 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
                                  tb.inv, st);
 }
 
+bool aligned4(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3u) == 0; }
+
 bool routing_ok(const moe_routing* r) {
   return r && r->topk_ids && r->topk_gates && r->expert_counts && r->expert_offsets && r->perm &&
          r->inv_perm && aligned16(r->topk_ids) && aligned16(r->topk_gates) &&
@@ -155,21 +162,24 @@ bool routing_ok(const moe_routing* r) {
 
 }  // namespace
 
+// The layer; `mx` selects MXFP8 (w13_scales / w2_scales are E8M0 code rows, uint8) over
+// the 128x128 block scales (fp32).
 static moe_status forward_impl(const uint16_t* x, const float* router_w, const float* router_b,
-                       const uint8_t* w13, const float* w13_scales, const uint16_t* b13,
-                       const uint8_t* w2, const float* w2_scales, const uint16_t* b2, int T,
+                       const uint8_t* w13, const void* w13_scales, const uint16_t* b13,
+                       const uint8_t* w2, const void* w2_scales, const uint16_t* b2, int T,
                        int H, int E, int top_k, int I, uint16_t* out,
                        const moe_routing* routing_out, void* workspace, size_t workspace_bytes,
-                       void* stream, hipEvent_t* ev) {
+                       void* stream, hipEvent_t* ev, bool mx = false) {
   if (!x || !router_w || !w13 || !w13_scales || !w2 || !w2_scales || !out || !workspace)
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(router_w) || !aligned16(w13) || !aligned16(w2) ||
       !aligned16(out) || !aligned16(workspace))
     return MOE_ERR_INVALID_ARG;
+  if (mx && (!aligned4(w13_scales) || !aligned4(w2_scales))) return MOE_ERR_INVALID_ARG;
   if (routing_out && !routing_ok(routing_out)) return MOE_ERR_INVALID_ARG;
   if (!shape_ok(T, H, E, top_k, I)) return MOE_ERR_UNSUPPORTED_SHAPE;
   Plan p;
-  make_plan(T, H, E, top_k, I, &p);
+  make_plan(T, H, E, top_k, I, &p, mx);
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -181,18 +191,26 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
                         : Tables{at<int32_t>(ws, p.ids), at<float>(ws, p.gates),
                                  at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
                                  at<int32_t>(ws, p.perm), at<int32_t>(ws, p.inv)};
-  enqueue_routing(p, x, router_w, router_b, tb, ws, st, ev, /*quant_x=*/true);
+  enqueue_routing(p, x, router_w, router_b, tb, ws, st, ev, /*quant_x=*/true, mx);
   mark(ev, 4, st);   // (the activation quantisation ran inside the router kernel)
   mark(ev, 5, st);
 
   moe::GemmArgs g1{};
   g1.A = at<uint8_t>(ws, p.xq);
   g1.A_rows = T;
-  g1.A_scale = at<float>(ws, p.sx);
   g1.perm = tb.perm;
   g1.top_k = top_k;
   g1.B = w13;
-  g1.B_scale = w13_scales;
+  g1.mx = mx;
+  if (mx) {
+    g1.A_mx = at<uint8_t>(ws, p.sx);
+    g1.B_mx = static_cast<const uint8_t*>(w13_scales);
+    g1.h_mx = at<uint8_t>(ws, p.sh);
+  } else {
+    g1.A_scale = at<float>(ws, p.sx);
+    g1.B_scale = static_cast<const float*>(w13_scales);
+    g1.h_scale = at<float>(ws, p.sh);
+  }
   g1.bias = b13;
   g1.tiles = at<moe::MTile>(ws, p.tiles);
   g1.num_tiles = at<int32_t>(ws, p.num_tiles);
@@ -202,7 +220,6 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g1.N = 2 * I;
   g1.I = I;
   g1.h_out = at<uint8_t>(ws, p.h);
-  g1.h_scale = at<float>(ws, p.sh);
   g1.queue = at<int32_t>(ws, p.num_tiles) + 1;
   moe::launch_gemm1(g1, p.bm, p.max_tiles, st);
   mark(ev, 6, st);
@@ -210,11 +227,17 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   moe::GemmArgs g2{};
   g2.A = at<uint8_t>(ws, p.h);
   g2.A_rows = static_cast<int>(p.rows);
-  g2.A_scale = at<float>(ws, p.sh);
   g2.perm = nullptr;
   g2.top_k = top_k;
   g2.B = w2;
-  g2.B_scale = w2_scales;
+  g2.mx = mx;
+  if (mx) {
+    g2.A_mx = at<uint8_t>(ws, p.sh);
+    g2.B_mx = static_cast<const uint8_t*>(w2_scales);
+  } else {
+    g2.A_scale = at<float>(ws, p.sh);
+    g2.B_scale = static_cast<const float*>(w2_scales);
+  }
   g2.bias = b2;
   g2.tiles = g1.tiles;
   g2.num_tiles = g1.num_tiles;
@@ -287,6 +310,28 @@ moe_status moe_quantize_activations(const uint16_t* x, int T, int H, uint8_t* co
   return finish();
 }
 
+moe_status moe_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t* codes,
+                                   uint8_t* scales, void* stream) {
+  if (!w || !codes || !scales || !aligned16(w) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARG;
+  if (K % 32 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (static_cast<long>(E) * N * 4 * ceil_div(K, 128) / 64 >= (1L << 31))
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  (void)hipGetLastError();
+  moe::launch_quantize_weights_mx(w, E, N, K, codes, scales, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+moe_status moe_quantize_activations_mx(const uint16_t* x, int T, int H, uint8_t* codes,
+                                       uint8_t* scales, void* stream) {
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+  if (H % 64 != 0 || static_cast<long>(T) * H >= (1L << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  (void)hipGetLastError();
+  moe::launch_quantize_act_mx(x, T, H, codes, scales, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
 moe_status moe_route(const uint16_t* x, const float* router_w, const float* router_b, int T,
                      int H, int E, int top_k, const moe_routing* out, void* workspace,
                      size_t workspace_bytes, void* stream) {
@@ -324,6 +369,30 @@ moe_status moe_forward_profiled(const uint16_t* x, const float* router_w, const 
   return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
                       top_k, I, out, routing_out, workspace, workspace_bytes, stream,
                       reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
+}
+
+moe_status moe_forward_mx(const uint16_t* x, const float* router_w, const float* router_b,
+                          const uint8_t* w13, const uint8_t* w13_scales, const uint16_t* b13,
+                          const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2, int T,
+                          int H, int E, int top_k, int I, uint16_t* out,
+                          const moe_routing* routing_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
+                      top_k, I, out, routing_out, workspace, workspace_bytes, stream, nullptr,
+                      /*mx=*/true);
+}
+
+moe_status moe_forward_mx_profiled(const uint16_t* x, const float* router_w,
+                                   const float* router_b, const uint8_t* w13,
+                                   const uint8_t* w13_scales, const uint16_t* b13,
+                                   const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2,
+                                   int T, int H, int E, int top_k, int I, uint16_t* out,
+                                   const moe_routing* routing_out, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
+                      top_k, I, out, routing_out, workspace, workspace_bytes, stream,
+                      reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), /*mx=*/true);
 }
 
 }  // extern "C"

@@ -1,9 +1,15 @@
-// FP8 e4m3 quantisers: 128x128 weight blocks and 1x128 activation groups.
+// FP8 e4m3 quantisers: 128x128 weight blocks and 1x128 activation groups, and the
+// MXFP8 variant (1x32 blocks along K with E8M0 scales) for both.
 //
 // "GPT-OSS on day 0", section "On Hopper": FP8 with 128x128 block scaling is the
 // weight scheme; "Hosting Qwen on Blackwell", section "Quantization": the weights
-// are converted once, statically.  The activation side uses per-token 1x128 groups
-// (a design choice of this implementation) with the same rounding rule.
+// are converted once, statically, and the MXFP8 (microscaling) format is the one its
+// Blackwell deployment takes.  The activation side uses per-token 1x128 groups (a
+// design choice of this implementation) with the same rounding rule, or 1x32 MX blocks.
+//
+// MX scale layout: a row of K elements has K/32 blocks; its E8M0 codes are stored in a
+// row of 4 ceil(K/128) bytes (whole dwords per 128-wide K-step, what the GEMMs stage),
+// the bytes past K/32 holding 127 (scale 1).
 #include "kernels.hpp"
 
 namespace moe {
@@ -66,6 +72,73 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __res
   const bool in = live && col < H;
   const float s = quantize_group16(x + t * H, col, in, codes + t * H);
   if (live && sub == 0) scales[g] = s;
+}
+
+// MXFP8: 4 lanes per 32-block, 8 elements per lane; a workgroup covers 64 block slots
+// of the padded scale rows (slots past K/32 write the pad code 127 and no elements).
+// Weights are fp32 [rows, K].
+__global__ __launch_bounds__(256) void quantize_weights_mx_kernel(const float* __restrict__ w,
+                                                                  long rows, int K,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales) {
+  const int RS = 4 * ceil_div(K, kBlock);               // scale bytes per row
+  const long slot = static_cast<long>(blockIdx.x) * 64 + (threadIdx.x >> 2);
+  const int sub = threadIdx.x & 3;
+  const bool live = slot < rows * RS;
+  const long row = live ? slot / RS : 0;
+  const int blk = live ? static_cast<int>(slot % RS) : 0;
+  const int col = blk * kMxBlock + sub * 8;
+  const bool in = live && col < K;
+  float f[8];
+  float amax = 0.0f;
+  if (in) {
+    const float4 a0 = *reinterpret_cast<const float4*>(w + row * K + col);
+    const float4 a1 = *reinterpret_cast<const float4*>(w + row * K + col + 4);
+    f[0] = a0.x; f[1] = a0.y; f[2] = a0.z; f[3] = a0.w;
+    f[4] = a1.x; f[5] = a1.y; f[6] = a1.z; f[7] = a1.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+  amax = group_max<4>(amax);
+  const int code = mx_scale_code(amax);
+  if (in) {
+    const float m = mx_inv_scale(code);
+    uint2 q;
+    q.x = encode4_mul(f[0], f[1], f[2], f[3], m);
+    q.y = encode4_mul(f[4], f[5], f[6], f[7], m);
+    *reinterpret_cast<uint2*>(codes + row * K + col) = q;
+  }
+  if (live && sub == 0) scales[slot] = static_cast<uint8_t>(code);
+}
+
+// Activations bf16 [T, H], the same block slots.
+__global__ __launch_bounds__(256) void quantize_act_mx_kernel(const uint16_t* __restrict__ x, int T,
+                                                              int H, uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+  const int RS = 4 * ceil_div(H, kBlock);
+  const long slot = static_cast<long>(blockIdx.x) * 64 + (threadIdx.x >> 2);
+  const int sub = threadIdx.x & 3;
+  const bool live = slot < static_cast<long>(T) * RS;
+  const long t = live ? slot / RS : 0;
+  const int blk = live ? static_cast<int>(slot % RS) : 0;
+  const int col = blk * kMxBlock + sub * 8;
+  const int code = quantize_mx8(x + t * H, col, live && col < H, codes + t * H);
+  if (live && sub == 0) scales[slot] = static_cast<uint8_t>(code);
+}
+
+void launch_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t* codes,
+                                uint8_t* scales, hipStream_t st) {
+  const long rows = static_cast<long>(E) * N;
+  const long slots = rows * 4 * ceil_div(K, kBlock);
+  quantize_weights_mx_kernel<<<dim3(static_cast<unsigned>((slots + 63) / 64)), dim3(256), 0, st>>>(
+      w, rows, K, codes, scales);
+}
+
+void launch_quantize_act_mx(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales,
+                            hipStream_t st) {
+  const long slots = static_cast<long>(T) * 4 * ceil_div(H, kBlock);
+  quantize_act_mx_kernel<<<dim3(static_cast<unsigned>((slots + 63) / 64)), dim3(256), 0, st>>>(
+      x, T, H, codes, scales);
 }
 
 void launch_quantize_weights(const float* w, int E, int N, int K, uint8_t* codes, float* scales,

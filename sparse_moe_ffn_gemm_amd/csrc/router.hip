@@ -30,8 +30,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // `acc`, folded into `tot`, so no long running sum absorbs small terms.
 //
 // The workgroups of the first expert tile also quantise the x tile they staged (one
-// 1x128 group per token and step, the same rule and code as the activation quantiser),
-// so x is read from HBM once for both uses.
+// 1x128 group per token and step, or four 1x32 MX blocks, the same rule and code as the
+// activation quantiser), so x is read from HBM once for both uses.
 // ------------------------------------------------------------------------------------
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kRC = 128;          // H columns staged per step (one quantisation group)
@@ -86,7 +86,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             int32_t* __restrict__ hist,
                                                             int hist_n, uint8_t* __restrict__ xq,
                                                             float* __restrict__ sx,
-                                                            const uint16_t* __restrict__ parts) {
+                                                            const uint16_t* __restrict__ parts,
+                                                            uint8_t* __restrict__ sx_mx) {
   __shared__ __align__(16) uint16_t xs[kRouterTile * kRS];
   __shared__ __align__(16) uint16_t wp[3][kRouterTile * kRS];   // hi, mid, lo parts of W
   {  // clear the dispatch histograms that the top-k step accumulates (a slice per block)
@@ -176,9 +177,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         const int row = pass * 16 + (tid >> 4), col = 8 * (tid & 15);
         const int t = t0 + row;
         const bool in = t < T && h0 + col < h_end;
-        const float sc = quantize_group16(xs + row * kRS, col, in,
-                                          xq + static_cast<size_t>(t < T ? t : 0) * H + h0);
-        if ((tid & 15) == 0 && t < T) sx[static_cast<size_t>(t) * KBH + g] = sc;
+        uint8_t* codes_row = xq + static_cast<size_t>(t < T ? t : 0) * H + h0;
+        if (sx_mx != nullptr) {   // MXFP8: four lanes per 32-block, pads past H get 127
+          const int code = quantize_mx8(xs + row * kRS, col, in, codes_row);
+          if ((tid & 3) == 0 && t < T)
+            sx_mx[static_cast<size_t>(t) * 4 * KBH + (h0 + col) / kMxBlock] = static_cast<uint8_t>(code);
+        } else {
+          const float sc = quantize_group16(xs + row * kRS, col, in, codes_row);
+          if ((tid & 15) == 0 && t < T) sx[static_cast<size_t>(t) * KBH + g] = sc;
+        }
       }
     }
 #pragma unroll
@@ -725,17 +732,17 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
 
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
                           int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
-                          uint8_t* xq, float* sx, uint16_t* parts) {
+                          uint8_t* xq, float* sx, uint16_t* parts, uint8_t* sx_mx) {
   dim3 grid(ceil_div(T, kRouterTile), ceil_div(E, kRouterTile), ksplit);
   if (parts != nullptr) {
     const long n4 = static_cast<long>(E) * H / 4;   // H is a multiple of 64
     router_split_kernel<<<dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st>>>(
         W, n4, static_cast<long>(E) * H, parts);
     router_logits_kernel<true><<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist,
-                                                           hist_n, xq, sx, parts);
+                                                           hist_n, xq, sx, parts, sx_mx);
   } else {
     router_logits_kernel<false><<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist,
-                                                            hist_n, xq, sx, nullptr);
+                                                            hist_n, xq, sx, nullptr, sx_mx);
   }
 }
 

@@ -1,8 +1,9 @@
 """A sparse MoE FFN layer object on one GPU: weights quantised once, workspace kept.
 
-Weights are converted statically to e4m3 codes with 128x128 block scales ("Hosting
-Qwen on Blackwell", section "Quantization") by the library's quantisation kernel;
-``forward`` runs the whole layer through ``moe_forward``.
+Weights are converted statically ("Hosting Qwen on Blackwell", section "Quantization")
+by the library's quantisation kernels, to e4m3 codes with 128x128 block scales or, with
+``fmt="mxfp8"``, to MXFP8 (1x32 blocks, E8M0 scales); ``forward`` runs the whole layer
+through ``moe_forward`` / ``moe_forward_mx``.
 """
 from __future__ import annotations
 
@@ -27,22 +28,32 @@ class MoELayer:
     @classmethod
     def from_expert_weights(cls, router_w, router_b, top_k: int, b13, b2,
                             w13_of: Callable[[int], torch.Tensor],
-                            w2_of: Callable[[int], torch.Tensor], device="cuda") -> "MoELayer":
+                            w2_of: Callable[[int], torch.Tensor], device="cuda",
+                            fmt: str = "block") -> "MoELayer":
         """Quantise expert by expert: ``w13_of(e)`` -> [2I, H] fp32, ``w2_of(e)`` -> [H, I] fp32
-        (on any device; moved to ``device`` one expert at a time)."""
+        (on any device; moved to ``device`` one expert at a time).  ``fmt``: "block"
+        (128x128 block scales) or "mxfp8"."""
         E, H = router_w.shape
         first = w2_of(0)
         I = first.shape[1]
         kb = _lib.kb
         w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
-        s13 = torch.empty((E, kb(2 * I), kb(H)), dtype=torch.float32, device=device)
         w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
-        s2 = torch.empty((E, kb(H), kb(I)), dtype=torch.float32, device=device)
+        if fmt == "mxfp8":
+            s13 = torch.empty((E, 2 * I, _lib.mx_row(H)), dtype=torch.uint8, device=device)
+            s2 = torch.empty((E, H, _lib.mx_row(I)), dtype=torch.uint8, device=device)
+            quant = _lib.quantize_weights_mx
+        elif fmt == "block":
+            s13 = torch.empty((E, kb(2 * I), kb(H)), dtype=torch.float32, device=device)
+            s2 = torch.empty((E, kb(H), kb(I)), dtype=torch.float32, device=device)
+            quant = _lib.quantize_weights
+        else:
+            raise ValueError(f"unknown weight format {fmt}")
         for e in range(E):
             a = w13_of(e).to(device=device, dtype=torch.float32).contiguous()
-            _lib.quantize_weights(a, w13[e:e + 1], s13[e:e + 1])
+            quant(a, w13[e:e + 1], s13[e:e + 1])
             b = (first if e == 0 else w2_of(e)).to(device=device, dtype=torch.float32).contiguous()
-            _lib.quantize_weights(b, w2[e:e + 1], s2[e:e + 1])
+            quant(b, w2[e:e + 1], s2[e:e + 1])
         return cls(router_w.to(device), None if router_b is None else router_b.to(device), top_k,
                    w13, s13, None if b13 is None else b13.to(device), w2, s2,
                    None if b2 is None else b2.to(device))

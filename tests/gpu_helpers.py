@@ -37,10 +37,12 @@ def bits_host(t: torch.Tensor) -> np.ndarray:
 
 
 class GpuLayer:
-    """Device tensors of one layer; expert weights quantised by the library."""
+    """Device tensors of one layer; expert weights quantised by the library (``fmt``
+    "block": 128x128 block scales, "mxfp8": MXFP8)."""
 
-    def __init__(self, shape: LayerShape, inputs=None, device="cuda"):
+    def __init__(self, shape: LayerShape, inputs=None, device="cuda", fmt="block"):
         self.shape = shape
+        self.fmt = fmt
         self.li = inputs if inputs is not None else make_inputs(shape)
         li = self.li
         self.x = bf16_dev(li.x, device)
@@ -49,15 +51,17 @@ class GpuLayer:
         self.layer = moe.MoELayer.from_expert_weights(
             torch.from_numpy(li.router_w), torch.from_numpy(li.router_b), shape.top_k, b13, b2,
             lambda e: expert_weights(shape, "w13", e, device),
-            lambda e: expert_weights(shape, "w2", e, device), device=device)
+            lambda e: expert_weights(shape, "w2", e, device), device=device, fmt=fmt)
         torch.cuda.synchronize()
 
 
 class OracleExperts:
-    """Lazily quantised experts for the oracle (from the generator's fp32 weights)."""
+    """Lazily quantised experts for the oracle (from the generator's fp32 weights), in the
+    block-scaled or the MXFP8 format."""
 
-    def __init__(self, shape: LayerShape, li):
+    def __init__(self, shape: LayerShape, li, fmt="block"):
         self.shape, self.li = shape, li
+        self.fmt = fmt
         self.cache = {}
         self.dev = "cuda" if _base(shape).weights_on_device else "cpu"
 
@@ -67,9 +71,11 @@ class OracleExperts:
         host = {e: (expert_weights(self.shape, "w13", e, self.dev).cpu().numpy(),
                     expert_weights(self.shape, "w2", e, self.dev).cpu().numpy()) for e in todo}
 
+        quant = R.quantize_mx if self.fmt == "mxfp8" else R.quantize_blocks
+
         def q(e):
-            c13, s13 = R.quantize_blocks(host[e][0])
-            c2, s2 = R.quantize_blocks(host[e][1])
+            c13, s13 = quant(host[e][0])
+            c2, s2 = quant(host[e][1])
             return e, (c13, s13, c2, s2)
 
         with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -91,25 +97,32 @@ class OracleExperts:
         self.prepare(need)
         ref = R.forward(li.x, li.router_w, li.router_b, self.shape.top_k, self.shape.I,
                         self.view(0), self.view(1), li.b13, self.view(2), self.view(3), li.b2,
-                        token_subset=token_subset)
+                        token_subset=token_subset, fmt=self.fmt)
         ref["allowance"] = self.flip_allowance(ref)
         return ref
+
+    def dequant_w(self, codes, scales):
+        return R.dequantize_mx(codes, scales) if self.fmt == "mxfp8" else R.dequantize_blocks(codes, scales)
 
     def flip_allowance(self, ref):
         """Per output element of the evaluated tokens: sum_j g_j * |W2_j| . flip_delta(h_j)."""
         li, k, I = self.li, self.shape.top_k, self.shape.I
         toks = ref["tokens"]
         x32 = R.bf16_to_f64(li.x[toks]).astype(np.float32)
-        xq, sx = R.quantize_activations(x32)
-        xd = R.dequantize_blocks(xq, sx, rows=1)
+        if self.fmt == "mxfp8":
+            xd = R.dequantize_mx(*R.quantize_mx(x32))
+        else:
+            xq, sx = R.quantize_activations(x32)
+            xd = R.dequantize_blocks(xq, sx, rows=1)
         allow = np.zeros((toks.size, li.x.shape[1]))
         for e in np.unique(ref["ids"][toks]):
             rt, rj = np.nonzero(ref["ids"][toks] == e)
             c13, s13, c2, s2 = self.cache[int(e)]
-            _, hq, hs, h64 = R.expert_ffn(xd[rt], c13, s13, li.b13[e], c2, s2, li.b2[e], I)
-            W2 = np.abs(R.dequantize_blocks(c2, s2))
-            contrib = flip_delta(h64, hq, hs) @ W2.T
-            allow[rt] += ref["gates"][toks[rt], rj][:, None] * contrib
+            _, hq, hs, h64 = R.expert_ffn(xd[rt], c13, s13, li.b13[e], c2, s2, li.b2[e], I,
+                                          self.fmt)
+            W2 = np.abs(self.dequant_w(c2, s2))
+            delta = flip_delta_mx(h64, hq, hs) if self.fmt == "mxfp8" else flip_delta(h64, hq, hs)
+            allow[rt] += ref["gates"][toks[rt], rj][:, None] * (delta @ W2.T)
         return allow
 
 
@@ -156,6 +169,43 @@ def flip_delta(h64: np.ndarray, hq: np.ndarray, hs: np.ndarray) -> np.ndarray:
     lo, hi, s = _h_window(h64, hs)
     dq = R.e4m3_decode(hq)
     return np.maximum(np.abs(lo - dq), np.abs(hi - dq)) * s
+
+
+def _group128_max(h64: np.ndarray) -> np.ndarray:
+    """max |h| over each element's 1x128 column group (the scale of the device's fp32
+    accumulation error in h, whatever the quantisation format)."""
+    I = h64.shape[1]
+    g = -(-I // 128)
+    pad = np.zeros((h64.shape[0], g * 128))
+    pad[:, :I] = np.abs(h64)
+    return np.repeat(pad.reshape(-1, g, 128).max(axis=2), 128, axis=1)[:, :I]
+
+
+def flip_delta_mx(h64: np.ndarray, hq: np.ndarray, hs: np.ndarray) -> np.ndarray:
+    """``flip_delta`` for MXFP8 h (1x32 blocks, E8M0 codes ``hs`` [rows, I/32]): the device's
+    h may differ from the oracle's by H_EPS of its 1x128 group maximum; every code a value
+    within that distance rounds to at the oracle's block scale is correct, and where the
+    block maximum itself lies within that distance of a power of two the device may take
+    the neighbouring exponent, so the codes of the block at that scale count too."""
+    I = h64.shape[1]
+    eps = H_EPS * _group128_max(h64)
+    X = np.repeat(hs.astype(np.int64) - 127, 32, axis=1)[:, :I]
+    dq = R.e4m3_decode(hq) * np.ldexp(1.0, X)
+    out = np.zeros_like(h64)
+    for dx in (0, -1, 1):
+        s = np.ldexp(1.0, X + dx)
+        lo = R.e4m3_decode(R.e4m3_encode(((h64 - eps) / s).astype(np.float32))) * s
+        hi = R.e4m3_decode(R.e4m3_encode(((h64 + eps) / s).astype(np.float32))) * s
+        d = np.maximum(np.abs(lo - dq), np.abs(hi - dq))
+        if dx != 0:
+            # only blocks whose maximum is within eps of the power of two between the scales
+            amax = np.abs(h64).reshape(h64.shape[0], -1, 32).max(axis=2)
+            edge = np.ldexp(1.0, (hs.astype(np.int64) - 127) + 8 + (1 if dx > 0 else 0))
+            e_blk = eps.reshape(h64.shape[0], -1, 32).max(axis=2)
+            near = np.abs(amax - edge) <= e_blk
+            d = d * np.repeat(near, 32, axis=1)[:, :I]
+        out = np.maximum(out, d)
+    return out
 
 
 def compare_out(gpu_bits: np.ndarray, ref: np.ndarray, what="", allowance=None):
