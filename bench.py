@@ -39,20 +39,26 @@ def kb(n):
     return (n + 127) // 128
 
 
-def algorithmic(shape, counts):
+def algorithmic(shape, counts, fmt="block"):
     """Algorithmic flops and compulsory HBM bytes of the layer and of its two GEMMs.
 
     Weights are counted once per *active* expert (an expert with no routed token is
     never read).  Intermediates (x codes, h, y) count where a kernel must read or write
-    them at least once."""
+    them at least once.  Scales: fp32 per 128x128 weight block and per 1x128 activation
+    group, or (MXFP8) one E8M0 byte per 32 elements along K."""
     T, H, E, k, I = shape.T, shape.H, shape.E, shape.top_k, shape.I
     rows = T * k
     active = int((counts > 0).sum())
-    w13 = active * (2 * I * H + kb(2 * I) * kb(H) * 4 + (2 * I * 2 if shape.expert_bias else 0))
-    w2 = active * (H * I + kb(H) * kb(I) * 4 + (H * 2 if shape.expert_bias else 0))
+    if fmt == "mxfp8":
+        sw13, sw2, sx, sh = 2 * I * H // 32, H * I // 32, T * H // 32, rows * I // 32
+    else:
+        sw13, sw2 = kb(2 * I) * kb(H) * 4, kb(H) * kb(I) * 4
+        sx, sh = T * kb(H) * 4, rows * kb(I) * 4
+    w13 = active * (2 * I * H + sw13 + (2 * I * 2 if shape.expert_bias else 0))
+    w2 = active * (H * I + sw2 + (H * 2 if shape.expert_bias else 0))
     layer_bytes = T * H * 2 + E * H * 4 + E * 4 + w13 + w2 + T * H * 2
-    xq = T * H + T * kb(H) * 4
-    hq = rows * I + rows * kb(I) * 4
+    xq = T * H + sx
+    hq = rows * I + sh
     g1_flops = 2 * rows * H * 2 * I
     g2_flops = 2 * rows * I * H
     return dict(
@@ -120,7 +126,7 @@ def device_copy_gbs(torch, dev, mib=1024, reps=5):
     return 2 * a.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def cpu_baseline(shape, li, n_tokens):
+def cpu_baseline(shape, li, n_tokens, fmt="block"):
     """The oracle's forward on the first ``n_tokens`` tokens (one thread)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -136,12 +142,13 @@ def cpu_baseline(shape, li, n_tokens):
         ids, _ = R.topk_softmax(R.router_logits(li.x, li.router_w, li.router_b), shape.top_k)
         need = np.unique(ids[toks])
         c13, s13, c2, s2 = {}, {}, {}, {}
+        quant = R.quantize_mx if fmt == "mxfp8" else R.quantize_blocks
         for e in need:   # offline weight conversion: not timed
-            c13[e], s13[e] = R.quantize_blocks(expert_weights(shape, "w13", int(e), dev).cpu().numpy())
-            c2[e], s2[e] = R.quantize_blocks(expert_weights(shape, "w2", int(e), dev).cpu().numpy())
+            c13[e], s13[e] = quant(expert_weights(shape, "w13", int(e), dev).cpu().numpy())
+            c2[e], s2[e] = quant(expert_weights(shape, "w2", int(e), dev).cpu().numpy())
         t0 = time.perf_counter()
         R.forward(li.x, li.router_w, li.router_b, shape.top_k, shape.I, c13, s13, li.b13, c2, s2,
-                  li.b2, token_subset=toks)
+                  li.b2, token_subset=toks, fmt=fmt)
         dt = time.perf_counter() - t0
     return {"value": round(toks.size / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {toks.size} of {shape.T} tokens ({need.size} experts), fp64 NumPy "
@@ -168,6 +175,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt-oss-120b-prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=96)
+    ap.add_argument("--format", choices=["block", "mxfp8"], default="block",
+                    help="expert weight format: 128x128 block scales (default) or MXFP8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
@@ -200,7 +209,7 @@ def main():
         torch.from_numpy(li.router_w), torch.from_numpy(li.router_b), shape.top_k,
         bf(li.b13) if shape.expert_bias else None, bf(li.b2) if shape.expert_bias else None,
         lambda e: expert_weights(shape, "w13", e, "cuda"),
-        lambda e: expert_weights(shape, "w2", e, "cuda"), device=dev)
+        lambda e: expert_weights(shape, "w2", e, "cuda"), device=dev, fmt=args.format)
     x = bf(li.x)
     out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=dev)
     routing = moe.new_routing(shape.T, shape.E, shape.top_k, dev)
@@ -305,7 +314,7 @@ def main():
     copy_gbs = device_copy_gbs(torch, dev)
 
     counts = routing["expert_counts"].cpu().numpy()
-    alg = algorithmic(shape, counts)
+    alg = algorithmic(shape, counts, args.format)
     step_s = ms_step / 1e3
     tflops = alg["layer_flops"] / step_s / 1e12
     gbs = alg["layer_bytes"] / step_s / 1e9
@@ -321,7 +330,8 @@ def main():
         roof = {"bound": "hbm", "achieved": k_alg["bytes"] / k_s / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    rec = pmc_record(shape.name, dom)
+    prof_name = shape.name if args.format == "block" else f"{shape.name}-mxfp8"
+    rec = pmc_record(prof_name, dom)
     roof["traffic"] = rec.get("hbm_bytes_per_launch") if rec else None
     if rec and "mfma_busy_frac" in rec:
         # matrix-core busy cycles / (active cycles x SIMDs), from the same counter run
@@ -334,10 +344,13 @@ def main():
     line = {
         "metric": METRIC, "value": round(shape.T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3" if args.format == "block" else "mxfp8-e4m3",
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "E": shape.E,
-                   "top_k": shape.top_k, "I": shape.I, "parallelism": "single-gpu"},
+                   "top_k": shape.top_k, "I": shape.I, "parallelism": "single-gpu",
+                   "weights": "fp8 128x128 block scales" if args.format == "block"
+                   else "mxfp8 1x32 E8M0 scales"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_FP8_TFLOPS, 4),
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "active_experts": alg["active_experts"],
@@ -352,7 +365,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(shape, li, args.cpu_sample_tokens)
+        line["cpu_baseline"] = cpu_baseline(shape, li, args.cpu_sample_tokens, args.format)
     print(json.dumps(line), flush=True)
 
 

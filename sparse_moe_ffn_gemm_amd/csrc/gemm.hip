@@ -1016,7 +1016,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
 // (L2 hits) and are scaled by zero.  Rows past the tile's end are staged from its first
 // row; their outputs are never stored.
 // ------------------------------------------------------------------------------------
-template <bool SWIGLU, int KS>
+template <bool SWIGLU, int KS, bool MX = false>
 __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs a, int ntiles) {
   constexpr int WAVES = 8;
   constexpr int NSUB = SWIGLU ? 2 : 1;       // weight sub-tiles per wave (gate, up)
@@ -1050,19 +1050,34 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
   const int nbp = (nb + 1) & ~1;             // padded to the two-slot ring
   unsigned b_off[NSUB];
   float sbg[NSUB];                           // lane j: weight block scale of K-block j
+  const uint8_t* bmx[NSUB];                  // MXFP8: the lane's weight row of E8M0 codes
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     const int row = (SWIGLU && s == 1 ? I : 0) + c0 + r;
     b_off[s] = static_cast<unsigned>(row) * K + 16 * g;
-    const int brow = ((SWIGLU && s == 1 ? I : 0) + c0) / kBlock;
-    sbg[s] = (live && lane < KB) ? Bsc[static_cast<size_t>(brow) * KB + lane] : 0.f;
+    if constexpr (MX) {
+      bmx[s] = a.B_mx + (static_cast<size_t>(e) * N + (live ? row : 0)) * (4 * KB);
+      sbg[s] = 0.f;
+    } else {
+      const int brow = ((SWIGLU && s == 1 ? I : 0) + c0) / kBlock;
+      sbg[s] = (live && lane < KB) ? Bsc[static_cast<size_t>(brow) * KB + lane] : 0.f;
+    }
   }
 
   v8i ring[2][KS];
-  auto issue = [&](int b, v8i (&bq)[KS]) {
+  uint32_t xring[2][KS];   // MXFP8: the burst's weight scale words (byte g is the lane's)
+  auto issue = [&](int b, v8i (&bq)[KS], uint32_t (&xq)[KS]) {
     const int bb = b < nb ? b : nb - 1;
     const int s = bb / bps, j0 = (bb % bps) * KS;
     const unsigned bo = (NSUB == 2 && s == 1) ? b_off[NSUB - 1] : b_off[0];
+    if constexpr (MX) {
+      const uint8_t* xr = (NSUB == 2 && s == 1) ? bmx[NSUB - 1] : bmx[0];
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const int jj = j0 + t < KB ? j0 + t : KB - 1;
+        xq[t] = *reinterpret_cast<const uint32_t*>(xr + 4 * jj);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       const int jj = j0 + t < KB ? j0 + t : KB - 1;
@@ -1077,11 +1092,29 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int b, const v8i (&bq)[KS]) {
+  auto compute = [&](int b, const v8i (&bq)[KS], const uint32_t (&xq)[KS]) {
     const bool bl = b < nb;
     const int bb = bl ? b : nb - 1;
     const int s = bb / bps, j0 = (bb % bps) * KS;
     const float sbs = (NSUB == 2 && s == 1) ? sbg[NSUB - 1] : sbg[0];
+    if constexpr (MX) {
+      // The matrix cores apply both E8M0 codes of the lane's block and accumulate in
+      // place (the result register is the live accumulator, never a scale operand's);
+      // blocks past K (padded bursts re-read the last one) are skipped: a wave-uniform
+      // branch.
+      v4f& ac = (NSUB == 2 && s == 1) ? acc[NSUB - 1] : acc[0];
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        if (bl && j0 + t < KB) {
+          const int jj = j0 + t;
+          const v8i af = lds_frag(sA + jj * 2048, r, g);
+          const int xa = reinterpret_cast<const uint8_t*>(sSa)[4 * (jj * 16 + r) + g];
+          const int xb = static_cast<int>((xq[t] >> (8 * g)) & 0xFFu);
+          ac = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[t], af, ac, 0, 0, 0, xb, 0, xa);
+        }
+      }
+      return;
+    }
     v4f pr[KS];
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
@@ -1110,8 +1143,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 
   // the first two weight bursts go out before the activation rows are even located
   if (live) {
-    issue(0, ring[0]);
-    issue(1, ring[1]);
+    issue(0, ring[0], xring[0]);
+    issue(1, ring[1], xring[1]);
   }
   // ---- stage the activation tile and its scales (all waves share the fetches) ----
   auto src_row = [&](int rr) {
@@ -1133,10 +1166,13 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
       load_lds16(src, sA + j * 2048 + 8 * (q & 1) * 128);
     }
     // scales: fetch q covers blocks 4q .. 4q+3, lane -> block 4q + (lane >> 4), row lane & 15
+    // (MXFP8: the row's 4-byte word of E8M0 codes of that block)
     const unsigned so = static_cast<unsigned>(src_row(r)) * KB;
     for (int q = wave; q < ceil_div(KB, 4); q += WAVES) {
       const int j = 4 * q + g;
-      const void* src = j < KB ? static_cast<const void*>(a.A_scale + so + j) : static_cast<const void*>(kZeroScale);
+      const void* src = j >= KB ? static_cast<const void*>(kZeroScale)
+                        : MX ? static_cast<const void*>(a.A_mx + 4 * (so + j))
+                             : static_cast<const void*>(a.A_scale + so + j);
       load_lds4(src, sSa + 64 * q);
     }
   }
@@ -1146,13 +1182,13 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 
   if (live) {
     for (int b0 = 0; b0 < nbp - 2; b0 += 2) {
-      compute(b0, ring[0]);
-      issue(b0 + 2, ring[0]);
-      compute(b0 + 1, ring[1]);
-      issue(b0 + 3, ring[1]);
+      compute(b0, ring[0], xring[0]);
+      issue(b0 + 2, ring[0], xring[0]);
+      compute(b0 + 1, ring[1], xring[1]);
+      issue(b0 + 3, ring[1], xring[1]);
     }
-    compute(nbp - 2, ring[0]);
-    compute(nbp - 1, ring[1]);
+    compute(nbp - 2, ring[0], xring[0]);
+    compute(nbp - 1, ring[1], xring[1]);
   }
 
   // ---- epilogue: lane holds row r and the four columns c0 + 4g + i ----
@@ -1184,6 +1220,19 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (lane < 16) red[wave * 16 + lane] = mx;
     __syncthreads();
+    if constexpr (MX) {
+      // 1x32 MX blocks: waves 2q and 2q+1 hold the 32 columns of block q of the tile;
+      // blocks past I (h = 0 there) get the pad code 127
+      if (p >= mt.row_end) return;
+      const float amax32 = fmaxf(red[(wave & ~1) * 16 + r], red[(wave | 1) * 16 + r]);
+      const int code = mx_scale_code(amax32);
+      if (live)
+        *reinterpret_cast<uint32_t*>(a.h_out + static_cast<size_t>(p) * I + cq) =
+            encode4_mul(hv[0], hv[1], hv[2], hv[3], mx_inv_scale(code));
+      if ((wave & 1) == 0 && g == 0)
+        a.h_mx[static_cast<size_t>(p) * 4 * KBI + (nt * kBlock + 16 * wave) / kMxBlock] = static_cast<uint8_t>(code);
+      return;
+    }
     if (!live || p >= mt.row_end) return;
     float amax = red[r];
 #pragma unroll
@@ -1244,17 +1293,19 @@ int gemm_tile_rows(long rows, int E) {
   return 256;
 }
 
+// Returns false if no kernel could take the launch (an MXFP8 decode launch whose LDS
+// opt-in failed); the caller reports an error.
 template <bool SWIGLU>
-static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
+static bool launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
   // decode-sized groups stream weights: gemm2 takes 128-column tiles there, twice as many
   // workgroups over the same bytes, so the last round of tiles is not half empty
   const int bn = (!SWIGLU && bm == 16) ? 128 : 256;
   const int ntiles = SWIGLU ? ceil_div(a.I, 128) : ceil_div(a.N, bn);
   const long total = static_cast<long>(max_tiles) * ntiles;
   const int grid = static_cast<int>((total + 7) / 8 * 8);
-  // MXFP8 layers take the large-group kernel at every group size (their tile list is
-  // built with 256-row tiles); so do block-scaled layers with large groups
-  if (bm == 256 || a.mx) {
+  // MXFP8 layers take the large-group kernel unless their tiles are decode-sized rows of
+  // the row-run kernel below (the plan picks 256-row tiles otherwise)
+  if (bm == 256 || (a.mx && bm != 16)) {
     constexpr int BN = SWIGLU ? kG1BN : kG2BN;
     const int nt_big = SWIGLU ? ceil_div(a.I, BN / 2) : ceil_div(a.N, BN);
     const long tot = static_cast<long>(max_tiles) * nt_big;
@@ -1271,7 +1322,7 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
     } else {
       grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS><<<g, 512, 0, st>>>(a, nt_big);
     }
-    return;
+    return true;
   }
   // Decode-sized groups whose weight rows are not whole 128-byte lines (K = 64 mod 128,
   // so every other row starts mid-line and each 128-byte block of it spans two lines):
@@ -1287,11 +1338,19 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
     static const bool lds_ok =
         hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, KS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
-    if (lds <= 64 * 1024 || lds_ok) {
+    static const bool lds_ok_mx =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, KS, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
+    if (a.mx && (lds <= 64 * 1024 || lds_ok_mx)) {
+      grouped_gemm_rowrun_kernel<SWIGLU, KS, true><<<g, 512, lds, st>>>(a, nts);
+      return true;
+    }
+    if (!a.mx && (lds <= 64 * 1024 || lds_ok)) {
       grouped_gemm_rowrun_kernel<SWIGLU, KS><<<g, 512, lds, st>>>(a, nts);
-      return;
+      return true;
     }
   }
+  if (a.mx) return false;   // the plan gives MXFP8 16-row tiles only for the row-run kernel
   switch (bm) {
     case 16:
       if constexpr (SWIGLU)
@@ -1306,13 +1365,14 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
       grouped_gemm_kernel<128, 256, 2, 2, SWIGLU, 3><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
       break;
   }
+  return true;
 }
 
-void launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
-  launch_gemm<true>(a, bm, max_tiles, st);
+bool launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
+  return launch_gemm<true>(a, bm, max_tiles, st);
 }
-void launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
-  launch_gemm<false>(a, bm, max_tiles, st);
+bool launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
+  return launch_gemm<false>(a, bm, max_tiles, st);
 }
 
 }  // namespace moe

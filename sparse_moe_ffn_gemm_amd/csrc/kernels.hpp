@@ -95,8 +95,9 @@ struct GemmArgs {
 
 // Rows per M-tile chosen for a layer with `rows` routed rows over E experts.
 int gemm_tile_rows(long rows, int E);
-void launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
-void launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
+// false: nothing was launched (see launch_gemm)
+bool launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
+bool launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
 
 // ---- combine ----
 void launch_combine(const uint16_t* y, const float* gates, const int32_t* inv, int T, int H,

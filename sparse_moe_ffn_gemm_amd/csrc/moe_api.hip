@@ -42,7 +42,8 @@ bool uses_route_tail(int T, int E, int k, int ksplit) {
          k <= moe::kTailTopK && ksplit <= moe::kTailSplit;
 }
 
-// `mx`: MXFP8 layers take 256-row M-tiles at every group size (one GEMM kernel family).
+// `mx`: MXFP8 layers take 256-row M-tiles (the large-group kernel) except for decode-sized
+// groups that the row-run kernel streams in both GEMMs.
 void make_plan(int T, int H, int E, int k, int I, Plan* p, bool mx = false) {
   p->T = T; p->H = H; p->E = E; p->k = k; p->I = I;
   p->rows = static_cast<long>(T) * k;
@@ -58,7 +59,10 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, bool mx = false) {
   // the tile list is sized for the block-scaled tile height, an upper bound for the
   // 256-row tiles of MXFP8 too, so both formats share one workspace layout
   const int bm_block = moe::gemm_tile_rows(p->rows, E);
-  p->bm = mx ? 256 : bm_block;
+  // MXFP8: decode-sized groups whose weight rows are not whole 128-byte lines in both GEMMs
+  // (H and I = 64 mod 128, the row-run kernel) keep 16-row tiles, all others 256
+  const bool mx_rowrun = bm_block == 16 && H % 128 != 0 && I % 128 != 0 && H <= 8192 && I <= 8192;
+  p->bm = mx ? (mx_rowrun ? 16 : 256) : bm_block;
   p->max_tiles = static_cast<int>(p->rows / bm_block + std::min<long>(E, p->rows));
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -221,7 +225,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g1.I = I;
   g1.h_out = at<uint8_t>(ws, p.h);
   g1.queue = at<int32_t>(ws, p.num_tiles) + 1;
-  moe::launch_gemm1(g1, p.bm, p.max_tiles, st);
+  if (!moe::launch_gemm1(g1, p.bm, p.max_tiles, st)) return MOE_ERR_HIP;
   mark(ev, 6, st);
 
   moe::GemmArgs g2{};
@@ -248,7 +252,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.I = I;
   g2.y_out = at<uint16_t>(ws, p.y);
   g2.queue = at<int32_t>(ws, p.num_tiles) + 1 + moe::kGemmQueues;
-  moe::launch_gemm2(g2, p.bm, p.max_tiles, st);
+  if (!moe::launch_gemm2(g2, p.bm, p.max_tiles, st)) return MOE_ERR_HIP;
   mark(ev, 7, st);
   moe::launch_combine(at<uint16_t>(ws, p.y), tb.gates, tb.inv, T, H, top_k, out, st);
   mark(ev, 8, st);
