@@ -168,6 +168,81 @@ def copy_calibration(gib=1.0, reps=5):
     print(json.dumps({"copy_bytes_per_launch": n, "reps": reps}))
 
 
+def one_token_per_expert(args):
+    """The pages' decode GEMM benchmark ("Hosting Qwen on Blackwell", section "MoE GEMM":
+    every expert activated with a single token, over expert-parallel degrees): one GPU's
+    share of the qwen3-235b layer (H 4096, I 1536, 128 experts) at EP degree d is 128/d
+    experts, each routed exactly one token (T = 128/d, top_k = 1, a router with each
+    token's own direction planted in its expert's row).  Prints a table on stderr and one
+    JSON line with the GEMM and layer times per (d, weight format)."""
+    import numpy as np
+    import torch
+
+    import sparse_moe_ffn_gemm_amd as moe
+    from sparse_moe_ffn_gemm_amd._lib import PROFILE_STAGES
+    from synth import expert_weights, make_inputs
+    from synth.cases import LayerShape
+
+    dev = torch.device("cuda:0")
+    results = []
+    for fmt in ("block", "mxfp8"):
+        for ep in (1, 2, 4, 8, 16, 32, 64):
+            n = 128 // ep
+            shape = LayerShape(f"qwen3-235b-one-token-per-expert-ep{ep}", T=n, H=4096, E=n,
+                               top_k=1, I=1536, seed=3, expert_bias=False,
+                               weights_on_device=True, router="one_per_expert")
+            li = make_inputs(shape)
+            bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+            layer = moe.MoELayer.from_expert_weights(
+                torch.from_numpy(li.router_w), torch.from_numpy(li.router_b), 1, None, None,
+                lambda e: expert_weights(shape, "w13", e, "cuda"),
+                lambda e: expert_weights(shape, "w2", e, "cuda"), device=dev, fmt=fmt)
+            x = bf(li.x)
+            out = torch.empty((n, shape.H), dtype=torch.bfloat16, device=dev)
+            routing = moe.new_routing(n, n, 1, dev)
+            ws = layer.workspace(n)
+            fa = (x, layer.router_w, layer.router_b, layer.w13, layer.w13_scales, None,
+                  layer.w2, layer.w2_scales, None, 1)
+            for _ in range(args.warmup):
+                moe.forward(*fa, out=out, routing=routing, workspace=ws)
+            torch.cuda.synchronize()
+            counts = routing["expert_counts"].cpu().numpy()
+            if not np.all(counts == 1):
+                raise RuntimeError(f"ep {ep}: expert counts {counts} (expected one token each)")
+            nprof = max(10, args.steps)
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PROFILE_STAGES) + 1)]
+                  for _ in range(nprof)]
+            for k in range(nprof):
+                moe.forward_profiled(ev[k], *fa, out=out, routing=routing, workspace=ws)
+            torch.cuda.synchronize()
+            st = {name: float(np.median([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(nprof)]))
+                  for i, name in enumerate(PROFILE_STAGES)}
+            steps = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(max(20, args.steps))]
+            for a_, b_ in steps:
+                a_.record()
+                moe.forward(*fa, out=out, routing=routing, workspace=ws)
+                b_.record()
+            torch.cuda.synchronize()
+            layer_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in steps]))
+            wbytes = n * 3 * shape.H * shape.I * (1 + (1 / 32 if fmt == "mxfp8" else 1 / 4096))
+            gemm_us = (st["gemm1"] + st["gemm2"]) * 1e3
+            r = {"ep": ep, "experts": n, "format": fmt, "gemm1_us": round(st["gemm1"] * 1e3, 2),
+                 "gemm2_us": round(st["gemm2"] * 1e3, 2), "gemm_us": round(gemm_us, 2),
+                 "layer_us_p50": round(layer_ms * 1e3, 2),
+                 "weight_gbs": round(wbytes / (gemm_us * 1e-6) / 1e9, 1)}
+            results.append(r)
+            print(f"[microbench] {fmt:6s} EP {ep:3d} ({n:3d} experts x 1 token): GEMM1 "
+                  f"{r['gemm1_us']:7.1f} us  GEMM2 {r['gemm2_us']:7.1f} us  layer p50 "
+                  f"{r['layer_us_p50']:7.1f} us  weights {r['weight_gbs']:7.1f} GB/s",
+                  file=sys.stderr, flush=True)
+            del layer, ws, x, out
+            torch.cuda.empty_cache()
+    print(json.dumps({"microbench": "one-token-per-expert",
+                      "layer": "qwen3-235b MoE (H 4096, I 1536, 128 experts), one GPU's share at EP degree d",
+                      "data": "synthetic", "results": results}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +253,9 @@ def main():
     ap.add_argument("--format", choices=["block", "mxfp8"], default="block",
                     help="expert weight format: 128x128 block scales (default) or MXFP8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--microbench", choices=["one-token-per-expert"],
+                    help="instead of the layer benchmark: the decode GEMM sweep over "
+                         "expert-parallel degrees, every expert given one token")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -192,6 +270,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.microbench:
+        one_token_per_expert(args)
         return
 
     import sparse_moe_ffn_gemm_amd as moe

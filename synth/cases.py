@@ -54,7 +54,8 @@ class LayerShape:
     I: int
     seed: int
     expert_bias: bool = True
-    router: str = "random"          # "random" | "zipf" | "hot" (expert 0 always chosen)
+    router: str = "random"          # "random" | "zipf" | "hot" (expert 0 always chosen) |
+                                    # "one_per_expert" (token t's first choice is expert t mod E)
     weights_on_device: bool = False  # draw expert weights with torch on the GPU
     token_slice_of: Optional[str] = None  # decode layer reusing a prefill layer's draw
 
@@ -175,6 +176,14 @@ def make_inputs(shape: LayerShape) -> LayerInputs:
         b = _normal(_rng(s, _TAG_RB), (E,), 0.01)
     if shape.router == "hot":          # edge case: expert 0 is every token's first choice
         b[0] += np.float32(1000.0)
+    if shape.router == "one_per_expert":
+        # the pages' decode GEMM benchmark: every expert activated by a single token.  Row
+        # e of W gains 40 x_e / |x_e|^2 (token e's own direction), so token e's logit for
+        # expert e exceeds the random ones (std 0.05 sqrt(H)) by a wide margin, and with
+        # T = E and top_k = 1 each expert gets exactly one token.
+        xf = bf16_bits_to_f32(x).astype(np.float64)
+        for e in range(min(E, T)):
+            W[e] += (40.0 * xf[e] / np.dot(xf[e], xf[e])).astype(np.float32)
     if shape.expert_bias:
         b13 = f32_to_bf16_bits(_normal(_rng(s, _TAG_B13), (E, 2 * I), 0.01))
         b2 = f32_to_bf16_bits(_normal(_rng(s, _TAG_B2), (E, H), 0.01))

@@ -29,6 +29,8 @@ SMALL = [
     # > 160 rows per expert: 256-row tiles, a short last tile per expert, ragged K and N
     custom_shape(T=600, H=320, E=4, top_k=2, I=320, seed=38),
     custom_shape(T=700, H=448, E=2, top_k=1, I=192, seed=39, expert_bias=False),
+    # every expert exactly one token (the pages' decode GEMM benchmark)
+    custom_shape(T=16, H=256, E=16, top_k=1, I=128, seed=43, router="one_per_expert"),
 ]
 
 

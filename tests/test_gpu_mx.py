@@ -73,6 +73,8 @@ SMALL = [
     custom_shape(T=150, H=320, E=4, top_k=4, I=384, seed=54),       # > 64 rows: full tile body
     custom_shape(T=600, H=320, E=4, top_k=2, I=320, seed=55),       # several 256-row tiles
     custom_shape(T=96, H=384, E=8, top_k=2, I=320, seed=56, expert_bias=False),
+    # every expert exactly one token (the pages' decode GEMM benchmark)
+    custom_shape(T=16, H=256, E=16, top_k=1, I=128, seed=58, router="one_per_expert"),
 ]
 
 
