@@ -40,6 +40,11 @@ consecutive elements along K share a power-of-two scale, stored as an E8M0 code
 [256, 512) before the e4m3 rounding (clamped to +-448); an all-zero block gets
 exponent 0; the activations (x, h) use the same 1x32 blocks along K.
 
+MXFP4 expert weights ("GPT-OSS on day 0": the checkpoints ship with MXFP4 expert weights):
+the same OCP MX blocks with e2m1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6),
+exponent floor(log2(amax)) - 2 (the block maximum lands in [4, 8) before the rounding,
+clamped to +-6), two codes per byte with element 2j in the low nibble; x and h stay MXFP8.
+
 Pins (tests/test_oracle_*.py): the e4m3 codec against its closed-form definition
 and torch's float8_e4m3fn, a brute-force nearest-code encoder and an independent
 scalar quantiser; router logits, top-k and gates against pure-Python loops and
@@ -252,15 +257,90 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
+# ----------------------------------------------------------------------------------------
+# MXFP4 expert weights ("GPT-OSS on day 0": the checkpoints ship with MXFP4 expert
+# weights): OCP MX blocks of 32 along K, E8M0 scales, e2m1 elements (sign, 2 exponent
+# bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two codes per
+# byte with element 2j in the low nibble.  The activations stay MXFP8.
+# ----------------------------------------------------------------------------------------
+
+E2M1_EMAX = 2          # exponent of the largest e2m1 value (6 = 1.5 * 2^2)
+E2M1_MAX = 6.0
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of each e2m1 code (0..15), float64."""
+    c = np.asarray(codes, np.int64)
+    e, m = (c >> 1) & 3, c & 1
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 2.0, e - 1), 0.5 * m)
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_encode(v) -> np.ndarray:
+    """Nearest e2m1 code (ties to the even code) of float values after clamping to +-6; the
+    sign is kept (a negative value that rounds to zero gives 0x8)."""
+    v = np.asarray(v, np.float64)
+    if np.isnan(v).any():
+        raise ValueError("NaN has no defined code here")
+    table = e2m1_decode(np.arange(8))                 # the 8 magnitudes, ascending
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    d = np.abs(a[..., None] - table)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # ties: the even code among the nearest ones
+    code = np.where(cand.sum(-1) > 1, np.argmax(cand & (np.arange(8) % 2 == 0), axis=-1),
+                    np.argmax(cand, axis=-1))
+    return (code | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def quantize_mxfp4(a):
+    """MXFP4 of a float32 array [..., K] along K (K a multiple of 32): per 32-block,
+    X = floor(log2(amax)) - 2 clamped to [-127, 127] (0 for an all-zero block), codes
+    e2m1_encode(v * 2^-X) (exact scaling, then clamped to +-6).  Returns (packed codes uint8
+    [..., K/2], element 2j in the low nibble of byte j; scale codes uint8 [..., K/32])."""
+    a = np.asarray(a, dtype=np.float32)
+    K = a.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = a.reshape(a.shape[:-1] + (K // MX_BLOCK, MX_BLOCK)).astype(np.float64)
+    amax = np.abs(blocks).max(axis=-1)
+    _, ex = np.frexp(amax)
+    X = np.where(amax > 0, np.clip(ex - 1 - E2M1_EMAX, -127, 127), 0).astype(np.int64)
+    codes = e2m1_encode(blocks * np.ldexp(1.0, -X)[..., None]).reshape(a.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
+
+
+def unpack_e2m1(packed) -> np.ndarray:
+    """Codes [..., 2 n] of packed bytes [..., n] (low nibble first)."""
+    p = np.asarray(packed, np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    out[..., 0::2] = p & 15
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def dequantize_mxfp4(packed, scales) -> np.ndarray:
+    """decode(code) * 2^(scale code - 127) of its 32-block, float64."""
+    vals = e2m1_decode(unpack_e2m1(packed))
+    K = vals.shape[-1]
+    X = np.asarray(scales, np.int64) - 127
+    v = vals.reshape(vals.shape[:-1] + (K // MX_BLOCK, MX_BLOCK)) * np.ldexp(1.0, X)[..., None]
+    return v.reshape(vals.shape)
+
+
 def _quantizer(fmt: str):
     """(quantise a float32 activation matrix, dequantise it, dequantise an expert matrix)
-    of the block-scaled ("block": 1x128 activations, 128x128 weights) or the MXFP8
-    ("mxfp8": 1x32 blocks along K for both) format."""
+    of the block-scaled ("block": 1x128 activations, 128x128 weights), the MXFP8 ("mxfp8":
+    1x32 blocks along K for both) or the MXFP4-weight ("mxfp4": MXFP4 weights, MXFP8
+    activations) format."""
     if fmt == "block":
         return (quantize_activations, lambda q, s: dequantize_blocks(q, s, rows=1, cols=BLOCK),
                 dequantize_blocks)
     if fmt == "mxfp8":
         return quantize_mx, dequantize_mx, dequantize_mx
+    if fmt == "mxfp4":              # MXFP4 weights, MXFP8 activations
+        return quantize_mx, dequantize_mx, dequantize_mxfp4
     raise ValueError(f"unknown format {fmt}")
 
 

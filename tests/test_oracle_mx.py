@@ -185,3 +185,132 @@ def test_dense_e1_k1_layer_equals_scalar_mx_ffn():
     hh = (C[:, :I] / (1 + np.exp(-C[:, :I])) * C[:, I:]).astype(np.float32)
     ref = deq_rows(hh) @ W2.T + bf16_bits_to_f32(b2[0])
     assert np.allclose(got["out"], ref, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# MXFP4 expert weights ("GPT-OSS on day 0": the checkpoints ship with MXFP4 expert weights):
+# e2m1 elements (sign, 2 exponent bits with bias 1, 1 mantissa bit) in OCP MX blocks of 32
+# along K with E8M0 scales, two codes per byte (element 2j in the low nibble).
+# ---------------------------------------------------------------------------------------
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_table():
+    want = E2M1 + [-v for v in E2M1]
+    got = R.e2m1_decode(np.arange(16))
+    assert np.array_equal(got, np.array(want))
+    assert np.signbit(got[8])                      # code 8 is negative zero
+
+
+def _brute_e2m1(v: float) -> int:
+    a = min(abs(v), 6.0)
+    d = [abs(a - t) for t in E2M1]
+    best = [i for i, x in enumerate(d) if x == min(d)]
+    c = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+    return c | (8 if math.copysign(1.0, v) < 0 else 0)
+
+
+def test_e2m1_encoder_matches_brute_force():
+    v = np.concatenate([np.linspace(-7.5, 7.5, 6001), np.array(E2M1) + 0.0,
+                        [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.0, 1e9, -1e9]])
+    assert [int(c) for c in R.e2m1_encode(v)] == [_brute_e2m1(float(x)) for x in v]
+
+
+def test_e2m1_ties_to_even_and_clamp():
+    v = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 100.0, -0.25, -5.0])
+    assert list(R.e2m1_encode(v)) == [0, 2, 2, 4, 4, 6, 6, 7, 7, 8, 14]
+
+
+def scalar_mxfp4_block(vals32):
+    amax = max(abs(float(v)) for v in vals32)
+    X = 0 if amax == 0 else min(127, max(-127, floor_log2(amax) - 2))
+    codes = [_brute_e2m1(float(v) * math.ldexp(1.0, -X)) for v in vals32]
+    deq = [R.e2m1_decode(np.array([c]))[0] * math.ldexp(1.0, X) for c in codes]
+    return codes, X + 127, deq
+
+
+@pytest.mark.parametrize("shape", [(3, 32), (4, 128), (2, 192)])
+def test_mxfp4_matches_scalar_quantiser_and_packing(shape):
+    rng = np.random.default_rng(8)
+    a = _wide_rows(rng, shape[0], shape[1])
+    a[0, :32] = 0.0
+    packed, s = R.quantize_mxfp4(a)
+    assert packed.shape == (shape[0], shape[1] // 2)
+    codes = R.unpack_e2m1(packed)
+    for i in range(shape[0]):
+        for j in range(shape[1] // 32):
+            c, sc, deq = scalar_mxfp4_block(a[i, 32 * j:32 * j + 32])
+            assert s[i, j] == sc
+            assert list(codes[i, 32 * j:32 * j + 32]) == c
+            assert np.array_equal(R.dequantize_mxfp4(packed[i:i + 1, 16 * j:16 * j + 16], s[i:i + 1, j:j + 1])[0],
+                                  np.array(deq))
+    # packing: element 2j in the low nibble of byte j
+    assert np.array_equal(packed & 15, codes[:, 0::2]) and np.array_equal(packed >> 4, codes[:, 1::2])
+
+
+def test_mxfp4_scale_rule_and_bounds():
+    rng = np.random.default_rng(9)
+    a = _wide_rows(rng, 48, 256)
+    packed, s = R.quantize_mxfp4(a)
+    blocks = a.reshape(48, 8, 32)
+    X = s.astype(np.int64) - 127
+    for i in range(48):
+        for j in range(8):
+            amax = float(np.abs(blocks[i, j]).max())
+            assert X[i, j] == min(127, max(-127, floor_log2(amax) - 2))
+    u = a.astype(np.float64) * np.ldexp(1.0, -np.repeat(X, 32, axis=1))   # in [-8, 8)
+    d = R.e2m1_decode(R.unpack_e2m1(packed))
+    clamped = np.abs(u) > 6
+    assert np.all(np.abs(d[clamped]) == 6.0)
+    # spacing of e2m1 at the decoded value: 0.5 below 2, 1 in [2, 4), 2 in [4, 6]
+    sp = np.where(np.abs(d) < 2, 0.5, np.where(np.abs(d) < 4, 1.0, 2.0))
+    ok = ~clamped
+    assert np.all(np.abs(u[ok] - d[ok]) <= 0.5 * sp[ok])
+    mx = np.abs(d).reshape(48, 8, 32).max(axis=-1)
+    assert np.all((mx == 4.0) | (mx == 6.0))       # the block maximum lands in [4, 8)
+
+
+def test_mxfp4_round_trip_and_power_of_two():
+    rng = np.random.default_rng(10)
+    codes = rng.integers(0, 16, size=(8, 64)).astype(np.uint8)
+    codes[:, 5] = 7                                   # each block holds a 6
+    codes[:, 37] = 15
+    X = rng.integers(-60, 60, size=(8, 2))
+    vals = R.e2m1_decode(codes) * np.ldexp(1.0, X).repeat(32, axis=1)
+    packed, s = R.quantize_mxfp4(vals.astype(np.float32))
+    assert np.array_equal(s.astype(int), X + 127)
+    assert np.array_equal(R.e2m1_decode(R.unpack_e2m1(packed)), R.e2m1_decode(codes))
+    a = (rng.standard_normal((4, 96)) * 0.02).astype(np.float32)
+    p0, s0 = R.quantize_mxfp4(a)
+    p1, s1 = R.quantize_mxfp4((a * np.float32(2.0 ** 9)).astype(np.float32))
+    assert np.array_equal(p0, p1) and np.array_equal(s1.astype(int), s0.astype(int) + 9)
+
+
+def test_dense_e1_k1_layer_mxfp4_weights_equals_scalar_ffn():
+    T, H, I = 4, 64, 64
+    rng = np.random.default_rng(11)
+    x_bits = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    W = (rng.standard_normal((1, H)) * 0.05).astype(np.float32)
+    b = np.zeros(1, np.float32)
+    w13 = (rng.standard_normal((1, 2 * I, H)) * 0.02).astype(np.float32)
+    w2 = (rng.standard_normal((1, H, I)) * 0.02).astype(np.float32)
+    b13 = f32_to_bf16_bits((rng.standard_normal((1, 2 * I)) * 0.01).astype(np.float32))
+    b2 = f32_to_bf16_bits((rng.standard_normal((1, H)) * 0.01).astype(np.float32))
+    c13, s13 = R.quantize_mxfp4(w13)
+    c2, s2 = R.quantize_mxfp4(w2)
+    got = R.forward(x_bits, W, b, 1, I, c13, s13, b13, c2, s2, b2, fmt="mxfp4")
+
+    def deq8(m):
+        return np.array([sum((scalar_mx_block(r[c:c + 32])[2] for c in range(0, len(r), 32)), [])
+                         for r in m])
+
+    def deq4(m):
+        return np.array([sum((scalar_mxfp4_block(r[c:c + 32])[2] for c in range(0, len(r), 32)), [])
+                         for r in m])
+
+    xd = deq8(bf16_bits_to_f32(x_bits))
+    C = xd @ deq4(w13[0]).T + bf16_bits_to_f32(b13[0])
+    hh = (C[:, :I] / (1 + np.exp(-C[:, :I])) * C[:, I:]).astype(np.float32)
+    ref = deq8(hh) @ deq4(w2[0]).T + bf16_bits_to_f32(b2[0])
+    assert np.allclose(got["out"], ref, rtol=1e-10, atol=1e-12)
