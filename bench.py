@@ -45,17 +45,19 @@ def algorithmic(shape, counts, fmt="block"):
     Weights are counted once per *active* expert (an expert with no routed token is
     never read).  Intermediates (x codes, h, y) count where a kernel must read or write
     them at least once.  Scales: fp32 per 128x128 weight block and per 1x128 activation
-    group, or (MXFP8) one E8M0 byte per 32 elements along K."""
+    group, or (MXFP8, MXFP4) one E8M0 byte per 32 elements along K.  MXFP4 weight
+    elements are half a byte."""
     T, H, E, k, I = shape.T, shape.H, shape.E, shape.top_k, shape.I
     rows = T * k
     active = int((counts > 0).sum())
-    if fmt == "mxfp8":
+    wb = 0.5 if fmt == "mxfp4" else 1
+    if fmt in ("mxfp8", "mxfp4"):
         sw13, sw2, sx, sh = 2 * I * H // 32, H * I // 32, T * H // 32, rows * I // 32
     else:
         sw13, sw2 = kb(2 * I) * kb(H) * 4, kb(H) * kb(I) * 4
         sx, sh = T * kb(H) * 4, rows * kb(I) * 4
-    w13 = active * (2 * I * H + sw13 + (2 * I * 2 if shape.expert_bias else 0))
-    w2 = active * (H * I + sw2 + (H * 2 if shape.expert_bias else 0))
+    w13 = active * int(2 * I * H * wb + sw13 + (2 * I * 2 if shape.expert_bias else 0))
+    w2 = active * int(H * I * wb + sw2 + (H * 2 if shape.expert_bias else 0))
     layer_bytes = T * H * 2 + E * H * 4 + E * 4 + w13 + w2 + T * H * 2
     xq = T * H + sx
     hq = rows * I + sh
@@ -142,10 +144,16 @@ def cpu_baseline(shape, li, n_tokens, fmt="block"):
         ids, _ = R.topk_softmax(R.router_logits(li.x, li.router_w, li.router_b), shape.top_k)
         need = np.unique(ids[toks])
         c13, s13, c2, s2 = {}, {}, {}, {}
-        quant = R.quantize_mx if fmt == "mxfp8" else R.quantize_blocks
+        quant = {"block": R.quantize_blocks, "mxfp8": R.quantize_mx,
+                 "mxfp4": R.quantize_mxfp4}[fmt]
+
+        def by_rows(w):   # 128-row slices (whole scale blocks): the same codes, cache-sized
+            parts = [quant(w[i:i + 128]) for i in range(0, w.shape[0], 128)]
+            return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
         for e in need:   # offline weight conversion: not timed
-            c13[e], s13[e] = quant(expert_weights(shape, "w13", int(e), dev).cpu().numpy())
-            c2[e], s2[e] = quant(expert_weights(shape, "w2", int(e), dev).cpu().numpy())
+            c13[e], s13[e] = by_rows(expert_weights(shape, "w13", int(e), dev).cpu().numpy())
+            c2[e], s2[e] = by_rows(expert_weights(shape, "w2", int(e), dev).cpu().numpy())
         t0 = time.perf_counter()
         R.forward(li.x, li.router_w, li.router_b, shape.top_k, shape.I, c13, s13, li.b13, c2, s2,
                   li.b2, token_subset=toks, fmt=fmt)
@@ -185,7 +193,7 @@ def one_token_per_expert(args):
 
     dev = torch.device("cuda:0")
     results = []
-    for fmt in ("block", "mxfp8"):
+    for fmt in ("block", "mxfp8", "mxfp4"):
         for ep in (1, 2, 4, 8, 16, 32, 64):
             n = 128 // ep
             shape = LayerShape(f"qwen3-235b-one-token-per-expert-ep{ep}", T=n, H=4096, E=n,
@@ -225,7 +233,8 @@ def one_token_per_expert(args):
                 b_.record()
             torch.cuda.synchronize()
             layer_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in steps]))
-            wbytes = n * 3 * shape.H * shape.I * (1 + (1 / 32 if fmt == "mxfp8" else 1 / 4096))
+            wbytes = n * 3 * shape.H * shape.I * {"block": 1 + 1 / 4096, "mxfp8": 1 + 1 / 32,
+                                                   "mxfp4": 0.5 + 1 / 32}[fmt]
             gemm_us = (st["gemm1"] + st["gemm2"]) * 1e3
             r = {"ep": ep, "experts": n, "format": fmt, "gemm1_us": round(st["gemm1"] * 1e3, 2),
                  "gemm2_us": round(st["gemm2"] * 1e3, 2), "gemm_us": round(gemm_us, 2),
@@ -250,8 +259,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt-oss-120b-prefill")
     ap.add_argument("--cpu-sample-tokens", type=int, default=96)
-    ap.add_argument("--format", choices=["block", "mxfp8"], default="block",
-                    help="expert weight format: 128x128 block scales (default) or MXFP8")
+    ap.add_argument("--format", choices=["block", "mxfp8", "mxfp4"], default="block",
+                    help="expert weight format: 128x128 block scales (default), MXFP8, or MXFP4 "
+                         "weights with MXFP8 activations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--microbench", choices=["one-token-per-expert"],
                     help="instead of the layer benchmark: the decode GEMM sweep over "
@@ -411,7 +421,7 @@ def main():
         roof = {"bound": "hbm", "achieved": k_alg["bytes"] / k_s / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    prof_name = shape.name if args.format == "block" else f"{shape.name}-mxfp8"
+    prof_name = shape.name if args.format == "block" else f"{shape.name}-{args.format}"
     rec = pmc_record(prof_name, dom)
     roof["traffic"] = rec.get("hbm_bytes_per_launch") if rec else None
     if rec and "mfma_busy_frac" in rec:
@@ -426,12 +436,13 @@ def main():
         "metric": METRIC, "value": round(shape.T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8-e4m3" if args.format == "block" else "mxfp8-e4m3",
+        "dtype": {"block": "fp8-e4m3", "mxfp8": "mxfp8-e4m3",
+                  "mxfp4": "mxfp4-e2m1 x mxfp8-e4m3"}[args.format],
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "E": shape.E,
                    "top_k": shape.top_k, "I": shape.I, "parallelism": "single-gpu",
-                   "weights": "fp8 128x128 block scales" if args.format == "block"
-                   else "mxfp8 1x32 E8M0 scales"},
+                   "weights": {"block": "fp8 128x128 block scales", "mxfp8": "mxfp8 1x32 E8M0 scales",
+                               "mxfp4": "mxfp4 (e2m1) 1x32 E8M0 scales"}[args.format]},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_FP8_TFLOPS, 4),
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "active_experts": alg["active_experts"],

@@ -209,6 +209,45 @@ moe_status moe_forward_mx_profiled(const uint16_t* x, const float* router_w,
                                    const moe_routing* routing_out, void* workspace,
                                    size_t workspace_bytes, void* stream, void* const* events);
 
+/* ---- MXFP4 expert weights ("GPT-OSS on day 0": the checkpoints ship with MXFP4 expert
+ * weights).  OCP Microscaling with e2m1 elements (sign, 2 exponent bits with bias 1, 1
+ * mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): every 32 consecutive elements
+ * along K share an E8M0 code c, c - 127 = floor(log2(amax)) - 2 clamped to [-127, 127] (0
+ * for an all-zero block); an element is the nearest e2m1 value (ties to the even code)
+ * of v * 2^-(c - 127), clamped to +-6.  Codes are packed two per byte, element 2j in the
+ * low nibble of byte j.  Activations (x, h) stay MXFP8 (1x32 blocks, e4m3). */
+
+/* MXFP4 quantisation of E stacked fp32 matrices.
+ *   w      [E, N, K] float      source weights
+ *   codes  [E, N, K/2] uint8    packed e2m1 codes (output)
+ *   scales [E, N, 4 ceil(K/128)] uint8   E8M0 codes, padded rows (pads 127) (output)
+ * Requires E, N >= 1 and K a positive multiple of 32. */
+moe_status moe_quantize_weights_mxfp4(const float* w, int E, int N, int K, uint8_t* codes,
+                                      uint8_t* scales, void* stream);
+
+/* The whole layer forward with MXFP4 expert weights: moe_forward_mx's arguments, with
+ *   w13 [E, 2I, H/2] and w2 [E, H, I/2] packed e2m1 codes (moe_quantize_weights_mxfp4),
+ *   w13_scales [E, 2I, 4 ceil(H/128)], w2_scales [E, H, 4 ceil(I/128)] uint8.
+ * x and h are quantised in 1x32 MXFP8 blocks.  Requires H, I <= 8192; the workspace is the
+ * same (moe_workspace_bytes).  The GEMMs stream the weights in 16-row tiles: built for
+ * decode-sized layers (at prefill sizes every 16-row tile re-reads its expert's weights). */
+moe_status moe_forward_mxfp4(const uint16_t* x, const float* router_w, const float* router_b,
+                             const uint8_t* w13, const uint8_t* w13_scales, const uint16_t* b13,
+                             const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2,
+                             int T, int H, int E, int top_k, int I, uint16_t* out,
+                             const moe_routing* routing_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* moe_forward_mxfp4 with the per-stage events of moe_forward_profiled. */
+moe_status moe_forward_mxfp4_profiled(const uint16_t* x, const float* router_w,
+                                      const float* router_b, const uint8_t* w13,
+                                      const uint8_t* w13_scales, const uint16_t* b13,
+                                      const uint8_t* w2, const uint8_t* w2_scales,
+                                      const uint16_t* b2, int T, int H, int E, int top_k, int I,
+                                      uint16_t* out, const moe_routing* routing_out,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED_SHAPE
 EXPORTS = ["moe_status_str", "moe_workspace_bytes", "moe_workspace_layout",
            "moe_quantize_weights", "moe_quantize_activations", "moe_route", "moe_forward",
            "moe_forward_profiled", "moe_quantize_weights_mx", "moe_quantize_activations_mx",
-           "moe_forward_mx", "moe_forward_mx_profiled"]
+           "moe_forward_mx", "moe_forward_mx_profiled", "moe_quantize_weights_mxfp4",
+           "moe_forward_mxfp4", "moe_forward_mxfp4_profiled"]
 
 PROFILE_STAGES = ["router_gemm", "topk_softmax", "dispatch_scan", "dispatch_scatter",
                   "act_quant", "gemm1", "gemm2", "combine"]
@@ -82,6 +83,12 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_mx.restype = i
         L.moe_forward_mx_profiled.argtypes = L.moe_forward_profiled.argtypes
         L.moe_forward_mx_profiled.restype = i
+        L.moe_quantize_weights_mxfp4.argtypes = [vp, i, i, i, vp, vp, vp]
+        L.moe_quantize_weights_mxfp4.restype = i
+        L.moe_forward_mxfp4.argtypes = L.moe_forward.argtypes
+        L.moe_forward_mxfp4.restype = i
+        L.moe_forward_mxfp4_profiled.argtypes = L.moe_forward_profiled.argtypes
+        L.moe_forward_mxfp4_profiled.restype = i
         _lib = L
     return _lib
 
@@ -191,6 +198,26 @@ def quantize_weights_mx(w: torch.Tensor, codes: torch.Tensor = None, scales: tor
     return codes, scales
 
 
+def quantize_weights_mxfp4(w: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
+    """MXFP4 quantisation of w [E, N, K] (or [N, K]) fp32 -> (packed e2m1 codes uint8
+    [E, N, K/2], E8M0 scale codes uint8 [E, N, 4 ceil(K/128)], pads 127)."""
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    E, N, K = w3.shape
+    if codes is None:
+        codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((E, N, mx_row(K)), dtype=torch.uint8, device=w.device)
+    st = lib().moe_quantize_weights_mxfp4(_dev(w3, torch.float32, "w"), E, N, K,
+                                          _dev(codes.view(E, N, K // 2), torch.uint8, "codes"),
+                                          _dev(scales.view(E, N, mx_row(K)), torch.uint8, "scales"),
+                                          _stream(w.device))
+    _check(st, "moe_quantize_weights_mxfp4")
+    if squeeze:
+        return codes.view(N, K // 2), scales.view(N, mx_row(K))
+    return codes, scales
+
+
 def quantize_activations_mx(x: torch.Tensor):
     """Per-token 1x32 MXFP8 quantisation of x [T, H] bf16 -> (codes uint8 [T, H], E8M0 scale
     codes uint8 [T, 4 ceil(H/128)])."""
@@ -241,13 +268,15 @@ def _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2
                   routing, workspace):
     T, H = x.shape
     E = router_w.shape[0]
-    I = w2.shape[2]
+    # MXFP4 weights are packed two codes per byte: w13 [E, 2I, H/2], w2 [E, H, I/2]
+    fp4 = w13_scales.dtype == torch.uint8 and w13.shape[2] * 2 == H
+    I = w2.shape[2] * (2 if fp4 else 1)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
         workspace = new_workspace(T, H, E, top_k, I, x.device)
     rs = _routing_struct(routing, T, E, top_k) if routing is not None else None
-    mx = w13_scales.dtype == torch.uint8          # MXFP8 E8M0 codes, else fp32 block scales
+    mx = w13_scales.dtype == torch.uint8          # MX E8M0 codes, else fp32 block scales
     if mx:
         s13 = _dev(w13_scales, torch.uint8, "w13_scales", (E, 2 * I, mx_row(H)))
         s2 = _dev(w2_scales, torch.uint8, "w2_scales", (E, H, mx_row(I)))
@@ -257,26 +286,25 @@ def _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2
     args = [
         _dev(x, torch.bfloat16, "x"), _dev(router_w, torch.float32, "router_w", (E, H)),
         _dev(router_b, torch.float32, "router_b", (E,)),
-        _fp8(w13, "w13", (E, 2 * I, H)), s13,
+        _fp8(w13, "w13", (E, 2 * I, H // 2 if fp4 else H)), s13,
         _dev(b13, torch.bfloat16, "b13", (E, 2 * I)),
-        _fp8(w2, "w2", (E, H, I)), s2,
+        _fp8(w2, "w2", (E, H, I // 2 if fp4 else I)), s2,
         _dev(b2, torch.bfloat16, "b2", (E, H)),
         T, H, E, top_k, I, _dev(out, torch.bfloat16, "out", (T, H)),
         ctypes.byref(rs) if rs is not None else None,
         _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(x.device)]
-    return out, args, (rs, workspace), mx
+    return out, args, (rs, workspace), ("mxfp4" if fp4 else "mxfp8") if mx else "block"
 
 
 def forward(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, top_k: int,
             out=None, routing: dict = None, workspace=None) -> torch.Tensor:
-    """The layer forward: out [T, H] bf16.  uint8 weight scales (E8M0 codes from
-    ``quantize_weights_mx``) select the MXFP8 layer, fp32 ones the block-scaled layer."""
-    out, args, _keep, mx = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2,
-                                         w2_scales, b2, top_k, out, routing, workspace)
-    if mx:
-        _check(lib().moe_forward_mx(*args), "moe_forward_mx")
-    else:
-        _check(lib().moe_forward(*args), "moe_forward")
+    """The layer forward: out [T, H] bf16.  uint8 weight scales (E8M0 codes) select the
+    MXFP8 layer (``quantize_weights_mx``) or, with packed weights (w13 [E, 2I, H/2]), the
+    MXFP4-weight layer (``quantize_weights_mxfp4``); fp32 scales the block-scaled layer."""
+    out, args, _keep, fmt = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2,
+                                          w2_scales, b2, top_k, out, routing, workspace)
+    fn = {"block": "moe_forward", "mxfp8": "moe_forward_mx", "mxfp4": "moe_forward_mxfp4"}[fmt]
+    _check(getattr(lib(), fn)(*args), fn)
     return out
 
 
@@ -287,14 +315,13 @@ def forward_profiled(events, x, router_w, router_b, w13, w13_scales, b13, w2, w2
     entry leaves that boundary unrecorded."""
     if len(events) != len(PROFILE_STAGES) + 1:
         raise ValueError("need one event per stage plus one")
-    out, args, _keep, mx = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2,
-                                         w2_scales, b2, top_k, out, routing, workspace)
+    out, args, _keep, fmt = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2,
+                                          w2_scales, b2, top_k, out, routing, workspace)
     for ev in events:          # materialise the underlying hipEvent_t
         if ev is not None and ev.cuda_event == 0:
             ev.record()
     arr = (ctypes.c_void_p * len(events))(*[0 if ev is None else ev.cuda_event for ev in events])
-    if mx:
-        _check(lib().moe_forward_mx_profiled(*args, arr), "moe_forward_mx_profiled")
-    else:
-        _check(lib().moe_forward_profiled(*args, arr), "moe_forward_profiled")
+    fn = {"block": "moe_forward_profiled", "mxfp8": "moe_forward_mx_profiled",
+          "mxfp4": "moe_forward_mxfp4_profiled"}[fmt]
+    _check(getattr(lib(), fn)(*args, arr), fn)
     return out

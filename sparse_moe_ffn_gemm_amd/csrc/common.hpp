@@ -172,4 +172,25 @@ __device__ __forceinline__ int quantize_mx8(const uint16_t* row, int col, bool i
   return code;
 }
 
+// ---- MXFP4 weights: e2m1 elements (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6) in MX blocks ----
+
+// E8M0 code of an MXFP4 block: floor(log2(amax)) - 2 (the block maximum lands in [4, 8)),
+// clamped below at -127, 0 for an all-zero block.
+__device__ __forceinline__ int mx4_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 127;
+  const int ex = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu) - 127;
+  return max(ex - 2, -127) + 127;
+}
+
+// e2m1 code of u (an exactly scaled value): the nearest magnitude, ties to the even code,
+// clamped to 6, counted against the midpoints (a tie sits on its midpoint and goes down
+// when the lower code is even: 0.25, 1.25, 2.5, 5; up when it is odd: 0.75, 1.75, 3.5);
+// the sign bit kept.
+__device__ __forceinline__ uint32_t e2m1_code(float u) {
+  const float m = fabsf(u);
+  const uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
+                     (m >= 3.5f) + (m > 5.0f);
+  return c | ((__float_as_uint(u) >> 28) & 8u);
+}
+
 }  // namespace moe

@@ -1016,8 +1016,13 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
 // (L2 hits) and are scaled by zero.  Rows past the tile's end are staged from its first
 // row; their outputs are never stored.
 // ------------------------------------------------------------------------------------
-template <bool SWIGLU, int KS, bool MX = false>
+// FP4 (with MX): the weights are MXFP4, K/2 bytes per row; the matrix cores take an e2m1
+// first operand, whose lane (r, g) holds the 32 consecutive K values [32 g, 32 g + 32) of
+// row r in 16 bytes (element 2j in the low nibble), against the e4m3 activation fragment.
+template <bool SWIGLU, int KS, bool MX = false, bool FP4 = false>
 __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs a, int ntiles) {
+  static_assert(MX || !FP4, "MXFP4 weights take E8M0 scales");
+  constexpr int WROW = FP4 ? 2 : 1;          // K elements per weight byte
   constexpr int WAVES = 8;
   constexpr int NSUB = SWIGLU ? 2 : 1;       // weight sub-tiles per wave (gate, up)
   extern __shared__ __align__(16) uint8_t dyn_lds[];
@@ -1043,7 +1048,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
   const bool live = c0 < (SWIGLU ? I : N);   // I, N multiples of 64: all 16 or none
 
   // ---- the wave's weight stream: sub-tile s, K-block j, in bursts of KS blocks ----
-  const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * K;
+  const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * (K / WROW);
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
   const int bps = ceil_div(KB, KS);          // bursts per sub-tile
   const int nb = NSUB * bps;                 // bursts of the wave
@@ -1054,7 +1059,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     const int row = (SWIGLU && s == 1 ? I : 0) + c0 + r;
-    b_off[s] = static_cast<unsigned>(row) * K + 16 * g;
+    b_off[s] = FP4 ? static_cast<unsigned>(row) * (K / 2) + 16 * g : static_cast<unsigned>(row) * K + 16 * g;
     if constexpr (MX) {
       bmx[s] = a.B_mx + (static_cast<size_t>(e) * N + (live ? row : 0)) * (4 * KB);
       sbg[s] = 0.f;
@@ -1081,11 +1086,19 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       const int jj = j0 + t < KB ? j0 + t : KB - 1;
-      const unsigned hoff = (jj + 1) * kBlock <= K ? 64u : 0u;   // half block: re-read chunks 0-3
-      const uint8_t* base = Bexp + jj * kBlock;
-      const uint4 lo = *reinterpret_cast<const uint4*>(base + bo);
-      const uint4 hi = *reinterpret_cast<const uint4*>(base + hoff + bo);
-      bq[t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (FP4) {
+        // 64 bytes per row and K-step; in a half-filled last block lanes g = 2, 3 (K past
+        // the row) re-read lanes 0, 1's bytes: their products meet zero activations
+        const unsigned back = ((jj + 1) * kBlock > K && g >= 2) ? 32u : 0u;
+        const uint4 lo = *reinterpret_cast<const uint4*>(Bexp + jj * 64 + bo - back);
+        bq[t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+      } else {
+        const unsigned hoff = (jj + 1) * kBlock <= K ? 64u : 0u;   // half block: re-read chunks 0-3
+        const uint8_t* base = Bexp + jj * kBlock;
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + bo);
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + hoff + bo);
+        bq[t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
     }
   };
   v4f acc[NSUB];
@@ -1110,7 +1123,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
           const v8i af = lds_frag(sA + jj * 2048, r, g);
           const int xa = reinterpret_cast<const uint8_t*>(sSa)[4 * (jj * 16 + r) + g];
           const int xb = static_cast<int>((xq[t] >> (8 * g)) & 0xFFu);
-          ac = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[t], af, ac, 0, 0, 0, xb, 0, xa);
+          ac = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[t], af, ac, FP4 ? 4 : 0, 0, 0, xb,
+                                                                0, xa);
         }
       }
       return;
@@ -1303,6 +1317,20 @@ static bool launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
   const int ntiles = SWIGLU ? ceil_div(a.I, 128) : ceil_div(a.N, bn);
   const long total = static_cast<long>(max_tiles) * ntiles;
   const int grid = static_cast<int>((total + 7) / 8 * 8);
+  // MXFP4 weights: the row-run kernel at every group size (16-row tiles)
+  if (a.fp4) {
+    const int KB4 = ceil_div(a.K, kBlock);
+    if (bm != 16 || KB4 > 64) return false;
+    const int nts = ceil_div(SWIGLU ? a.I : a.N, 128);
+    const int g = static_cast<int>((static_cast<long>(max_tiles) * nts + 7) / 8 * 8);
+    const size_t lds = static_cast<size_t>(KB4) * 2048 + ceil_div(KB4, 4) * 256 + 8 * 16 * 4;
+    static const bool lds_ok4 =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
+    if (lds > 64 * 1024 && !lds_ok4) return false;
+    grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true><<<g, 512, lds, st>>>(a, nts);
+    return true;
+  }
   // MXFP8 layers take the large-group kernel unless their tiles are decode-sized rows of
   // the row-run kernel below (the plan picks 256-row tiles otherwise)
   if (bm == 256 || (a.mx && bm != 16)) {

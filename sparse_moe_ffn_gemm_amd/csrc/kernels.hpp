@@ -24,6 +24,9 @@ void launch_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t* co
                                 uint8_t* scales, hipStream_t st);
 void launch_quantize_act_mx(const uint16_t* x, int T, int H, uint8_t* codes, uint8_t* scales,
                             hipStream_t st);
+// MXFP4 weights: codes [E, N, K/2] (two e2m1 codes per byte, element 2j low), scales as MX
+void launch_quantize_weights_mxfp4(const float* w, int E, int N, int K, uint8_t* codes,
+                                   uint8_t* scales, hipStream_t st);
 
 // ---- routing ----
 constexpr int kRouterTile = 64;     // tokens / experts per router GEMM workgroup
@@ -88,6 +91,7 @@ struct GemmArgs {
   // MXFP8 instead of the block scales (A_scale, B_scale, h_scale unused): E8M0 codes in
   // rows of 4 ceil(K/128) bytes -- A_mx [*, ...], B_mx [E, N, ...], h_mx [rows, 4 ceil(I/128)]
   bool mx;
+  bool fp4;                  // with mx: B holds MXFP4 (e2m1) codes [E, N, K/2]
   const uint8_t* A_mx;
   const uint8_t* B_mx;
   uint8_t* h_mx;

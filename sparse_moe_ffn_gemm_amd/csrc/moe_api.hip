@@ -42,9 +42,13 @@ bool uses_route_tail(int T, int E, int k, int ksplit) {
          k <= moe::kTailTopK && ksplit <= moe::kTailSplit;
 }
 
-// `mx`: MXFP8 layers take 256-row M-tiles (the large-group kernel) except for decode-sized
-// groups that the row-run kernel streams in both GEMMs.
-void make_plan(int T, int H, int E, int k, int I, Plan* p, bool mx = false) {
+// Weight formats of the forward: 128x128 block scales, MXFP8, MXFP4 (MXFP8 activations).
+enum WeightFormat { kBlockFp8 = 0, kMxfp8 = 1, kMxfp4 = 2 };
+
+// MXFP8 layers take 256-row M-tiles (the large-group kernel) except for decode-sized groups
+// that the row-run kernel streams in both GEMMs; MXFP4 layers take 16-row tiles (the
+// row-run kernel) at every size.
+void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) {
   p->T = T; p->H = H; p->E = E; p->k = k; p->I = I;
   p->rows = static_cast<long>(T) * k;
   // split H across workgroups when there are few token x expert tiles (decode)
@@ -62,8 +66,10 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, bool mx = false) {
   // MXFP8: decode-sized groups whose weight rows are not whole 128-byte lines in both GEMMs
   // (H and I = 64 mod 128, the row-run kernel) keep 16-row tiles, all others 256
   const bool mx_rowrun = bm_block == 16 && H % 128 != 0 && I % 128 != 0 && H <= 8192 && I <= 8192;
-  p->bm = mx ? (mx_rowrun ? 16 : 256) : bm_block;
-  p->max_tiles = static_cast<int>(p->rows / bm_block + std::min<long>(E, p->rows));
+  p->bm = fmt == kMxfp4 ? 16 : fmt == kMxfp8 ? (mx_rowrun ? 16 : 256) : bm_block;
+  p->max_tiles = static_cast<int>(p->rows / p->bm + std::min<long>(E, p->rows));
+  // the tile list is sized for 16-row tiles, the most of any format, so that every format
+  // shares one workspace layout
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -75,7 +81,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, bool mx = false) {
   p->presplit = ceil_div(T, moe::kRouterTile) >= 8;
   p->wparts = take(p->presplit ? sizeof(uint16_t) * 3 * static_cast<size_t>(E) * H : 0);
   p->chunk_base = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
-  p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->max_tiles));
+  p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->rows / 16 + std::min<long>(E, p->rows)));
   p->num_tiles = take(sizeof(int32_t) * (1 + 2 * moe::kGemmQueues));   // + the GEMMs' queues
   p->expert_tile_off = take(sizeof(int32_t) * (E + 1));
   p->ids = take(sizeof(int32_t) * p->rows);
@@ -166,14 +172,15 @@ bool routing_ok(const moe_routing* r) {
 
 }  // namespace
 
-// The layer; `mx` selects MXFP8 (w13_scales / w2_scales are E8M0 code rows, uint8) over
-// the 128x128 block scales (fp32).
+// The layer; `fmt` selects MXFP8 or MXFP4 weights (w13_scales / w2_scales are E8M0 code
+// rows, uint8; MXFP4 codes are packed two per byte) over the 128x128 block scales (fp32).
 static moe_status forward_impl(const uint16_t* x, const float* router_w, const float* router_b,
                        const uint8_t* w13, const void* w13_scales, const uint16_t* b13,
                        const uint8_t* w2, const void* w2_scales, const uint16_t* b2, int T,
                        int H, int E, int top_k, int I, uint16_t* out,
                        const moe_routing* routing_out, void* workspace, size_t workspace_bytes,
-                       void* stream, hipEvent_t* ev, bool mx = false) {
+                       void* stream, hipEvent_t* ev, int fmt = kBlockFp8) {
+  const bool mx = fmt != kBlockFp8;
   if (!x || !router_w || !w13 || !w13_scales || !w2 || !w2_scales || !out || !workspace)
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(router_w) || !aligned16(w13) || !aligned16(w2) ||
@@ -183,7 +190,8 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   if (routing_out && !routing_ok(routing_out)) return MOE_ERR_INVALID_ARG;
   if (!shape_ok(T, H, E, top_k, I)) return MOE_ERR_UNSUPPORTED_SHAPE;
   Plan p;
-  make_plan(T, H, E, top_k, I, &p, mx);
+  make_plan(T, H, E, top_k, I, &p, fmt);
+  if (fmt == kMxfp4 && (H > 8192 || I > 8192)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -206,6 +214,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g1.top_k = top_k;
   g1.B = w13;
   g1.mx = mx;
+  g1.fp4 = fmt == kMxfp4;
   if (mx) {
     g1.A_mx = at<uint8_t>(ws, p.sx);
     g1.B_mx = static_cast<const uint8_t*>(w13_scales);
@@ -235,6 +244,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.top_k = top_k;
   g2.B = w2;
   g2.mx = mx;
+  g2.fp4 = fmt == kMxfp4;
   if (mx) {
     g2.A_mx = at<uint8_t>(ws, p.sh);
     g2.B_mx = static_cast<const uint8_t*>(w2_scales);
@@ -326,6 +336,18 @@ moe_status moe_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t*
   return finish();
 }
 
+moe_status moe_quantize_weights_mxfp4(const float* w, int E, int N, int K, uint8_t* codes,
+                                      uint8_t* scales, void* stream) {
+  if (!w || !codes || !scales || !aligned16(w) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARG;
+  if (K % 32 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (static_cast<long>(E) * N * 4 * ceil_div(K, 128) / 64 >= (1L << 31))
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  (void)hipGetLastError();
+  moe::launch_quantize_weights_mxfp4(w, E, N, K, codes, scales, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
 moe_status moe_quantize_activations_mx(const uint16_t* x, int T, int H, uint8_t* codes,
                                        uint8_t* scales, void* stream) {
   if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
@@ -383,7 +405,7 @@ moe_status moe_forward_mx(const uint16_t* x, const float* router_w, const float*
                           void* stream) {
   return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
                       top_k, I, out, routing_out, workspace, workspace_bytes, stream, nullptr,
-                      /*mx=*/true);
+                      kMxfp8);
 }
 
 moe_status moe_forward_mx_profiled(const uint16_t* x, const float* router_w,
@@ -396,7 +418,32 @@ moe_status moe_forward_mx_profiled(const uint16_t* x, const float* router_w,
   if (!events) return MOE_ERR_INVALID_ARG;
   return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
                       top_k, I, out, routing_out, workspace, workspace_bytes, stream,
-                      reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), /*mx=*/true);
+                      reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), kMxfp8);
+}
+
+moe_status moe_forward_mxfp4(const uint16_t* x, const float* router_w, const float* router_b,
+                             const uint8_t* w13, const uint8_t* w13_scales, const uint16_t* b13,
+                             const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2,
+                             int T, int H, int E, int top_k, int I, uint16_t* out,
+                             const moe_routing* routing_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
+                      top_k, I, out, routing_out, workspace, workspace_bytes, stream, nullptr,
+                      kMxfp4);
+}
+
+moe_status moe_forward_mxfp4_profiled(const uint16_t* x, const float* router_w,
+                                      const float* router_b, const uint8_t* w13,
+                                      const uint8_t* w13_scales, const uint16_t* b13,
+                                      const uint8_t* w2, const uint8_t* w2_scales,
+                                      const uint16_t* b2, int T, int H, int E, int top_k, int I,
+                                      uint16_t* out, const moe_routing* routing_out,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* events) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
+                      top_k, I, out, routing_out, workspace, workspace_bytes, stream,
+                      reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), kMxfp4);
 }
 
 }  // extern "C"

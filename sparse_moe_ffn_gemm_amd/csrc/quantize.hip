@@ -126,6 +126,50 @@ __global__ __launch_bounds__(256) void quantize_act_mx_kernel(const uint16_t* __
   if (live && sub == 0) scales[slot] = static_cast<uint8_t>(code);
 }
 
+// MXFP4 weights: the same block slots; a lane's 8 elements pack into 4 bytes (element
+// 2j in the low nibble of byte j of the row's K/2).
+__global__ __launch_bounds__(256) void quantize_weights_mxfp4_kernel(const float* __restrict__ w,
+                                                                     long rows, int K,
+                                                                     uint8_t* __restrict__ codes,
+                                                                     uint8_t* __restrict__ scales) {
+  const int RS = 4 * ceil_div(K, kBlock);
+  const long slot = static_cast<long>(blockIdx.x) * 64 + (threadIdx.x >> 2);
+  const int sub = threadIdx.x & 3;
+  const bool live = slot < rows * RS;
+  const long row = live ? slot / RS : 0;
+  const int blk = live ? static_cast<int>(slot % RS) : 0;
+  const int col = blk * kMxBlock + sub * 8;
+  const bool in = live && col < K;
+  float f[8];
+  float amax = 0.0f;
+  if (in) {
+    const float4 a0 = *reinterpret_cast<const float4*>(w + row * K + col);
+    const float4 a1 = *reinterpret_cast<const float4*>(w + row * K + col + 4);
+    f[0] = a0.x; f[1] = a0.y; f[2] = a0.z; f[3] = a0.w;
+    f[4] = a1.x; f[5] = a1.y; f[6] = a1.z; f[7] = a1.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+  amax = group_max<4>(amax);
+  const int code = mx4_scale_code(amax);
+  if (in) {
+    const float m = mx_inv_scale(code);
+    uint32_t q = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q |= e2m1_code(f[i] * m) << (4 * i);
+    *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + col / 2) = q;
+  }
+  if (live && sub == 0) scales[slot] = static_cast<uint8_t>(code);
+}
+
+void launch_quantize_weights_mxfp4(const float* w, int E, int N, int K, uint8_t* codes,
+                                   uint8_t* scales, hipStream_t st) {
+  const long rows = static_cast<long>(E) * N;
+  const long slots = rows * 4 * ceil_div(K, kBlock);
+  quantize_weights_mxfp4_kernel<<<dim3(static_cast<unsigned>((slots + 63) / 64)), dim3(256), 0,
+                                  st>>>(w, rows, K, codes, scales);
+}
+
 void launch_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t* codes,
                                 uint8_t* scales, hipStream_t st) {
   const long rows = static_cast<long>(E) * N;

@@ -2,8 +2,9 @@
 
 Weights are converted statically ("Hosting Qwen on Blackwell", section "Quantization")
 by the library's quantisation kernels, to e4m3 codes with 128x128 block scales or, with
-``fmt="mxfp8"``, to MXFP8 (1x32 blocks, E8M0 scales); ``forward`` runs the whole layer
-through ``moe_forward`` / ``moe_forward_mx``.
+``fmt="mxfp8"``, to MXFP8 (1x32 blocks, E8M0 scales), with ``fmt="mxfp4"`` to MXFP4 (e2m1
+codes packed two per byte, 1x32 blocks); ``forward`` runs the whole layer through
+``moe_forward`` / ``moe_forward_mx`` / ``moe_forward_mxfp4``.
 """
 from __future__ import annotations
 
@@ -22,7 +23,8 @@ class MoELayer:
         self.w13, self.w13_scales, self.b13 = w13, w13_scales, b13
         self.w2, self.w2_scales, self.b2 = w2, w2_scales, b2
         self.E, self.H = router_w.shape
-        self.I = w2.shape[2]
+        packed = w13_scales.dtype == torch.uint8 and w13.shape[2] * 2 == self.H
+        self.I = w2.shape[2] * (2 if packed else 1)
         self._ws = {}
 
     @classmethod
@@ -32,14 +34,18 @@ class MoELayer:
                             fmt: str = "block") -> "MoELayer":
         """Quantise expert by expert: ``w13_of(e)`` -> [2I, H] fp32, ``w2_of(e)`` -> [H, I] fp32
         (on any device; moved to ``device`` one expert at a time).  ``fmt``: "block"
-        (128x128 block scales) or "mxfp8"."""
+        (128x128 block scales), "mxfp8" or "mxfp4" (MXFP4 weights, MXFP8 activations)."""
         E, H = router_w.shape
         first = w2_of(0)
         I = first.shape[1]
         kb = _lib.kb
-        w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
-        w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
-        if fmt == "mxfp8":
+        w13 = torch.empty((E, 2 * I, H // 2 if fmt == "mxfp4" else H), dtype=torch.uint8, device=device)
+        w2 = torch.empty((E, H, I // 2 if fmt == "mxfp4" else I), dtype=torch.uint8, device=device)
+        if fmt == "mxfp4":
+            s13 = torch.empty((E, 2 * I, _lib.mx_row(H)), dtype=torch.uint8, device=device)
+            s2 = torch.empty((E, H, _lib.mx_row(I)), dtype=torch.uint8, device=device)
+            quant = _lib.quantize_weights_mxfp4
+        elif fmt == "mxfp8":
             s13 = torch.empty((E, 2 * I, _lib.mx_row(H)), dtype=torch.uint8, device=device)
             s2 = torch.empty((E, H, _lib.mx_row(I)), dtype=torch.uint8, device=device)
             quant = _lib.quantize_weights_mx

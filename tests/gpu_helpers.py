@@ -38,7 +38,7 @@ def bits_host(t: torch.Tensor) -> np.ndarray:
 
 class GpuLayer:
     """Device tensors of one layer; expert weights quantised by the library (``fmt``
-    "block": 128x128 block scales, "mxfp8": MXFP8)."""
+    "block": 128x128 block scales, "mxfp8": MXFP8, "mxfp4": MXFP4 weights)."""
 
     def __init__(self, shape: LayerShape, inputs=None, device="cuda", fmt="block"):
         self.shape = shape
@@ -55,9 +55,17 @@ class GpuLayer:
         torch.cuda.synchronize()
 
 
+def quantize_by_rows(quant, w: np.ndarray, rows: int = 128):
+    """The oracle's weight quantiser applied to 128-row slices of w (every format's scale
+    blocks lie within one slice, so the result is the whole-matrix one; the slices keep the
+    oracle's per-element temporaries in cache)."""
+    parts = [quant(w[i:i + rows]) for i in range(0, w.shape[0], rows)]
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
 class OracleExperts:
     """Lazily quantised experts for the oracle (from the generator's fp32 weights), in the
-    block-scaled or the MXFP8 format."""
+    block-scaled, the MXFP8 or the MXFP4-weight format."""
 
     def __init__(self, shape: LayerShape, li, fmt="block"):
         self.shape, self.li = shape, li
@@ -71,11 +79,12 @@ class OracleExperts:
         host = {e: (expert_weights(self.shape, "w13", e, self.dev).cpu().numpy(),
                     expert_weights(self.shape, "w2", e, self.dev).cpu().numpy()) for e in todo}
 
-        quant = R.quantize_mx if self.fmt == "mxfp8" else R.quantize_blocks
+        quant = {"block": R.quantize_blocks, "mxfp8": R.quantize_mx,
+                 "mxfp4": R.quantize_mxfp4}[self.fmt]
 
         def q(e):
-            c13, s13 = quant(host[e][0])
-            c2, s2 = quant(host[e][1])
+            c13, s13 = quantize_by_rows(quant, host[e][0])
+            c2, s2 = quantize_by_rows(quant, host[e][1])
             return e, (c13, s13, c2, s2)
 
         with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -102,14 +111,16 @@ class OracleExperts:
         return ref
 
     def dequant_w(self, codes, scales):
-        return R.dequantize_mx(codes, scales) if self.fmt == "mxfp8" else R.dequantize_blocks(codes, scales)
+        deq = {"block": R.dequantize_blocks, "mxfp8": R.dequantize_mx,
+               "mxfp4": R.dequantize_mxfp4}[self.fmt]
+        return deq(codes, scales)
 
     def flip_allowance(self, ref):
         """Per output element of the evaluated tokens: sum_j g_j * |W2_j| . flip_delta(h_j)."""
         li, k, I = self.li, self.shape.top_k, self.shape.I
         toks = ref["tokens"]
         x32 = R.bf16_to_f64(li.x[toks]).astype(np.float32)
-        if self.fmt == "mxfp8":
+        if self.fmt != "block":                 # MXFP8 activations
             xd = R.dequantize_mx(*R.quantize_mx(x32))
         else:
             xq, sx = R.quantize_activations(x32)
@@ -121,7 +132,7 @@ class OracleExperts:
             _, hq, hs, h64 = R.expert_ffn(xd[rt], c13, s13, li.b13[e], c2, s2, li.b2[e], I,
                                           self.fmt)
             W2 = np.abs(self.dequant_w(c2, s2))
-            delta = flip_delta_mx(h64, hq, hs) if self.fmt == "mxfp8" else flip_delta(h64, hq, hs)
+            delta = flip_delta(h64, hq, hs) if self.fmt == "block" else flip_delta_mx(h64, hq, hs)
             allow[rt] += ref["gates"][toks[rt], rj][:, None] * (delta @ W2.T)
         return allow
 

@@ -137,7 +137,7 @@ def test_forward_mx_small_full_parity(shape):
     compare_out(bits_host(out), ref["out"], shape.name, allowance=ref["allowance"])
 
 
-def _check_h_dispatched(g, ox, ref, hq, hs):
+def _check_h_dispatched(g, ox, ref, hq, hs, fmt=FMT):
     """The oracle's h per routed row in dispatch order (expert segments of perm)."""
     shape, li = g.shape, g.li
     x32 = R.bf16_to_f64(li.x).astype(np.float32)
@@ -150,7 +150,7 @@ def _check_h_dispatched(g, ox, ref, hq, hs):
             continue
         c13, s13, c2, s2 = ox.cache[e]
         _, rq, rs, h64 = R.expert_ffn(xd[tok[p0:p1]], c13, s13, li.b13[e], c2, s2, li.b2[e],
-                                      shape.I, FMT)
+                                      shape.I, fmt)
         d, m = _check_h(hq[p0:p1], hs[p0:p1], h64, rq, rs, f"expert {e}")
         ndiff, n = ndiff + d, n + m
     say(f"  h codes differing over the layer: {ndiff} of {n}")
