@@ -214,23 +214,29 @@ moe_status moe_forward_mx_profiled(const uint16_t* x, const float* router_w,
  * mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6): every 32 consecutive elements
  * along K share an E8M0 code c, c - 127 = floor(log2(amax)) - 2 clamped to [-127, 127] (0
  * for an all-zero block); an element is the nearest e2m1 value (ties to the even code)
- * of v * 2^-(c - 127), clamped to +-6.  Codes are packed two per byte, element 2j in the
- * low nibble of byte j.  Activations (x, h) stay MXFP8 (1x32 blocks, e4m3). */
+ * of v * 2^-(c - 127), clamped to +-6.  Activations (x, h) stay MXFP8 (1x32 blocks, e4m3).
+ *
+ * Storage: 16-row x 128-K tiles, in the order the GEMMs stream them.  With KB =
+ * ceil(K/128), a matrix [N, K] (N a multiple of 16) is N/16 x KB tiles, tile (n, j) at
+ * index n * KB + j:
+ *   codes:  1024 bytes per tile; row r of the tile (matrix row 16 n + r) at byte 64 r holds
+ *           K [128 j, 128 j + 128), two codes per byte (element 2i in the low nibble of
+ *           byte i); codes past K are 0.  N * KB * 64 bytes per matrix.
+ *   scales: 64 bytes per tile; row r's four E8M0 codes of the tile's K-block at byte 4 r
+ *           (codes of blocks past K are 127).  N * 4 KB bytes per matrix. */
 
-/* MXFP4 quantisation of E stacked fp32 matrices.
- *   w      [E, N, K] float      source weights
- *   codes  [E, N, K/2] uint8    packed e2m1 codes (output)
- *   scales [E, N, 4 ceil(K/128)] uint8   E8M0 codes, padded rows (pads 127) (output)
- * Requires E, N >= 1 and K a positive multiple of 32. */
+/* MXFP4 quantisation of E stacked fp32 matrices [E, N, K] into the tiled storage above
+ * (codes [E][N/16][KB][16][64], scales [E][N/16][KB][16][4], uint8, device memory).
+ * Requires E >= 1, N a positive multiple of 16 and K a positive multiple of 32. */
 moe_status moe_quantize_weights_mxfp4(const float* w, int E, int N, int K, uint8_t* codes,
                                       uint8_t* scales, void* stream);
 
-/* The whole layer forward with MXFP4 expert weights: moe_forward_mx's arguments, with
- *   w13 [E, 2I, H/2] and w2 [E, H, I/2] packed e2m1 codes (moe_quantize_weights_mxfp4),
- *   w13_scales [E, 2I, 4 ceil(H/128)], w2_scales [E, H, 4 ceil(I/128)] uint8.
- * x and h are quantised in 1x32 MXFP8 blocks.  Requires H, I <= 8192; the workspace is the
- * same (moe_workspace_bytes).  The GEMMs stream the weights in 16-row tiles: built for
- * decode-sized layers (at prefill sizes every 16-row tile re-reads its expert's weights). */
+/* The whole layer forward with MXFP4 expert weights: moe_forward_mx's arguments, with w13
+ * ([E] matrices [2I, H]), w2 ([E] matrices [H, I]) and their scales in the tiled storage
+ * of moe_quantize_weights_mxfp4.  x and h are quantised in 1x32 MXFP8 blocks.  Requires
+ * H, I <= 8192; the workspace is the same (moe_workspace_bytes).  The GEMMs stream the
+ * weights in 16-row tiles: built for decode-sized layers (at prefill sizes every 16-row
+ * tile of tokens re-reads its expert's weights). */
 moe_status moe_forward_mxfp4(const uint16_t* x, const float* router_w, const float* router_b,
                              const uint8_t* w13, const uint8_t* w13_scales, const uint16_t* b13,
                              const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2,

@@ -198,23 +198,32 @@ def quantize_weights_mx(w: torch.Tensor, codes: torch.Tensor = None, scales: tor
     return codes, scales
 
 
+def mxfp4_shapes(N: int, K: int):
+    """Shapes of one matrix's MXFP4 storage: 16-row x 128-K tiles (tile (n, j) holds rows
+    16n..16n+15 over K [128j, 128j+128)): codes [N/16, ceil(K/128), 16, 64] (64 bytes per
+    tile row, two codes a byte, zeros past K) and E8M0 codes [N/16, ceil(K/128), 16, 4]."""
+    return (N // 16, kb(K), 16, 64), (N // 16, kb(K), 16, 4)
+
+
 def quantize_weights_mxfp4(w: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
-    """MXFP4 quantisation of w [E, N, K] (or [N, K]) fp32 -> (packed e2m1 codes uint8
-    [E, N, K/2], E8M0 scale codes uint8 [E, N, 4 ceil(K/128)], pads 127)."""
+    """MXFP4 quantisation of w [E, N, K] (or [N, K]) fp32 (N a multiple of 16, K of 32) ->
+    (e2m1 codes uint8 [E, *mxfp4_shapes(N, K)[0]], E8M0 codes uint8 [E, *mxfp4_shapes[1]])
+    in the tiled layout of ``mxfp4_shapes`` (scale pads 127)."""
     squeeze = w.dim() == 2
     w3 = w.unsqueeze(0) if squeeze else w
     E, N, K = w3.shape
+    cs, ss = mxfp4_shapes(N, K)
     if codes is None:
-        codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+        codes = torch.empty((E,) + cs, dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty((E, N, mx_row(K)), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((E,) + ss, dtype=torch.uint8, device=w.device)
     st = lib().moe_quantize_weights_mxfp4(_dev(w3, torch.float32, "w"), E, N, K,
-                                          _dev(codes.view(E, N, K // 2), torch.uint8, "codes"),
-                                          _dev(scales.view(E, N, mx_row(K)), torch.uint8, "scales"),
+                                          _dev(codes.view((E,) + cs), torch.uint8, "codes"),
+                                          _dev(scales.view((E,) + ss), torch.uint8, "scales"),
                                           _stream(w.device))
     _check(st, "moe_quantize_weights_mxfp4")
     if squeeze:
-        return codes.view(N, K // 2), scales.view(N, mx_row(K))
+        return codes.view(cs), scales.view(ss)
     return codes, scales
 
 
@@ -268,16 +277,19 @@ def _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2
                   routing, workspace):
     T, H = x.shape
     E = router_w.shape[0]
-    # MXFP4 weights are packed two codes per byte: w13 [E, 2I, H/2], w2 [E, H, I/2]
-    fp4 = w13_scales.dtype == torch.uint8 and w13.shape[2] * 2 == H
-    I = w2.shape[2] * (2 if fp4 else 1)
+    # MXFP4 weights are 16-row tiles: w13 [E, 2I/16, ceil(H/128), 16, 64]
+    fp4 = w13.dim() == 5
+    I = w13.shape[1] * 8 if fp4 else w2.shape[2]
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if workspace is None:
         workspace = new_workspace(T, H, E, top_k, I, x.device)
     rs = _routing_struct(routing, T, E, top_k) if routing is not None else None
     mx = w13_scales.dtype == torch.uint8          # MX E8M0 codes, else fp32 block scales
-    if mx:
+    if fp4:
+        s13 = _dev(w13_scales, torch.uint8, "w13_scales", (E,) + mxfp4_shapes(2 * I, H)[1])
+        s2 = _dev(w2_scales, torch.uint8, "w2_scales", (E,) + mxfp4_shapes(H, I)[1])
+    elif mx:
         s13 = _dev(w13_scales, torch.uint8, "w13_scales", (E, 2 * I, mx_row(H)))
         s2 = _dev(w2_scales, torch.uint8, "w2_scales", (E, H, mx_row(I)))
     else:
@@ -286,9 +298,9 @@ def _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2
     args = [
         _dev(x, torch.bfloat16, "x"), _dev(router_w, torch.float32, "router_w", (E, H)),
         _dev(router_b, torch.float32, "router_b", (E,)),
-        _fp8(w13, "w13", (E, 2 * I, H // 2 if fp4 else H)), s13,
+        _fp8(w13, "w13", (E,) + mxfp4_shapes(2 * I, H)[0] if fp4 else (E, 2 * I, H)), s13,
         _dev(b13, torch.bfloat16, "b13", (E, 2 * I)),
-        _fp8(w2, "w2", (E, H, I // 2 if fp4 else I)), s2,
+        _fp8(w2, "w2", (E,) + mxfp4_shapes(H, I)[0] if fp4 else (E, H, I)), s2,
         _dev(b2, torch.bfloat16, "b2", (E, H)),
         T, H, E, top_k, I, _dev(out, torch.bfloat16, "out", (T, H)),
         ctypes.byref(rs) if rs is not None else None,
@@ -299,8 +311,8 @@ def _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2
 def forward(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, top_k: int,
             out=None, routing: dict = None, workspace=None) -> torch.Tensor:
     """The layer forward: out [T, H] bf16.  uint8 weight scales (E8M0 codes) select the
-    MXFP8 layer (``quantize_weights_mx``) or, with packed weights (w13 [E, 2I, H/2]), the
-    MXFP4-weight layer (``quantize_weights_mxfp4``); fp32 scales the block-scaled layer."""
+    MXFP8 layer (``quantize_weights_mx``) or, with tiled MXFP4 weights (5-d, from
+    ``quantize_weights_mxfp4``), the MXFP4-weight layer; fp32 scales the block-scaled layer."""
     out, args, _keep, fmt = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2,
                                           w2_scales, b2, top_k, out, routing, workspace)
     fn = {"block": "moe_forward", "mxfp8": "moe_forward_mx", "mxfp4": "moe_forward_mxfp4"}[fmt]

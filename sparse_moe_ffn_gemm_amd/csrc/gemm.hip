@@ -1016,13 +1016,16 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
 // (L2 hits) and are scaled by zero.  Rows past the tile's end are staged from its first
 // row; their outputs are never stored.
 // ------------------------------------------------------------------------------------
-// FP4 (with MX): the weights are MXFP4, K/2 bytes per row; the matrix cores take an e2m1
-// first operand, whose lane (r, g) holds the 32 consecutive K values [32 g, 32 g + 32) of
-// row r in 16 bytes (element 2j in the low nibble), against the e4m3 activation fragment.
+// FP4 (with MX): the weights are MXFP4, stored in 16-row x 128-K tiles (1024 code bytes,
+// row r at byte 64 r, K past the row zero; 64 scale bytes, row r's four E8M0 codes at byte
+// 4 r), so a wave's sub-tile is one contiguous run of KB tiles and each burst reads KS
+// whole kilobytes; scattered per-row pieces and per-row scale words streamed about 30 %
+// slower.  The matrix cores take an e2m1 first operand, whose lane (r, g) holds the 32
+// consecutive K values [32 g, 32 g + 32) of row r in 16 bytes (element 2j in the low
+// nibble), against the e4m3 activation fragment.
 template <bool SWIGLU, int KS, bool MX = false, bool FP4 = false>
 __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs a, int ntiles) {
   static_assert(MX || !FP4, "MXFP4 weights take E8M0 scales");
-  constexpr int WROW = FP4 ? 2 : 1;          // K elements per weight byte
   constexpr int WAVES = 8;
   constexpr int NSUB = SWIGLU ? 2 : 1;       // weight sub-tiles per wave (gate, up)
   extern __shared__ __align__(16) uint8_t dyn_lds[];
@@ -1048,7 +1051,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
   const bool live = c0 < (SWIGLU ? I : N);   // I, N multiples of 64: all 16 or none
 
   // ---- the wave's weight stream: sub-tile s, K-block j, in bursts of KS blocks ----
-  const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * (K / WROW);
+  const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * (FP4 ? KB * 64 : K);
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
   const int bps = ceil_div(KB, KS);          // bursts per sub-tile
   const int nb = NSUB * bps;                 // bursts of the wave
@@ -1059,9 +1062,12 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     const int row = (SWIGLU && s == 1 ? I : 0) + c0 + r;
-    b_off[s] = FP4 ? static_cast<unsigned>(row) * (K / 2) + 16 * g : static_cast<unsigned>(row) * K + 16 * g;
+    b_off[s] = FP4 ? static_cast<unsigned>(row - r) * KB * 64 + 64 * r + 16 * g
+                   : static_cast<unsigned>(row) * K + 16 * g;
     if constexpr (MX) {
-      bmx[s] = a.B_mx + (static_cast<size_t>(e) * N + (live ? row : 0)) * (4 * KB);
+      // MXFP8: the row's code row; MXFP4: the tile row's 4 codes, 64 bytes per K-block
+      bmx[s] = FP4 ? a.B_mx + (static_cast<size_t>(e) * N + (live ? row - r : 0)) * (4 * KB) + 4 * r
+                   : a.B_mx + (static_cast<size_t>(e) * N + (live ? row : 0)) * (4 * KB);
       sbg[s] = 0.f;
     } else {
       const int brow = ((SWIGLU && s == 1 ? I : 0) + c0) / kBlock;
@@ -1080,17 +1086,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
         const int jj = j0 + t < KB ? j0 + t : KB - 1;
-        xq[t] = *reinterpret_cast<const uint32_t*>(xr + 4 * jj);
+        xq[t] = *reinterpret_cast<const uint32_t*>(xr + (FP4 ? 64 : 4) * jj);
       }
     }
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       const int jj = j0 + t < KB ? j0 + t : KB - 1;
       if constexpr (FP4) {
-        // 64 bytes per row and K-step; in a half-filled last block lanes g = 2, 3 (K past
-        // the row) re-read lanes 0, 1's bytes: their products meet zero activations
-        const unsigned back = ((jj + 1) * kBlock > K && g >= 2) ? 32u : 0u;
-        const uint4 lo = *reinterpret_cast<const uint4*>(Bexp + jj * 64 + bo - back);
+        // one 1024-byte tile per K-step (a half-filled last block holds zero codes past K)
+        const uint4 lo = *reinterpret_cast<const uint4*>(Bexp + jj * 1024 + bo);
         bq[t] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
       } else {
         const unsigned hoff = (jj + 1) * kBlock <= K ? 64u : 0u;   // half block: re-read chunks 0-3

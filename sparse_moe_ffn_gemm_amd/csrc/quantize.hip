@@ -126,13 +126,17 @@ __global__ __launch_bounds__(256) void quantize_act_mx_kernel(const uint16_t* __
   if (live && sub == 0) scales[slot] = static_cast<uint8_t>(code);
 }
 
-// MXFP4 weights: the same block slots; a lane's 8 elements pack into 4 bytes (element
-// 2j in the low nibble of byte j of the row's K/2).
+// MXFP4 weights: the same block slots, stored in 16-row x 128-K tiles (the order in which
+// the GEMMs stream them): tile (n16, j) of a matrix is 1024 code bytes, row r of the tile
+// at byte 64 r holding K [128 j, 128 j + 128) two codes per byte (element 2i in the low
+// nibble of byte i), K past the row zero; and 64 scale bytes, row r's four E8M0 codes of
+// the K-block at byte 4 r (pads 127).  Rows are counted over all E matrices (N is a
+// multiple of 16, so no tile straddles two experts).
 __global__ __launch_bounds__(256) void quantize_weights_mxfp4_kernel(const float* __restrict__ w,
                                                                      long rows, int K,
                                                                      uint8_t* __restrict__ codes,
                                                                      uint8_t* __restrict__ scales) {
-  const int RS = 4 * ceil_div(K, kBlock);
+  const int KB = ceil_div(K, kBlock), RS = 4 * KB;
   const long slot = static_cast<long>(blockIdx.x) * 64 + (threadIdx.x >> 2);
   const int sub = threadIdx.x & 3;
   const bool live = slot < rows * RS;
@@ -152,14 +156,18 @@ __global__ __launch_bounds__(256) void quantize_weights_mxfp4_kernel(const float
   }
   amax = group_max<4>(amax);
   const int code = mx4_scale_code(amax);
-  if (in) {
-    const float m = mx_inv_scale(code);
+  const long tile = (row >> 4) * KB + (blk >> 2);   // the row's 16-row tile, its K-block
+  const int rr = static_cast<int>(row & 15);
+  if (live) {
     uint32_t q = 0;
+    if (in) {
+      const float m = mx_inv_scale(code);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q |= e2m1_code(f[i] * m) << (4 * i);
-    *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + col / 2) = q;
+      for (int i = 0; i < 8; ++i) q |= e2m1_code(f[i] * m) << (4 * i);
+    }
+    *reinterpret_cast<uint32_t*>(codes + tile * 1024 + rr * 64 + (blk & 3) * 16 + sub * 4) = q;
+    if (sub == 0) scales[tile * 64 + rr * 4 + (blk & 3)] = static_cast<uint8_t>(code);
   }
-  if (live && sub == 0) scales[slot] = static_cast<uint8_t>(code);
 }
 
 void launch_quantize_weights_mxfp4(const float* w, int E, int N, int K, uint8_t* codes,

@@ -23,8 +23,7 @@ class MoELayer:
         self.w13, self.w13_scales, self.b13 = w13, w13_scales, b13
         self.w2, self.w2_scales, self.b2 = w2, w2_scales, b2
         self.E, self.H = router_w.shape
-        packed = w13_scales.dtype == torch.uint8 and w13.shape[2] * 2 == self.H
-        self.I = w2.shape[2] * (2 if packed else 1)
+        self.I = w13.shape[1] * 8 if w13.dim() == 5 else w2.shape[2]   # MXFP4 tiles: 2I/16 rows
         self._ws = {}
 
     @classmethod
@@ -39,17 +38,22 @@ class MoELayer:
         first = w2_of(0)
         I = first.shape[1]
         kb = _lib.kb
-        w13 = torch.empty((E, 2 * I, H // 2 if fmt == "mxfp4" else H), dtype=torch.uint8, device=device)
-        w2 = torch.empty((E, H, I // 2 if fmt == "mxfp4" else I), dtype=torch.uint8, device=device)
         if fmt == "mxfp4":
-            s13 = torch.empty((E, 2 * I, _lib.mx_row(H)), dtype=torch.uint8, device=device)
-            s2 = torch.empty((E, H, _lib.mx_row(I)), dtype=torch.uint8, device=device)
+            (c13, t13), (c2, t2) = _lib.mxfp4_shapes(2 * I, H), _lib.mxfp4_shapes(H, I)
+            w13 = torch.empty((E,) + c13, dtype=torch.uint8, device=device)
+            w2 = torch.empty((E,) + c2, dtype=torch.uint8, device=device)
+            s13 = torch.empty((E,) + t13, dtype=torch.uint8, device=device)
+            s2 = torch.empty((E,) + t2, dtype=torch.uint8, device=device)
             quant = _lib.quantize_weights_mxfp4
         elif fmt == "mxfp8":
+            w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
+            w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
             s13 = torch.empty((E, 2 * I, _lib.mx_row(H)), dtype=torch.uint8, device=device)
             s2 = torch.empty((E, H, _lib.mx_row(I)), dtype=torch.uint8, device=device)
             quant = _lib.quantize_weights_mx
         elif fmt == "block":
+            w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
+            w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
             s13 = torch.empty((E, kb(2 * I), kb(H)), dtype=torch.float32, device=device)
             s2 = torch.empty((E, kb(H), kb(I)), dtype=torch.float32, device=device)
             quant = _lib.quantize_weights

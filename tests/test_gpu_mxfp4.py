@@ -2,7 +2,8 @@
 MXFP4; "Hosting Qwen on Blackwell", section "Quantization": activations quantised per
 token at run time, here MXFP8) against the oracle's "mxfp4" layer.
 
-Packed e2m1 weight codes and their E8M0 scales are bit-exact (scale-row pads 127); x codes
+Packed e2m1 weight codes and their E8M0 scales are bit-exact in the tiled storage (code
+bytes past K zero, scale pads 127); x codes
 and scales are bit-exact; the routing tables are exact; h codes may differ only inside the
 accumulation window; outputs meet the tolerance of the other formats.
 """
@@ -21,6 +22,15 @@ pytestmark = pytest.mark.gpu
 FMT = "mxfp4"
 
 
+def untile(codes: np.ndarray, scales: np.ndarray, N: int, K: int):
+    """Row-major packed codes [E, N, K/2] and E8M0 rows [E, N, 4 ceil(K/128)] of the tiled
+    storage (16-row x 128-K tiles), and the code bytes past K."""
+    E, KB = codes.shape[0], -(-K // 128)
+    c = codes.reshape(E, N // 16, KB, 16, 64).transpose(0, 1, 3, 2, 4).reshape(E, N, KB * 64)
+    s = scales.reshape(E, N // 16, KB, 16, 4).transpose(0, 1, 3, 2, 4).reshape(E, N, KB * 4)
+    return c[..., :K // 2], s, c[..., K // 2:]
+
+
 @pytest.mark.parametrize("E,N,K", [(2, 192, 2880), (3, 64, 256), (1, 96, 96), (2, 16, 32)])
 def test_weight_quantiser_bit_exact(E, N, K):
     rng = np.random.default_rng(E * 1000 + K + 4)
@@ -33,10 +43,12 @@ def test_weight_quantiser_bit_exact(E, N, K):
     codes, scales = moe.quantize_weights_mxfp4(torch.from_numpy(w).cuda())
     torch.cuda.synchronize()
     rc, rs = R.quantize_mxfp4(w)
-    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
-    assert codes.shape == (E, N, K // 2) and scales.shape == (E, N, moe.mx_row(K))
-    real, pad = _split(scales, K)
-    assert np.array_equal(codes, rc)
+    cs, ss = moe.mxfp4_shapes(N, K)
+    assert codes.shape == (E,) + cs and scales.shape == (E,) + ss
+    c, s, tail = untile(codes.cpu().numpy(), scales.cpu().numpy(), N, K)
+    real, pad = _split(s, K)
+    assert np.array_equal(c, rc)
+    assert np.all(tail == 0)
     assert np.array_equal(real, rs)
     assert np.all(pad == 127)
 
