@@ -233,10 +233,10 @@ moe_status moe_quantize_weights_mxfp4(const float* w, int E, int N, int K, uint8
 
 /* The whole layer forward with MXFP4 expert weights: moe_forward_mx's arguments, with w13
  * ([E] matrices [2I, H]), w2 ([E] matrices [H, I]) and their scales in the tiled storage
- * of moe_quantize_weights_mxfp4.  x and h are quantised in 1x32 MXFP8 blocks.  Requires
- * H, I <= 8192; the workspace is the same (moe_workspace_bytes).  The GEMMs stream the
- * weights in 16-row tiles: built for decode-sized layers (at prefill sizes every 16-row
- * tile of tokens re-reads its expert's weights). */
+ * of moe_quantize_weights_mxfp4.  x and h are quantised in 1x32 MXFP8 blocks.  The
+ * workspace is the same (moe_workspace_bytes).  Decode-sized layers (at most 24 routed rows
+ * per expert on average) stream the weights in 16-row tiles and require H, I <= 8192
+ * (MOE_ERR_UNSUPPORTED_SHAPE otherwise); larger ones take 256-row tiles. */
 moe_status moe_forward_mxfp4(const uint16_t* x, const float* router_w, const float* router_b,
                              const uint8_t* w13, const uint8_t* w13_scales, const uint16_t* b13,
                              const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2,

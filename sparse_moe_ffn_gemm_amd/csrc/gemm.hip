@@ -71,6 +71,17 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int g) {
   return r;
 }
 
+// MXFP4 weight tiles in LDS: 16 rows x 64 bytes (1 KB, one tile of the tiled storage per
+// K-step), 16-byte chunk c of row r in slot c ^ ((r >> 1) & 3), so the rows that one read
+// phase serves fall in distinct banks.  The e2m1 fragment of lane (row r, group g) is the
+// row's chunk g (K [32 g, 32 g + 32)), in the low four dwords of the operand.
+__device__ __forceinline__ int swz4_key(int row) { return (row >> 1) & 3; }
+
+__device__ __forceinline__ v8i lds_frag4(const uint8_t* base, int row, int g) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 64 + ((g ^ swz4_key(row)) << 4));
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+}
+
 // LDS address (32-bit) of a shared-memory pointer.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
@@ -514,23 +525,25 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
 // ------------------------------------------------------------------------------------
 // LDS bytes of one tile body: A and B rings, scale slots, row sources, row-amax exchange,
 // bias
-template <int BN, int WM, int SM, int SA, int SB>
+template <int BN, int WM, int SM, int SA, int SB, bool FP4 = false>
 constexpr int big_tile_lds() {
-  return SA * (16 * SM * WM) * 128 + SB * BN * 128 + SA * 8 * 64 * 4 + (16 * SM * WM) * 4 +
+  return SA * (16 * SM * WM) * 128 + SB * BN * (FP4 ? 64 : 128) + SA * 8 * 64 * 4 + (16 * SM * WM) * 4 +
          (8 / WM) * (16 * SM * WM) * 4 + BN * 2;
 }
 
 // One M-tile x n-tile: WM x (8 / WM) waves, each SM 16-row sub-tiles by BN / (8 / WM)
-// columns; SA / SB ring slots.
-template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX>
+// columns; SA / SB ring slots.  FP4 (with MX): MXFP4 weights in the tiled storage; a
+// B-ring slot is BN / 16 weight tiles of 1 KB, each fetched whole by one load.
+template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX, bool FP4 = false>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile mt, uint8_t* lds) {
   constexpr int WAVES = 8, NT = WAVES * 64, WN = WAVES / WM, BM = 16 * SM * WM;
   constexpr int WR = 16 * SM, WC = BN / WN;          // rows / columns of a wave
   constexpr int SN = WC / 16;                        // sub-tiles per wave along N
   constexpr int NG = SN / 2, GW = BN / (2 * WN);     // gemm1: gate sub-tiles / columns per wave
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * (FP4 ? 64 : 128);
   constexpr int A_ROWS = BM / WAVES, B_ROWS = BN / WAVES;   // rows each wave fetches per step
-  constexpr int A_INSTR = A_ROWS / 8, B_INSTR = B_ROWS / 8;
+  constexpr int A_INSTR = A_ROWS / 8, B_INSTR = FP4 ? B_ROWS / 16 : B_ROWS / 8;
+  static_assert(!FP4 || (MX && B_ROWS % 16 == 0), "MXFP4 weights: E8M0 scales, whole tiles per wave");
   static_assert(WC % 16 == 0 && BN % 64 == 0 && (!SWIGLU || SN % 2 == 0), "tile");
   static_assert(SA >= 2 && SB >= SA, "rings");
   static_assert(A_ROWS % 8 == 0 && A_ROWS <= 32 && WN * SN <= 32 && B_ROWS % 8 == 0, "scale lanes");
@@ -551,7 +564,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   const int KB = ceil_div(K, kBlock), NBs = ceil_div(N, kBlock);
   const int e = mt.expert;
   const bool wave_live = wm * WR < mt.row_end - mt.row_begin;
-  const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * K;
+  const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * (FP4 ? KB * 64 : K);
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
 
   for (int r = tid; r < BM; r += NT) {
@@ -586,12 +599,23 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   }
 #pragma unroll
   for (int i = 0; i < B_INSTR; ++i) {
-    const int row = wave * B_ROWS + i * 8 + a_r8;
-    const int g = b_global_row(row);
-    b_ok[i] = g >= 0;
-    // a row past the matrix re-reads the tile's first row (already in flight: no HBM
-    // traffic); it only feeds output columns that are never stored
-    b_off[i] = static_cast<unsigned>(g < 0 ? b_global_row(0) : g) * K + ((a_slot ^ swz_key(row)) << 4);
+    if constexpr (FP4) {
+      // load i of the wave fetches weight tile (wave B_ROWS / 16 + i) of the B tile: lane
+      // l lands at LDS byte 16 l of it, tile row l >> 2, slot l & 3, so it fetches that
+      // row's chunk (l & 3) ^ swz4_key(row) (tiles past the matrix re-read the first)
+      const int tr = lane >> 2, row = wave * B_ROWS + 16 * i + tr;
+      const int g = b_global_row(row - tr);
+      b_ok[i] = g >= 0;
+      b_off[i] = static_cast<unsigned>(g < 0 ? b_global_row(0) : g) * KB * 64 + tr * 64 +
+                 (((lane & 3) ^ swz4_key(tr)) << 4);
+    } else {
+      const int row = wave * B_ROWS + i * 8 + a_r8;
+      const int g = b_global_row(row);
+      b_ok[i] = g >= 0;
+      // a row past the matrix re-reads the tile's first row (already in flight: no HBM
+      // traffic); it only feeds output columns that are never stored
+      b_off[i] = static_cast<unsigned>(g < 0 ? b_global_row(0) : g) * K + ((a_slot ^ swz_key(row)) << 4);
+    }
   }
   const float* s_ptr = kZeroScale;
   bool s_live = false;
@@ -616,8 +640,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // MXFP8: every thread stages one 4-byte E8M0 row of K-step kt (the four 32-blocks of
   // its 128 columns): thread t < BM the A row t, BM <= t < BM + BN the B row t - BM; one
   // load per wave and step, like the block scales above
+  // (MXFP4: a B row's 4 codes of step kt sit in its tile's 64-byte scale block)
   const uint8_t* x_ptr = reinterpret_cast<const uint8_t*>(kZeroScale);
   bool x_live = false;
+  int x_step = 4;
   if constexpr (MX) {
     const int RS = 4 * KB;
     if (tid < BM) {
@@ -627,7 +653,13 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     } else if (tid < BM + BN) {
       const int g = b_global_row(tid - BM);
       x_live = g >= 0;
-      x_ptr = a.B_mx + (static_cast<size_t>(e) * N + (g < 0 ? 0 : g)) * RS;
+      const int gg = g < 0 ? 0 : g;
+      if constexpr (FP4) {
+        x_ptr = a.B_mx + (static_cast<size_t>(e) * N + (gg & ~15)) * RS + 4 * (gg & 15);
+        x_step = 64;
+      } else {
+        x_ptr = a.B_mx + (static_cast<size_t>(e) * N + gg) * RS;
+      }
     }
   }
 
@@ -647,7 +679,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       }
     }
     if constexpr (MX) {
-      const void* src = x_live ? static_cast<const void*>(x_ptr + 4 * kt) : kZeroScale;
+      const void* src = x_live ? static_cast<const void*>(x_ptr + x_step * kt) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
     } else if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN)) {   // lanes 0.. always: one instruction
       const void* src = s_live ? static_cast<const void*>(s_ptr + kt) : kZeroScale;
@@ -657,7 +689,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   auto issue_b = [&](int kt) {
     uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
     const int k0 = kt * kBlock;
-    if (k0 + kBlock <= K) {
+    if constexpr (FP4) {   // whole tiles (zero codes past K)
+#pragma unroll
+      for (int i = 0; i < B_INSTR; ++i) load_lds16_s(b_off[i], Bexp + kt * 1024, Bs + (wave * B_ROWS + 16 * i) * 64);
+    } else if (k0 + kBlock <= K) {
 #pragma unroll
       for (int i = 0; i < B_INSTR; ++i) load_lds16_s(b_off[i], Bexp + k0, Bs + (wave * B_ROWS + i * 8) * 128);
     } else {
@@ -718,6 +753,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // scale is one value per (m, n) and the epilogue stores are 4 or 16 bytes wide.
   v8i af[SM], bq[3];
   float sav[SM], sbv[SN];
+  auto bfrag = [&](const uint8_t* Bs, int row, int g) {
+    if constexpr (FP4) return lds_frag4(Bs, row, g);
+    else return lds_frag(Bs, row, g);
+  };
   int xa[SM], xb[SN];   // MXFP8: the lane's E8M0 codes (row lane & 15, 32-block lane >> 4)
   auto read_step = [&](int kt) {   // scales, A fragments and the first B fragment
     const int sl = kt % SA;
@@ -742,8 +781,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
         sav[m] = sS[sl][r / A_ROWS][r % A_ROWS];
       }
     }
-    bq[0] = lds_frag(ringB + (kt % SB) * B_BYTES, sub_brow(0) + (lane & 15), lane >> 4);
-    bq[1] = lds_frag(ringB + (kt % SB) * B_BYTES, sub_brow(1) + (lane & 15), lane >> 4);
+    bq[0] = bfrag(ringB + (kt % SB) * B_BYTES, sub_brow(0) + (lane & 15), lane >> 4);
+    bq[1] = bfrag(ringB + (kt % SB) * B_BYTES, sub_brow(1) + (lane & 15), lane >> 4);
   };
 
   // Software pipeline over the NP = SM x SN products of a step (column-major): product j
@@ -777,9 +816,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
         const int n = j / SM, m = j % SM;
-        if (m == 0 && n + 2 < SN) bq[(n + 2) % 3] = lds_frag(Bs, sub_brow(n + 2) + (lane & 15), lane >> 4);
-        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n % 3], af[m], acc[m][n], 0, 0,
-                                                                     0, xb[n], 0, xa[m]);
+        if (m == 0 && n + 2 < SN) bq[(n + 2) % 3] = bfrag(Bs, sub_brow(n + 2) + (lane & 15), lane >> 4);
+        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n % 3], af[m], acc[m][n], FP4 ? 4 : 0,
+                                                                     0, 0, xb[n], 0, xa[m]);
       }
     } else if (wave_live) {
       const uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
@@ -962,9 +1001,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
 // activation rows and weight tiles in their L2; a workgroup whose XCD's queue is empty
 // takes from the other XCDs' queues.  Every queue head only grows, so every workgroup
 // leaves after at most total + 8 of its fetches.
-template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN, bool MX = false>
+template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN, bool MX = false, bool FP4 = false>
 __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int ntiles) {
-  constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN>();
+  constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB, FP4>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN, FP4>();
   __shared__ __align__(16) uint8_t lds[kFull > kNarrow ? kFull : kNarrow];
   __shared__ int s_next;
   const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
@@ -984,9 +1023,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
       MTile mt;
       tile_of(a, ntiles, lo + t, nt, mt);
       if (mt.row_end - mt.row_begin <= 64) {
-        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX>(a, nt, mt, lds);
+        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4>(a, nt, mt, lds);
       } else {
-        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX>(a, nt, mt, lds);
+        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4>(a, nt, mt, lds);
       }
     }
   }
@@ -1287,6 +1326,8 @@ constexpr int kG1BN = 256, kG1SA = 2, kG1SB = 2;
 constexpr int kG2BN = 192, kG2SA = 2, kG2SB = 3;
 // Ring depth of narrow (at most 64-row) tiles in the large-group launch.
 constexpr int kNarrowS = 3;
+// MXFP4 weights (half the B bytes per step): both GEMMs 256 wide, B rings one deeper.
+constexpr int kF4BN = 256, kF4SA = 2, kF4SB = 3;
 // Dynamic LDS of the row-run kernel at its largest K (64 blocks).
 constexpr int kRowrunMaxLds = 64 * 2048 + 16 * 256 + 8 * 16 * 4;
 
@@ -1321,7 +1362,16 @@ static bool launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
   const int ntiles = SWIGLU ? ceil_div(a.I, 128) : ceil_div(a.N, bn);
   const long total = static_cast<long>(max_tiles) * ntiles;
   const int grid = static_cast<int>((total + 7) / 8 * 8);
-  // MXFP4 weights: the row-run kernel at every group size (16-row tiles)
+  // MXFP4 weights: decode-sized groups on the row-run kernel (16-row tiles), larger ones
+  // on the large-group kernel (256-row tiles)
+  if (a.fp4 && bm == 256) {
+    const int nt_big = SWIGLU ? ceil_div(a.I, kF4BN / 2) : ceil_div(a.N, kF4BN);
+    const long tot = static_cast<long>(max_tiles) * nt_big;
+    const long cus = device_cus();
+    const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
+    grouped_gemm_big_kernel<SWIGLU, kF4BN, kF4SA, kF4SB, kNarrowS, kNarrowS, true, true><<<g, 512, 0, st>>>(a, nt_big);
+    return true;
+  }
   if (a.fp4) {
     const int KB4 = ceil_div(a.K, kBlock);
     if (bm != 16 || KB4 > 64) return false;

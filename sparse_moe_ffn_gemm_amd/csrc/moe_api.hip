@@ -47,7 +47,7 @@ enum WeightFormat { kBlockFp8 = 0, kMxfp8 = 1, kMxfp4 = 2 };
 
 // MXFP8 layers take 256-row M-tiles (the large-group kernel) except for decode-sized groups
 // that the row-run kernel streams in both GEMMs; MXFP4 layers take 16-row tiles (the
-// row-run kernel) at every size.
+// row-run kernel) for decode-sized groups and 256-row tiles otherwise.
 void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) {
   p->T = T; p->H = H; p->E = E; p->k = k; p->I = I;
   p->rows = static_cast<long>(T) * k;
@@ -66,7 +66,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   // MXFP8: decode-sized groups whose weight rows are not whole 128-byte lines in both GEMMs
   // (H and I = 64 mod 128, the row-run kernel) keep 16-row tiles, all others 256
   const bool mx_rowrun = bm_block == 16 && H % 128 != 0 && I % 128 != 0 && H <= 8192 && I <= 8192;
-  p->bm = fmt == kMxfp4 ? 16 : fmt == kMxfp8 ? (mx_rowrun ? 16 : 256) : bm_block;
+  p->bm = fmt == kMxfp4 ? (bm_block == 16 ? 16 : 256) : fmt == kMxfp8 ? (mx_rowrun ? 16 : 256) : bm_block;
   p->max_tiles = static_cast<int>(p->rows / p->bm + std::min<long>(E, p->rows));
   // the tile list is sized for 16-row tiles, the most of any format, so that every format
   // shares one workspace layout
@@ -191,7 +191,8 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   if (!shape_ok(T, H, E, top_k, I)) return MOE_ERR_UNSUPPORTED_SHAPE;
   Plan p;
   make_plan(T, H, E, top_k, I, &p, fmt);
-  if (fmt == kMxfp4 && (H > 8192 || I > 8192)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // the row-run kernel stages a 16-row activation tile of all of K in LDS
+  if (fmt == kMxfp4 && p.bm == 16 && (H > 8192 || I > 8192)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);

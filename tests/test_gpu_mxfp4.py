@@ -58,7 +58,10 @@ SMALL = [
     custom_shape(T=37, H=192, E=5, top_k=2, I=192, seed=61),        # K tails (K = 64 mod 128)
     custom_shape(T=9, H=128, E=1, top_k=1, I=128, seed=62),         # dense FFN
     custom_shape(T=4, H=256, E=64, top_k=2, I=128, seed=63),        # most experts idle
-    custom_shape(T=150, H=320, E=4, top_k=4, I=384, seed=64),       # many 16-row tiles
+    custom_shape(T=150, H=320, E=4, top_k=4, I=384, seed=64),       # 256-row tile kernel
+    custom_shape(T=600, H=320, E=4, top_k=2, I=320, seed=65),       # full + narrow 256-row tiles
+    custom_shape(T=300, H=192, E=4, top_k=2, I=192, seed=67),       # 256-row tiles, K tails
+    custom_shape(T=40, H=256, E=2, top_k=1, I=128, seed=60),        # 20 rows per expert: 16-row tiles
     custom_shape(T=96, H=384, E=8, top_k=2, I=320, seed=66, expert_bias=False),
     custom_shape(T=16, H=256, E=16, top_k=1, I=128, seed=68, router="one_per_expert"),
 ]
@@ -98,8 +101,28 @@ def test_forward_mxfp4_decode_layer_all_tokens():
     compare_out(bits_host(out), ref["out"], shape.name, allowance=ref["allowance"])
 
 
+@pytest.mark.timeout(1200)
+def test_forward_mxfp4_prefill_layer_sampled():
+    """The prefill-sized layer (every expert ~256 rows: the 256-row tile kernel and its
+    narrow overflow tiles), checked on sampled tokens (the last one included)."""
+    shape = SHAPES["gpt-oss-120b-prefill"]
+    g = GpuLayer(shape, fmt=FMT)
+    routing = moe.new_routing(shape.T, shape.E, shape.top_k)
+    say(f"mxfp4 forward {shape.name}")
+    out = g.layer(g.x, routing=routing)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(97)
+    toks = np.sort(rng.choice(shape.T, size=6, replace=False))
+    toks[-1] = shape.T - 1
+    ref = OracleExperts(shape, g.li, fmt=FMT).forward(token_subset=toks)
+    routing_exact(routing, ref, shape.T, shape.top_k, shape.name)
+    compare_out(bits_host(out)[toks], ref["out"], f"{shape.name} tokens {toks.tolist()}",
+                allowance=ref["allowance"])
+
+
 def test_forward_mxfp4_rejects_wide_layers():
-    """The MXFP4 GEMMs stage a 16-row activation tile of all of K in LDS: H, I <= 8192."""
+    """The decode-sized MXFP4 GEMMs stage a 16-row activation tile of all of K in LDS:
+    H, I <= 8192 there."""
     shape = custom_shape(T=4, H=8192 + 256, E=2, top_k=1, I=128, seed=69)
     g = GpuLayer(shape, fmt=FMT)
     with pytest.raises(RuntimeError):
