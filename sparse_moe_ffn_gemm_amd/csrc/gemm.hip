@@ -1326,8 +1326,10 @@ constexpr int kG1BN = 256, kG1SA = 2, kG1SB = 2;
 constexpr int kG2BN = 192, kG2SA = 2, kG2SB = 3;
 // Ring depth of narrow (at most 64-row) tiles in the large-group launch.
 constexpr int kNarrowS = 3;
-// MXFP4 weights (half the B bytes per step): both GEMMs 256 wide, B rings one deeper.
-constexpr int kF4BN = 256, kF4SA = 2, kF4SB = 3;
+// MXFP4 weights (half the B bytes per step): both GEMMs 256 wide, B rings one deeper,
+// gemm2's A ring too (gemm2 352 vs 372 us on the gpt-oss-120b prefill layer; gemm1 no
+// faster; 128-wide gemm2 tiles 495 us).
+constexpr int kF4BN = 256, kF4SA1 = 2, kF4SA2 = 3, kF4SB = 3;
 // Dynamic LDS of the row-run kernel at its largest K (64 blocks).
 constexpr int kRowrunMaxLds = 64 * 2048 + 16 * 256 + 8 * 16 * 4;
 
@@ -1369,7 +1371,8 @@ static bool launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
     const long tot = static_cast<long>(max_tiles) * nt_big;
     const long cus = device_cus();
     const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
-    grouped_gemm_big_kernel<SWIGLU, kF4BN, kF4SA, kF4SB, kNarrowS, kNarrowS, true, true><<<g, 512, 0, st>>>(a, nt_big);
+    grouped_gemm_big_kernel<SWIGLU, kF4BN, SWIGLU ? kF4SA1 : kF4SA2, kF4SB, kNarrowS, kNarrowS, true, true>
+        <<<g, 512, 0, st>>>(a, nt_big);
     return true;
   }
   if (a.fp4) {
