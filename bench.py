@@ -130,6 +130,8 @@ def device_copy_gbs(torch, dev, mib=1024, reps=5):
 
 def cpu_baseline(shape, li, n_tokens, fmt="block"):
     """The oracle's forward on the first ``n_tokens`` tokens (one thread)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -151,9 +153,14 @@ def cpu_baseline(shape, li, n_tokens, fmt="block"):
             parts = [quant(w[i:i + 128]) for i in range(0, w.shape[0], 128)]
             return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
-        for e in need:   # offline weight conversion: not timed
-            c13[e], s13[e] = by_rows(expert_weights(shape, "w13", int(e), dev).cpu().numpy())
-            c2[e], s2[e] = by_rows(expert_weights(shape, "w2", int(e), dev).cpu().numpy())
+        # offline weight conversion, not timed: drawn serially, converted on a thread pool
+        host = {int(e): (expert_weights(shape, "w13", int(e), dev).cpu().numpy(),
+                         expert_weights(shape, "w2", int(e), dev).cpu().numpy()) for e in need}
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            conv = dict(zip(host, ex.map(lambda ws: (by_rows(ws[0]), by_rows(ws[1])), host.values())))
+        del host
+        for e, ((q13, t13), (q2, t2)) in conv.items():
+            c13[e], s13[e], c2[e], s2[e] = q13, t13, q2, t2
         t0 = time.perf_counter()
         R.forward(li.x, li.router_w, li.router_b, shape.top_k, shape.I, c13, s13, li.b13, c2, s2,
                   li.b2, token_subset=toks, fmt=fmt)
