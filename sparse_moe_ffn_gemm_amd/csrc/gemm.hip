@@ -1062,10 +1062,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
 // slower.  The matrix cores take an e2m1 first operand, whose lane (r, g) holds the 32
 // consecutive K values [32 g, 32 g + 32) of row r in 16 bytes (element 2j in the low
 // nibble), against the e4m3 activation fragment.
-template <bool SWIGLU, int KS, bool MX = false, bool FP4 = false>
+template <bool SWIGLU, int KS, bool MX = false, bool FP4 = false, int NW = 8>
 __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs a, int ntiles) {
   static_assert(MX || !FP4, "MXFP4 weights take E8M0 scales");
-  constexpr int WAVES = 8;
+  // NW = 2 (MX only: h blocks of 32 columns are wave pairs; the block-scaled 1x128 groups
+  // need all eight waves): 32-column workgroups, four times as many, for launches that
+  // would otherwise leave most CUs idle
+  static_assert(NW == 8 || (MX && NW == 2), "workgroup width");
+  constexpr int WAVES = NW;
   constexpr int NSUB = SWIGLU ? 2 : 1;       // weight sub-tiles per wave (gate, up)
   extern __shared__ __align__(16) uint8_t dyn_lds[];
 
@@ -1086,7 +1090,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
   float* sSa = reinterpret_cast<float*>(dyn_lds + KB * 2048);
   float* red = sSa + ceil_div(KB, 4) * 64;
 
-  const int c0 = nt * 128 + 16 * wave;       // the wave's first output column
+  const int c0 = nt * 16 * WAVES + 16 * wave;   // the wave's first output column
   const bool live = c0 < (SWIGLU ? I : N);   // I, N multiples of 64: all 16 or none
 
   // ---- the wave's weight stream: sub-tile s, K-block j, in bursts of KS blocks ----
@@ -1287,7 +1291,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
         *reinterpret_cast<uint32_t*>(a.h_out + static_cast<size_t>(p) * I + cq) =
             encode4_mul(hv[0], hv[1], hv[2], hv[3], mx_inv_scale(code));
       if ((wave & 1) == 0 && g == 0)
-        a.h_mx[static_cast<size_t>(p) * 4 * KBI + (nt * kBlock + 16 * wave) / kMxBlock] = static_cast<uint8_t>(code);
+        a.h_mx[static_cast<size_t>(p) * 4 * KBI + (nt * 16 * WAVES + 16 * wave) / kMxBlock] = static_cast<uint8_t>(code);
       return;
     }
     if (!live || p >= mt.row_end) return;
@@ -1378,14 +1382,25 @@ static bool launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
   if (a.fp4) {
     const int KB4 = ceil_div(a.K, kBlock);
     if (bm != 16 || KB4 > 64) return false;
-    const int nts = ceil_div(SWIGLU ? a.I : a.N, 128);
-    const int g = static_cast<int>((static_cast<long>(max_tiles) * nts + 7) / 8 * 8);
+    const int cols = SWIGLU ? a.I : a.N;
     const size_t lds = static_cast<size_t>(KB4) * 2048 + ceil_div(KB4, 4) * 256 + 8 * 16 * 4;
+    // fewer 128-column workgroups than CUs (a few experts of a few tokens): 32-column ones
+    const bool narrow = static_cast<long>(max_tiles) * ceil_div(cols, 128) < device_cus() / 2;
+    // (gemm1 still covers whole 128-column groups: the idle waves past I write the pad
+    // codes 127 of h's last scale word)
+    const int nts = !narrow ? ceil_div(cols, 128) : SWIGLU ? 4 * ceil_div(cols, 128) : ceil_div(cols, 32);
+    const int g = static_cast<int>((static_cast<long>(max_tiles) * nts + 7) / 8 * 8);
     static const bool lds_ok4 =
         hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
-    if (lds > 64 * 1024 && !lds_ok4) return false;
-    grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true><<<g, 512, lds, st>>>(a, nts);
+    static const bool lds_ok4n =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true, 2>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
+    if (lds > 64 * 1024 && !(narrow ? lds_ok4n : lds_ok4)) return false;
+    if (narrow)
+      grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true, 2><<<g, 128, lds, st>>>(a, nts);
+    else
+      grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true><<<g, 512, lds, st>>>(a, nts);
     return true;
   }
   // MXFP8 layers take the large-group kernel unless their tiles are decode-sized rows of

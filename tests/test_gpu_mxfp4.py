@@ -64,6 +64,9 @@ SMALL = [
     custom_shape(T=40, H=256, E=2, top_k=1, I=128, seed=60),        # 20 rows per expert: 16-row tiles
     custom_shape(T=96, H=384, E=8, top_k=2, I=320, seed=66, expert_bias=False),
     custom_shape(T=16, H=256, E=16, top_k=1, I=128, seed=68, router="one_per_expert"),
+    # the decode GEMM benchmark's shape at a high expert-parallel degree (32-column tiles)
+    custom_shape(T=4, H=4096, E=4, top_k=1, I=1536, seed=3, expert_bias=False,
+                 router="one_per_expert"),
 ]
 
 
