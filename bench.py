@@ -278,8 +278,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this layer runs on one GPU; multi-GPU runs (--gpus > 1) are not part "
-              "of this build", file=sys.stderr)
+        print("bench.py: the layer runs on one GPU; multi-GPU runs (--gpus > 1) are not "
+              "supported (expert-parallel sharding is a design, not an implementation)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
