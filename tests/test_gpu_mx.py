@@ -75,6 +75,10 @@ SMALL = [
     custom_shape(T=96, H=384, E=8, top_k=2, I=320, seed=56, expert_bias=False),
     # every expert exactly one token (the pages' decode GEMM benchmark)
     custom_shape(T=16, H=256, E=16, top_k=1, I=128, seed=58, router="one_per_expert"),
+    custom_shape(T=1, H=256, E=8, top_k=2, I=256, seed=71),         # single token
+    custom_shape(T=200, H=256, E=16, top_k=3, I=128, seed=72, router="hot"),  # one hot expert
+    custom_shape(T=33, H=64, E=256, top_k=8, I=64, seed=73),        # smallest H, I; most experts, top-8
+    custom_shape(T=700, H=448, E=2, top_k=1, I=192, seed=74, expert_bias=False),  # large groups, K tails
 ]
 
 

@@ -67,6 +67,10 @@ SMALL = [
     # the decode GEMM benchmark's shape at a high expert-parallel degree (32-column tiles)
     custom_shape(T=4, H=4096, E=4, top_k=1, I=1536, seed=3, expert_bias=False,
                  router="one_per_expert"),
+    custom_shape(T=1, H=256, E=8, top_k=2, I=256, seed=81),         # single token
+    custom_shape(T=200, H=256, E=16, top_k=3, I=128, seed=82, router="hot"),  # one hot expert
+    custom_shape(T=33, H=64, E=256, top_k=8, I=64, seed=83),        # smallest H, I; most experts, top-8
+    custom_shape(T=700, H=448, E=2, top_k=1, I=192, seed=84, expert_bias=False),  # large groups, K tails
 ]
 
 
