@@ -168,16 +168,19 @@ moe_status moe_forward_profiled(const uint16_t* x, const float* router_w, const 
  * (ties to even) of v * 2^-(c - 127), clamped to +-448.  Weights, x and h all use 1x32
  * blocks along K.
  *
- * Scale layout: a row of K elements has K/32 codes, stored in a row of
- * 4 * ceil(K/128) bytes (whole 4-byte words per 128-wide K-step, as the GEMMs stage
- * them); the bytes past K/32 hold 127.  Scale arrays of moe_forward_mx must be 4-byte
- * aligned. */
+ * Scale layout: a row of K elements has K/32 codes, padded to 4 * ceil(K/128) bytes
+ * (whole 4-byte words per 128-wide K-step, as the GEMMs stage them); the bytes past K/32
+ * hold 127.  Activation scales (x, h) are such rows, one per token.  Weight scales are
+ * stored in 16-row x 128-K tiles, the order the GEMMs read them: with KB = ceil(K/128),
+ * a matrix [N, K] (N a multiple of 16) has N/16 x KB tiles of 64 bytes, tile (n, j) at
+ * index n * KB + j holding row 16 n + r's four codes of K-block j at byte 4 r.  Scale
+ * arrays of moe_forward_mx must be 4-byte aligned. */
 
 /* MXFP8 quantisation of E stacked fp32 matrices.
  *   w      [E, N, K] float      source weights
  *   codes  [E, N, K] uint8      e4m3 codes (output)
- *   scales [E, N, 4 ceil(K/128)] uint8   E8M0 codes, padded rows (output)
- * Requires E, N >= 1 and K a positive multiple of 32. */
+ *   scales [E][N/16][KB][16][4] uint8   E8M0 codes in scale tiles (output)
+ * Requires E >= 1, N a positive multiple of 16 and K a positive multiple of 32. */
 moe_status moe_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t* codes,
                                    uint8_t* scales, void* stream);
 
@@ -190,9 +193,9 @@ moe_status moe_quantize_activations_mx(const uint16_t* x, int T, int H, uint8_t*
                                        uint8_t* scales, void* stream);
 
 /* The whole layer forward with MXFP8 experts: moe_forward's arguments and semantics, with
- *   w13_scales [E, 2I, 4 ceil(H/128)] uint8 and w2_scales [E, H, 4 ceil(I/128)] uint8
- * (moe_quantize_weights_mx), and x and h quantised in 1x32 MX blocks.  The workspace is
- * the same (moe_workspace_bytes). */
+ * w13_scales and w2_scales the scale tiles of moe_quantize_weights_mx (2I x H and H x I
+ * matrices), and x and h quantised in 1x32 MX blocks.  The workspace is the same
+ * (moe_workspace_bytes). */
 moe_status moe_forward_mx(const uint16_t* x, const float* router_w, const float* router_b,
                           const uint8_t* w13, const uint8_t* w13_scales, const uint16_t* b13,
                           const uint8_t* w2, const uint8_t* w2_scales, const uint16_t* b2, int T,
@@ -216,9 +219,9 @@ moe_status moe_forward_mx_profiled(const uint16_t* x, const float* router_w,
  * for an all-zero block); an element is the nearest e2m1 value (ties to the even code)
  * of v * 2^-(c - 127), clamped to +-6.  Activations (x, h) stay MXFP8 (1x32 blocks, e4m3).
  *
- * Storage: 16-row x 128-K tiles, in the order the GEMMs stream them.  With KB =
- * ceil(K/128), a matrix [N, K] (N a multiple of 16) is N/16 x KB tiles, tile (n, j) at
- * index n * KB + j:
+ * Storage: 16-row x 128-K tiles, in the order the GEMMs stream them (the MXFP8 weight
+ * scale tiles above, and code tiles of the same shape).  With KB = ceil(K/128), a
+ * matrix [N, K] (N a multiple of 16) is N/16 x KB tiles, tile (n, j) at index n * KB + j:
  *   codes:  1024 bytes per tile; row r of the tile (matrix row 16 n + r) at byte 64 r holds
  *           K [128 j, 128 j + 128), two codes per byte (element 2i in the low nibble of
  *           byte i); codes past K are 0.  N * KB * 64 bytes per matrix.

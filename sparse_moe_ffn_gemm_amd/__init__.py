@@ -7,11 +7,12 @@ include/moe.h); this package is its Python binding.  Build with
 """
 from ._lib import (PROFILE_STAGES, MoEError, Routing, WorkspaceRegions, forward, forward_profiled, lib, mx_row,
                    new_routing, new_workspace, quantize_activations, quantize_activations_mx,
-                   quantize_weights, quantize_weights_mx, quantize_weights_mxfp4, mxfp4_shapes, route,
+                   quantize_weights, quantize_weights_mx, quantize_weights_mxfp4, mxfp4_shapes, mx_scale_shape,
+                   route,
                    workspace_bytes, workspace_layout)
 from .layer import MoELayer
 
 __all__ = ["PROFILE_STAGES", "MoEError", "Routing", "WorkspaceRegions", "forward", "forward_profiled", "lib", "new_routing",
            "new_workspace", "quantize_activations", "quantize_activations_mx", "quantize_weights",
-           "quantize_weights_mx", "quantize_weights_mxfp4", "mxfp4_shapes", "mx_row", "route",
+           "quantize_weights_mx", "quantize_weights_mxfp4", "mxfp4_shapes", "mx_scale_shape", "mx_row", "route",
            "workspace_bytes", "workspace_layout", "MoELayer"]

@@ -179,30 +179,37 @@ def mx_row(K: int) -> int:
 
 
 def quantize_weights_mx(w: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
-    """MXFP8 quantisation of w [E, N, K] (or [N, K]) fp32 -> (codes uint8, E8M0 scale codes
-    uint8 [E, N, 4 ceil(K/128)], pads 127)."""
+    """MXFP8 quantisation of w [E, N, K] (or [N, K]) fp32, N a multiple of 16 -> (e4m3 codes
+    uint8 [E, N, K], E8M0 codes uint8 [E, *mx_scale_shape(N, K)] in scale tiles, pads 127)."""
     squeeze = w.dim() == 2
     w3 = w.unsqueeze(0) if squeeze else w
     E, N, K = w3.shape
+    ss = mx_scale_shape(N, K)
     if codes is None:
         codes = torch.empty((E, N, K), dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty((E, N, mx_row(K)), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((E,) + ss, dtype=torch.uint8, device=w.device)
     st = lib().moe_quantize_weights_mx(_dev(w3, torch.float32, "w"), E, N, K,
                                        _fp8(codes.view(E, N, K), "codes"),
-                                       _dev(scales.view(E, N, mx_row(K)), torch.uint8, "scales"),
+                                       _dev(scales.view((E,) + ss), torch.uint8, "scales"),
                                        _stream(w.device))
     _check(st, "moe_quantize_weights_mx")
     if squeeze:
-        return codes.view(N, K), scales.view(N, mx_row(K))
+        return codes.view(N, K), scales.view(ss)
     return codes, scales
 
 
+def mx_scale_shape(N: int, K: int):
+    """Shape of one weight matrix's E8M0 scale tiles (MXFP8 and MXFP4): 16-row x 128-K
+    tiles (tile (n, j) holds rows 16n..16n+15 over K [128j, 128j+128)), each row's four
+    codes of the K-block: [N/16, ceil(K/128), 16, 4]."""
+    return (N // 16, kb(K), 16, 4)
+
+
 def mxfp4_shapes(N: int, K: int):
-    """Shapes of one matrix's MXFP4 storage: 16-row x 128-K tiles (tile (n, j) holds rows
-    16n..16n+15 over K [128j, 128j+128)): codes [N/16, ceil(K/128), 16, 64] (64 bytes per
-    tile row, two codes a byte, zeros past K) and E8M0 codes [N/16, ceil(K/128), 16, 4]."""
-    return (N // 16, kb(K), 16, 64), (N // 16, kb(K), 16, 4)
+    """Shapes of one matrix's MXFP4 storage, in the same tiles: codes [N/16, ceil(K/128),
+    16, 64] (64 bytes per tile row, two codes a byte, zeros past K) and the scale tiles."""
+    return (N // 16, kb(K), 16, 64), mx_scale_shape(N, K)
 
 
 def quantize_weights_mxfp4(w: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None):
@@ -286,12 +293,9 @@ def _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2
         workspace = new_workspace(T, H, E, top_k, I, x.device)
     rs = _routing_struct(routing, T, E, top_k) if routing is not None else None
     mx = w13_scales.dtype == torch.uint8          # MX E8M0 codes, else fp32 block scales
-    if fp4:
-        s13 = _dev(w13_scales, torch.uint8, "w13_scales", (E,) + mxfp4_shapes(2 * I, H)[1])
-        s2 = _dev(w2_scales, torch.uint8, "w2_scales", (E,) + mxfp4_shapes(H, I)[1])
-    elif mx:
-        s13 = _dev(w13_scales, torch.uint8, "w13_scales", (E, 2 * I, mx_row(H)))
-        s2 = _dev(w2_scales, torch.uint8, "w2_scales", (E, H, mx_row(I)))
+    if mx:                                         # MXFP8 / MXFP4: scale tiles
+        s13 = _dev(w13_scales, torch.uint8, "w13_scales", (E,) + mx_scale_shape(2 * I, H))
+        s2 = _dev(w2_scales, torch.uint8, "w2_scales", (E,) + mx_scale_shape(H, I))
     else:
         s13 = _dev(w13_scales, torch.float32, "w13_scales", (E, kb(2 * I), kb(H)))
         s2 = _dev(w2_scales, torch.float32, "w2_scales", (E, kb(H), kb(I)))

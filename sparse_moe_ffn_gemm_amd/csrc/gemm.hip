@@ -640,7 +640,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // MXFP8: every thread stages one 4-byte E8M0 row of K-step kt (the four 32-blocks of
   // its 128 columns): thread t < BM the A row t, BM <= t < BM + BN the B row t - BM; one
   // load per wave and step, like the block scales above
-  // (MXFP4: a B row's 4 codes of step kt sit in its tile's 64-byte scale block)
+  // (a B row's 4 codes of step kt sit in its 16-row tile's 64-byte scale block)
   const uint8_t* x_ptr = reinterpret_cast<const uint8_t*>(kZeroScale);
   bool x_live = false;
   int x_step = 4;
@@ -654,12 +654,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       const int g = b_global_row(tid - BM);
       x_live = g >= 0;
       const int gg = g < 0 ? 0 : g;
-      if constexpr (FP4) {
-        x_ptr = a.B_mx + (static_cast<size_t>(e) * N + (gg & ~15)) * RS + 4 * (gg & 15);
-        x_step = 64;
-      } else {
-        x_ptr = a.B_mx + (static_cast<size_t>(e) * N + gg) * RS;
-      }
+      x_ptr = a.B_mx + (static_cast<size_t>(e) * N + (gg & ~15)) * RS + 4 * (gg & 15);
+      x_step = 64;
     }
   }
 
@@ -1101,16 +1097,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
   const int nbp = (nb + 1) & ~1;             // padded to the two-slot ring
   unsigned b_off[NSUB];
   float sbg[NSUB];                           // lane j: weight block scale of K-block j
-  const uint8_t* bmx[NSUB];                  // MXFP8: the lane's weight row of E8M0 codes
+  const uint8_t* bmx[NSUB];                  // MX: the lane's E8M0 codes in the scale tiles
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     const int row = (SWIGLU && s == 1 ? I : 0) + c0 + r;
     b_off[s] = FP4 ? static_cast<unsigned>(row - r) * KB * 64 + 64 * r + 16 * g
                    : static_cast<unsigned>(row) * K + 16 * g;
     if constexpr (MX) {
-      // MXFP8: the row's code row; MXFP4: the tile row's 4 codes, 64 bytes per K-block
-      bmx[s] = FP4 ? a.B_mx + (static_cast<size_t>(e) * N + (live ? row - r : 0)) * (4 * KB) + 4 * r
-                   : a.B_mx + (static_cast<size_t>(e) * N + (live ? row : 0)) * (4 * KB);
+      // the tile row's 4 codes of K-block 0 (64 bytes per K-block)
+      bmx[s] = a.B_mx + (static_cast<size_t>(e) * N + (live ? row - r : 0)) * (4 * KB) + 4 * r;
       sbg[s] = 0.f;
     } else {
       const int brow = ((SWIGLU && s == 1 ? I : 0) + c0) / kBlock;
@@ -1129,7 +1124,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
         const int jj = j0 + t < KB ? j0 + t : KB - 1;
-        xq[t] = *reinterpret_cast<const uint32_t*>(xr + (FP4 ? 64 : 4) * jj);
+        xq[t] = *reinterpret_cast<const uint32_t*>(xr + 64 * jj);
       }
     }
 #pragma unroll

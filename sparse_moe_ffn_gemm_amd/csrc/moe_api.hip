@@ -329,7 +329,7 @@ moe_status moe_quantize_weights_mx(const float* w, int E, int N, int K, uint8_t*
                                    uint8_t* scales, void* stream) {
   if (!w || !codes || !scales || !aligned16(w) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
   if (E < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARG;
-  if (K % 32 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (K % 32 != 0 || N % 16 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (static_cast<long>(E) * N * 4 * ceil_div(K, 128) / 64 >= (1L << 31))
     return MOE_ERR_UNSUPPORTED_SHAPE;
   (void)hipGetLastError();

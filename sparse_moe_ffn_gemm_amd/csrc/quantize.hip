@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __res
 
 // MXFP8: 4 lanes per 32-block, 8 elements per lane; a workgroup covers 64 block slots
 // of the padded scale rows (slots past K/32 write the pad code 127 and no elements).
-// Weights are fp32 [rows, K].
+// Weights are fp32 [rows, K] (rows a multiple of 16); their scales are stored in 16-row
+// x 128-K tiles, as the GEMMs read them.
 __global__ __launch_bounds__(256) void quantize_weights_mx_kernel(const float* __restrict__ w,
                                                                   long rows, int K,
                                                                   uint8_t* __restrict__ codes,
@@ -108,10 +109,12 @@ __global__ __launch_bounds__(256) void quantize_weights_mx_kernel(const float* _
     q.y = encode4_mul(f[4], f[5], f[6], f[7], m);
     *reinterpret_cast<uint2*>(codes + row * K + col) = q;
   }
-  if (live && sub == 0) scales[slot] = static_cast<uint8_t>(code);
+  // weight scales in 16-row x 128-K tiles: row r of tile (row / 16, blk / 4) at byte 4 r
+  if (live && sub == 0)
+    scales[((row >> 4) * (RS / 4) + (blk >> 2)) * 64 + (row & 15) * 4 + (blk & 3)] = static_cast<uint8_t>(code);
 }
 
-// Activations bf16 [T, H], the same block slots.
+// Activations bf16 [T, H], the same block slots (scale rows per token).
 __global__ __launch_bounds__(256) void quantize_act_mx_kernel(const uint16_t* __restrict__ x, int T,
                                                               int H, uint8_t* __restrict__ codes,
                                                               uint8_t* __restrict__ scales) {

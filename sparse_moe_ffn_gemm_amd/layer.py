@@ -48,8 +48,8 @@ class MoELayer:
         elif fmt == "mxfp8":
             w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)
             w2 = torch.empty((E, H, I), dtype=torch.uint8, device=device)
-            s13 = torch.empty((E, 2 * I, _lib.mx_row(H)), dtype=torch.uint8, device=device)
-            s2 = torch.empty((E, H, _lib.mx_row(I)), dtype=torch.uint8, device=device)
+            s13 = torch.empty((E,) + _lib.mx_scale_shape(2 * I, H), dtype=torch.uint8, device=device)
+            s2 = torch.empty((E,) + _lib.mx_scale_shape(H, I), dtype=torch.uint8, device=device)
             quant = _lib.quantize_weights_mx
         elif fmt == "block":
             w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device=device)

@@ -25,6 +25,12 @@ def _split(scales: np.ndarray, K: int):
     return scales[..., :K // 32], scales[..., K // 32:]
 
 
+def untile_scales(scales: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Padded E8M0 rows [E, N, 4 ceil(K/128)] of weight scale tiles [E, N/16, KB, 16, 4]."""
+    E, KB = scales.shape[0], -(-K // 128)
+    return scales.reshape(E, N // 16, KB, 16, 4).transpose(0, 1, 3, 2, 4).reshape(E, N, KB * 4)
+
+
 def _wide(rng, shape, blocks_axis_len):
     a = rng.standard_normal(shape) * 0.02
     a *= np.exp2(rng.integers(-20, 20, size=shape[:-1] + (blocks_axis_len // 32,))).repeat(32, axis=-1)
@@ -41,8 +47,8 @@ def test_weight_quantiser_bit_exact(E, N, K):
     torch.cuda.synchronize()
     rc, rs = R.quantize_mx(w)
     codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
-    assert scales.shape == (E, N, moe.mx_row(K))
-    real, pad = _split(scales, K)
+    assert scales.shape == (E,) + moe.mx_scale_shape(N, K)
+    real, pad = _split(untile_scales(scales, N, K), K)
     assert np.array_equal(codes, rc)
     assert np.array_equal(real, rs)
     assert np.all(pad == 127)

@@ -15,7 +15,7 @@ import sparse_moe_ffn_gemm_amd as moe
 from oracle import moe_ref as R
 from synth import SHAPES, custom_shape
 from gpu_helpers import GpuLayer, OracleExperts, bits_host, compare_out, routing_exact, say
-from test_gpu_mx import _split, _wide, _ws_view, _check_h_dispatched
+from test_gpu_mx import _split, _wide, _ws_view, _check_h_dispatched, untile_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +27,7 @@ def untile(codes: np.ndarray, scales: np.ndarray, N: int, K: int):
     storage (16-row x 128-K tiles), and the code bytes past K."""
     E, KB = codes.shape[0], -(-K // 128)
     c = codes.reshape(E, N // 16, KB, 16, 64).transpose(0, 1, 3, 2, 4).reshape(E, N, KB * 64)
-    s = scales.reshape(E, N // 16, KB, 16, 4).transpose(0, 1, 3, 2, 4).reshape(E, N, KB * 4)
-    return c[..., :K // 2], s, c[..., K // 2:]
+    return c[..., :K // 2], untile_scales(scales, N, K), c[..., K // 2:]
 
 
 @pytest.mark.parametrize("E,N,K", [(2, 192, 2880), (3, 64, 256), (1, 96, 96), (2, 16, 32)])
