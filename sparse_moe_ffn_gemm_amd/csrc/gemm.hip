@@ -617,12 +617,20 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       b_off[i] = static_cast<unsigned>(g < 0 ? b_global_row(0) : g) * K + ((a_slot ^ swz_key(row)) << 4);
     }
   }
+  // A rows' scales: per token row (stride 1 per K-step), or gathered in dispatch order
+  // with the K-step major (A_sd: the tile's rows of a K-step are one contiguous run)
   const float* s_ptr = kZeroScale;
   bool s_live = false;
+  int s_step = 1;
   if (lane < A_ROWS) {
     const int src = rowsrc[wave * A_ROWS + lane];
     s_live = src >= 0;
-    s_ptr = a.A_scale + static_cast<size_t>(src < 0 ? 0 : src) * KB;
+    if (a.A_sd != nullptr) {
+      s_ptr = reinterpret_cast<const float*>(a.A_sd) + (s_live ? mt.row_begin + wave * A_ROWS + lane : 0);
+      s_step = a.sd_rows;
+    } else {
+      s_ptr = a.A_scale + static_cast<size_t>(src < 0 ? 0 : src) * KB;
+    }
   } else if (lane >= 32 && lane < 32 + WN * SN) {
     const int q = lane - 32, qw = q / SN, n = q % SN;   // column wave qw, sub-tile n
     int row;
@@ -649,7 +657,12 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     if (tid < BM) {
       const int src = rowsrc[tid];
       x_live = src >= 0;
-      x_ptr = a.A_mx + static_cast<size_t>(src < 0 ? 0 : src) * RS;
+      if (a.A_sd != nullptr) {
+        x_ptr = reinterpret_cast<const uint8_t*>(a.A_sd + (x_live ? mt.row_begin + tid : 0));
+        x_step = 4 * a.sd_rows;
+      } else {
+        x_ptr = a.A_mx + static_cast<size_t>(src < 0 ? 0 : src) * RS;
+      }
     } else if (tid < BM + BN) {
       const int g = b_global_row(tid - BM);
       x_live = g >= 0;
@@ -675,10 +688,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       }
     }
     if constexpr (MX) {
-      const void* src = x_live ? static_cast<const void*>(x_ptr + x_step * kt) : kZeroScale;
+      const void* src = x_live ? static_cast<const void*>(x_ptr + static_cast<size_t>(x_step) * kt) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
     } else if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN)) {   // lanes 0.. always: one instruction
-      const void* src = s_live ? static_cast<const void*>(s_ptr + kt) : kZeroScale;
+      const void* src = s_live ? static_cast<const void*>(s_ptr + static_cast<size_t>(kt) * s_step) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
     }
   };

@@ -206,6 +206,12 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
                                  at<int32_t>(ws, p.perm), at<int32_t>(ws, p.inv)};
   enqueue_routing(p, x, router_w, router_b, tb, ws, st, ev, /*quant_x=*/true, mx);
   mark(ev, 4, st);   // (the activation quantisation ran inside the router kernel)
+  // large-group GEMM1: the x scale words of the routed rows in dispatch order, K-block
+  // major, staged in the y region (written only later, by GEMM2)
+  const bool gather_sx = p.bm == 256;
+  if (gather_sx)
+    moe::launch_gather_row_scales(at<uint32_t>(ws, p.sx), ceil_div(H, moe::kBlock), tb.perm, top_k,
+                                  static_cast<int>(p.rows), at<uint32_t>(ws, p.y), st);
   mark(ev, 5, st);
 
   moe::GemmArgs g1{};
@@ -235,6 +241,10 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g1.I = I;
   g1.h_out = at<uint8_t>(ws, p.h);
   g1.queue = at<int32_t>(ws, p.num_tiles) + 1;
+  if (gather_sx) {
+    g1.A_sd = at<uint32_t>(ws, p.y);
+    g1.sd_rows = static_cast<int>(p.rows);
+  }
   if (!moe::launch_gemm1(g1, p.bm, p.max_tiles, st)) return MOE_ERR_HIP;
   mark(ev, 6, st);
 

@@ -770,6 +770,28 @@ void launch_route_tail(const float* partial, int ksplit, const float* bias, int 
                                                     num_tiles, expert_tile_off, perm, inv);
 }
 
+// The activation scale words of the routed rows, in dispatch order and K-block major, for
+// the large-group GEMM1 (the 256 rows of its tile then read one contiguous run per K-step
+// instead of a word from each gathered token row).  Thread i = j * rows + p.
+__global__ __launch_bounds__(256) void gather_row_scales_kernel(const uint32_t* __restrict__ src,
+                                                                int KB,
+                                                                const int32_t* __restrict__ perm,
+                                                                int top_k, int rows,
+                                                                uint32_t* __restrict__ dst) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<long>(rows) * KB) return;
+  const int j = static_cast<int>(i / rows), p = static_cast<int>(i % rows);
+  const int t = perm[p] / top_k;
+  dst[i] = src[static_cast<long>(t) * KB + j];
+}
+
+void launch_gather_row_scales(const uint32_t* src, int KB, const int32_t* perm, int top_k,
+                              int rows, uint32_t* dst, hipStream_t st) {
+  const long n = static_cast<long>(rows) * KB;
+  gather_row_scales_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st>>>(
+      src, KB, perm, top_k, rows, dst);
+}
+
 void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,
                              int top_k, int32_t* perm, int32_t* inv, hipStream_t st) {
   dispatch_scatter_kernel<<<dim3(ceil_div(T, kChunk)), dim3(256), 0, st>>>(ids, chunk_base, T, E,
