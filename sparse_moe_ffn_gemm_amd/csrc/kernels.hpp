@@ -56,8 +56,8 @@ void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32
                           int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
                           int32_t* expert_tile_off, hipStream_t st, const int32_t* ids = nullptr,
                           int T = 0, int top_k = 0, int32_t* perm = nullptr, int32_t* inv = nullptr);
-// dst[j * rows + p] = src[(perm[p] / top_k) * KB + j]: the per-token scale words of the
-// routed rows in dispatch order, K-block major
+// dst[j * rows + p] = src[(perm[p] / top_k) * KB + j] (perm NULL: src[p * KB + j]): the
+// scale words of the routed rows in dispatch order, K-block major
 void launch_gather_row_scales(const uint32_t* src, int KB, const int32_t* perm, int top_k,
                               int rows, uint32_t* dst, hipStream_t st);
 void launch_dispatch_scatter(const int32_t* ids, const int32_t* chunk_base, int T, int E,
@@ -99,8 +99,8 @@ struct GemmArgs {
   const uint8_t* A_mx;
   const uint8_t* B_mx;
   uint8_t* h_mx;
-  // large-group gemm1: the A rows' scale words (fp32 block scale or 4 E8M0 codes) per
-  // K-step gathered in dispatch order, [ceil(K/128)][sd_rows]; NULL: read A_scale / A_mx
+  // large-group GEMMs: the A rows' scale words (fp32 block scale or 4 E8M0 codes) per
+  // K-step in dispatch order, [ceil(K/128)][sd_rows]; NULL: read A_scale / A_mx
   const uint32_t* A_sd;
   int sd_rows;
 };

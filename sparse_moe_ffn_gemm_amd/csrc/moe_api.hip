@@ -24,6 +24,7 @@ struct Plan {
   size_t partial, hist, wparts, chunk_base, tiles, num_tiles, expert_tile_off;
   size_t ids, gates, counts, offsets, perm, inv;
   size_t xq, sx, h, sh, y;
+  size_t shd;      // h scale words in dispatch order, K-block major (large-group GEMMs)
   size_t total;
 };
 
@@ -95,6 +96,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   p->h = take(static_cast<size_t>(p->rows) * I);
   p->sh = take(sizeof(float) * static_cast<size_t>(p->rows) * ceil_div(I, moe::kBlock));
   p->y = take(sizeof(uint16_t) * static_cast<size_t>(p->rows) * H);
+  p->shd = take(sizeof(uint32_t) * static_cast<size_t>(p->rows) * ceil_div(I, moe::kBlock));
   p->total = off;
 }
 
@@ -273,6 +275,12 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.I = I;
   g2.y_out = at<uint16_t>(ws, p.y);
   g2.queue = at<int32_t>(ws, p.num_tiles) + 1 + moe::kGemmQueues;
+  if (gather_sx) {   // h's scale words K-block major
+    moe::launch_gather_row_scales(at<uint32_t>(ws, p.sh), ceil_div(I, moe::kBlock), nullptr, 1,
+                                  static_cast<int>(p.rows), at<uint32_t>(ws, p.shd), st);
+    g2.A_sd = at<uint32_t>(ws, p.shd);
+    g2.sd_rows = static_cast<int>(p.rows);
+  }
   if (!moe::launch_gemm2(g2, p.bm, p.max_tiles, st)) return MOE_ERR_HIP;
   mark(ev, 7, st);
   moe::launch_combine(at<uint16_t>(ws, p.y), tb.gates, tb.inv, T, H, top_k, out, st);

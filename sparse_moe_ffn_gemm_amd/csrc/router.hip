@@ -771,8 +771,9 @@ void launch_route_tail(const float* partial, int ksplit, const float* bias, int 
 }
 
 // The activation scale words of the routed rows, in dispatch order and K-block major, for
-// the large-group GEMM1 (the 256 rows of its tile then read one contiguous run per K-step
-// instead of a word from each gathered token row).  Thread i = j * rows + p.
+// the large-group GEMMs (the 256 rows of a tile then read one contiguous run per K-step
+// instead of a word from each row): x's gathered through perm for GEMM1, h's (already in
+// dispatch order, perm NULL) for GEMM2.  Thread i = j * rows + p.
 __global__ __launch_bounds__(256) void gather_row_scales_kernel(const uint32_t* __restrict__ src,
                                                                 int KB,
                                                                 const int32_t* __restrict__ perm,
@@ -781,7 +782,7 @@ __global__ __launch_bounds__(256) void gather_row_scales_kernel(const uint32_t* 
   const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= static_cast<long>(rows) * KB) return;
   const int j = static_cast<int>(i / rows), p = static_cast<int>(i % rows);
-  const int t = perm[p] / top_k;
+  const int t = perm != nullptr ? perm[p] / top_k : p;
   dst[i] = src[static_cast<long>(t) * KB + j];
 }
 
