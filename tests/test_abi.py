@@ -95,3 +95,35 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros((4, 128), dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         moe.quantize_activations(x)
+
+
+def _fwd_mx(fn, **kw):
+    a = dict(x=FAKE, rw=FAKE, rb=None, w13=FAKE, s13=FAKE, b13=None, w2=FAKE, s2=FAKE, b2=None,
+             T=16, H=256, E=8, k=2, I=256, out=FAKE, routing=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return fn(a["x"], a["rw"], a["rb"], a["w13"], a["s13"], a["b13"], a["w2"], a["s2"], a["b2"],
+              a["T"], a["H"], a["E"], a["k"], a["I"], a["out"], a["routing"], a["ws"], a["wsb"], None)
+
+
+def test_mx_error_paths():
+    """MXFP8 / MXFP4 entry points: null and misaligned arguments, shapes the quantisers'
+    tiled storage cannot hold (N not a multiple of 16, K not of 32), and decode-sized
+    MXFP4 layers wider than the row-run kernel's LDS tile."""
+    L = moe.lib()
+    for q in (L.moe_quantize_weights_mx, L.moe_quantize_weights_mxfp4):
+        assert q(None, 1, 128, 128, FAKE, FAKE, None) == -1
+        assert q(FAKE, 0, 128, 128, FAKE, FAKE, None) == -1
+        assert q(FAKE, 1, 120, 128, FAKE, FAKE, None) == -2      # N % 16
+        assert q(FAKE, 1, 128, 48, FAKE, FAKE, None) == -2       # K % 32
+        assert q(FAKE + 4, 1, 128, 128, FAKE, FAKE, None) == -1  # misaligned source
+    assert L.moe_quantize_activations_mx(FAKE, 4, 96, FAKE, FAKE, None) == -2
+    for fn in (L.moe_forward_mx, L.moe_forward_mxfp4):
+        assert _fwd_mx(fn, x=None) == -1
+        assert _fwd_mx(fn, s13=FAKE + 2) == -1                  # scale words need 4-byte alignment
+        assert _fwd_mx(fn, T=0) == -2
+        need = L.moe_workspace_bytes(16, 256, 8, 2, 256)
+        assert _fwd_mx(fn, wsb=need - 1) == -3
+    # 4 tokens over 2 experts (16-row tiles) with H = 8448: MXFP4 refuses, MXFP8 does not
+    # reach a launch either way here (its workspace is too small on purpose)
+    assert _fwd_mx(L.moe_forward_mxfp4, T=4, H=8448, E=2, k=1, I=128) == -2
+    assert _fwd_mx(L.moe_forward_mx, T=4, H=8448, E=2, k=1, I=128, wsb=16) == -3
