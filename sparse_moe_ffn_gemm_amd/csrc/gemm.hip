@@ -683,7 +683,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       for (int i = 0; i < A_INSTR; ++i) {
         const int row = wave * A_ROWS + i * 8 + a_r8;
         const int kk = k0 + ((a_slot ^ swz_key(row)) << 4);
-        const void* src = (a_ok[i] && kk < K) ? static_cast<const void*>(a.A + a_off[i] + k0) : kZeroChunk;
+        unsigned off = a_off[i];
+        asm volatile("" : "+v"(off));   // recompute the address here: no hoisted 64-bit copies
+        const void* src = (a_ok[i] && kk < K) ? static_cast<const void*>(a.A + off + k0) : kZeroChunk;
         load_lds16(src, As + (wave * A_ROWS + i * 8) * 128);
       }
     }
@@ -709,7 +711,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       for (int i = 0; i < B_INSTR; ++i) {
         const int row = wave * B_ROWS + i * 8 + a_r8;
         const int kk = k0 + ((a_slot ^ swz_key(row)) << 4);
-        const void* src = (b_ok[i] && kk < K) ? static_cast<const void*>(Bexp + b_off[i] + k0) : kZeroChunk;
+        unsigned off = b_off[i];
+        asm volatile("" : "+v"(off));
+        const void* src = (b_ok[i] && kk < K) ? static_cast<const void*>(Bexp + off + k0) : kZeroChunk;
         load_lds16(src, Bs + (wave * B_ROWS + i * 8) * 128);
       }
     }
