@@ -25,7 +25,10 @@
  *     no host synchronisation and no device allocation happen inside the library.
  *   - Inputs are read-only and must not alias outputs or the workspace.
  *   - Calls are re-entrant; concurrent calls must use distinct workspaces.
- *   - A launch failure reported by the HIP runtime returns MOE_ERR_HIP.
+ *   - Every kernel a call will launch is chosen (and any large-LDS opt-in made) during
+ *     validation.  MOE_ERR_HIP is returned only if the HIP runtime reports a launch
+ *     failure after enqueueing began; the kernels enqueued before the failing one stay
+ *     enqueued, and the outputs are then undefined.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -46,7 +49,10 @@ typedef enum {
 } moe_status;
 
 /* Supported envelope: 1 <= T, 1 <= E <= 256, 1 <= top_k <= min(E, 8),
- * H and I positive multiples of 64, T * top_k < 2^31, T * H < 2^31. */
+ * H and I positive multiples of 64, T * top_k < 2^31, T * H < 2^31, T * top_k * I < 2^31,
+ * 2 * I * H < 2^31 (the GEMMs address A rows and one expert's weight rows with 32-bit
+ * byte offsets), T * top_k * H < 2^40.  Outside it the calls return
+ * MOE_ERR_UNSUPPORTED_SHAPE and moe_workspace_bytes returns 0. */
 
 /* Routing tables, all caller-owned device buffers:
  *   topk_ids       [T, top_k] int32   expert ids per token, descending logit,
@@ -141,14 +147,15 @@ moe_status moe_forward(const uint16_t* x, const float* router_w, const float* ro
 /* moe_forward with per-stage timing: identical work and results, plus
  * MOE_PROFILE_EVENTS hipEvent_t handles (created by the caller) recorded on `stream`
  * before each stage and after the last one:
- *   0 router GEMM  1 top-k + softmax  2 dispatch scan  3 dispatch scatter
- *   4 activation quantisation  5 GEMM1 (+ bias, SwiGLU, requantisation)
- *   6 GEMM2 (+ bias)  7 combine  8 end
- * so hipEventElapsedTime(events[i], events[i+1]) is stage i's device time (the
- * activation quantisation runs inside stage 0's kernel, so stage 4 is empty; for
- * T <= 256 the scatter runs inside stage 2's kernel and stage 3 is empty, and when also
- * top_k <= 4 and T * E <= 16384 one kernel does top-k, scan and scatter in stage 1 and
- * stages 2 and 3 are both empty).
+ *   0 router GEMM (with the 1x128 quantisation of x fused in)  1 top-k + softmax
+ *   2 dispatch scan  3 dispatch scatter  4 x scale-word regrouping  5 GEMM1 (+ bias,
+ *   SwiGLU, requantisation)  6 GEMM2 (+ bias; for 256-row tiles, the h scale-word
+ *   regrouping runs first)  7 combine  8 end
+ * so hipEventElapsedTime(events[i], events[i+1]) is stage i's device time.  Stage 4
+ * regroups the x scale words into dispatch order, K-block major, for the 256-row GEMM
+ * tiles, and is empty for the other tile heights; for T <= 256 the scatter runs inside
+ * stage 2's kernel and stage 3 is empty, and when also top_k <= 4 and T * E <= 16384 one
+ * kernel does top-k, scan and scatter in stage 1 and stages 2 and 3 are both empty.
  * `events` must point to MOE_PROFILE_EVENTS entries (NULL array: MOE_ERR_INVALID_ARG);
  * a NULL entry is not recorded, so a caller can time some stages only (each recorded
  * event adds a small gap between kernels). */

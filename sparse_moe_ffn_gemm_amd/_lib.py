@@ -22,10 +22,13 @@ EXPORTS = ["moe_status_str", "moe_workspace_bytes", "moe_workspace_layout",
            "moe_quantize_weights", "moe_quantize_activations", "moe_route", "moe_forward",
            "moe_forward_profiled", "moe_quantize_weights_mx", "moe_quantize_activations_mx",
            "moe_forward_mx", "moe_forward_mx_profiled", "moe_quantize_weights_mxfp4",
-           "moe_forward_mxfp4", "moe_forward_mxfp4_profiled"]
+           "moe_forward_mxfp4", "moe_forward_mxfp4_profiled",
+           # test-only (include/moe_test.h)
+           "moe_test_gemm_raw_workspace_bytes", "moe_test_gemm_raw"]
 
+# stage i runs between profiling events i and i + 1 (include/moe.h, moe_forward_profiled)
 PROFILE_STAGES = ["router_gemm", "topk_softmax", "dispatch_scan", "dispatch_scatter",
-                  "act_quant", "gemm1", "gemm2", "combine"]
+                  "x_scale_gather", "gemm1", "gemm2", "combine"]
 
 
 class MoEError(RuntimeError):
@@ -89,6 +92,11 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_mxfp4.restype = i
         L.moe_forward_mxfp4_profiled.argtypes = L.moe_forward_profiled.argtypes
         L.moe_forward_mxfp4_profiled.restype = i
+        L.moe_test_gemm_raw_workspace_bytes.argtypes = [i, i, i]
+        L.moe_test_gemm_raw_workspace_bytes.restype = sz
+        L.moe_test_gemm_raw.argtypes = [i, i, i, vp, vp, i, vp, i, ctypes.POINTER(ctypes.c_int32), i,
+                                        vp, vp, i, i, vp, vp, sz, vp]
+        L.moe_test_gemm_raw.restype = i
         _lib = L
     return _lib
 
@@ -341,3 +349,31 @@ def forward_profiled(events, x, router_w, router_b, w13, w13_scales, b13, w2, w2
           "mxfp4": "moe_forward_mxfp4_profiled"}[fmt]
     _check(getattr(lib(), fn)(*args, arr), fn)
     return out
+
+
+def gemm_raw_accumulators(gemm: int, fmt: str, bm: int, A: torch.Tensor, A_scales: torch.Tensor,
+                  counts, B: torch.Tensor, B_scales: torch.Tensor, N: int, K: int,
+                  perm: torch.Tensor = None, top_k: int = 1) -> torch.Tensor:
+    """TEST-ONLY (include/moe_test.h): one grouped GEMM (``gemm`` 1 or 2) of the layer's
+    kernels with its raw fp32 accumulators as the output, C [sum(counts), N].  ``counts`` are
+    the routed rows per expert (host ints); ``fmt`` "block", "mxfp8" or "mxfp4"; ``bm`` the
+    M-tile rows that select the kernel family as in the forward."""
+    import numpy as np
+    cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+    rows, E = int(cnt.sum()), int(cnt.size)
+    dev = A.device
+    C = torch.empty((rows, N), dtype=torch.float32, device=dev)
+    n = int(lib().moe_test_gemm_raw_workspace_bytes(rows, E, K))
+    if n == 0:
+        raise MoEError(-2, "moe_test_gemm_raw_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    f = {"block": 0, "mxfp8": 1, "mxfp4": 2}[fmt]
+    sdt = torch.float32 if fmt == "block" else torch.uint8
+    st = lib().moe_test_gemm_raw(
+        gemm, f, bm, _fp8(A, "A"), _dev(A_scales, sdt, "A_scales"), A.shape[0],
+        _dev(perm, torch.int32, "perm"), top_k,
+        cnt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), E, _fp8(B, "B"),
+        _dev(B_scales, sdt, "B_scales"), N, K, _dev(C, torch.float32, "C"),
+        _dev(ws, torch.uint8, "workspace"), ws.numel(), _stream(dev))
+    _check(st, "moe_test_gemm_raw")
+    return C

@@ -159,7 +159,7 @@ __device__ __forceinline__ bool pick_tile(const GemmArgs& a, int ntiles, int& nt
 // waited for explicitly); the "memory" clobber keeps LDS accesses on their side of it.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BM, int BN, int WM, int WN, bool SWIGLU, int STAGES>
+template <int BM, int BN, int WM, int WN, bool SWIGLU, int STAGES, bool RAW = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
                                                            int ntiles, int grid) {
@@ -429,6 +429,28 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
   __syncthreads();   // every wave is done with the ring before its LDS is reused
 
   const int rbase = wm * WTM + 4 * (lane >> 4);   // + 16 m + i
+  if constexpr (RAW) {   // the fp32 accumulators, at the B row's global column of C [rows, N]
+#pragma unroll
+    for (int n = 0; n < SN; ++n) {
+      const int br = sub_brow(n) + (lane & 15);
+      int g = -1;
+      if (SWIGLU) {
+        const int j = nt * 128 + (br & 127);
+        if (j < I) g = (br >> 7) * I + j;
+      } else if (nt * BN + br < N) {
+        g = nt * BN + br;
+      }
+      if (g < 0) continue;
+#pragma unroll
+      for (int m = 0; m < SM; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = mt.row_begin + rbase + 16 * m + i;
+          if (p < mt.row_end) a.c_raw[static_cast<size_t>(p) * N + g] = acc[m][n][i];
+        }
+    }
+    return;
+  }
   if constexpr (SWIGLU) {
     const uint16_t* bias = a.bias ? a.bias + static_cast<size_t>(e) * N : nullptr;
     float hv[SM][NG][4];
@@ -534,7 +556,7 @@ constexpr int big_tile_lds() {
 // One M-tile x n-tile: WM x (8 / WM) waves, each SM 16-row sub-tiles by BN / (8 / WM)
 // columns; SA / SB ring slots.  FP4 (with MX): MXFP4 weights in the tiled storage; a
 // B-ring slot is BN / 16 weight tiles of 1 KB, each fetched whole by one load.
-template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX, bool FP4 = false>
+template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX, bool FP4 = false, bool RAW = false>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile mt, uint8_t* lds) {
   constexpr int WAVES = 8, NT = WAVES * 64, WN = WAVES / WM, BM = 16 * SM * WM;
   constexpr int WR = 16 * SM, WC = BN / WN;          // rows / columns of a wave
@@ -875,6 +897,21 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // ---- epilogue: lane holds rows r(m) = wm*WR + 16m + (lane & 15) and, per sub-tile n,
   // the four adjacent columns 16n + 4 (lane >> 4) + i of its column range ----
   const int cq = 4 * (lane >> 4);
+  if constexpr (RAW) {   // the fp32 accumulators, at the B rows' global columns of C [rows, N]
+#pragma unroll
+    for (int n = 0; n < SN; ++n) {
+      const int g = b_global_row(sub_brow(n) + cq);   // four consecutive rows: all or none
+      if (g < 0) continue;
+#pragma unroll
+      for (int m = 0; m < SM; ++m) {
+        const int p = mt.row_begin + wm * WR + 16 * m + (lane & 15);
+        if (p < mt.row_end)
+          *reinterpret_cast<float4*>(a.c_raw + static_cast<size_t>(p) * N + g) =
+              make_float4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
+      }
+    }
+    return;
+  }
   if constexpr (SWIGLU) {
     const int KBI = ceil_div(I, kBlock);
     float hv[SM][NG][4];
@@ -1014,7 +1051,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
 // activation rows and weight tiles in their L2; a workgroup whose XCD's queue is empty
 // takes from the other XCDs' queues.  Every queue head only grows, so every workgroup
 // leaves after at most total + 8 of its fetches.
-template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN, bool MX = false, bool FP4 = false>
+template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN, bool MX = false, bool FP4 = false,
+          bool RAW = false>
 __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int ntiles) {
   constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB, FP4>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN, FP4>();
   __shared__ __align__(16) uint8_t lds[kFull > kNarrow ? kFull : kNarrow];
@@ -1036,9 +1074,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
       MTile mt;
       tile_of(a, ntiles, lo + t, nt, mt);
       if (mt.row_end - mt.row_begin <= 64) {
-        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4>(a, nt, mt, lds);
+        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4, RAW>(a, nt, mt, lds);
       } else {
-        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4>(a, nt, mt, lds);
+        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4, RAW>(a, nt, mt, lds);
       }
     }
   }
@@ -1075,7 +1113,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
 // slower.  The matrix cores take an e2m1 first operand, whose lane (r, g) holds the 32
 // consecutive K values [32 g, 32 g + 32) of row r in 16 bytes (element 2j in the low
 // nibble), against the e4m3 activation fragment.
-template <bool SWIGLU, int KS, bool MX = false, bool FP4 = false, int NW = 8>
+template <bool SWIGLU, int KS, bool MX = false, bool FP4 = false, int NW = 8, bool RAW = false>
 __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs a, int ntiles) {
   static_assert(MX || !FP4, "MXFP4 weights take E8M0 scales");
   // NW = 2 (MX only: h blocks of 32 columns are wave pairs; the block-scaled 1x128 groups
@@ -1267,6 +1305,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
   // ---- epilogue: lane holds row r and the four columns c0 + 4g + i ----
   const int p = mt.row_begin + r;
   const int cq = c0 + 4 * g;
+  if constexpr (RAW) {   // the fp32 accumulators (gate columns, then up columns I + ...)
+    if (!live || p >= mt.row_end) return;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+      *reinterpret_cast<float4*>(a.c_raw + static_cast<size_t>(p) * N + (s == 1 ? I : 0) + cq) =
+          make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
+    return;
+  }
   const uint16_t* bias = a.bias ? a.bias + static_cast<size_t>(e) * N : nullptr;
   if constexpr (SWIGLU) {
     const int KBI = ceil_div(I, kBlock);
@@ -1370,121 +1416,159 @@ int gemm_tile_rows(long rows, int E) {
   return 256;
 }
 
-// Returns false if no kernel could take the launch (an MXFP8 decode launch whose LDS
-// opt-in failed); the caller reports an error.
-template <bool SWIGLU>
-static bool launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
+// Large dynamic LDS (above 64 KB) must be opted into per kernel; the row-run kernels stage
+// up to 64 K-blocks of their 16-row activation tile.
+template <bool SWIGLU, int KS, bool MX, bool FP4, int NW, bool RAW>
+static bool rowrun_lds_ok(size_t lds) {
+  if (lds <= 64 * 1024) return true;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, KS, MX, FP4, NW, RAW>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
+}
+
+static size_t rowrun_lds(int K) {
+  const int KB = ceil_div(K, kBlock);
+  return static_cast<size_t>(KB) * 2048 + ceil_div(KB, 4) * 256 + 8 * 16 * 4;
+}
+
+// Which kernel family takes a launch of bm-row M-tiles over K (the order of the tests in
+// launch_gemm below).
+enum class Family { kBig, kBigFp4, kRowrunFp4, kRowrun, kRing, kNone };
+
+static Family family(bool mx, bool fp4, int K, int bm) {
+  const int KB = ceil_div(K, kBlock);
+  if (fp4) return bm == 256 ? Family::kBigFp4 : (bm == 16 && KB <= 64) ? Family::kRowrunFp4 : Family::kNone;
+  if (bm == 256 || (mx && bm != 16)) return Family::kBig;
+  if (bm == 16 && K % kBlock != 0 && KB <= 64) return Family::kRowrun;
+  return mx ? Family::kNone : Family::kRing;
+}
+
+template <bool SWIGLU, bool RAW>
+static bool prepare(bool mx, bool fp4, int K, int bm) {
+  constexpr int KS = 4;
+  const size_t lds = rowrun_lds(K);
+  switch (family(mx, fp4, K, bm)) {
+    case Family::kNone:
+      return false;
+    case Family::kRowrunFp4:
+      return rowrun_lds_ok<SWIGLU, 4, true, true, 8, RAW>(lds) && rowrun_lds_ok<SWIGLU, 4, true, true, 2, RAW>(lds);
+    case Family::kRowrun:
+      // block-scaled: without the opt-in the LDS-ring kernel takes the launch instead
+      return mx ? rowrun_lds_ok<SWIGLU, KS, true, false, 8, RAW>(lds)
+                : (rowrun_lds_ok<SWIGLU, KS, false, false, 8, RAW>(lds), true);
+    default:
+      return true;
+  }
+}
+
+bool gemm_prepare(bool swiglu, bool mx, bool fp4, int K, int bm, bool raw) {
+  if (raw) return swiglu ? prepare<true, true>(mx, fp4, K, bm) : prepare<false, true>(mx, fp4, K, bm);
+  return swiglu ? prepare<true, false>(mx, fp4, K, bm) : prepare<false, false>(mx, fp4, K, bm);
+}
+
+// Enqueues one grouped GEMM; gemm_prepare has accepted (mx, fp4, K, bm) on this device.
+template <bool SWIGLU, bool RAW>
+static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
   // decode-sized groups stream weights: gemm2 takes 128-column tiles there, twice as many
   // workgroups over the same bytes, so the last round of tiles is not half empty
   const int bn = (!SWIGLU && bm == 16) ? 128 : 256;
   const int ntiles = SWIGLU ? ceil_div(a.I, 128) : ceil_div(a.N, bn);
   const long total = static_cast<long>(max_tiles) * ntiles;
   const int grid = static_cast<int>((total + 7) / 8 * 8);
-  // MXFP4 weights: decode-sized groups on the row-run kernel (16-row tiles), larger ones
-  // on the large-group kernel (256-row tiles)
-  if (a.fp4 && bm == 256) {
-    const int nt_big = SWIGLU ? ceil_div(a.I, kF4BN / 2) : ceil_div(a.N, kF4BN);
-    const long tot = static_cast<long>(max_tiles) * nt_big;
-    const long cus = device_cus();
-    const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
-    grouped_gemm_big_kernel<SWIGLU, kF4BN, SWIGLU ? kF4SA1 : kF4SA2, kF4SB, kNarrowS, kNarrowS, true, true>
-        <<<g, 512, 0, st>>>(a, nt_big);
-    return true;
-  }
-  if (a.fp4) {
-    const int KB4 = ceil_div(a.K, kBlock);
-    if (bm != 16 || KB4 > 64) return false;
-    const int cols = SWIGLU ? a.I : a.N;
-    const size_t lds = static_cast<size_t>(KB4) * 2048 + ceil_div(KB4, 4) * 256 + 8 * 16 * 4;
-    // fewer 128-column workgroups than CUs (a few experts of a few tokens): 32-column ones
-    const bool narrow = static_cast<long>(max_tiles) * ceil_div(cols, 128) < device_cus() / 2;
-    // (gemm1 still covers whole 128-column groups: the idle waves past I write the pad
-    // codes 127 of h's last scale word)
-    const int nts = !narrow ? ceil_div(cols, 128) : SWIGLU ? 4 * ceil_div(cols, 128) : ceil_div(cols, 32);
-    const int g = static_cast<int>((static_cast<long>(max_tiles) * nts + 7) / 8 * 8);
-    static const bool lds_ok4 =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
-    static const bool lds_ok4n =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true, 2>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
-    if (lds > 64 * 1024 && !(narrow ? lds_ok4n : lds_ok4)) return false;
-    if (narrow)
-      grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true, 2><<<g, 128, lds, st>>>(a, nts);
-    else
-      grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true><<<g, 512, lds, st>>>(a, nts);
-    return true;
-  }
-  // MXFP8 layers take the large-group kernel unless their tiles are decode-sized rows of
-  // the row-run kernel below (the plan picks 256-row tiles otherwise)
-  if (bm == 256 || (a.mx && bm != 16)) {
-    constexpr int BN = SWIGLU ? kG1BN : kG2BN;
-    const int nt_big = SWIGLU ? ceil_div(a.I, BN / 2) : ceil_div(a.N, BN);
-    const long tot = static_cast<long>(max_tiles) * nt_big;
-    // persistent: one workgroup per CU (a multiple of the queue count), at most one per tile
-    const long cus = device_cus();
-    const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
-    if (a.mx) {
-      if constexpr (SWIGLU)
-        grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, true><<<g, 512, 0, st>>>(a, nt_big);
+  const long cus = device_cus();
+  switch (family(a.mx, a.fp4, a.K, bm)) {
+    case Family::kNone:
+      return;
+    case Family::kBigFp4: {
+      // MXFP4 weights, large groups: 256-row tiles, persistent (one workgroup per CU)
+      const int nt_big = SWIGLU ? ceil_div(a.I, kF4BN / 2) : ceil_div(a.N, kF4BN);
+      const long tot = static_cast<long>(max_tiles) * nt_big;
+      const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
+      grouped_gemm_big_kernel<SWIGLU, kF4BN, SWIGLU ? kF4SA1 : kF4SA2, kF4SB, kNarrowS, kNarrowS, true, true, RAW>
+          <<<g, 512, 0, st>>>(a, nt_big);
+      return;
+    }
+    case Family::kRowrunFp4: {
+      const int cols = SWIGLU ? a.I : a.N;
+      const size_t lds = rowrun_lds(a.K);
+      // fewer 128-column workgroups than half the CUs (a few experts of a few tokens):
+      // 32-column ones (gemm1 still covers whole 128-column groups: the idle waves past I
+      // write the pad codes 127 of h's last scale word)
+      const bool narrow = static_cast<long>(max_tiles) * ceil_div(cols, 128) < cus / 2;
+      const int nts = !narrow ? ceil_div(cols, 128) : SWIGLU ? 4 * ceil_div(cols, 128) : ceil_div(cols, 32);
+      const int g = static_cast<int>((static_cast<long>(max_tiles) * nts + 7) / 8 * 8);
+      if (narrow)
+        grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true, 2, RAW><<<g, 128, lds, st>>>(a, nts);
       else
-        grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS, true><<<g, 512, 0, st>>>(a, nt_big);
-    } else if constexpr (SWIGLU) {
-      grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS><<<g, 512, 0, st>>>(a, nt_big);
-    } else {
-      grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS><<<g, 512, 0, st>>>(a, nt_big);
+        grouped_gemm_rowrun_kernel<SWIGLU, 4, true, true, 8, RAW><<<g, 512, lds, st>>>(a, nts);
+      return;
     }
-    return true;
+    case Family::kBig: {
+      constexpr int BN = SWIGLU ? kG1BN : kG2BN;
+      const int nt_big = SWIGLU ? ceil_div(a.I, BN / 2) : ceil_div(a.N, BN);
+      const long tot = static_cast<long>(max_tiles) * nt_big;
+      // persistent: one workgroup per CU (a multiple of the queue count), at most one per tile
+      const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
+      if (a.mx) {
+        if constexpr (SWIGLU)
+          grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, true, false, RAW><<<g, 512, 0, st>>>(a, nt_big);
+        else
+          grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS, true, false, RAW><<<g, 512, 0, st>>>(a, nt_big);
+      } else if constexpr (SWIGLU) {
+        grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, false, false, RAW><<<g, 512, 0, st>>>(a, nt_big);
+      } else {
+        grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS, false, false, RAW><<<g, 512, 0, st>>>(a, nt_big);
+      }
+      return;
+    }
+    case Family::kRowrun: {
+      // Decode-sized groups whose weight rows are not whole 128-byte lines (K = 64 mod 128,
+      // so every other row starts mid-line and each 128-byte block of it spans two lines):
+      // the row-run kernel, which fetches 64-byte pieces (always within one line) in long
+      // per-row runs.  Rows that are whole lines stream faster through the LDS ring below.
+      constexpr int KS = 4;
+      const int nts = ceil_div(SWIGLU ? a.I : a.N, 128);
+      const int g = static_cast<int>((static_cast<long>(max_tiles) * nts + 7) / 8 * 8);
+      const size_t lds = rowrun_lds(a.K);
+      if (a.mx) {
+        grouped_gemm_rowrun_kernel<SWIGLU, KS, true, false, 8, RAW><<<g, 512, lds, st>>>(a, nts);
+        return;
+      }
+      if (rowrun_lds_ok<SWIGLU, KS, false, false, 8, RAW>(lds)) {
+        grouped_gemm_rowrun_kernel<SWIGLU, KS, false, false, 8, RAW><<<g, 512, lds, st>>>(a, nts);
+        return;
+      }
+      break;   // no large-LDS opt-in: the LDS-ring kernel
+    }
+    case Family::kRing:
+      break;
   }
-  // Decode-sized groups whose weight rows are not whole 128-byte lines (K = 64 mod 128,
-  // so every other row starts mid-line and each 128-byte block of it spans two lines):
-  // the row-run kernel, which fetches 64-byte pieces (always within one line) in long
-  // per-row runs.  Rows that are whole lines stream faster through the LDS ring below.
-  const int KB = ceil_div(a.K, kBlock);
-  if (bm == 16 && a.K % kBlock != 0 && KB <= 64) {
-    constexpr int KS = 4;
-    const int nts = ceil_div(SWIGLU ? a.I : a.N, 128);
-    const int g = static_cast<int>((static_cast<long>(max_tiles) * nts + 7) / 8 * 8);
-    const size_t lds = static_cast<size_t>(KB) * 2048 + ceil_div(KB, 4) * 256 + 8 * 16 * 4;
-    // above 64 KB of dynamic LDS a kernel must opt in (once per process)
-    static const bool lds_ok =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, KS>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
-    static const bool lds_ok_mx =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, KS, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
-    if (a.mx && (lds <= 64 * 1024 || lds_ok_mx)) {
-      grouped_gemm_rowrun_kernel<SWIGLU, KS, true><<<g, 512, lds, st>>>(a, nts);
-      return true;
-    }
-    if (!a.mx && (lds <= 64 * 1024 || lds_ok)) {
-      grouped_gemm_rowrun_kernel<SWIGLU, KS><<<g, 512, lds, st>>>(a, nts);
-      return true;
-    }
-  }
-  if (a.mx) return false;   // the plan gives MXFP8 16-row tiles only for the row-run kernel
   switch (bm) {
     case 16:
       if constexpr (SWIGLU)
-        grouped_gemm_kernel<16, 256, 1, 4, true, 4><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+        grouped_gemm_kernel<16, 256, 1, 4, true, 4, RAW><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
       else
-        grouped_gemm_kernel<16, 128, 1, 4, false, 4><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+        grouped_gemm_kernel<16, 128, 1, 4, false, 4, RAW><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
       break;
     case 64:
-      grouped_gemm_kernel<64, 256, 1, 4, SWIGLU, 3><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+      grouped_gemm_kernel<64, 256, 1, 4, SWIGLU, 3, RAW><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
       break;
     default:
-      grouped_gemm_kernel<128, 256, 2, 2, SWIGLU, 3><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
+      grouped_gemm_kernel<128, 256, 2, 2, SWIGLU, 3, RAW><<<grid, 256, 0, st>>>(a, max_tiles, ntiles, grid);
       break;
   }
-  return true;
 }
 
-bool launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
-  return launch_gemm<true>(a, bm, max_tiles, st);
+void launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
+  launch_gemm<true, false>(a, bm, max_tiles, st);
 }
-bool launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
-  return launch_gemm<false>(a, bm, max_tiles, st);
+void launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
+  launch_gemm<false, false>(a, bm, max_tiles, st);
+}
+void launch_gemm_raw(bool gemm1, const GemmArgs& a, int bm, int max_tiles, hipStream_t st) {
+  if (gemm1)
+    launch_gemm<true, true>(a, bm, max_tiles, st);
+  else
+    launch_gemm<false, true>(a, bm, max_tiles, st);
 }
 
 }  // namespace moe

@@ -103,13 +103,22 @@ struct GemmArgs {
   // K-step in dispatch order, [ceil(K/128)][sd_rows]; NULL: read A_scale / A_mx
   const uint32_t* A_sd;
   int sd_rows;
+  float* c_raw;              // launch_gemm_raw only: [rows, N] fp32 accumulators
 };
 
 // Rows per M-tile chosen for a layer with `rows` routed rows over E experts.
 int gemm_tile_rows(long rows, int E);
-// false: nothing was launched (see launch_gemm)
-bool launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
-bool launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
+// Whether a kernel takes GEMM1 (swiglu) or GEMM2 launches of bm-row M-tiles over K in this
+// format, with any large-LDS opt-in it needs done (a host-side call that enqueues nothing);
+// launch_gemm1/2 may only be called for accepted launches.
+// raw: the test-only variants that store the fp32 accumulators (launch_gemm_raw).
+bool gemm_prepare(bool swiglu, bool mx, bool fp4, int K, int bm, bool raw = false);
+void launch_gemm1(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
+void launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
+// The same kernels with the epilogue replaced by a store of the fp32 accumulators (no
+// bias, SwiGLU or quantisation) into a.c_raw [rows, N] at each B row's matrix row: gemm1
+// gate rows j at column j, up rows I + j at column I + j.  Test infrastructure only.
+void launch_gemm_raw(bool gemm1, const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
 
 // ---- combine ----
 void launch_combine(const uint16_t* y, const float* gates, const int32_t* inv, int T, int H,

@@ -28,12 +28,16 @@ struct Plan {
   size_t total;
 };
 
+// The GEMMs address their operands with 32-bit byte offsets from a 64-bit base: row x K
+// inside A (x codes [T, H] for GEMM1, h codes [T k, I] for GEMM2) and inside one expert's
+// weight matrix (w13 [2I, H], w2 [H, I]).  Every such product must stay below 2^31.
 bool shape_ok(int T, int H, int E, int k, int I) {
   if (T < 1 || E < 1 || E > 256 || k < 1 || k > 8 || k > E) return false;
   if (H < 64 || H % 64 != 0 || I < 64 || I % 64 != 0) return false;
   const long rows = static_cast<long>(T) * k;
   if (rows >= (1L << 31) || static_cast<long>(T) * H >= (1L << 31)) return false;
-  if (rows * H >= (1L << 40) || rows * I >= (1L << 40)) return false;
+  if (rows * I >= (1L << 31) || 2L * I * H >= (1L << 31)) return false;
+  if (rows * H >= (1L << 40)) return false;
   return true;
 }
 
@@ -196,6 +200,11 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   // the row-run kernel stages a 16-row activation tile of all of K in LDS
   if (fmt == kMxfp4 && p.bm == 16 && (H > 8192 || I > 8192)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  // which GEMM kernels take this plan (and their large-LDS opt-in), decided before
+  // anything is enqueued
+  if (!moe::gemm_prepare(true, mx, fmt == kMxfp4, H, p.bm) ||
+      !moe::gemm_prepare(false, mx, fmt == kMxfp4, I, p.bm))
+    return MOE_ERR_UNSUPPORTED_SHAPE;
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* ws = workspace;
@@ -207,7 +216,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
                                  at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
                                  at<int32_t>(ws, p.perm), at<int32_t>(ws, p.inv)};
   enqueue_routing(p, x, router_w, router_b, tb, ws, st, ev, /*quant_x=*/true, mx);
-  mark(ev, 4, st);   // (the activation quantisation ran inside the router kernel)
+  mark(ev, 4, st);   // (the x quantisation ran inside the router kernel; stage 4: scale regrouping)
   // large-group GEMM1: the x scale words of the routed rows in dispatch order, K-block
   // major, staged in the y region (written only later, by GEMM2)
   const bool gather_sx = p.bm == 256;
@@ -247,7 +256,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
     g1.A_sd = at<uint32_t>(ws, p.y);
     g1.sd_rows = static_cast<int>(p.rows);
   }
-  if (!moe::launch_gemm1(g1, p.bm, p.max_tiles, st)) return MOE_ERR_HIP;
+  moe::launch_gemm1(g1, p.bm, p.max_tiles, st);
   mark(ev, 6, st);
 
   moe::GemmArgs g2{};
@@ -281,7 +290,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
     g2.A_sd = at<uint32_t>(ws, p.shd);
     g2.sd_rows = static_cast<int>(p.rows);
   }
-  if (!moe::launch_gemm2(g2, p.bm, p.max_tiles, st)) return MOE_ERR_HIP;
+  moe::launch_gemm2(g2, p.bm, p.max_tiles, st);
   mark(ev, 7, st);
   moe::launch_combine(at<uint16_t>(ws, p.y), tb.gates, tb.inv, T, H, top_k, out, st);
   mark(ev, 8, st);

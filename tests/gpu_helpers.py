@@ -1,5 +1,20 @@
-"""Shared helpers of the GPU parity tests: upload a synthetic layer, build the oracle's
-own quantised weights for the experts a check needs, and compare outputs."""
+"""Shared helpers of the GPU parity tests.
+
+A layer on the GPU is checked against the oracle in two halves that meet at h, the one
+intermediate with several correct values (an fp32 evaluation may put an h value on the
+other side of an e4m3 rounding boundary than the exact value):
+
+1. routing tables bit-exact, gates within the fp32 bound, x codes and scales bit-exact,
+   the GPU's weight codes and scales equal to the oracle quantiser's;
+2. every GPU h code and scale of the checked rows inside the analytic window of
+   ``windows.py`` (derived from the oracle's exact GEMM1 and its sum of |x w|, never
+   from the device);
+3. the oracle's GEMM2 + b2 evaluated in float64 on the GPU's own h codes and scales
+   ("oracle(GPU h)"): the GPU's y within the fp32-accumulation + fp16-storage bound, and
+   the GPU's out within the literal tolerance max(2e-2 RMS(oracle out), one bf16 ulp)
+   of sum_j g_j y_j, and within the analytic combine bound;
+4. the GPU's out against the plain oracle (its own h): relative Frobenius <= 5e-3.
+"""
 from __future__ import annotations
 
 import sys
@@ -11,16 +26,12 @@ import torch
 import sparse_moe_ffn_gemm_amd as moe
 from oracle import moe_ref as R
 from synth import LayerShape, expert_weights, make_inputs
+import windows as W
+from layouts import untile_fp4, untile_scales
 
 REL_FRO_TOL = 5e-3
 MAX_ELT_TOL = 2e-2
 GATE_TOL = 1e-6
-# Device error of h relative to its 1x128 group maximum.  Each K=128 FP8 matrix-core
-# dot product on gfx950 carries up to ~6e-5 of the tile maximum (measured with random
-# codes; every single product is exact); over up to 56 promoted K-blocks that stays below
-# 2^-13.  Every code that a quotient within that distance (times 448 code units) of the
-# oracle's h / s rounds to is a correct code; near zero that window spans several codes.
-H_EPS = 2.0 ** -13
 
 
 def say(*a):
@@ -54,6 +65,21 @@ class GpuLayer:
             lambda e: expert_weights(shape, "w2", e, device), device=device, fmt=fmt)
         torch.cuda.synchronize()
 
+    def run(self):
+        s = self.shape
+        routing = moe.new_routing(s.T, s.E, s.top_k)
+        say(f"forward [{self.fmt}] {s.name}: T={s.T} H={s.H} E={s.E} k={s.top_k} I={s.I}")
+        out = self.layer(self.x, routing=routing)
+        torch.cuda.synchronize()
+        return out, routing
+
+    def ws_view(self, region: str, dtype, shape) -> torch.Tensor:
+        s = self.shape
+        r = moe.workspace_layout(s.T, s.H, s.E, s.top_k, s.I)
+        off = getattr(r, region)
+        nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        return self.layer.workspace(s.T)[off:off + nbytes].view(dtype).view(*shape)
+
 
 def quantize_by_rows(quant, w: np.ndarray, rows: int = 128):
     """The oracle's weight quantiser applied to 128-row slices of w (every format's scale
@@ -63,9 +89,14 @@ def quantize_by_rows(quant, w: np.ndarray, rows: int = 128):
     return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
+def _base(shape):
+    from synth.cases import _base_shape
+    return _base_shape(shape)
+
+
 class OracleExperts:
-    """Lazily quantised experts for the oracle (from the generator's fp32 weights), in the
-    block-scaled, the MXFP8 or the MXFP4-weight format."""
+    """Lazily quantised experts for the oracle (from the generator's fp32 weights, by the
+    oracle's own quantiser), in the block-scaled, the MXFP8 or the MXFP4-weight format."""
 
     def __init__(self, shape: LayerShape, li, fmt="block"):
         self.shape, self.li = shape, li
@@ -75,21 +106,23 @@ class OracleExperts:
 
     def prepare(self, experts, threads=16):
         todo = [int(e) for e in experts if int(e) not in self.cache]
-        # draw on the device serially, quantise on the host in parallel
-        host = {e: (expert_weights(self.shape, "w13", e, self.dev).cpu().numpy(),
-                    expert_weights(self.shape, "w2", e, self.dev).cpu().numpy()) for e in todo}
-
         quant = {"block": R.quantize_blocks, "mxfp8": R.quantize_mx,
                  "mxfp4": R.quantize_mxfp4}[self.fmt]
 
-        def q(e):
-            c13, s13 = quantize_by_rows(quant, host[e][0])
-            c2, s2 = quantize_by_rows(quant, host[e][1])
+        def q(item):
+            e, (w13, w2) = item
+            c13, s13 = quantize_by_rows(quant, w13)
+            c2, s2 = quantize_by_rows(quant, w2)
             return e, (c13, s13, c2, s2)
 
-        with ThreadPoolExecutor(max_workers=threads) as ex:
-            for e, v in ex.map(q, todo):
-                self.cache[e] = v
+        # draw on the device serially (a few experts at a time), quantise on the host in parallel
+        for i in range(0, len(todo), 32):
+            host = {e: (expert_weights(self.shape, "w13", e, self.dev).cpu().numpy(),
+                        expert_weights(self.shape, "w2", e, self.dev).cpu().numpy())
+                    for e in todo[i:i + 32]}
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                for e, v in ex.map(q, host.items()):
+                    self.cache[e] = v
 
     def view(self, idx):
         cache = self.cache
@@ -99,150 +132,15 @@ class OracleExperts:
                 return cache[int(e)][idx]
         return _V()
 
-    def forward(self, token_subset=None):
-        li = self.li
-        ids = R.topk_softmax(R.router_logits(li.x, li.router_w, li.router_b), self.shape.top_k)[0]
-        need = np.unique(ids if token_subset is None else ids[np.asarray(token_subset)])
-        self.prepare(need)
-        ref = R.forward(li.x, li.router_w, li.router_b, self.shape.top_k, self.shape.I,
-                        self.view(0), self.view(1), li.b13, self.view(2), self.view(3), li.b2,
-                        token_subset=token_subset, fmt=self.fmt)
-        ref["allowance"] = self.flip_allowance(ref)
-        return ref
-
     def dequant_w(self, codes, scales):
         deq = {"block": R.dequantize_blocks, "mxfp8": R.dequantize_mx,
                "mxfp4": R.dequantize_mxfp4}[self.fmt]
         return deq(codes, scales)
 
-    def flip_allowance(self, ref):
-        """Per output element of the evaluated tokens: sum_j g_j * |W2_j| . flip_delta(h_j)."""
-        li, k, I = self.li, self.shape.top_k, self.shape.I
-        toks = ref["tokens"]
-        x32 = R.bf16_to_f64(li.x[toks]).astype(np.float32)
-        if self.fmt != "block":                 # MXFP8 activations
-            xd = R.dequantize_mx(*R.quantize_mx(x32))
-        else:
-            xq, sx = R.quantize_activations(x32)
-            xd = R.dequantize_blocks(xq, sx, rows=1)
-        allow = np.zeros((toks.size, li.x.shape[1]))
-        for e in np.unique(ref["ids"][toks]):
-            rt, rj = np.nonzero(ref["ids"][toks] == e)
-            c13, s13, c2, s2 = self.cache[int(e)]
-            _, hq, hs, h64 = R.expert_ffn(xd[rt], c13, s13, li.b13[e], c2, s2, li.b2[e], I,
-                                          self.fmt)
-            W2 = np.abs(self.dequant_w(c2, s2))
-            delta = flip_delta(h64, hq, hs) if self.fmt == "block" else flip_delta_mx(h64, hq, hs)
-            allow[rt] += ref["gates"][toks[rt], rj][:, None] * (delta @ W2.T)
-        return allow
-
-
-def dispatched_allowance(ref, experts: "OracleExperts", T: int, k: int):
-    """flip allowance for a full dispatched oracle result (all tokens)."""
-    rows = ref["h"].shape[0]
-    contrib = np.zeros((rows, ref["y"].shape[1]))
-    delta = flip_delta(ref["h"], ref["hq"], ref["hs"])
-    for e in range(len(ref["counts"])):
-        p0, p1 = ref["offsets"][e], ref["offsets"][e + 1]
-        if p1 > p0:
-            c2, s2 = experts.cache[e][2], experts.cache[e][3]
-            contrib[p0:p1] = delta[p0:p1] @ np.abs(R.dequantize_blocks(c2, s2)).T
-    return R.combine(contrib, ref["gates"], ref["inv"], T, k)
-
-
-def _base(shape):
-    from synth.cases import _base_shape
-    return _base_shape(shape)
-
 
 def bf16_ulp(ref: np.ndarray) -> np.ndarray:
     a = np.maximum(np.abs(ref), 2.0 ** -126)
     return np.ldexp(1.0, np.floor(np.log2(a)).astype(int) - 7)
-
-
-def _h_window(h64: np.ndarray, hs: np.ndarray):
-    """Decoded values of the lowest and highest codes that a quotient within H_EPS * 448 code
-    units of the oracle's h / s can round to (the codes a correct kernel may produce given its
-    fp32 accumulation error), and the per-element scale."""
-    I = h64.shape[1]
-    s = np.repeat(hs.astype(np.float64), 128, axis=1)[:, :I]
-    v = h64 / s
-    eps = H_EPS * 448
-    return R.e4m3_decode(R.e4m3_encode(v - eps)), R.e4m3_decode(R.e4m3_encode(v + eps)), s
-
-
-def flip_delta(h64: np.ndarray, hq: np.ndarray, hs: np.ndarray) -> np.ndarray:
-    """For oracle h rows: the largest value change between the oracle's code and any code of
-    the window ``_h_window`` (0 where the window holds only the oracle's code).  Near zero the
-    window can span several codes, since the e4m3 spacing there is much finer than the
-    accumulation error, which scales with the group's largest value.  Uses the oracle's own
-    h, codes and scales only."""
-    lo, hi, s = _h_window(h64, hs)
-    dq = R.e4m3_decode(hq)
-    return np.maximum(np.abs(lo - dq), np.abs(hi - dq)) * s
-
-
-def _group128_max(h64: np.ndarray) -> np.ndarray:
-    """max |h| over each element's 1x128 column group (the scale of the device's fp32
-    accumulation error in h, whatever the quantisation format)."""
-    I = h64.shape[1]
-    g = -(-I // 128)
-    pad = np.zeros((h64.shape[0], g * 128))
-    pad[:, :I] = np.abs(h64)
-    return np.repeat(pad.reshape(-1, g, 128).max(axis=2), 128, axis=1)[:, :I]
-
-
-def flip_delta_mx(h64: np.ndarray, hq: np.ndarray, hs: np.ndarray) -> np.ndarray:
-    """``flip_delta`` for MXFP8 h (1x32 blocks, E8M0 codes ``hs`` [rows, I/32]): the device's
-    h may differ from the oracle's by H_EPS of its 1x128 group maximum; every code a value
-    within that distance rounds to at the oracle's block scale is correct, and where the
-    block maximum itself lies within that distance of a power of two the device may take
-    the neighbouring exponent, so the codes of the block at that scale count too."""
-    I = h64.shape[1]
-    eps = H_EPS * _group128_max(h64)
-    X = np.repeat(hs.astype(np.int64) - 127, 32, axis=1)[:, :I]
-    dq = R.e4m3_decode(hq) * np.ldexp(1.0, X)
-    out = np.zeros_like(h64)
-    for dx in (0, -1, 1):
-        s = np.ldexp(1.0, X + dx)
-        lo = R.e4m3_decode(R.e4m3_encode(((h64 - eps) / s).astype(np.float32))) * s
-        hi = R.e4m3_decode(R.e4m3_encode(((h64 + eps) / s).astype(np.float32))) * s
-        d = np.maximum(np.abs(lo - dq), np.abs(hi - dq))
-        if dx != 0:
-            # only blocks whose maximum is within eps of the power of two between the scales
-            amax = np.abs(h64).reshape(h64.shape[0], -1, 32).max(axis=2)
-            edge = np.ldexp(1.0, (hs.astype(np.int64) - 127) + 8 + (1 if dx > 0 else 0))
-            e_blk = eps.reshape(h64.shape[0], -1, 32).max(axis=2)
-            near = np.abs(amax - edge) <= e_blk
-            d = d * np.repeat(near, 32, axis=1)[:, :I]
-        out = np.maximum(out, d)
-    return out
-
-
-def compare_out(gpu_bits: np.ndarray, ref: np.ndarray, what="", allowance=None):
-    """Relative Frobenius <= 5e-3.  An element fails the max-elementwise bound only if its
-    error exceeds max(2e-2 * RMS(ref), one bf16 ulp of the reference value) -- the output
-    format cannot resolve less -- plus ``allowance``: the largest change that legitimate
-    h code changes within the accumulation window can cause (``flip_delta`` through |W2|,
-    gated).
-    The literal max |err| / RMS is always reported."""
-    g = R.bf16_to_f64(gpu_bits)
-    d = g - ref
-    rel = np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)
-    rms = np.sqrt(np.mean(ref * ref))
-    lit = np.abs(d).max() / rms if rms > 0 else 0.0
-    base = np.maximum(MAX_ELT_TOL * rms, bf16_ulp(ref))
-    over = np.abs(d) > base
-    bad = np.abs(d) > base + (0.0 if allowance is None else allowance)
-    floor = np.abs(R.bf16_to_f64(R.f64_to_bf16_bits(ref)) - ref).max() / rms if rms > 0 else 0.0
-    info = dict(rel_fro=rel, max_over_rms=lit, n_over_literal=int(over.sum()), n_bad=int(bad.sum()),
-                n=d.size, floor=floor)
-    say(f"  out parity {what}: rel_fro={rel:.3e} max/rms={lit:.3e} (bf16 floor {floor:.3e}) "
-        f"over 2e-2*RMS (and 1 ulp): {int(over.sum())}, beyond h-flip allowance: {int(bad.sum())}"
-        f" of {d.size}")
-    assert rel <= REL_FRO_TOL, info
-    assert not bad.any(), info
-    return info
 
 
 def gate_tolerance(ref_logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
@@ -258,7 +156,7 @@ def gate_tolerance(ref_logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
     return GATE_TOL + 4.0 * ulp
 
 
-def routing_exact(gpu: dict, ref: dict, T: int, k: int, what=""):
+def routing_exact(gpu: dict, ref: dict, what=""):
     ids = gpu["topk_ids"].cpu().numpy()
     assert np.array_equal(ids, ref["ids"]), f"{what}: ids differ at {np.argwhere(ids != ref['ids'])[:5]}"
     assert np.array_equal(gpu["expert_counts"].cpu().numpy(), ref["counts"]), what
@@ -273,23 +171,232 @@ def routing_exact(gpu: dict, ref: dict, T: int, k: int, what=""):
     assert np.all(err <= tol), np.argwhere(err > tol)[:5]
 
 
-def h_codes_close(gpu_hq: np.ndarray, ref: dict, max_frac=0.01):
-    """h codes may differ from the oracle's only within the window of ``_h_window`` (a
-    quotient within H_EPS * 448 code units of the oracle's), and at most ``max_frac`` of
-    them may differ."""
-    ref_hq = ref["hq"]
-    diff = gpu_hq != ref_hq
-    frac = diff.mean()
-    lo, hi, _ = _h_window(ref["h"], ref["hs"])
-    g = R.e4m3_decode(gpu_hq)
-    ok = (g >= lo) & (g <= hi)
-    say(f"  h: {int(diff.sum())} of {diff.size} codes differ ({frac:.2e}); "
-        f"all within the accumulation window: {bool(ok.all())}")
-    if not ok.all():
-        I = ref["h"].shape[1]
-        for rr, cc in np.argwhere(~ok)[:5]:
-            grp = slice((cc // 128) * 128, min((cc // 128 + 1) * 128, I))
-            gmax = np.abs(ref["h"][rr, grp]).max()
-            say(f"    row {rr} col {cc}: oracle code {ref_hq[rr, cc]:#04x} gpu {gpu_hq[rr, cc]:#04x} "
-                f"h={ref['h'][rr, cc]:.6g} group max {gmax:.6g} scale {ref['hs'][rr, cc // 128]:.6g}")
-    assert frac <= max_frac and ok.all()
+_E4M3_POS = np.sort(R.e4m3_decode(np.arange(0x7F)))
+
+
+def _codes_between(lo, hi):
+    """Number of e4m3 values in [lo, hi] (decoded bounds), zero counted once."""
+    n_hi = np.searchsorted(_E4M3_POS, np.abs(hi), side="right")
+    n_lo = np.searchsorted(_E4M3_POS, np.abs(lo), side="right")
+    same = np.sign(lo) * np.sign(hi) >= 0
+    return np.where(same, np.abs(n_hi - n_lo) + 1, n_hi + n_lo - 1)
+
+
+class LayerCheck:
+    """The checks of the module docstring for one forward of ``g`` (``out``, ``routing``)."""
+
+    def __init__(self, g: GpuLayer, out: torch.Tensor, routing: dict):
+        self.g, self.shape, self.fmt = g, g.shape, g.fmt
+        s, li = self.shape, g.li
+        self.T, self.H, self.E, self.k, self.I = s.T, s.H, s.E, s.top_k, s.I
+        self.rows = s.T * s.top_k
+        self.ox = OracleExperts(s, li, g.fmt)
+        self.q_act, self.dq_act, _ = R._quantizer(g.fmt)
+        self.out_bits = bits_host(out)
+        # routing (all tokens)
+        self.logits = R.router_logits(li.x, li.router_w, li.router_b)
+        self.ids, self.gates = R.topk_softmax(self.logits, s.top_k)
+        self.counts, self.offsets, self.perm, self.inv = R.permute(self.ids, s.E)
+        routing_exact(routing, dict(ids=self.ids, gates=self.gates, counts=self.counts,
+                                    offsets=self.offsets, perm=self.perm, inv=self.inv,
+                                    logits=self.logits), s.name)
+        self.gates_dev = routing["topk_gates"].cpu().numpy()
+        # x codes and scales, bit-exact (all tokens)
+        x32 = R.bf16_to_f64(li.x).astype(np.float32)
+        xq, sx = self.q_act(x32)
+        gxq = g.ws_view("xq", torch.uint8, (s.T, s.H)).cpu().numpy()
+        assert np.array_equal(gxq, xq), "x codes"
+        if g.fmt == "block":
+            gsx = g.ws_view("sx", torch.float32, (s.T, -(-s.H // 128))).cpu().numpy()
+            assert np.array_equal(gsx.view(np.uint32), sx.view(np.uint32)), "x scales"
+        else:
+            gsx = g.ws_view("sx", torch.uint8, (s.T, moe.mx_row(s.H))).cpu().numpy()
+            assert np.array_equal(gsx[:, :s.H // 32], sx) and np.all(gsx[:, s.H // 32:] == 127), "x scales"
+        self.xd = self.dq_act(xq, sx)
+        self.tok = self.perm // s.top_k
+        self.weights_checked = set()
+        self.rms = None
+
+    # ---- device data ----
+    def _rows(self, region, dtype, width, p):
+        v = self.g.ws_view(region, dtype, (self.rows, width))
+        return v[torch.as_tensor(np.asarray(p, np.int64), device=v.device)].cpu().numpy()
+
+    def gpu_h(self, p):
+        """(codes [n, I], scales: fp32 [n, ceil(I/128)] or E8M0 [n, I/32]) of dispatch rows p."""
+        I = self.I
+        hq = self._rows("h", torch.uint8, I, p)
+        if self.fmt == "block":
+            return hq, self._rows("sh", torch.float32, -(-I // 128), p)
+        hs = self._rows("sh", torch.uint8, moe.mx_row(I), p)
+        assert np.all(hs[:, I // 32:] == 127), "h scale pads"
+        return hq, hs[:, :I // 32]
+
+    def gpu_y(self, p):
+        return self._rows("y", torch.float16, self.H, p).astype(np.float64)
+
+    def h_dequant(self, hq, hs):
+        if self.fmt == "block":
+            return R.dequantize_blocks(hq, hs, rows=1)
+        return R.dequantize_mx(hq, hs)
+
+    def check_weights(self, e):
+        """The GPU's codes and scales of expert e equal the oracle quantiser's."""
+        if e in self.weights_checked:
+            return
+        L, (c13, s13, c2, s2) = self.g.layer, self.ox.cache[e]
+        H, I = self.H, self.I
+        if self.fmt == "block":
+            got = (L.w13[e].cpu().numpy(), L.w13_scales[e].cpu().numpy(), L.w2[e].cpu().numpy(),
+                   L.w2_scales[e].cpu().numpy())
+            for a, b in zip(got, (c13, s13, c2, s2)):
+                assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"expert {e} weights"
+        else:
+            def sc(t, N, K):
+                rows = untile_scales(t[e:e + 1].cpu().numpy(), N, K)[0]
+                assert np.all(rows[:, K // 32:] == 127)
+                return rows[:, :K // 32]
+            if self.fmt == "mxfp4":
+                w13 = untile_fp4(L.w13[e:e + 1].cpu().numpy(), 2 * I, H)[0][0]
+                w2 = untile_fp4(L.w2[e:e + 1].cpu().numpy(), H, I)[0][0]
+            else:
+                w13, w2 = L.w13[e].cpu().numpy(), L.w2[e].cpu().numpy()
+            assert np.array_equal(w13, c13) and np.array_equal(w2, c2), f"expert {e} codes"
+            assert np.array_equal(sc(L.w13_scales, 2 * I, H), s13), f"expert {e} w13 scales"
+            assert np.array_equal(sc(L.w2_scales, H, I), s2), f"expert {e} w2 scales"
+        self.weights_checked.add(e)
+
+    # ---- the two halves ----
+    def check_h(self, e, p, what=""):
+        """GPU h codes and scales of expert e's dispatch rows p inside the analytic window."""
+        self.ox.prepare([e])
+        self.check_weights(e)
+        c13, s13, _, _ = self.ox.cache[e]
+        W13 = self.ox.dequant_w(c13, s13)
+        C, C_abs, C_gmax = W.product_sums(self.xd[self.tok[p]], W13)
+        C += R.bf16_to_f64(self.g.li.b13[e])
+        del W13
+        h, dh = W.swiglu_window(C, C_abs, self.H, self.I, C_gmax)
+        del C, C_abs, C_gmax
+        hq, hs = self.gpu_h(p)
+        if self.fmt == "block":
+            sok, cok, diag = W.block_h_check(h, dh, hq, hs)
+        else:
+            sok, cok, diag = W.mx_h_check(h, dh, hq, hs)
+        oq, osc = self.q_act(h.astype(np.float32))
+        nd = int((hq != oq).sum())
+        width = np.mean(_codes_between(diag["lo"], diag["hi"]))
+        say(f"  h {what}expert {e} ({len(p)} rows): scales outside the window {int((~sok).sum())} "
+            f"of {sok.size}, codes outside {int((~cok).sum())} of {cok.size}; codes unlike the "
+            f"oracle's own {nd} ({nd / max(hq.size, 1):.1e}); admissible codes per element "
+            f"{width:.2f} on average")
+        if not (sok.all() and cok.all()):
+            for rr, cc in np.argwhere(~cok)[:5]:
+                say(f"    row {rr} col {cc}: gpu code {hq[rr, cc]:#04x} oracle {oq[rr, cc]:#04x} "
+                    f"h={h[rr, cc]:.6g} dh={dh[rr, cc]:.3g}")
+        assert sok.all() and cok.all()
+
+    def y_ref(self, e, p):
+        """oracle(GPU h): y_ref and its bound for expert e's dispatch rows p."""
+        self.ox.prepare([e])
+        self.check_weights(e)
+        _, _, c2, s2 = self.ox.cache[e]
+        W2 = self.ox.dequant_w(c2, s2)
+        y, y_abs, y_gmax = W.product_sums(self.h_dequant(*self.gpu_h(p)), W2)
+        y += R.bf16_to_f64(self.g.li.b2[e])
+        dy = W.y_bound(y, y_abs, self.I, y_gmax)
+        assert np.abs(y).max() < W.F16_MAX
+        return y, dy
+
+    def check_y(self, e, p, what=""):
+        y, dy = self.y_ref(e, p)
+        gy = self.gpu_y(p)
+        bad = np.abs(gy - y) > dy
+        say(f"  y {what}expert {e} ({len(p)} rows): max |err| / bound {np.max(np.abs(gy - y) / dy):.3f}, "
+            f"outside {int(bad.sum())} of {bad.size}")
+        assert not bad.any()
+
+    def check_experts(self, experts=None):
+        """h window and y bound on every dispatch row of the experts (all active ones by default)."""
+        experts = [e for e in (range(self.E) if experts is None else experts) if self.counts[e] > 0]
+        for e in experts:
+            p = np.arange(self.offsets[e], self.offsets[e + 1])
+            self.check_h(e, p)
+            self.check_y(e, p)
+
+    def check_tokens(self, toks=None, h_window=True):
+        """out of the tokens: oracle(GPU h) at the literal bound and the combine bound; the
+        plain oracle at rel. Frobenius <= 5e-3.  With h_window the tokens' h rows are
+        checked against the window too."""
+        T, k, H = self.T, self.k, self.H
+        toks = np.arange(T) if toks is None else np.asarray(toks)
+        flat = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+        p_all = self.inv[flat]
+        e_all = self.ids[toks].reshape(-1)
+        yr = np.zeros((toks.size * k, H))
+        dy = np.zeros((toks.size * k, H))
+        for e in np.unique(e_all):
+            sel = np.nonzero(e_all == e)[0]
+            p = p_all[sel]
+            if h_window:
+                self.check_h(int(e), p, "of the sampled tokens, " if toks.size < T else "")
+            yr[sel], dy[sel] = self.y_ref(int(e), p)
+        yr = yr.reshape(toks.size, k, H)
+        dy = dy.reshape(toks.size, k, H)
+        out2 = np.einsum("tk,tkh->th", self.gates[toks], yr)
+        got = R.bf16_to_f64(self.out_bits[toks])
+        # the plain oracle (its own h) on the same tokens
+        self.ox.prepare(np.unique(e_all))
+        ox = self.ox
+        ref = R.forward(self.g.li.x, self.g.li.router_w, self.g.li.router_b, k, self.I, ox.view(0),
+                        ox.view(1), self.g.li.b13, ox.view(2), ox.view(3), self.g.li.b2,
+                        token_subset=toks, fmt=self.fmt)
+        rms = np.sqrt(np.mean(ref["out"] ** 2))
+        d2 = np.abs(got - out2)
+        lit = np.maximum(MAX_ELT_TOL * rms, bf16_ulp(out2))
+        cb = W.combine_bound(self.gates[toks], self.gates_dev[toks], yr, dy, out2)
+        rel2 = np.linalg.norm(got - out2) / np.linalg.norm(out2)
+        rel = np.linalg.norm(got - ref["out"]) / np.linalg.norm(ref["out"])
+        lit_plain = np.abs(got - ref["out"]).max() / rms
+        say(f"  out ({toks.size} tokens): vs oracle(GPU h) max/RMS {d2.max() / rms:.3e}, over the literal "
+            f"bound {int((d2 > lit).sum())}, over the combine bound {int((d2 > cb).sum())}, rel_fro "
+            f"{rel2:.3e}; vs plain oracle rel_fro {rel:.3e} (max/RMS {lit_plain:.3e}) of {d2.size}")
+        assert not (d2 > lit).any()
+        assert not (d2 > cb).any()
+        assert rel2 <= REL_FRO_TOL and rel <= REL_FRO_TOL
+        return dict(rel_fro=rel, max_over_rms=d2.max() / rms, rel_fro_gpu_h=rel2)
+
+
+def pick_experts(counts, bm=256):
+    """Experts whose every row the prefill checks cover: one with a full 256-row tile and a
+    narrow overflow tile (256 < rows <= 320) if any, the hottest, and the least busy active
+    one."""
+    act = np.nonzero(counts > 0)[0]
+    pick = [int(act[np.argmax(counts[act])]), int(act[np.argmin(counts[act])])]
+    over = np.nonzero((counts > bm) & (counts <= bm + 64))[0]
+    if over.size:
+        pick.insert(0, int(over[0]))
+    return list(dict.fromkeys(pick))
+
+
+def check_all_rows(shape, fmt="block"):
+    """Every routed row's h and y and every token's out (small and decode-sized layers)."""
+    g = GpuLayer(shape, fmt=fmt)
+    out, routing = g.run()
+    chk = LayerCheck(g, out, routing)
+    chk.check_experts()
+    chk.check_tokens(h_window=False)
+
+
+def check_prefill(shape, fmt, n_sample, seed):
+    """A full-size layer: whole experts (pick_experts) and sampled tokens, the last included."""
+    g = GpuLayer(shape, fmt=fmt)
+    out, routing = g.run()
+    chk = LayerCheck(g, out, routing)
+    experts = pick_experts(chk.counts)
+    say(f"  whole experts {experts} with {[int(chk.counts[e]) for e in experts]} rows")
+    chk.check_experts(experts)
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(shape.T, size=n_sample, replace=False))
+    toks[-1] = shape.T - 1                                   # the last token (ragged tiles)
+    chk.check_tokens(toks)

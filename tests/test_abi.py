@@ -10,14 +10,18 @@ import pytest
 import sparse_moe_ffn_gemm_amd as moe
 from sparse_moe_ffn_gemm_amd import _lib
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 FAKE = 1 << 20          # an aligned non-null address; never dereferenced by these calls
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+    """Every function declared in include/*.h (the layer's API and the test-only export)."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, h)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -38,6 +42,10 @@ def test_status_strings():
 @pytest.mark.parametrize("shape,ok", [
     ((16, 256, 8, 2, 256), True), ((1, 64, 1, 1, 64), True), ((8192, 2880, 128, 4, 2880), True),
     ((16384, 7168, 256, 8, 2048), True), ((0, 256, 8, 2, 256), False), ((16, 250, 8, 2, 256), False),
+    # 32-bit GEMM offsets: T k I (the h rows GEMM2 reads) and 2 I H (one expert's w13) < 2^31
+    ((262144, 7168, 256, 8, 2048), False), ((131072, 7168, 256, 8, 2048), False),
+    ((131071, 7168, 256, 8, 2048), True), ((64, 65536, 8, 2, 16384), False),
+    ((64, 32768, 8, 2, 32704), True),
     ((16, 256, 8, 2, 100), False), ((16, 256, 300, 2, 256), False), ((16, 256, 8, 9, 256), False),
     ((16, 256, 4, 5, 256), False), ((16, 256, 8, 0, 256), False)])
 def test_workspace_bytes_envelope(shape, ok):
@@ -127,3 +135,39 @@ def test_mx_error_paths():
     # reach a launch either way here (its workspace is too small on purpose)
     assert _fwd_mx(L.moe_forward_mxfp4, T=4, H=8448, E=2, k=1, I=128) == -2
     assert _fwd_mx(L.moe_forward_mx, T=4, H=8448, E=2, k=1, I=128, wsb=16) == -3
+
+
+def test_forward_rejects_shapes_past_32bit_gemm_offsets():
+    """Shapes whose GEMM operand offsets would pass 2^31 bytes are refused before anything
+    is enqueued (MOE_ERR_UNSUPPORTED_SHAPE), by every forward entry point."""
+    L = moe.lib()
+    for fn in (L.moe_forward_mx, L.moe_forward_mxfp4):
+        assert _fwd_mx(fn, T=262144, H=7168, E=256, k=8, I=2048) == -2
+        assert _fwd_mx(fn, T=64, H=65536, E=8, k=2, I=16384) == -2
+    assert _fwd(L, T=262144, H=7168, E=256, k=8, I=2048) == -2
+    assert _fwd(L, T=64, H=65536, E=8, k=2, I=16384) == -2
+    r = _lib.Routing(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    # routing alone reads only x [T, H] and W: its envelope is T H < 2^31
+    assert L.moe_route(FAKE, FAKE, None, 262144, 8192, 256, 8, ctypes.byref(r), FAKE, 16, None) == -2
+
+
+def test_raw_gemm_export_error_paths():
+    """The test-only GEMM export validates its arguments on the host."""
+    L = moe.lib()
+    cnt = (ctypes.c_int32 * 2)(10, 20)
+    raw = lambda **kw: L.moe_test_gemm_raw(
+        kw.get("gemm", 2), kw.get("fmt", 0), kw.get("bm", 64), kw.get("A", FAKE), FAKE,
+        kw.get("A_rows", 30), kw.get("perm", None), 1, kw.get("cnt", cnt), 2, FAKE, FAKE,
+        kw.get("N", 128), kw.get("K", 128), FAKE, FAKE, kw.get("wsb", 1 << 30), None)
+    assert raw(gemm=3) == -1
+    assert raw(fmt=3) == -1
+    assert raw(A=None) == -1
+    assert raw(gemm=1) == -1                     # GEMM1 needs perm
+    assert raw(A=FAKE + 4) == -1
+    assert raw(bm=32) == -2
+    assert raw(N=96) == -2 and raw(K=100) == -2
+    assert raw(fmt=1, bm=64) == -2               # MX formats: 16- or 256-row tiles only
+    assert raw(A_rows=20) == -2                  # GEMM2 reads one A row per routed row
+    assert raw(wsb=16) == -3
+    assert L.moe_test_gemm_raw_workspace_bytes(30, 2, 128) > 0
+    assert L.moe_test_gemm_raw_workspace_bytes(30, 0, 128) == 0

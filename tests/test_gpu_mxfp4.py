@@ -4,8 +4,8 @@ token at run time, here MXFP8) against the oracle's "mxfp4" layer.
 
 Packed e2m1 weight codes and their E8M0 scales are bit-exact in the tiled storage (code
 bytes past K zero, scale pads 127); x codes
-and scales are bit-exact; the routing tables are exact; h codes may differ only inside the
-accumulation window; outputs meet the tolerance of the other formats.
+and scales are bit-exact; the layers are checked by ``gpu_helpers.LayerCheck`` like the other
+formats.
 """
 import numpy as np
 import pytest
@@ -14,8 +14,9 @@ import torch
 import sparse_moe_ffn_gemm_amd as moe
 from oracle import moe_ref as R
 from synth import SHAPES, custom_shape
-from gpu_helpers import GpuLayer, OracleExperts, bits_host, compare_out, routing_exact, say
-from test_gpu_mx import _split, _wide, _ws_view, _check_h_dispatched, untile_scales
+from gpu_helpers import GpuLayer, check_all_rows, check_prefill, say
+from layouts import untile_fp4, untile_scales
+from test_gpu_mx import _split, _wide
 
 pytestmark = pytest.mark.gpu
 
@@ -25,9 +26,8 @@ FMT = "mxfp4"
 def untile(codes: np.ndarray, scales: np.ndarray, N: int, K: int):
     """Row-major packed codes [E, N, K/2] and E8M0 rows [E, N, 4 ceil(K/128)] of the tiled
     storage (16-row x 128-K tiles), and the code bytes past K."""
-    E, KB = codes.shape[0], -(-K // 128)
-    c = codes.reshape(E, N // 16, KB, 16, 64).transpose(0, 1, 3, 2, 4).reshape(E, N, KB * 64)
-    return c[..., :K // 2], untile_scales(scales, N, K), c[..., K // 2:]
+    c, tail = untile_fp4(codes, N, K)
+    return c, untile_scales(scales, N, K), tail
 
 
 @pytest.mark.parametrize("E,N,K", [(2, 192, 2880), (3, 64, 256), (1, 96, 96), (2, 16, 32)])
@@ -75,55 +75,21 @@ SMALL = [
 
 @pytest.mark.parametrize("shape", SMALL, ids=[s.name for s in SMALL])
 def test_forward_mxfp4_small_full_parity(shape):
-    g = GpuLayer(shape, fmt=FMT)
-    routing = moe.new_routing(shape.T, shape.E, shape.top_k)
-    say(f"mxfp4 forward {shape.name}: T={shape.T} H={shape.H} E={shape.E} k={shape.top_k} I={shape.I}")
-    out = g.layer(g.x, routing=routing)
-    torch.cuda.synchronize()
-    ox = OracleExperts(shape, g.li, fmt=FMT)
-    ref = ox.forward()
-    routing_exact(routing, ref, shape.T, shape.top_k, shape.name)
-    T, H, I, rows = shape.T, shape.H, shape.I, shape.T * shape.top_k
-    xq = _ws_view(g.layer, T, "xq", torch.uint8, (T, H)).cpu().numpy()
-    sx = _ws_view(g.layer, T, "sx", torch.uint8, (T, moe.mx_row(H))).cpu().numpy()
-    real, pad = _split(sx, H)
-    assert np.array_equal(xq, ref["xq"]) and np.array_equal(real, ref["sx"]) and np.all(pad == 127)
-    hq = _ws_view(g.layer, T, "h", torch.uint8, (rows, I)).cpu().numpy()
-    hs = _ws_view(g.layer, T, "sh", torch.uint8, (rows, moe.mx_row(I))).cpu().numpy()
-    _check_h_dispatched(g, ox, ref, hq, hs, fmt=FMT)
-    compare_out(bits_host(out), ref["out"], shape.name, allowance=ref["allowance"])
+    check_all_rows(shape, FMT)
 
 
+@pytest.mark.parametrize("name", ["gpt-oss-20b-decode", "qwen3-235b-decode"])
 @pytest.mark.timeout(900)
-def test_forward_mxfp4_decode_layer_all_tokens():
-    shape = SHAPES["gpt-oss-20b-decode"]
-    g = GpuLayer(shape, fmt=FMT)
-    routing = moe.new_routing(shape.T, shape.E, shape.top_k)
-    say(f"mxfp4 forward {shape.name}")
-    out = g.layer(g.x, routing=routing)
-    torch.cuda.synchronize()
-    ref = OracleExperts(shape, g.li, fmt=FMT).forward()
-    routing_exact(routing, ref, shape.T, shape.top_k, shape.name)
-    compare_out(bits_host(out), ref["out"], shape.name, allowance=ref["allowance"])
+def test_forward_mxfp4_decode_layers_all_tokens(name):
+    check_all_rows(SHAPES[name], FMT)
 
 
-@pytest.mark.timeout(1200)
-def test_forward_mxfp4_prefill_layer_sampled():
-    """The prefill-sized layer (every expert ~256 rows: the 256-row tile kernel and its
-    narrow overflow tiles), checked on sampled tokens (the last one included)."""
-    shape = SHAPES["gpt-oss-120b-prefill"]
-    g = GpuLayer(shape, fmt=FMT)
-    routing = moe.new_routing(shape.T, shape.E, shape.top_k)
-    say(f"mxfp4 forward {shape.name}")
-    out = g.layer(g.x, routing=routing)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(97)
-    toks = np.sort(rng.choice(shape.T, size=6, replace=False))
-    toks[-1] = shape.T - 1
-    ref = OracleExperts(shape, g.li, fmt=FMT).forward(token_subset=toks)
-    routing_exact(routing, ref, shape.T, shape.top_k, shape.name)
-    compare_out(bits_host(out)[toks], ref["out"], f"{shape.name} tokens {toks.tolist()}",
-                allowance=ref["allowance"])
+@pytest.mark.parametrize("name,n_sample", [("gpt-oss-120b-prefill", 16), ("qwen3-235b-prefill", 16)])
+@pytest.mark.timeout(1500)
+def test_forward_mxfp4_prefill_layers(name, n_sample):
+    """The prefill-sized layers (the 256-row tile kernel and its narrow overflow tiles) on
+    whole experts and sampled tokens (the last one included)."""
+    check_prefill(SHAPES[name], FMT, n_sample, 97)
 
 
 def test_forward_mxfp4_rejects_wide_layers():

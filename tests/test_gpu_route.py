@@ -39,7 +39,7 @@ def _run(shape, li):
     ids, gates = R.topk_softmax(lg, shape.top_k)
     counts, offsets, perm, inv = R.permute(ids, shape.E)
     ref = dict(logits=lg, ids=ids, gates=gates, counts=counts, offsets=offsets, perm=perm, inv=inv)
-    routing_exact(r, ref, shape.T, shape.top_k, shape.name)
+    routing_exact(r, ref, shape.name)
     return r
 
 
