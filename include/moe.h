@@ -264,6 +264,25 @@ moe_status moe_forward_mxfp4_profiled(const uint16_t* x, const float* router_w,
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       void* const* events);
 
+/* ---- An entry point that allocates nothing ----
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  moe_forward with the
+ * workspace replaced by a fixed 64 MiB array that the library holds on every device it runs
+ * on (allocated with its code object when the library's kernels are first loaded on that
+ * device, kept until the process ends; its address is looked up once per device).  The
+ * caller still owns x, the weights, out and the optional routing tables.
+ * Limit: moe_workspace_bytes(T, H, E, top_k, I) must be at most 64 MiB (67108864 bytes),
+ * else MOE_ERR_WORKSPACE_TOO_SMALL is returned before anything is touched; decode-sized
+ * layers fit (e.g. 64 tokens at H = I = 2880, top-4), prefill-sized ones do not.
+ * All calls on one device share its array: calls that overlap on one device (different
+ * streams, or host threads without ordering) race and give undefined outputs.  Nothing in
+ * the array has to start at zero: the forward clears what it counts into. */
+moe_status moe_forward_noalloc(const uint16_t* x, const float* router_w, const float* router_b,
+                               const uint8_t* w13, const float* w13_scales, const uint16_t* b13,
+                               const uint8_t* w2, const float* w2_scales, const uint16_t* b2,
+                               int T, int H, int E, int top_k, int I, uint16_t* out,
+                               const moe_routing* routing_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ EXPORTS = ["moe_status_str", "moe_workspace_bytes", "moe_workspace_layout",
            "moe_forward_profiled", "moe_quantize_weights_mx", "moe_quantize_activations_mx",
            "moe_forward_mx", "moe_forward_mx_profiled", "moe_quantize_weights_mxfp4",
            "moe_forward_mxfp4", "moe_forward_mxfp4_profiled",
+           "moe_forward_noalloc",
            # test-only (include/moe_test.h)
            "moe_test_gemm_raw_workspace_bytes", "moe_test_gemm_raw"]
 
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_mxfp4.restype = i
         L.moe_forward_mxfp4_profiled.argtypes = L.moe_forward_profiled.argtypes
         L.moe_forward_mxfp4_profiled.restype = i
+        L.moe_forward_noalloc.argtypes = L.moe_forward.argtypes[:16] + [vp]
+        L.moe_forward_noalloc.restype = i
         L.moe_test_gemm_raw_workspace_bytes.argtypes = [i, i, i]
         L.moe_test_gemm_raw_workspace_bytes.restype = sz
         L.moe_test_gemm_raw.argtypes = [i, i, i, vp, vp, i, vp, i, ctypes.POINTER(ctypes.c_int32), i,
@@ -329,6 +332,33 @@ def forward(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, top_
                                           w2_scales, b2, top_k, out, routing, workspace)
     fn = {"block": "moe_forward", "mxfp8": "moe_forward_mx", "mxfp4": "moe_forward_mxfp4"}[fmt]
     _check(getattr(lib(), fn)(*args), fn)
+    return out
+
+
+NOALLOC_BYTES = 64 << 20   # the library's fixed workspace of moe_forward_noalloc
+
+
+def forward_noalloc(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, top_k: int,
+                    out=None, routing: dict = None) -> torch.Tensor:
+    """``forward`` (block-scaled weights) through moe_forward_noalloc: no workspace argument,
+    the library's fixed per-device array instead (layers whose workspace is at most
+    64 MiB)."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    I = w2.shape[2]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    rs = _routing_struct(routing, T, E, top_k) if routing is not None else None
+    args = [
+        _dev(x, torch.bfloat16, "x"), _dev(router_w, torch.float32, "router_w", (E, H)),
+        _dev(router_b, torch.float32, "router_b", (E,)),
+        _fp8(w13, "w13", (E, 2 * I, H)), _dev(w13_scales, torch.float32, "w13_scales", (E, kb(2 * I), kb(H))),
+        _dev(b13, torch.bfloat16, "b13", (E, 2 * I)),
+        _fp8(w2, "w2", (E, H, I)), _dev(w2_scales, torch.float32, "w2_scales", (E, kb(H), kb(I))),
+        _dev(b2, torch.bfloat16, "b2", (E, H)),
+        T, H, E, top_k, I, _dev(out, torch.bfloat16, "out", (T, H)),
+        ctypes.byref(rs) if rs is not None else None, _stream(x.device)]
+    _check(lib().moe_forward_noalloc(*args), "moe_forward_noalloc")
     return out
 
 

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe.h"
 #include "kernels.hpp"
@@ -298,7 +299,53 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
 }
 
 
+// ---- the workspace of moe_forward_noalloc: one fixed array per device ----
+//
+// A module-scope device array, allocated with the code object when it is loaded on a device
+// (each device has its own copy at its own address) and held until the process ends.  In
+// host code its name is only a stand-in: the address kernels must receive comes from
+// hipGetSymbolAddress, looked up once per device with that device current.  Every call on a
+// device shares that device's array; the forward clears what it needs cleared itself (the
+// dispatch histograms in the router kernel, the GEMM work queues in the dispatch scan), so
+// the contents a previous call left behind are never read.
+constexpr size_t kNoallocBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch[kMaxDevices] = {};
+
+// The current device's scratch address (NULL on failure).
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
 extern "C" {
+
+moe_status moe_forward_noalloc(const uint16_t* x, const float* router_w, const float* router_b,
+                               const uint8_t* w13, const float* w13_scales, const uint16_t* b13,
+                               const uint8_t* w2, const float* w2_scales, const uint16_t* b2,
+                               int T, int H, int E, int top_k, int I, uint16_t* out,
+                               const moe_routing* routing_out, void* stream) {
+  if (!shape_ok(T, H, E, top_k, I)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  Plan p;
+  make_plan(T, H, E, top_k, I, &p);
+  if (p.total > kNoallocBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!x || !router_w || !w13 || !w13_scales || !w2 || !w2_scales || !out)
+    return MOE_ERR_INVALID_ARG;   // (before the device is touched)
+  void* ws = scratch_address();
+  if (!ws) return MOE_ERR_HIP;
+  return forward_impl(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, T, H, E,
+                      top_k, I, out, routing_out, ws, kNoallocBytes, stream, nullptr);
+}
 
 const char* moe_status_str(moe_status s) {
   switch (s) {

@@ -171,3 +171,17 @@ def test_raw_gemm_export_error_paths():
     assert raw(wsb=16) == -3
     assert L.moe_test_gemm_raw_workspace_bytes(30, 2, 128) > 0
     assert L.moe_test_gemm_raw_workspace_bytes(30, 0, 128) == 0
+
+
+def test_noalloc_entry_point_rejects_before_touching_the_device():
+    """moe_forward_noalloc refuses layers whose workspace exceeds its fixed 64 MiB
+    (MOE_ERR_WORKSPACE_TOO_SMALL), bad shapes and null pointers, all before any HIP call."""
+    L = moe.lib()
+    na = lambda **kw: L.moe_forward_noalloc(
+        kw.get("x", FAKE), FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None, kw.get("T", 64),
+        kw.get("H", 2880), kw.get("E", 32), kw.get("k", 4), kw.get("I", 2880), FAKE, None, None)
+    assert L.moe_workspace_bytes(8192, 2880, 128, 4, 2880) > _lib.NOALLOC_BYTES
+    assert na(T=8192, E=128) == -3                  # the prefill layer does not fit
+    assert na(T=64, H=100) == -2
+    assert na(x=None) == -1
+    assert L.moe_workspace_bytes(64, 2880, 32, 4, 2880) <= _lib.NOALLOC_BYTES
