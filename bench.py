@@ -10,11 +10,12 @@ default workload is the gpt-oss-120b-shaped prefill layer (T=8192, H=2880, E=128
 top-4, I=2880).  The timed region brackets the dominant GEMM of every step with HIP
 events recorded between the library's kernels on the same stream
 (``moe_forward_profiled``), which gives the roofline's live kernel time; the other stage
-times come from a separate, untimed pass that records every stage boundary.  One JSON
-line.
+times come from a separate, untimed pass that records every stage boundary.  The same
+run also times the two decode-sized layers (gpt-oss-20b and qwen3-235b shapes) with the
+caches evicted before every step.  One JSON line.
 
-The CPU baseline is the fp64 oracle (test infrastructure) timed on a bounded sample of
-tokens of the same layer, on one host thread.
+The CPU baseline is the fp64 oracle (test infrastructure) on the whole layer, with the
+BLAS threads on every core of the process's affinity mask.
 """
 from __future__ import annotations
 
@@ -42,32 +43,29 @@ def kb(n):
 def algorithmic(shape, counts, fmt="block"):
     """Algorithmic flops and compulsory HBM bytes of the layer and of its two GEMMs.
 
-    Weights are counted once per *active* expert (an expert with no routed token is
-    never read).  Intermediates (x codes, h, y) count where a kernel must read or write
-    them at least once.  Scales: fp32 per 128x128 weight block and per 1x128 activation
-    group, or (MXFP8, MXFP4) one E8M0 byte per 32 elements along K.  MXFP4 weight
-    elements are half a byte."""
+    Compulsory bytes: x and out (bf16), the router, and the weights of every *active*
+    expert (codes, scales, biases; an expert with no routed token is never read).  The
+    intermediates (x codes, h, y) are implementation traffic and are not counted.  Per
+    GEMM: its own weights.  Scales: fp32 per 128x128 weight block, or (MXFP8, MXFP4) one
+    E8M0 byte per 32 elements along K.  MXFP4 weight elements are half a byte."""
     T, H, E, k, I = shape.T, shape.H, shape.E, shape.top_k, shape.I
     rows = T * k
     active = int((counts > 0).sum())
     wb = 0.5 if fmt == "mxfp4" else 1
     if fmt in ("mxfp8", "mxfp4"):
-        sw13, sw2, sx, sh = 2 * I * H // 32, H * I // 32, T * H // 32, rows * I // 32
+        sw13, sw2 = 2 * I * H // 32, H * I // 32
     else:
         sw13, sw2 = kb(2 * I) * kb(H) * 4, kb(H) * kb(I) * 4
-        sx, sh = T * kb(H) * 4, rows * kb(I) * 4
     w13 = active * int(2 * I * H * wb + sw13 + (2 * I * 2 if shape.expert_bias else 0))
     w2 = active * int(H * I * wb + sw2 + (H * 2 if shape.expert_bias else 0))
     layer_bytes = T * H * 2 + E * H * 4 + E * 4 + w13 + w2 + T * H * 2
-    xq = T * H + sx
-    hq = rows * I + sh
     g1_flops = 2 * rows * H * 2 * I
     g2_flops = 2 * rows * I * H
     return dict(
         active_experts=active,
         layer_flops=g1_flops + g2_flops, layer_bytes=layer_bytes,
-        gemm1=dict(flops=g1_flops, bytes=w13 + xq + hq),
-        gemm2=dict(flops=g2_flops, bytes=w2 + hq + rows * H * 2))
+        gemm1=dict(flops=g1_flops, bytes=w13),
+        gemm2=dict(flops=g2_flops, bytes=w2))
 
 
 def pmc_record(workload, kernel):
@@ -128,8 +126,19 @@ def device_copy_gbs(torch, dev, mib=1024, reps=5):
     return 2 * a.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def cpu_baseline(shape, li, n_tokens, fmt="block"):
-    """The oracle's forward on the first ``n_tokens`` tokens (one thread)."""
+def blas_vendor():
+    import numpy as np
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:
+        return "unknown"
+
+
+def cpu_baseline(shape, li, fmt="block"):
+    """The oracle's forward on the whole layer (every token, every expert), float64 NumPy,
+    BLAS threads on every core of the affinity mask.  The weight conversion (the oracle's
+    own quantiser, from the generator's fp32 weights) is offline work and is not timed."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -139,35 +148,134 @@ def cpu_baseline(shape, li, n_tokens, fmt="block"):
     from synth import expert_weights
     from synth.cases import _base_shape
 
+    cores = len(os.sched_getaffinity(0))
+    vendor = blas_vendor()
+    print(f"[bench] cpu baseline: oracle on the whole layer, {cores} cores, BLAS {vendor}",
+          file=sys.stderr, flush=True)
     base = _base_shape(shape)
     dev = "cuda" if base.weights_on_device else "cpu"
-    toks = np.arange(min(n_tokens, shape.T))
-    with threadpool_limits(limits=1):
-        ids, _ = R.topk_softmax(R.router_logits(li.x, li.router_w, li.router_b), shape.top_k)
-        need = np.unique(ids[toks])
-        c13, s13, c2, s2 = {}, {}, {}, {}
-        quant = {"block": R.quantize_blocks, "mxfp8": R.quantize_mx,
-                 "mxfp4": R.quantize_mxfp4}[fmt]
+    quant = {"block": R.quantize_blocks, "mxfp8": R.quantize_mx, "mxfp4": R.quantize_mxfp4}[fmt]
 
-        def by_rows(w):   # 128-row slices (whole scale blocks): the same codes, cache-sized
-            parts = [quant(w[i:i + 128]) for i in range(0, w.shape[0], 128)]
-            return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+    def by_rows(w):   # 128-row slices (whole scale blocks): the same codes, cache-sized
+        parts = [quant(w[i:i + 128]) for i in range(0, w.shape[0], 128)]
+        return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
-        # offline weight conversion, not timed: drawn serially, converted on a thread pool
-        host = {int(e): (expert_weights(shape, "w13", int(e), dev).cpu().numpy(),
-                         expert_weights(shape, "w2", int(e), dev).cpu().numpy()) for e in need}
-        with ThreadPoolExecutor(max_workers=16) as ex:
+    t_conv = time.perf_counter()
+    c13, s13, c2, s2 = {}, {}, {}, {}
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        for e0 in range(0, shape.E, 32):     # draw 32 experts at a time, convert in parallel
+            host = {e: (expert_weights(shape, "w13", e, dev).cpu().numpy(),
+                        expert_weights(shape, "w2", e, dev).cpu().numpy())
+                    for e in range(e0, min(shape.E, e0 + 32))}
             conv = dict(zip(host, ex.map(lambda ws: (by_rows(ws[0]), by_rows(ws[1])), host.values())))
-        del host
-        for e, ((q13, t13), (q2, t2)) in conv.items():
-            c13[e], s13[e], c2[e], s2[e] = q13, t13, q2, t2
+            del host
+            for e, ((q13, t13), (q2, t2)) in conv.items():
+                c13[e], s13[e], c2[e], s2[e] = q13, t13, q2, t2
+    t_conv = time.perf_counter() - t_conv
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         R.forward(li.x, li.router_w, li.router_b, shape.top_k, shape.I, c13, s13, li.b13, c2, s2,
-                  li.b2, token_subset=toks, fmt=fmt)
+                  li.b2, fmt=fmt)
         dt = time.perf_counter() - t0
-    return {"value": round(toks.size / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {toks.size} of {shape.T} tokens ({need.size} experts), fp64 NumPy "
-                      f"forward incl. weight dequantisation, {dt:.1f} s"}
+    return {"value": round(shape.T / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "blas": vendor, "seconds": round(dt, 2),
+            "sample": f"the whole layer: all {shape.T} tokens, all {shape.E} experts; fp64 NumPy "
+                      f"forward incl. per-expert weight dequantisation, {dt:.1f} s (weight "
+                      f"conversion {t_conv:.1f} s, untimed)"}
+
+
+def roofline(k_alg, k_s, shape, fmt, kernel):
+    """Roofline of the dominant kernel, both fractions: algorithmic FP8 flops against the
+    5.0 PFLOP/s FP8 peak and algorithmic (compulsory) bytes against 8 TB/s, over the
+    kernel's live launch time.  The line leads with the one the layer's target is stated
+    on: the matrix cores when the kernel's intensity is within 4x of the ridge (625 flop/B)
+    or above it (prefill-sized groups), HBM for weight-streaming (decode-sized) layers.
+    ``traffic`` is the kernel's measured HBM bytes per launch from the committed rocprofv3
+    counter summary, when it was taken on the current kernel source (else null)."""
+    flops, nbytes = k_alg["flops"], k_alg["bytes"]
+    mfma = flops / k_s / 1e12
+    hbm = nbytes / k_s / 1e9
+    ridge = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / nbytes >= ridge / 4:
+        roof = {"bound": "mfma", "achieved": round(mfma, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(mfma / PEAK_FP8_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(hbm / PEAK_HBM_GBS, 4)}
+    prof_name = shape.name if fmt == "block" else f"{shape.name}-{fmt}"
+    rec = pmc_record(prof_name, kernel)
+    roof["traffic"] = rec.get("hbm_bytes_per_launch") if rec else None
+    roof["traffic_source"] = (f"profiles/pmc_{kernel}_{prof_name}.json: rocprofv3 --pmc FETCH_SIZE, "
+                              f"WRITE_SIZE, scaled by a 1 GiB copy" if rec else None)
+    roof.update({
+        "kernel": kernel, "kernel_us": round(k_s * 1e6, 2),
+        "algorithmic_flops": flops, "algorithmic_bytes": nbytes,
+        "intensity_flop_per_byte": round(flops / nbytes, 1),
+        "mfma_tflops": round(mfma, 2), "mfma_frac": round(mfma / PEAK_FP8_TFLOPS, 4),
+        "hbm_gbs": round(hbm, 1), "hbm_frac": round(hbm / PEAK_HBM_GBS, 4)})
+    if rec and "mfma_busy_frac" in rec:
+        # matrix-core busy cycles / (active cycles x SIMDs), from the same counter run
+        roof["mfma_busy_frac_counter"] = rec["mfma_busy_frac"]
+    return roof
+
+
+def decode_layer(shape, fmt, dev, steps=40, warmup=5):
+    """A decode-sized (weight-streaming) layer timed in the same run: per-step times with
+    the caches evicted before every step by reading a 1 GiB buffer (outside the events),
+    and warm; the compulsory bytes (bench.algorithmic) over the cold median against 8 TB/s."""
+    import numpy as np
+    import torch
+
+    import sparse_moe_ffn_gemm_amd as moe
+    from synth import expert_weights, make_inputs
+
+    li = make_inputs(shape)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    layer = moe.MoELayer.from_expert_weights(
+        torch.from_numpy(li.router_w), torch.from_numpy(li.router_b), shape.top_k,
+        bf(li.b13) if shape.expert_bias else None, bf(li.b2) if shape.expert_bias else None,
+        lambda e: expert_weights(shape, "w13", e, "cuda"),
+        lambda e: expert_weights(shape, "w2", e, "cuda"), device=dev, fmt=fmt)
+    x = bf(li.x)
+    out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=dev)
+    routing = moe.new_routing(shape.T, shape.E, shape.top_k, dev)
+    ws = layer.workspace(shape.T)
+    fa = (x, layer.router_w, layer.router_b, layer.w13, layer.w13_scales, layer.b13, layer.w2,
+          layer.w2_scales, layer.b2, shape.top_k)
+    for _ in range(warmup):
+        moe.forward(*fa, out=out, routing=routing, workspace=ws)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def run(cold):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            if cold:
+                torch.sum(flush, dim=0, out=sink)
+            a.record()
+            moe.forward(*fa, out=out, routing=routing, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    cold, warm = run(True), run(False)
+    counts = routing["expert_counts"].cpu().numpy()
+    alg = algorithmic(shape, counts, fmt)
+    p50 = float(np.median(cold))
+    gbs = alg["layer_bytes"] / (p50 * 1e-6) / 1e9
+    print(f"[bench] {shape.name}: cold p50 {p50:.1f} us, warm p50 {np.median(warm):.1f} us, "
+          f"{gbs:.0f} GB/s of compulsory bytes ({gbs / PEAK_HBM_GBS:.1%} of 8 TB/s)",
+          file=sys.stderr, flush=True)
+    r = {"T": shape.T, "H": shape.H, "E": shape.E, "top_k": shape.top_k, "I": shape.I,
+         "cold_us": {"p10": round(float(np.percentile(cold, 10)), 1), "p50": round(p50, 1),
+                     "p90": round(float(np.percentile(cold, 90)), 1)},
+         "warm_us_p50": round(float(np.median(warm)), 1),
+         "tokens_per_s": round(shape.T / (p50 * 1e-6), 1),
+         "compulsory_bytes": alg["layer_bytes"], "active_experts": alg["active_experts"],
+         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "steps": steps}
+    del layer, ws, flush
+    torch.cuda.empty_cache()
+    return r
 
 
 def copy_calibration(gib=1.0, reps=5):
@@ -265,7 +373,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt-oss-120b-prefill")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=96)
+    ap.add_argument("--no-decode-layers", action="store_true",
+                    help="skip the two decode-sized layers timed after the workload")
     ap.add_argument("--format", choices=["block", "mxfp8", "mxfp4"], default="block",
                     help="expert weight format: 128x128 block scales (default), MXFP8, or MXFP4 "
                          "weights with MXFP8 activations")
@@ -370,7 +479,7 @@ def main():
     def per_step(n, flush=None):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
-        sink = torch.empty(1, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
         for a, b in ev:
             if flush is not None:
                 torch.sum(flush, dim=0, out=sink)
@@ -417,27 +526,7 @@ def main():
     tflops = alg["layer_flops"] / step_s / 1e12
     gbs = alg["layer_bytes"] / step_s / 1e9
 
-    k_s = dom_ms / 1e3
-    k_alg = alg[dom]
-    intensity = k_alg["flops"] / k_alg["bytes"]
-    ridge = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if intensity >= ridge:
-        roof = {"bound": "mfma", "achieved": k_alg["flops"] / k_s / 1e12, "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": k_alg["bytes"] / k_s / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    prof_name = shape.name if args.format == "block" else f"{shape.name}-{args.format}"
-    rec = pmc_record(prof_name, dom)
-    roof["traffic"] = rec.get("hbm_bytes_per_launch") if rec else None
-    if rec and "mfma_busy_frac" in rec:
-        # matrix-core busy cycles / (active cycles x SIMDs), from the same counter run
-        roof["mfma_busy_frac_counter"] = rec["mfma_busy_frac"]
-    roof["kernel"] = dom
-    roof["kernel_us"] = round(dom_ms * 1e3, 2)
-    roof["achieved"] = round(roof["achieved"], 2)
-    roof["frac"] = round(roof["frac"], 4)
+    roof = roofline(alg[dom], dom_ms / 1e3, shape, args.format, dom)
 
     line = {
         "metric": METRIC, "value": round(shape.T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -461,10 +550,16 @@ def main():
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "step_ms_dist": step_dist,
         "roofline": roof,
+        "decode_layers": None,
         "cpu_baseline": None,
     }
+    if not args.no_decode_layers and shape.T * shape.top_k > 4096:
+        del layer, ws, x, out
+        torch.cuda.empty_cache()
+        line["decode_layers"] = {n: decode_layer(SHAPES[n], args.format, dev)
+                                 for n in ("gpt-oss-20b-decode", "qwen3-235b-decode")}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(shape, li, args.cpu_sample_tokens, args.format)
+        line["cpu_baseline"] = cpu_baseline(shape, li, args.format)
     print(json.dumps(line), flush=True)
 
 

@@ -31,25 +31,38 @@ def test_flops_are_format_independent():
 
 def test_weight_bytes_per_format():
     """Per active expert: e4m3 codes one byte per element, e2m1 half a byte; block scales
-    4 bytes per 128x128 block, MX scales one byte per 32 elements along K."""
+    4 bytes per 128x128 block, MX scales one byte per 32 elements along K.  The GEMMs'
+    algorithmic bytes are their weights only (the intermediates x codes, h and y are
+    implementation traffic); the layer adds x, the router and out."""
     sh = _shape(expert_bias=False)
     counts = np.array([1, 1, 0, 0])
-    H, I = sh.H, sh.I
-    rows, T = sh.T * sh.top_k, sh.T
-    xq_block, xq_mx = T * H + T * 2 * 4, T * H + T * H // 32
-    hq_block, hq_mx = rows * I + rows * 3 * 4, rows * I + rows * I // 32
+    H, I, T, E = sh.H, sh.I, sh.T, sh.E
     exp = {
-        "block": (2 * (2 * I * H + 5 * 2 * 4) + xq_block + hq_block,
-                  2 * (H * I + 2 * 3 * 4) + hq_block + rows * H * 2),
-        "mxfp8": (2 * (2 * I * H + 2 * I * H // 32) + xq_mx + hq_mx,
-                  2 * (H * I + H * I // 32) + hq_mx + rows * H * 2),
-        "mxfp4": (2 * (I * H + 2 * I * H // 32) + xq_mx + hq_mx,
-                  2 * (H * I // 2 + H * I // 32) + hq_mx + rows * H * 2),
+        "block": (2 * (2 * I * H + 5 * 2 * 4), 2 * (H * I + 2 * 3 * 4)),
+        "mxfp8": (2 * (2 * I * H + 2 * I * H // 32), 2 * (H * I + H * I // 32)),
+        "mxfp4": (2 * (I * H + 2 * I * H // 32), 2 * (H * I // 2 + H * I // 32)),
     }
     for fmt, (g1, g2) in exp.items():
         a = bench.algorithmic(sh, counts, fmt)
         assert a["gemm1"]["bytes"] == g1, fmt
         assert a["gemm2"]["bytes"] == g2, fmt
+        assert a["layer_bytes"] == g1 + g2 + 2 * T * H * 2 + E * H * 4 + E * 4, fmt
+
+
+def test_roofline_reports_both_fractions_and_leads_by_intensity():
+    """The dominant kernel's line carries the FP8-MFMA and the HBM fraction; it leads with
+    the matrix cores for a prefill-sized GEMM (intensity near the 625 flop/B ridge) and
+    with HBM for a weight stream."""
+    from synth import SHAPES
+    for name, lead in (("gpt-oss-120b-prefill", "mfma"), ("gpt-oss-20b-decode", "hbm")):
+        sh = SHAPES[name]
+        counts = np.full(sh.E, sh.T * sh.top_k // sh.E)
+        k = bench.algorithmic(sh, counts)["gemm1"]
+        r = bench.roofline(k, 1e-3, sh, "block", "gemm1")
+        assert r["bound"] == lead
+        assert r["mfma_frac"] == round(k["flops"] / 1e-3 / 1e12 / 5000.0, 4)
+        assert r["hbm_frac"] == round(k["bytes"] / 1e-3 / 1e9 / 8000.0, 4)
+        assert r["frac"] == (r["mfma_frac"] if lead == "mfma" else r["hbm_frac"])
 
 
 def test_biases_are_read_once_per_active_expert():
