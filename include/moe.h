@@ -45,7 +45,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1,         /* null / misaligned pointer, non-positive size */
     MOE_ERR_UNSUPPORTED_SHAPE = -2,   /* shape outside the supported envelope below */
     MOE_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes < moe_workspace_bytes(...) */
-    MOE_ERR_HIP = -4                  /* the HIP runtime reported a launch error */
+    MOE_ERR_HIP = -4,                 /* the HIP runtime reported a launch error */
+    MOE_ERR_DEVICE_WAIT = -5          /* moe_fused_status: a wait inside the fused kernel
+                                         ran out (see moe_forward_fused) */
 } moe_status;
 
 /* Supported envelope: 1 <= T, 1 <= E <= 256, 1 <= top_k <= min(E, 8),
@@ -263,6 +265,42 @@ moe_status moe_forward_mxfp4_profiled(const uint16_t* x, const float* router_w,
                                       uint16_t* out, const moe_routing* routing_out,
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       void* const* events);
+
+/* ---- Decode: the whole layer in one persistent kernel ("Hosting Qwen on Blackwell",
+ * section "Expert Parallel": for decode, dispatch, expert GEMMs and combine fuse into a
+ * single kernel).  The forward of moe_forward / moe_forward_mx / moe_forward_mxfp4 for a
+ * decode-sized layer, computed by one kernel launch (preceded by a one-block clear of the
+ * call's counters in the workspace): router tiles, then the routing tail (top-k + softmax,
+ * scan, scatter), GEMM1 and GEMM2 in 16-row M-tiles of 128-column n-tiles, and the combine,
+ * taken from one work queue in dependency order, each GEMM2 tile starting as soon as its
+ * M-tile's GEMM1 tiles are done.  The arithmetic of every stage is the multi-kernel path's,
+ * so the results are identical to moe_forward's whenever that path also takes the
+ * one-workgroup routing tail (top_k <= 4) and the row-run GEMM tiles (H and I not multiples
+ * of 128); in every case they satisfy the same definitions.
+ *   weight_format  0: 128x128 block scales (w13_scales / w2_scales float, as moe_forward)
+ *                  1: MXFP8 (E8M0 scale tiles, as moe_forward_mx)
+ *                  2: MXFP4 weights (tiled storage, as moe_forward_mxfp4)
+ *   other arguments as moe_forward (scale pointers 4-byte aligned); the workspace layout
+ *   is moe_workspace_layout's.
+ * Envelope (MOE_ERR_UNSUPPORTED_SHAPE outside it, nothing enqueued): the general one, and
+ * T <= 128, T * E <= 16384, at most 24 routed rows per expert on average
+ * (T * top_k / E <= 24), H, I <= 8192.
+ * Every wait of a workgroup inside the kernel is on work taken from the queue before its
+ * own, so it ends once that work does; each wait is nevertheless bounded (about 2^21 polls)
+ * and, past the bound, the workgroup records an error in the workspace and exits, leaving
+ * `out` incomplete.  moe_fused_status reports it. */
+moe_status moe_forward_fused(const uint16_t* x, const float* router_w, const float* router_b,
+                             const uint8_t* w13, const void* w13_scales, const uint16_t* b13,
+                             const uint8_t* w2, const void* w2_scales, const uint16_t* b2,
+                             int T, int H, int E, int top_k, int I, int weight_format,
+                             uint16_t* out, const moe_routing* routing_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Synchronises `stream` and returns MOE_OK if the last moe_forward_fused call on this
+ * workspace (same shape) completed every wait, MOE_ERR_DEVICE_WAIT if a wait ran out
+ * (MOE_ERR_HIP if the status word cannot be read). */
+moe_status moe_fused_status(const void* workspace, int T, int H, int E, int top_k, int I,
+                            void* stream);
 
 /* ---- An entry point that allocates nothing ----
  * For callers that cannot allocate device memory or pass a workspace: code under HIP graph

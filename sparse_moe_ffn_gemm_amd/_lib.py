@@ -16,16 +16,16 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED_SHAPE",
-          -3: "MOE_ERR_WORKSPACE_TOO_SMALL", -4: "MOE_ERR_HIP"}
+          -3: "MOE_ERR_WORKSPACE_TOO_SMALL", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_WAIT"}
 
 EXPORTS = ["moe_status_str", "moe_workspace_bytes", "moe_workspace_layout",
            "moe_quantize_weights", "moe_quantize_activations", "moe_route", "moe_forward",
            "moe_forward_profiled", "moe_quantize_weights_mx", "moe_quantize_activations_mx",
            "moe_forward_mx", "moe_forward_mx_profiled", "moe_quantize_weights_mxfp4",
            "moe_forward_mxfp4", "moe_forward_mxfp4_profiled",
-           "moe_forward_noalloc",
+           "moe_forward_noalloc", "moe_forward_fused", "moe_fused_status",
            # test-only (include/moe_test.h)
-           "moe_test_gemm_raw_workspace_bytes", "moe_test_gemm_raw"]
+           "moe_test_gemm_raw_workspace_bytes", "moe_test_gemm_raw", "moe_test_set_fused_spin_limit"]
 
 # stage i runs between profiling events i and i + 1 (include/moe.h, moe_forward_profiled)
 PROFILE_STAGES = ["router_gemm", "topk_softmax", "dispatch_scan", "dispatch_scatter",
@@ -95,6 +95,12 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_mxfp4_profiled.restype = i
         L.moe_forward_noalloc.argtypes = L.moe_forward.argtypes[:16] + [vp]
         L.moe_forward_noalloc.restype = i
+        L.moe_forward_fused.argtypes = L.moe_forward.argtypes[:14] + [i] + L.moe_forward.argtypes[14:]
+        L.moe_forward_fused.restype = i
+        L.moe_fused_status.argtypes = [vp, i, i, i, i, i, vp]
+        L.moe_fused_status.restype = i
+        L.moe_test_set_fused_spin_limit.argtypes = [i]
+        L.moe_test_set_fused_spin_limit.restype = i
         L.moe_test_gemm_raw_workspace_bytes.argtypes = [i, i, i]
         L.moe_test_gemm_raw_workspace_bytes.restype = sz
         L.moe_test_gemm_raw.argtypes = [i, i, i, vp, vp, i, vp, i, ctypes.POINTER(ctypes.c_int32), i,
@@ -333,6 +339,36 @@ def forward(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, top_
     fn = {"block": "moe_forward", "mxfp8": "moe_forward_mx", "mxfp4": "moe_forward_mxfp4"}[fmt]
     _check(getattr(lib(), fn)(*args), fn)
     return out
+
+
+FORMATS = {"block": 0, "mxfp8": 1, "mxfp4": 2}   # weight_format of moe_forward_fused
+
+
+def forward_fused(x, router_w, router_b, w13, w13_scales, b13, w2, w2_scales, b2, top_k: int,
+                  out=None, routing: dict = None, workspace=None) -> torch.Tensor:
+    """``forward`` through moe_forward_fused: a decode-sized layer in one persistent kernel
+    (the weight format is read off the scales as in ``forward``)."""
+    out, args, _keep, fmt = _forward_args(x, router_w, router_b, w13, w13_scales, b13, w2,
+                                          w2_scales, b2, top_k, out, routing, workspace)
+    args = args[:14] + [FORMATS[fmt]] + args[14:]
+    _check(lib().moe_forward_fused(*args), "moe_forward_fused")
+    return out
+
+
+def fused_status(workspace: torch.Tensor, T: int, H: int, E: int, top_k: int, I: int) -> int:
+    """moe_fused_status of the last moe_forward_fused on ``workspace`` (synchronises the
+    current stream): 0 (MOE_OK) or -5 (MOE_ERR_DEVICE_WAIT)."""
+    st = lib().moe_fused_status(_dev(workspace, torch.uint8, "workspace"), T, H, E, top_k, I,
+                                _stream(workspace.device))
+    if st not in (0, -5):
+        _check(st, "moe_fused_status")
+    return st
+
+
+def set_fused_spin_limit(polls: int) -> int:
+    """Test hook (include/moe_test.h): bound on the polls of every wait in later fused
+    launches; negative = give up at once.  Returns the previous bound."""
+    return lib().moe_test_set_fused_spin_limit(polls)
 
 
 NOALLOC_BYTES = 64 << 20   # the library's fixed workspace of moe_forward_noalloc

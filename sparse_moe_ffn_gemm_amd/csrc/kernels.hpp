@@ -120,6 +120,54 @@ void launch_gemm2(const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
 // gate rows j at column j, up rows I + j at column I + j.  Test infrastructure only.
 void launch_gemm_raw(bool gemm1, const GemmArgs& a, int bm, int max_tiles, hipStream_t st);
 
+// ---- decode: the whole layer in one persistent kernel ----
+// Counters of one fused call in the workspace (kFusedCtrTile + M-tiles words), zeroed by the
+// launch's clear kernel: the work-queue head, router tiles done, the routing-done flag,
+// GEMM2 items done, the error code, and from kFusedCtrTile on the GEMM1 items done per
+// M-tile.
+constexpr int kFusedHead = 0, kFusedRouterDone = 1, kFusedRouted = 2, kFusedDone2 = 3,
+              kFusedError = 4, kFusedCtrTile = 8;
+constexpr int kFusedCombineCols = 2048;   // columns of one combine item (512 lanes x 4)
+constexpr int kFusedMaxT = 128;           // tokens of a fused call (4 ceil(T / 64) <= 8 waves)
+// error codes in the kFusedError word
+constexpr int kFusedErrWait = 1;          // a bounded wait ran out
+
+struct FusedArgs {
+  const uint16_t* x;
+  const float* rw;
+  const float* rb;
+  int T, H, E, top_k, I;
+  int ksplit, kslice, ntx, ney;   // router tiles: token tiles x expert tiles x H slices
+  float* partial;
+  uint8_t* xq;
+  float* sx;                       // block-scaled x scales (NULL for MX)
+  uint8_t* sx_mx;                  // MX x scale codes (NULL for block scales)
+  int32_t* ids;
+  float* gates;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* chunk_base;
+  int32_t* perm;
+  int32_t* inv;
+  GemmArgs g1, g2;                 // the GEMMs (tiles, num_tiles, expert_tile_off shared)
+  uint16_t* y;
+  uint16_t* out;
+  int32_t* ctr;
+  int spin_limit;                  // polls per wait before giving up (< 0: give up at once)
+};
+
+// Dynamic LDS of the fused kernel for a shape (the largest of its stages).
+size_t fused_lds_bytes(int T, int H, int E, int top_k, int I);
+// Whether the fused kernel takes this format (0 block, 1 MXFP8, 2 MXFP4) with `lds` bytes
+// of dynamic LDS on the current device (its large-LDS opt-in done); enqueues nothing.
+bool fused_prepare(int fmt, size_t lds);
+// Clears the counters (kFusedCtrTile + max_tiles words) and launches the fused kernel with
+// as many workgroups as the device holds at once (at most max_items).
+void launch_fused(const FusedArgs& f, int fmt, size_t lds, int max_tiles, long max_items,
+                  hipStream_t st);
+// Polls per wait of later launches (test hook; default 1 << 21); returns the previous bound.
+int set_fused_spin_limit(int polls);
+
 // ---- combine ----
 void launch_combine(const uint16_t* y, const float* gates, const int32_t* inv, int T, int H,
                     int top_k, uint16_t* out, hipStream_t st);

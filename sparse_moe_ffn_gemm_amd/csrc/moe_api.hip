@@ -26,6 +26,8 @@ struct Plan {
   size_t ids, gates, counts, offsets, perm, inv;
   size_t xq, sx, h, sh, y;
   size_t shd;      // h scale words in dispatch order, K-block major (large-group GEMMs)
+  size_t sync;     // the fused decode kernel's counters
+  int max_tiles16; // M-tiles of 16 rows at most (the tile list's capacity)
   size_t total;
 };
 
@@ -87,7 +89,8 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   p->presplit = ceil_div(T, moe::kRouterTile) >= 8;
   p->wparts = take(p->presplit ? sizeof(uint16_t) * 3 * static_cast<size_t>(E) * H : 0);
   p->chunk_base = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
-  p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->rows / 16 + std::min<long>(E, p->rows)));
+  p->max_tiles16 = static_cast<int>(p->rows / 16 + std::min<long>(E, p->rows));
+  p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->max_tiles16));
   p->num_tiles = take(sizeof(int32_t) * (1 + 2 * moe::kGemmQueues));   // + the GEMMs' queues
   p->expert_tile_off = take(sizeof(int32_t) * (E + 1));
   p->ids = take(sizeof(int32_t) * p->rows);
@@ -102,6 +105,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   p->sh = take(sizeof(float) * static_cast<size_t>(p->rows) * ceil_div(I, moe::kBlock));
   p->y = take(sizeof(uint16_t) * static_cast<size_t>(p->rows) * H);
   p->shd = take(sizeof(uint32_t) * static_cast<size_t>(p->rows) * ceil_div(I, moe::kBlock));
+  p->sync = take(sizeof(int32_t) * static_cast<size_t>(moe::kFusedCtrTile + p->max_tiles16));
   p->total = off;
 }
 
@@ -299,6 +303,145 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
 }
 
 
+// ---- decode: the whole layer in one persistent kernel ----
+
+// The fused kernel's envelope (beyond shape_ok): decode-sized groups (16-row M-tiles), a
+// token count and logit count the one-workgroup routing tail holds, row-run GEMM tiles.
+static bool fused_shape_ok(const Plan& p) {
+  if (p.T > moe::kFusedMaxT || static_cast<long>(p.T) * p.E > moe::kTailLogits) return false;
+  if (p.ksplit > moe::kTailSplit) return false;
+  if (moe::gemm_tile_rows(p.rows, p.E) != 16) return false;
+  if (p.H > 8192 || p.I > 8192) return false;   // the row-run tiles stage all of K in LDS
+  return true;
+}
+
+extern "C" moe_status moe_forward_fused(const uint16_t* x, const float* router_w,
+                                        const float* router_b, const uint8_t* w13,
+                                        const void* w13_scales, const uint16_t* b13,
+                                        const uint8_t* w2, const void* w2_scales,
+                                        const uint16_t* b2, int T, int H, int E, int top_k, int I,
+                                        int weight_format, uint16_t* out,
+                                        const moe_routing* routing_out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (weight_format < 0 || weight_format > 2) return MOE_ERR_INVALID_ARG;
+  const bool mx = weight_format != kBlockFp8;
+  if (!x || !router_w || !w13 || !w13_scales || !w2 || !w2_scales || !out || !workspace)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(w13) || !aligned16(w2) ||
+      !aligned16(out) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned4(w13_scales) || !aligned4(w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (routing_out && !routing_ok(routing_out)) return MOE_ERR_INVALID_ARG;
+  if (!shape_ok(T, H, E, top_k, I)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  Plan p;
+  make_plan(T, H, E, top_k, I, &p, weight_format);
+  if (!fused_shape_ok(p)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const size_t lds = moe::fused_lds_bytes(T, H, E, top_k, I);
+  if (!moe::fused_prepare(weight_format, lds)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  (void)hipGetLastError();
+  void* ws = workspace;
+  const Tables tb = routing_out
+                        ? Tables{routing_out->topk_ids, routing_out->topk_gates,
+                                 routing_out->expert_counts, routing_out->expert_offsets,
+                                 routing_out->perm, routing_out->inv_perm}
+                        : Tables{at<int32_t>(ws, p.ids), at<float>(ws, p.gates),
+                                 at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
+                                 at<int32_t>(ws, p.perm), at<int32_t>(ws, p.inv)};
+  moe::FusedArgs f{};
+  f.x = x;
+  f.rw = router_w;
+  f.rb = router_b;
+  f.T = T; f.H = H; f.E = E; f.top_k = top_k; f.I = I;
+  f.ksplit = p.ksplit;
+  f.kslice = p.kslice;
+  f.ntx = ceil_div(T, moe::kRouterTile);
+  f.ney = ceil_div(E, moe::kRouterTile);
+  f.partial = at<float>(ws, p.partial);
+  f.xq = at<uint8_t>(ws, p.xq);
+  f.sx = mx ? nullptr : at<float>(ws, p.sx);
+  f.sx_mx = mx ? at<uint8_t>(ws, p.sx) : nullptr;
+  f.ids = tb.ids;
+  f.gates = tb.gates;
+  f.counts = tb.counts;
+  f.offsets = tb.offsets;
+  f.chunk_base = at<int32_t>(ws, p.chunk_base);
+  f.perm = tb.perm;
+  f.inv = tb.inv;
+  moe::GemmArgs& g1 = f.g1;
+  g1.A = at<uint8_t>(ws, p.xq);
+  g1.A_rows = T;
+  g1.perm = tb.perm;
+  g1.top_k = top_k;
+  g1.B = w13;
+  g1.mx = mx;
+  g1.fp4 = weight_format == kMxfp4;
+  if (mx) {
+    g1.A_mx = at<uint8_t>(ws, p.sx);
+    g1.B_mx = static_cast<const uint8_t*>(w13_scales);
+    g1.h_mx = at<uint8_t>(ws, p.sh);
+  } else {
+    g1.A_scale = at<float>(ws, p.sx);
+    g1.B_scale = static_cast<const float*>(w13_scales);
+    g1.h_scale = at<float>(ws, p.sh);
+  }
+  g1.bias = b13;
+  g1.tiles = at<moe::MTile>(ws, p.tiles);
+  g1.num_tiles = at<int32_t>(ws, p.num_tiles);
+  g1.expert_tile_off = at<int32_t>(ws, p.expert_tile_off);
+  g1.E = E;
+  g1.K = H;
+  g1.N = 2 * I;
+  g1.I = I;
+  g1.h_out = at<uint8_t>(ws, p.h);
+  moe::GemmArgs& g2 = f.g2;
+  g2.A = at<uint8_t>(ws, p.h);
+  g2.A_rows = static_cast<int>(p.rows);
+  g2.top_k = top_k;
+  g2.B = w2;
+  g2.mx = mx;
+  g2.fp4 = weight_format == kMxfp4;
+  if (mx) {
+    g2.A_mx = at<uint8_t>(ws, p.sh);
+    g2.B_mx = static_cast<const uint8_t*>(w2_scales);
+  } else {
+    g2.A_scale = at<float>(ws, p.sh);
+    g2.B_scale = static_cast<const float*>(w2_scales);
+  }
+  g2.bias = b2;
+  g2.tiles = g1.tiles;
+  g2.num_tiles = g1.num_tiles;
+  g2.expert_tile_off = g1.expert_tile_off;
+  g2.E = E;
+  g2.K = I;
+  g2.N = H;
+  g2.I = I;
+  g2.y_out = at<uint16_t>(ws, p.y);
+  f.y = at<uint16_t>(ws, p.y);
+  f.out = out;
+  f.ctr = at<int32_t>(ws, p.sync);
+  const long items = static_cast<long>(f.ntx) * f.ney * f.ksplit +
+                     static_cast<long>(p.max_tiles16) * (ceil_div(I, 128) + ceil_div(H, 128)) +
+                     static_cast<long>(T) * ceil_div(H, moe::kFusedCombineCols);
+  moe::launch_fused(f, weight_format, lds, p.max_tiles16, items, static_cast<hipStream_t>(stream));
+  return finish();
+}
+
+extern "C" moe_status moe_fused_status(const void* workspace, int T, int H, int E, int top_k,
+                                       int I, void* stream) {
+  if (!workspace) return MOE_ERR_INVALID_ARG;
+  if (!shape_ok(T, H, E, top_k, I)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  Plan p;
+  make_plan(T, H, E, top_k, I, &p);
+  int32_t code = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&code, at<int32_t>(const_cast<void*>(workspace), p.sync) + moe::kFusedError,
+                     sizeof(code), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return MOE_ERR_HIP;
+  return code == 0 ? MOE_OK : MOE_ERR_DEVICE_WAIT;
+}
+
 // ---- the workspace of moe_forward_noalloc: one fixed array per device ----
 //
 // A module-scope device array, allocated with the code object when it is loaded on a device
@@ -354,6 +497,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_DEVICE_WAIT: return "MOE_ERR_DEVICE_WAIT";
   }
   return "MOE_ERR_UNKNOWN";
 }

@@ -143,4 +143,6 @@ moe_status moe_test_gemm_raw(int gemm, int format, int bm, const uint8_t* A,
   return ok ? MOE_OK : MOE_ERR_HIP;
 }
 
+int moe_test_set_fused_spin_limit(int polls) { return moe::set_fused_spin_limit(polls); }
+
 }  // extern "C"

@@ -75,9 +75,13 @@ class MoELayer:
             self._ws[T] = ws
         return ws
 
-    def forward(self, x: torch.Tensor, out: torch.Tensor = None, routing: dict = None) -> torch.Tensor:
-        return _lib.forward(x, self.router_w, self.router_b, self.w13, self.w13_scales, self.b13,
-                            self.w2, self.w2_scales, self.b2, self.top_k, out=out, routing=routing,
-                            workspace=self.workspace(x.shape[0]))
+    def forward(self, x: torch.Tensor, out: torch.Tensor = None, routing: dict = None,
+                fused: bool = False) -> torch.Tensor:
+        """The layer on x [T, H] bf16; ``fused``: the decode-sized layer in one persistent
+        kernel (moe_forward_fused) instead of the multi-kernel path."""
+        fn = _lib.forward_fused if fused else _lib.forward
+        return fn(x, self.router_w, self.router_b, self.w13, self.w13_scales, self.b13,
+                  self.w2, self.w2_scales, self.b2, self.top_k, out=out, routing=routing,
+                  workspace=self.workspace(x.shape[0]))
 
     __call__ = forward

@@ -65,12 +65,17 @@ class GpuLayer:
             lambda e: expert_weights(shape, "w2", e, device), device=device, fmt=fmt)
         torch.cuda.synchronize()
 
-    def run(self):
+    def run(self, fused=False):
+        """The layer on the GPU (``fused``: moe_forward_fused, whose bounded waits must all
+        have completed) -> (out, routing tables)."""
         s = self.shape
         routing = moe.new_routing(s.T, s.E, s.top_k)
-        say(f"forward [{self.fmt}] {s.name}: T={s.T} H={s.H} E={s.E} k={s.top_k} I={s.I}")
-        out = self.layer(self.x, routing=routing)
+        say(f"forward{' fused' if fused else ''} [{self.fmt}] {s.name}: T={s.T} H={s.H} E={s.E} "
+            f"k={s.top_k} I={s.I}")
+        out = self.layer(self.x, routing=routing, fused=fused)
         torch.cuda.synchronize()
+        if fused:
+            assert moe.fused_status(self.layer.workspace(s.T), s.T, s.H, s.E, s.top_k, s.I) == 0
         return out, routing
 
     def ws_view(self, region: str, dtype, shape) -> torch.Tensor:
@@ -123,6 +128,7 @@ class OracleExperts:
             with ThreadPoolExecutor(max_workers=threads) as ex:
                 for e, v in ex.map(q, host.items()):
                     self.cache[e] = v
+            say(f"  oracle quantised {min(i + 32, len(todo))}/{len(todo)} experts ({self.fmt})")
 
     def view(self, idx):
         cache = self.cache
@@ -379,10 +385,11 @@ def pick_experts(counts, bm=256):
     return list(dict.fromkeys(pick))
 
 
-def check_all_rows(shape, fmt="block"):
-    """Every routed row's h and y and every token's out (small and decode-sized layers)."""
+def check_all_rows(shape, fmt="block", fused=False):
+    """Every routed row's h and y and every token's out (small and decode-sized layers);
+    ``fused``: the layer through the one-kernel decode path."""
     g = GpuLayer(shape, fmt=fmt)
-    out, routing = g.run()
+    out, routing = g.run(fused=fused)
     chk = LayerCheck(g, out, routing)
     chk.check_experts()
     chk.check_tokens(h_window=False)

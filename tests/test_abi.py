@@ -185,3 +185,30 @@ def test_noalloc_entry_point_rejects_before_touching_the_device():
     assert na(T=64, H=100) == -2
     assert na(x=None) == -1
     assert L.moe_workspace_bytes(64, 2880, 32, 4, 2880) <= _lib.NOALLOC_BYTES
+
+
+def test_fused_entry_point_rejects_before_touching_the_device():
+    """moe_forward_fused validates the format, pointers, the general envelope and its own
+    decode envelope (T <= 128, T E <= 16384, at most 24 rows per expert, H, I <= 8192) and
+    the workspace size before any HIP call."""
+    L = moe.lib()
+
+    def fz(**kw):
+        a = dict(x=FAKE, s13=FAKE, T=64, H=2880, E=32, k=4, I=2880, fmt=0, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return L.moe_forward_fused(a["x"], FAKE, None, FAKE, a["s13"], None, FAKE, FAKE, None,
+                                   a["T"], a["H"], a["E"], a["k"], a["I"], a["fmt"], FAKE, None,
+                                   a["ws"], a["wsb"], None)
+    assert fz(fmt=3) == -1 and fz(fmt=-1) == -1
+    assert fz(x=None) == -1
+    assert fz(s13=FAKE + 2) == -1                   # scale pointers 4-byte aligned
+    assert fz(H=100) == -2
+    assert fz(T=129, E=128, k=1) == -2              # more tokens than the routing tail holds
+    assert fz(T=128, E=256, k=1) == -2              # T E > 16384
+    assert fz(T=64, E=8, k=4) == -2                 # 32 rows per expert: not decode-sized
+    assert fz(T=8192, E=128) == -2                  # the prefill layer
+    assert fz(H=8256) == -2                         # H > 8192
+    need = L.moe_workspace_bytes(64, 2880, 32, 4, 2880)
+    assert fz(wsb=need - 1) == -3
+    assert L.moe_fused_status(None, 64, 2880, 32, 4, 2880, None) == -1
+    assert L.moe_fused_status(FAKE, 64, 100, 32, 4, 2880, None) == -2

@@ -4,8 +4,10 @@ v_mfma_scale_f32_16x16x128_f8f6f4 reads its two E8M0 scale operands from VGPRs. 
 compiler does not keep its result registers apart from those scale registers (seen with
 a result that overwrote the activation scale it still had to read, which gave products
 off by powers of two).  The kernels accumulate every scaled MFMA in place, so the result
-is the live accumulator; this test compiles the GEMM source with the library's flags and
-checks that no scaled MFMA anywhere in it writes a register that holds one of its scales.
+is the live accumulator, and the row-run tiles keep both scales live past each instruction;
+this test compiles the GEMM source and the fused decode kernel (which inlines the row-run
+tiles) with the library's flags and checks that no scaled MFMA anywhere in them writes a
+register that holds one of its scales.
 """
 import os
 import re
@@ -25,9 +27,10 @@ def _regs(tok: str):
 
 
 @pytest.mark.timeout(600)
-def test_no_scaled_mfma_result_overlaps_its_scale_operands(tmp_path):
-    src = os.path.join(B.CSRC, "gemm.hip")
-    asm = tmp_path / "gemm.s"
+@pytest.mark.parametrize("source", ["gemm.hip", "fused.hip"])
+def test_no_scaled_mfma_result_overlaps_its_scale_operands(tmp_path, source):
+    src = os.path.join(B.CSRC, source)
+    asm = tmp_path / (source[:-4] + ".s")
     flags = [f for f in B.FLAGS if f != "-fPIC"]
     r = subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", str(asm)],
                        capture_output=True, text=True)
