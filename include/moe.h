@@ -271,7 +271,8 @@ moe_status moe_forward_mxfp4_profiled(const uint16_t* x, const float* router_w,
  * single kernel).  The forward of moe_forward / moe_forward_mx / moe_forward_mxfp4 for a
  * decode-sized layer, computed by one kernel launch (preceded by a one-block clear of the
  * call's counters in the workspace): router tiles, then the routing tail (top-k + softmax,
- * scan, scatter), GEMM1 and GEMM2 in 16-row M-tiles of 128-column n-tiles, and the combine,
+ * scan, scatter), GEMM1 and GEMM2 in 16-row M-tiles (128 h columns, 256 output columns per
+ * item), and the combine,
  * taken from one work queue in dependency order, each GEMM2 tile starting as soon as its
  * M-tile's GEMM1 tiles are done.  The arithmetic of every stage is the multi-kernel path's,
  * so the results are identical to moe_forward's whenever that path also takes the

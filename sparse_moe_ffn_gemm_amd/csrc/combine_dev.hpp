@@ -8,8 +8,9 @@ namespace moe {
 
 // out[t, c .. c + 3] = sum_j gates[t, j] * y[inv[t k + j], c .. c + 3], summed in fp32 in j
 // order (deterministic) and rounded once to bf16; the k 8-byte loads of y are issued before
-// the sum.  `rows` bounds the y rows (an out-of-range inv entry reads row 0).  COH: y is
-// read with device-coherent loads (written by other workgroups of the same launch).
+// the sum.  `rows` bounds the y rows (an out-of-range inv entry reads row 0).  COH: gates,
+// inv and y are read with device-coherent loads (written by other workgroups of the same
+// launch).
 template <bool COH = false>
 __device__ __forceinline__ void combine_quad(const uint16_t* __restrict__ y,
                                              const float* __restrict__ gates,
@@ -23,8 +24,8 @@ __device__ __forceinline__ void combine_quad(const uint16_t* __restrict__ y,
     g[j] = 0.f;
     v[j] = make_uint2(0u, 0u);
     if (j < top_k) {
-      g[j] = gates[static_cast<size_t>(t) * top_k + j];
-      int r = inv[static_cast<size_t>(t) * top_k + j];
+      g[j] = load_c<COH>(gates + static_cast<size_t>(t) * top_k + j);
+      int r = load_c<COH>(inv + static_cast<size_t>(t) * top_k + j);
       if (static_cast<unsigned>(r) >= static_cast<unsigned>(rows)) r = 0;   // never read past y
       const uint16_t* row = y + static_cast<size_t>(r) * H;
       if constexpr (COH) {

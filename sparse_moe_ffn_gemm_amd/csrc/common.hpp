@@ -82,9 +82,28 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Stores and loads at device scope (the sc1 cache policy) when COH: data that workgroups of
+// one launch hand to each other after a counter says it is complete, visible across the
+// XCDs' L2 caches without cache-wide write-back or invalidation.
+template <bool COH, typename T>
+__device__ __forceinline__ void store_c(T* p, T v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+template <bool COH, typename T>
+__device__ __forceinline__ T load_c(const T* p) {
+  if constexpr (COH)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
 // Quantises columns [col, col + 8) of one 1x128 group of a bf16 row (16 lanes of a DPP row
 // cover the group; `in` is false for lanes past the row's end) and returns the group's
 // scale, the same in all 16 lanes.  Codes go to codes_row + col.
+template <bool COH = false>
 __device__ __forceinline__ float quantize_group16(const uint16_t* row, int col, bool in,
                                                   uint8_t* codes_row) {
   float f[8];
@@ -103,10 +122,9 @@ __device__ __forceinline__ float quantize_group16(const uint16_t* row, int col, 
   amax = group_max<16>(amax);
   const float s = group_scale(amax);
   if (in) {
-    uint2 q;
-    q.x = encode4(f[0], f[1], f[2], f[3], s);
-    q.y = encode4(f[4], f[5], f[6], f[7], s);
-    *reinterpret_cast<uint2*>(codes_row + col) = q;
+    const uint64_t lo = encode4(f[0], f[1], f[2], f[3], s);
+    const uint64_t hi = encode4(f[4], f[5], f[6], f[7], s);
+    store_c<COH>(reinterpret_cast<uint64_t*>(codes_row + col), lo | (hi << 32));
   }
   return s;
 }
@@ -145,6 +163,7 @@ __device__ __forceinline__ uint32_t encode4_mul(float v0, float v1, float v2, fl
 // MX-quantises columns [col, col + 8) of one 32-block of a bf16 row (4 aligned lanes cover
 // the block; `in` is false for lanes past the row's end, whose codes are not written) and
 // returns the block's E8M0 code, the same in all 4 lanes.  Codes go to codes_row + col.
+template <bool COH = false>
 __device__ __forceinline__ int quantize_mx8(const uint16_t* row, int col, bool in,
                                             uint8_t* codes_row) {
   float f[8];
@@ -164,10 +183,9 @@ __device__ __forceinline__ int quantize_mx8(const uint16_t* row, int col, bool i
   const int code = mx_scale_code(amax);
   if (in) {
     const float m = mx_inv_scale(code);
-    uint2 q;
-    q.x = encode4_mul(f[0], f[1], f[2], f[3], m);
-    q.y = encode4_mul(f[4], f[5], f[6], f[7], m);
-    *reinterpret_cast<uint2*>(codes_row + col) = q;
+    const uint64_t lo = encode4_mul(f[0], f[1], f[2], f[3], m);
+    const uint64_t hi = encode4_mul(f[4], f[5], f[6], f[7], m);
+    store_c<COH>(reinterpret_cast<uint64_t*>(codes_row + col), lo | (hi << 32));
   }
   return code;
 }

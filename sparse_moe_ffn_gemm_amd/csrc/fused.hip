@@ -14,7 +14,7 @@
 //             the last of them runs the routing tail (logits, top-k + softmax, scan, the
 //             16-row M-tile list, scatter) and then raises the routing flag;
 //   then M-tile by M-tile the GEMM1 n-tiles (128 h columns each), then M-tile by M-tile
-//   the GEMM2 n-tiles (128 output columns each), then the combine items (a token and 2048
+//   the GEMM2 n-tiles (256 output columns each), then the combine items (a token and 2048
 //   output columns).
 // An item waits only on items taken before it (GEMM1 on the routing flag, GEMM2 of tile m
 // on m's GEMM1 n-tiles, the combine on all GEMM2 items), and only running workgroups take
@@ -23,13 +23,13 @@
 // waits for a slot.  Each wait is still bounded: past its bound the workgroup records an
 // error code in the workspace and leaves (the layer's output is then incomplete).
 //
-// Hand-offs between workgroups: the router partials, x codes and routing tables (written
-// once per call) are released by a device-scope fence before the counter update and
-// acquired by one after the poll (cache-wide L2 write-back / invalidation, a few hundred
-// times per call); h and y, handed over item by item, are written and read with
-// device-coherent (sc1) accesses instead, so those counters need no fence at all
-// (measured on the gpt-oss-20b decode layer: fences at every item made the kernel 2.4x
-// slower).
+// Hand-offs between workgroups (the router partials, x codes and scales, the routing
+// tables, h and its scales, y) are written and read with device-coherent accesses (the sc1
+// cache policy: store_c / load_c, load_lds16_c), so a counter update needs no memory fence:
+// each wave waits for its own stores to be acknowledged before the workgroup's one atomic.
+// Device-scope fences would write back or invalidate a whole L2 each time (measured on the
+// gpt-oss-20b decode layer: with a fence pair at every item the kernel ran 2.4x slower, and
+// the routing hand-offs alone cost about 8 us).
 #include <algorithm>
 
 #include "combine_dev.hpp"
@@ -43,8 +43,10 @@ namespace {
 
 int g_spin_limit = 1 << 21;
 
-// Work items: thread 0 claims a ticket (one atomic on the queue head) one item ahead, so the
-// atomic's round trip overlaps the current item; `next_item` hands the claimed ticket to the
+// Work items: workgroup b's first ticket is b (the queue head starts at the grid size, so
+// the launch does not begin with one atomic per workgroup on one address); after that,
+// thread 0 claims a ticket (one atomic on the queue head) one item ahead, so the atomic's
+// round trip overlaps the current item; `next_item` hands the claimed ticket to the
 // workgroup through LDS and claims the one after it.  A workgroup processes its tickets in
 // order, so holding the next one never blocks an earlier item another workgroup waits for.
 __device__ __forceinline__ int claim(int32_t* head) {
@@ -59,12 +61,9 @@ __device__ __forceinline__ int next_item(int32_t* head, int& claimed, int* word)
   return q;
 }
 
-// Waits until *w >= target: thread 0 polls (relaxed device-scope loads) and, with ACQUIRE,
-// fences (acquire: later plain loads see what the writers published with a release); the
-// workgroup follows.  Without ACQUIRE the workgroup must read the handed-off data with
-// device-coherent loads.  False (and the error code recorded) after `limit` unsuccessful
-// polls.
-template <bool ACQUIRE>
+// Waits until *w >= target: thread 0 polls (relaxed device-scope loads), the workgroup
+// follows; the handed-off data is then read with device-coherent loads.  False (and the
+// error code recorded) after `limit` unsuccessful polls.
 __device__ __forceinline__ bool wait_at_least(int32_t* w, int target, int32_t* err, int limit,
                                               int* word) {
   __syncthreads();
@@ -82,30 +81,34 @@ __device__ __forceinline__ bool wait_at_least(int32_t* w, int target, int32_t* e
         __builtin_amdgcn_s_sleep(2);
       }
     }
-    if (!ok)
-      atomicOr(err, kFusedErrWait);
-    else if (ACQUIRE)
-      __threadfence();
+    if (!ok) atomicOr(err, kFusedErrWait);
     *word = ok;
   }
   __syncthreads();
   return *word != 0;
 }
 
-// Publishes the workgroup's writes with one counter update; returns the counter's previous
-// value (in every thread).  Every wave first waits until its own stores are acknowledged;
-// with RELEASE, thread 0 then fences (release: the XCD's L2 written back, so plain stores
-// become visible to other XCDs), without it the stores must have been device-coherent.
-template <bool RELEASE>
+// Publishes the workgroup's device-coherent stores with one counter update; returns the
+// counter's previous value (in every thread).  Every wave first waits until its own stores
+// are acknowledged.
 __device__ __forceinline__ int publish(int32_t* w, int* word) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    if (RELEASE) __threadfence();
-    *word = atomicAdd(w, 1);
-  }
+  if (threadIdx.x == 0) *word = atomicAdd(w, 1);
   __syncthreads();
   return *word;
+}
+
+// M-tile m of the list the routing tail wrote (device-coherent loads), wave-uniform.
+__device__ __forceinline__ MTile tile_at(const MTile* tiles, int m) {
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(tiles + m);
+  const uint64_t a = load_c<true>(w), b = load_c<true>(w + 1);
+  MTile mt;
+  mt.expert = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  mt.row_begin = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32));
+  mt.row_end = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b)));
+  mt.pad = 0;
+  return mt;
 }
 
 // LDS carve of the routing tail (see fused_lds_bytes).
@@ -139,60 +142,55 @@ __global__ __launch_bounds__(512) void moe_decode_fused_kernel(const FusedArgs f
   const int R = f.ntx * f.ney * f.ksplit;
   int32_t* const err = f.ctr + kFusedError;
   int32_t* const head = f.ctr + kFusedHead;
+  int q = static_cast<int>(blockIdx.x);
   int claimed = claim(head);
-  int q = next_item(head, claimed, &word);
   // ---- router tiles: partial logits of one H slice, x codes of its columns ----
   for (; q < R; q = next_item(head, claimed, &word)) {
     const int s = q % f.ksplit, rest = q / f.ksplit;
     const int ey = rest % f.ney, tx = rest / f.ney;
     uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
     auto wp = reinterpret_cast<uint16_t(*)[kRouterTile * kRS]>(lds + kRouterTile * kRS * 2);
-    router_tile<false, 512>(f.x, f.rw, f.T, f.H, f.E, f.kslice, tx, ey, s, f.partial, f.xq, f.sx,
-                            nullptr, f.sx_mx, xs, wp);
-    if (publish<true>(f.ctr + kFusedRouterDone, &word) == R - 1) {
+    router_tile<false, 512, true>(f.x, f.rw, f.T, f.H, f.E, f.kslice, tx, ey, s, f.partial, f.xq,
+                                  f.sx, nullptr, f.sx_mx, xs, wp);
+    if (publish(f.ctr + kFusedRouterDone, &word) == R - 1) {
       // the last router tile: every partial and x code is published; route
-      __threadfence();
-      route_tail_body(f.partial, f.ksplit, f.rb, f.T, f.E, f.top_k, 16, f.ids, f.gates, f.counts,
+      route_tail_body<true>(f.partial, f.ksplit, f.rb, f.T, f.E, f.top_k, 16, f.ids, f.gates, f.counts,
                       f.offsets, f.chunk_base, const_cast<MTile*>(f.g1.tiles),
                       const_cast<int32_t*>(f.g1.num_tiles),
                       const_cast<int32_t*>(f.g1.expert_tile_off), f.perm, f.inv,
                       tail_lds(lds, f.T, f.E, f.top_k));
-      publish<true>(f.ctr + kFusedRouted, &word);
+      publish(f.ctr + kFusedRouted, &word);
     }
   }
   // ---- everything after the router waits for the routing tables ----
-  if (!wait_at_least<true>(f.ctr + kFusedRouted, 1, err, f.spin_limit, &word)) return;
-  const int ntiles = __builtin_amdgcn_readfirstlane(*f.g1.num_tiles);
-  const int NT1 = ceil_div(f.I, 128), NT2 = ceil_div(f.H, 128);
+  if (!wait_at_least(f.ctr + kFusedRouted, 1, err, f.spin_limit, &word)) return;
+  const int ntiles = __builtin_amdgcn_readfirstlane(load_c<true>(f.g1.num_tiles));
+  const int NT1 = ceil_div(f.I, 128), NT2 = ceil_div(f.H, 256);   // GEMM2 items 256 columns wide
   const int end1 = R + ntiles * NT1, end2 = end1 + ntiles * NT2;
   const int end3 = end2 + f.T * ceil_div(f.H, kFusedCombineCols);
   // ---- GEMM1 n-tile (128 h columns) of M-tile m ----
   for (; q < end1; q = next_item(head, claimed, &word)) {
     const int m = (q - R) / NT1;
-    MTile mt = f.g1.tiles[m];
-    mt.expert = __builtin_amdgcn_readfirstlane(mt.expert);
-    mt.row_begin = __builtin_amdgcn_readfirstlane(mt.row_begin);
-    mt.row_end = __builtin_amdgcn_readfirstlane(mt.row_end);
+    const MTile mt = tile_at(f.g1.tiles, m);
     rowrun_tile<true, KS, MX, FP4, 8, false, 2, true>(f.g1, (q - R) % NT1, mt, lds);
-    publish<false>(f.ctr + kFusedCtrTile + m, &word);
+    publish(f.ctr + kFusedCtrTile + m, &word);
   }
-  // ---- GEMM2 n-tile (128 output columns) of M-tile m, once m's h is complete ----
+  // ---- GEMM2 n-tile (256 output columns: two w2 sub-tiles per wave, the same bytes per
+  // item as a GEMM1 n-tile, so the per-item start and drain weigh half as much) of M-tile
+  // m, once m's h is complete ----
   int ready_tile = -1;   // the last M-tile whose GEMM1 items this workgroup saw finished
   for (; q < end2; q = next_item(head, claimed, &word)) {
     const int m = (q - end1) / NT2;
     if (m != ready_tile) {
-      if (!wait_at_least<false>(f.ctr + kFusedCtrTile + m, NT1, err, f.spin_limit, &word)) return;
+      if (!wait_at_least(f.ctr + kFusedCtrTile + m, NT1, err, f.spin_limit, &word)) return;
       ready_tile = m;
     }
-    MTile mt = f.g2.tiles[m];
-    mt.expert = __builtin_amdgcn_readfirstlane(mt.expert);
-    mt.row_begin = __builtin_amdgcn_readfirstlane(mt.row_begin);
-    mt.row_end = __builtin_amdgcn_readfirstlane(mt.row_end);
-    rowrun_tile<false, KS, MX, FP4, 8, false, 2, true>(f.g2, (q - end1) % NT2, mt, lds);
-    publish<false>(f.ctr + kFusedDone2, &word);
+    const MTile mt = tile_at(f.g2.tiles, m);
+    rowrun_tile<false, KS, MX, FP4, 8, false, 2, true, true>(f.g2, (q - end1) % NT2, mt, lds);
+    publish(f.ctr + kFusedDone2, &word);
   }
   // ---- combine: token t, columns [2048 c, 2048 c + 2048), once every y row is in ----
-  if (q < end3 && !wait_at_least<false>(f.ctr + kFusedDone2, ntiles * NT2, err, f.spin_limit, &word))
+  if (q < end3 && !wait_at_least(f.ctr + kFusedDone2, ntiles * NT2, err, f.spin_limit, &word))
     return;
   const int NCC = ceil_div(f.H, kFusedCombineCols);
   for (; q < end3; q = next_item(head, claimed, &word)) {
@@ -203,9 +201,12 @@ __global__ __launch_bounds__(512) void moe_decode_fused_kernel(const FusedArgs f
   // the queue is drained
 }
 
-__global__ __launch_bounds__(256) void fused_clear_kernel(int32_t* __restrict__ ctr, int n) {
+// Zeroes the call's counters, except the queue head: the grid size (the first tickets are
+// the workgroups' own indices).
+__global__ __launch_bounds__(256) void fused_clear_kernel(int32_t* __restrict__ ctr, int n,
+                                                          int grid) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) ctr[i] = 0;
+  if (i < n) ctr[i] = i == kFusedHead ? grid : 0;
 }
 
 template <bool MX, bool FP4>
@@ -253,7 +254,7 @@ void launch_fused(const FusedArgs& f0, int fmt, size_t lds, int max_tiles, long 
   long grid = static_cast<long>(std::max(1, cus)) * std::max(1, per_cu);
   grid = std::max(1L, std::min(grid, max_items));
   const int n = kFusedCtrTile + max_tiles;
-  fused_clear_kernel<<<dim3(ceil_div(n, 256)), dim3(256), 0, st>>>(f.ctr, n);
+  fused_clear_kernel<<<dim3(ceil_div(n, 256)), dim3(256), 0, st>>>(f.ctr, n, static_cast<int>(grid));
   const dim3 g(static_cast<unsigned>(grid)), b(512);
   if (fmt == 0)
     moe_decode_fused_kernel<false, false><<<g, b, lds, st>>>(f);

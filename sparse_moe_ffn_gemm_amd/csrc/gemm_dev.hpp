@@ -64,10 +64,8 @@ __device__ __forceinline__ void load_lds4(const void* g, const void* lds) {
                :: "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
 }
 
-// Device-coherent variants (COH = true): loads and stores at device scope (the sc1 cache
-// policy), which observe / publish data across the XCDs' L2 caches without cache-wide
-// write-back or invalidation.  Used for data that workgroups of one launch hand to each
-// other after a counter says it is complete.
+// Device-coherent variants of the direct-to-LDS loads (COH = true: the sc1 cache policy,
+// as store_c / load_c in common.hpp).
 template <bool COH>
 __device__ __forceinline__ void load_lds16_c(const void* g, const void* lds) {
   if constexpr (COH)
@@ -83,13 +81,6 @@ __device__ __forceinline__ void load_lds4_c(const void* g, const void* lds) {
                  :: "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
   else
     load_lds4(g, lds);
-}
-template <bool COH, typename T>
-__device__ __forceinline__ void store_c(T* p, T v) {
-  if constexpr (COH)
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    *p = v;
 }
 
 // Wait until at most N of this wave's vector-memory loads are outstanding.
@@ -180,11 +171,14 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 // One M-tile (mt) x n-tile (nt) of the row-run variant by a workgroup of NW waves;
 // dyn_lds: the tile's LDS (rowrun_lds_bytes(K)).  Every thread must call it.
 //
-// COH: the activation tile of GEMM2 (h) is read and the tile's outputs (h and its scales, or
-// y) are written with device-coherent accesses (load_lds16_c / store_c), for a launch whose
-// workgroups hand h and y to each other.
+// COH: the activation tile (x codes through perm, or h) and its scales are read and the
+// tile's outputs (h and its scales, or y) are written with device-coherent accesses
+// (load_c, load_lds16_c, store_c), for a launch whose workgroups hand them to each other.
+// WIDE (gemm2 only): each wave streams two 16-row sub-tiles of w2, 128 rows apart, so the
+// workgroup covers 256 output columns (n-tile nt: [256 nt, 256 nt + 256)); every column's
+// sum is formed exactly as in the 128-column tile.
 template <bool SWIGLU, int KS, bool MX = false, bool FP4 = false, int NW = 8, bool RAW = false,
-          int NB = 2, bool COH = false>
+          int NB = 2, bool COH = false, bool WIDE = false>
 __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, const MTile& mt,
                                             uint8_t* dyn_lds) {
   static_assert(MX || !FP4, "MXFP4 weights take E8M0 scales");
@@ -193,7 +187,10 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
   // would otherwise leave most CUs idle
   static_assert(NW == 8 || (MX && NW == 2), "workgroup width");
   constexpr int WAVES = NW;
-  constexpr int NSUB = SWIGLU ? 2 : 1;       // weight sub-tiles per wave (gate, up)
+  static_assert(!(SWIGLU && WIDE), "wide tiles are gemm2 tiles");
+  constexpr int NSUB = (SWIGLU || WIDE) ? 2 : 1;   // weight sub-tiles per wave (gate, up)
+  // B rows of sub-tile 1 past those of sub-tile 0: the up half of w13, or 128 rows of w2
+  const int s1_rows = SWIGLU ? a.I : 128;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -208,30 +205,32 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
   float* sSa = reinterpret_cast<float*>(dyn_lds + KB * 2048);
   float* red = sSa + ceil_div(KB, 4) * 64;
 
-  const int c0 = nt * 16 * WAVES + 16 * wave;   // the wave's first output column
+  const int c0 = nt * 16 * WAVES * (WIDE ? 2 : 1) + 16 * wave;   // the wave's first output column
   const bool live = c0 < (SWIGLU ? I : N);   // I, N multiples of 64: all 16 or none
+  const bool live1 = WIDE ? c0 + 128 < N : live;   // the wide tile's second sub-tile
 
   // ---- the wave's weight stream: sub-tile s, K-block j, in bursts of KS blocks ----
   const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * (FP4 ? KB * 64 : K);
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
   const int bps = ceil_div(KB, KS);          // bursts per sub-tile
-  const int nb = NSUB * bps;                 // bursts of the wave
+  const int nb = (live1 ? NSUB : 1) * bps;   // bursts of the wave (sub-tile major)
   const int nbp = (nb + NB - 1) / NB * NB;   // padded to the NB-slot ring
   unsigned b_off[NSUB];
   float sbg[NSUB];                           // lane j: weight block scale of K-block j
   const uint8_t* bmx[NSUB];                  // MX: the lane's E8M0 codes in the scale tiles
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    const int row = (SWIGLU && s == 1 ? I : 0) + c0 + r;
+    const bool ls = s == 1 ? live1 : live;   // dead sub-tiles address row 0
+    const int row = ls ? (s == 1 ? s1_rows : 0) + c0 + r : r;
     b_off[s] = FP4 ? static_cast<unsigned>(row - r) * KB * 64 + 64 * r + 16 * g
                    : static_cast<unsigned>(row) * K + 16 * g;
     if constexpr (MX) {
       // the tile row's 4 codes of K-block 0 (64 bytes per K-block)
-      bmx[s] = a.B_mx + (static_cast<size_t>(e) * N + (live ? row - r : 0)) * (4 * KB) + 4 * r;
+      bmx[s] = a.B_mx + (static_cast<size_t>(e) * N + (row - r)) * (4 * KB) + 4 * r;
       sbg[s] = 0.f;
     } else {
-      const int brow = ((SWIGLU && s == 1 ? I : 0) + c0) / kBlock;
-      sbg[s] = (live && lane < KB) ? Bsc[static_cast<size_t>(brow) * KB + lane] : 0.f;
+      const int brow = (row - r) / kBlock;
+      sbg[s] = (ls && lane < KB) ? Bsc[static_cast<size_t>(brow) * KB + lane] : 0.f;
     }
   }
 
@@ -330,7 +329,7 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
   // ---- stage the activation tile and its scales (all waves share the fetches) ----
   auto src_row = [&](int rr) {
     const int q = mt.row_begin + rr < mt.row_end ? mt.row_begin + rr : mt.row_begin;
-    const int s = SWIGLU ? a.perm[q] / a.top_k : q;
+    const int s = SWIGLU ? load_c<COH>(a.perm + q) / a.top_k : q;
     return static_cast<unsigned>(s) < static_cast<unsigned>(a.A_rows) ? s : 0;   // never read past A
   };
   {
@@ -344,7 +343,7 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
       const int kk = j * kBlock + ((slot ^ swz_key(row)) << 4);
       const void* src = kk < K ? static_cast<const void*>(a.A + ((q & 1) ? off1 : off0) + kk)
                                : static_cast<const void*>(kZeroChunk);
-      load_lds16_c<COH && !SWIGLU>(src, sA + j * 2048 + 8 * (q & 1) * 128);
+      load_lds16_c<COH>(src, sA + j * 2048 + 8 * (q & 1) * 128);
     }
     // scales: fetch q covers blocks 4q .. 4q+3, lane -> block 4q + (lane >> 4), row lane & 15
     // (MXFP8: the row's 4-byte word of E8M0 codes of that block)
@@ -354,7 +353,7 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
       const void* src = j >= KB ? static_cast<const void*>(kZeroScale)
                         : MX ? static_cast<const void*>(a.A_mx + 4 * (so + j))
                              : static_cast<const void*>(a.A_scale + so + j);
-      load_lds4_c<COH && !SWIGLU>(src, sSa + 64 * q);
+      load_lds4_c<COH>(src, sSa + 64 * q);
     }
   }
 
@@ -380,8 +379,9 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
     if (!live || p >= mt.row_end) return;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
-      *reinterpret_cast<float4*>(a.c_raw + static_cast<size_t>(p) * N + (s == 1 ? I : 0) + cq) =
-          make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
+      if (s == 0 || live1)
+        *reinterpret_cast<float4*>(a.c_raw + static_cast<size_t>(p) * N + (s == 1 ? s1_rows : 0) + cq) =
+            make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
     return;
   }
   const uint16_t* bias = a.bias ? a.bias + static_cast<size_t>(e) * N : nullptr;
@@ -442,18 +442,23 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
     store_c<COH>(reinterpret_cast<uint32_t*>(a.h_out + static_cast<size_t>(p) * I + cq), lo | (hi << 16));
     if (wave == 0 && lane < 16) store_c<COH>(a.h_scale + static_cast<size_t>(p) * KBI + nt, sc);
   } else {
-    if (!live || p >= mt.row_end) return;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
-      const uint2 b2 = *reinterpret_cast<const uint2*>(bias + cq);
-      bv[0] = __uint_as_float(b2.x << 16); bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
-      bv[2] = __uint_as_float(b2.y << 16); bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+    if (p >= mt.row_end) return;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {   // (WIDE: sub-tile 1 holds columns 128 further on)
+      if (!(s == 1 ? live1 : live)) continue;
+      const int cs = cq + (s == 1 ? 128 : 0);
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+        const uint2 b2 = *reinterpret_cast<const uint2*>(bias + cs);
+        bv[0] = __uint_as_float(b2.x << 16); bv[1] = __uint_as_float(b2.x & 0xFFFF0000u);
+        bv[2] = __uint_as_float(b2.y << 16); bv[3] = __uint_as_float(b2.y & 0xFFFF0000u);
+      }
+      const uint64_t ylo = f32_to_f16_sat(acc[s][0] + bv[0]) |
+                           (static_cast<uint32_t>(f32_to_f16_sat(acc[s][1] + bv[1])) << 16);
+      const uint64_t yhi = f32_to_f16_sat(acc[s][2] + bv[2]) |
+                           (static_cast<uint32_t>(f32_to_f16_sat(acc[s][3] + bv[3])) << 16);
+      store_c<COH>(reinterpret_cast<uint64_t*>(a.y_out + static_cast<size_t>(p) * N + cs), ylo | (yhi << 32));
     }
-    const uint64_t ylo = f32_to_f16_sat(acc[0][0] + bv[0]) |
-                         (static_cast<uint32_t>(f32_to_f16_sat(acc[0][1] + bv[1])) << 16);
-    const uint64_t yhi = f32_to_f16_sat(acc[0][2] + bv[2]) |
-                         (static_cast<uint32_t>(f32_to_f16_sat(acc[0][3] + bv[3])) << 16);
-    store_c<COH>(reinterpret_cast<uint64_t*>(a.y_out + static_cast<size_t>(p) * N + cq), ylo | (yhi << 32));
   }
 }
 

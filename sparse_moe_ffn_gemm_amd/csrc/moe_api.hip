@@ -421,7 +421,7 @@ extern "C" moe_status moe_forward_fused(const uint16_t* x, const float* router_w
   f.out = out;
   f.ctr = at<int32_t>(ws, p.sync);
   const long items = static_cast<long>(f.ntx) * f.ney * f.ksplit +
-                     static_cast<long>(p.max_tiles16) * (ceil_div(I, 128) + ceil_div(H, 128)) +
+                     static_cast<long>(p.max_tiles16) * (ceil_div(I, 128) + ceil_div(H, 256)) +
                      static_cast<long>(T) * ceil_div(H, moe::kFusedCombineCols);
   moe::launch_fused(f, weight_format, lds, p.max_tiles16, items, static_cast<hipStream_t>(stream));
   return finish();

@@ -67,7 +67,8 @@ constexpr int kRouterLds = 4 * kRouterTile * kRS * 2;
 // workgroup of NTHR threads (256: four waves of 32 tokens x 32 experts; 512: eight waves
 // of 32 x 16).  Each 16 x 16 output sub-tile sees the same sequence of matrix-core steps
 // in either width, so the partials do not depend on it.  xs / wp: kRouterLds bytes of LDS.
-template <bool PRESPLIT, int NTHR>
+// COH: the partials, x codes and scales are stored device-coherently (store_c).
+template <bool PRESPLIT, int NTHR, bool COH = false>
 __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
                                             const float* __restrict__ W, int T, int H, int E,
                                             int kslice, int tx, int ey, int s,
@@ -163,12 +164,13 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
         const bool in = t < T && h0 + col < h_end;
         uint8_t* codes_row = xq + static_cast<size_t>(t < T ? t : 0) * H + h0;
         if (sx_mx != nullptr) {   // MXFP8: four lanes per 32-block, pads past H get 127
-          const int code = quantize_mx8(xs + row * kRS, col, in, codes_row);
+          const int code = quantize_mx8<COH>(xs + row * kRS, col, in, codes_row);
           if ((tid & 3) == 0 && t < T)
-            sx_mx[static_cast<size_t>(t) * 4 * KBH + (h0 + col) / kMxBlock] = static_cast<uint8_t>(code);
+            store_c<COH>(sx_mx + static_cast<size_t>(t) * 4 * KBH + (h0 + col) / kMxBlock,
+                         static_cast<uint8_t>(code));
         } else {
-          const float sc = quantize_group16(xs + row * kRS, col, in, codes_row);
-          if ((tid & 15) == 0 && t < T) sx[static_cast<size_t>(t) * KBH + g] = sc;
+          const float sc = quantize_group16<COH>(xs + row * kRS, col, in, codes_row);
+          if ((tid & 15) == 0 && t < T) store_c<COH>(sx + static_cast<size_t>(t) * KBH + g, sc);
         }
       }
     }
@@ -210,7 +212,7 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
       for (int r = 0; r < 4; ++r) {
         const int t = t0 + wm * 32 + 16 * i + 4 * (lane >> 4) + r;
         const int e = e0 + wn * 16 * NJ + 16 * j + (lane & 15);
-        if (t < T && e < E) out[static_cast<size_t>(t) * E + e] = tot[i][j][r];
+        if (t < T && e < E) store_c<COH>(out + static_cast<size_t>(t) * E + e, tot[i][j][r]);
       }
 }
 // ------------------------------------------------------------------------------------
@@ -343,8 +345,9 @@ __device__ __forceinline__ float logit_of(const float* __restrict__ partial, int
 // for bit (eight ballots) give its rank; waves before it in the same round and earlier
 // rounds (a running per-expert count) give the rest of its slot.  run[e] holds the
 // chunk's first slot of expert e on entry.  Every thread of the workgroup passes the
-// barriers; threads [0, 256) do the work.
+// barriers; threads [0, 256) do the work.  COH: perm and inv are stored device-coherently.
 // ------------------------------------------------------------------------------------
+template <bool COH = false>
 __device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ ids, int chunk, int T,
                                               int E, int top_k, int32_t* __restrict__ perm,
                                               int32_t* __restrict__ inv, int* run, int (*wc)[256]) {
@@ -376,8 +379,8 @@ __device__ __forceinline__ void scatter_chunk(const int32_t* __restrict__ ids, i
       int pos = run[ex] + rank;
       for (int ww = 0; ww < w; ++ww) pos += wc[ww][ex];
       const int flat = static_cast<int>(flat0) + i;   // = t * top_k + j
-      perm[pos] = flat;
-      inv[flat] = pos;
+      store_c<COH>(perm + pos, flat);
+      store_c<COH>(inv + flat, pos);
     }
     __syncthreads();
     if (tid < E) run[tid] += wc[0][tid] + wc[1][tid] + wc[2][tid] + wc[3][tid];
@@ -419,7 +422,8 @@ __device__ int exclusive_scan256(int v, int* tmp) {
 }
 
 // The scan's body for a workgroup of 512 or 1024 lanes; `hist` and `ids` may point to global
-// memory or to this workgroup's LDS.
+// memory or to this workgroup's LDS.  COH: the tables are stored device-coherently.
+template <bool COH = false>
 __device__ __forceinline__ void dispatch_scan_body(const int32_t* hist, int nchunks, int E, int bm,
                                                    int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets,
@@ -449,13 +453,13 @@ __device__ __forceinline__ void dispatch_scan_body(const int32_t* hist, int nchu
     int run = tmp[e];
     for (int qq = 0; qq < q; ++qq) run += part[qq][e];
     for (int c = c0; c < c1; ++c) {
-      chunk_base[static_cast<size_t>(c) * E + e] = run;
+      store_c<COH>(chunk_base + static_cast<size_t>(c) * E + e, run);
       run += hist[static_cast<size_t>(c) * E + e];
     }
     if (q == 0) {
-      counts[e] = cnt;
-      offsets[e] = tmp[e];
-      if (e == E - 1) offsets[E] = tmp[e] + cnt;
+      store_c<COH>(counts + e, cnt);
+      store_c<COH>(offsets + e, tmp[e]);
+      if (e == E - 1) store_c<COH>(offsets + E, tmp[e] + cnt);
     }
   }
   __syncthreads();
@@ -464,24 +468,24 @@ __device__ __forceinline__ void dispatch_scan_body(const int32_t* hist, int nchu
   if (q == 0) {
     const int base = off;
     for (int i = 0; i < ntl; ++i) {
-      MTile m;
-      m.expert = e;
-      m.row_begin = base + i * bm;
-      m.row_end = min(base + (i + 1) * bm, base + cnt);
-      m.pad = 0;
-      tiles[toff + i] = m;
+      // (expert, row_begin) and (row_end, pad) as two 8-byte words
+      const uint32_t rb = static_cast<uint32_t>(base + i * bm);
+      const uint32_t re = static_cast<uint32_t>(min(base + (i + 1) * bm, base + cnt));
+      uint64_t* w = reinterpret_cast<uint64_t*>(tiles + toff + i);
+      store_c<COH>(w, static_cast<uint64_t>(static_cast<uint32_t>(e)) | (static_cast<uint64_t>(rb) << 32));
+      store_c<COH>(w + 1, static_cast<uint64_t>(re));
     }
-    if (e < E) expert_tile_off[e] = toff;
+    if (e < E) store_c<COH>(expert_tile_off + e, toff);
     if (e == 255) {
-      num_tiles[0] = toff + ntl;
-      expert_tile_off[E] = toff + ntl;
+      store_c<COH>(num_tiles, toff + ntl);
+      store_c<COH>(expert_tile_off + E, toff + ntl);
     }
   }
-  if (tid >= 1 && tid <= 2 * kGemmQueues) num_tiles[tid] = 0;   // the GEMMs' work queues
+  if (tid >= 1 && tid <= 2 * kGemmQueues) store_c<COH>(num_tiles + tid, 0);   // the GEMMs' work queues
   if (ids != nullptr) {   // a single chunk (T <= kChunk): its scatter follows in this workgroup
     __syncthreads();      // every thread is past the tile scan's use of tmp and part
     if (tid < E) tmp[tid] = off;   // the chunk's first slot of each expert = its offset
-    scatter_chunk(ids, 0, T, E, top_k, perm, inv, tmp, part);
+    scatter_chunk<COH>(ids, 0, T, E, top_k, perm, inv, tmp, part);
   }
 }
 
@@ -489,13 +493,14 @@ __device__ __forceinline__ void dispatch_scan_body(const int32_t* hist, int nchu
 // The same logit with every slice load issued at once (MAXS >= ksplit registers; the
 // indices past ksplit are clamped to the last slice, so every load stays inside the
 // partials, and their values are dropped), summed pairwise: one memory round trip.
-template <int MAXS>
+template <int MAXS, bool COH = false>
 __device__ __forceinline__ float logit_wide(const float* __restrict__ partial, int ksplit,
                                             const float* __restrict__ bias, size_t TE, size_t idx,
                                             int e) {
   float r[MAXS];
 #pragma unroll
-  for (int u = 0; u < MAXS; ++u) r[u] = partial[static_cast<size_t>(min(u, ksplit - 1)) * TE + idx];
+  for (int u = 0; u < MAXS; ++u)
+    r[u] = load_c<COH>(partial + static_cast<size_t>(min(u, ksplit - 1)) * TE + idx);
 #pragma unroll
   for (int u = 0; u < MAXS; ++u) r[u] = u < ksplit ? r[u] : 0.f;
 #pragma unroll
@@ -506,14 +511,26 @@ __device__ __forceinline__ float logit_wide(const float* __restrict__ partial, i
 }
 
 // logits[t * SE + e] for every (t, e), a NaN logit stored as -inf (it never wins).
-template <int MAXS>
+// G logits per thread and pass, so that G x MAXS loads are in flight together.
+template <int MAXS, bool COH = false>
 __device__ __forceinline__ void tail_logits(const float* __restrict__ partial, int ksplit,
                                             const float* __restrict__ bias, int T, int E, int SE,
                                             float* logits) {
+  constexpr int G = MAXS >= 64 ? 1 : 64 / MAXS;
   const int TE = T * E;
-  for (int i = threadIdx.x; i < TE; i += blockDim.x) {
-    const float v = logit_wide<MAXS>(partial, ksplit, bias, TE, i, i % E);
-    logits[(i / E) * SE + i % E] = v == v ? v : -INFINITY;
+  const int step = static_cast<int>(blockDim.x);
+  for (int i0 = threadIdx.x; i0 < TE; i0 += G * step) {
+    float v[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int i = min(i0 + g * step, TE - 1);   // past the end: recompute the last logit
+      v[g] = logit_wide<MAXS, COH>(partial, ksplit, bias, TE, i, i % E);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int i = i0 + g * step;
+      if (i < TE) logits[(i / E) * SE + i % E] = v[g] == v[g] ? v[g] : -INFINITY;
+    }
   }
 }
 
@@ -544,7 +561,7 @@ __device__ __forceinline__ void list_insert(float (&lv)[K], int (&li)[K], float 
 // ascending expert order), takes the softmax over the first top_k and writes ids, gates,
 // the LDS copy of the ids and the LDS histogram.  The partial lists are kept as
 // cv/ci[(p K + s) cs + t] (cs >= T).  Needs 4 ceil(T / 64) waves.
-template <int K>
+template <int K, bool COH = false>
 __device__ __forceinline__ void tail_topk(const float* logits, int SE, int T, int E, int top_k,
                                           float* cv, int* ci, int cs, int32_t* __restrict__ ids,
                                           float* __restrict__ gates, int* sids, int* hist) {
@@ -601,8 +618,8 @@ __device__ __forceinline__ void tail_topk(const float* logits, int SE, int T, in
 #pragma unroll
     for (int j = 0; j < K; ++j)
       if (j < top_k) {
-        ids[static_cast<size_t>(t) * top_k + j] = li[j];
-        gates[static_cast<size_t>(t) * top_k + j] = z[j] / sum;
+        store_c<COH>(ids + static_cast<size_t>(t) * top_k + j, li[j]);
+        store_c<COH>(gates + static_cast<size_t>(t) * top_k + j, z[j] / sum);
         sids[t * top_k + j] = li[j];
         atomicAdd(&hist[li[j]], 1);
       }
@@ -627,7 +644,9 @@ struct TailLds {
 // kTailLogits, at most kTailSplit H slices, 4 ceil(T / 64) <= waves of the workgroup) in
 // one workgroup of 512 or 1024 lanes: the router partials summed into LDS logits (all
 // slice loads of a logit in flight together), top-k + softmax with a lane per token
-// (tail_topk), then the scan, the M-tile list of bm-row tiles and the scatter.
+// (tail_topk), then the scan, the M-tile list of bm-row tiles and the scatter.  COH: the
+// partials are read and every table is written device-coherently.
+template <bool COH = false>
 __device__ __forceinline__ void route_tail_body(const float* __restrict__ partial, int ksplit,
                                                 const float* __restrict__ bias, int T, int E,
                                                 int top_k, int bm, int32_t* __restrict__ ids,
@@ -644,23 +663,23 @@ __device__ __forceinline__ void route_tail_body(const float* __restrict__ partia
   const int SE = E | 1;
   if (tid < 256) L.hist[tid] = 0;
   if (ksplit <= 8)
-    tail_logits<8>(partial, ksplit, bias, T, E, SE, L.logits);
+    tail_logits<8, COH>(partial, ksplit, bias, T, E, SE, L.logits);
   else if (ksplit <= 16)
-    tail_logits<16>(partial, ksplit, bias, T, E, SE, L.logits);
+    tail_logits<16, COH>(partial, ksplit, bias, T, E, SE, L.logits);
   else if (ksplit <= 32)
-    tail_logits<32>(partial, ksplit, bias, T, E, SE, L.logits);
+    tail_logits<32, COH>(partial, ksplit, bias, T, E, SE, L.logits);
   else
-    tail_logits<64>(partial, ksplit, bias, T, E, SE, L.logits);
+    tail_logits<64, COH>(partial, ksplit, bias, T, E, SE, L.logits);
   __syncthreads();
   if (top_k <= 2)
-    tail_topk<2>(L.logits, SE, T, E, top_k, L.cv, L.ci, L.cs, ids, gates, L.sids, L.hist);
+    tail_topk<2, COH>(L.logits, SE, T, E, top_k, L.cv, L.ci, L.cs, ids, gates, L.sids, L.hist);
   else if (top_k <= 4)
-    tail_topk<4>(L.logits, SE, T, E, top_k, L.cv, L.ci, L.cs, ids, gates, L.sids, L.hist);
+    tail_topk<4, COH>(L.logits, SE, T, E, top_k, L.cv, L.ci, L.cs, ids, gates, L.sids, L.hist);
   else
-    tail_topk<8>(L.logits, SE, T, E, top_k, L.cv, L.ci, L.cs, ids, gates, L.sids, L.hist);
+    tail_topk<8, COH>(L.logits, SE, T, E, top_k, L.cv, L.ci, L.cs, ids, gates, L.sids, L.hist);
   __syncthreads();
-  dispatch_scan_body(L.hist, 1, E, bm, counts, offsets, chunk_base, tiles, num_tiles,
-                     expert_tile_off, L.sids, T, top_k, perm, inv, L.part, L.tmp);
+  dispatch_scan_body<COH>(L.hist, 1, E, bm, counts, offsets, chunk_base, tiles, num_tiles,
+                          expert_tile_off, L.sids, T, top_k, perm, inv, L.part, L.tmp);
 }
 
 }  // namespace moe
