@@ -155,7 +155,9 @@ moe_status moe_forward(const uint16_t* x, const float* router_w, const float* ro
  *   regrouping runs first)  7 combine  8 end
  * so hipEventElapsedTime(events[i], events[i+1]) is stage i's device time.  Stage 4
  * regroups the x scale words into dispatch order, K-block major, for the 256-row GEMM
- * tiles, and is empty for the other tile heights; for T <= 256 the scatter runs inside
+ * tiles, and is empty for the other tile heights; for T > 448 the top-k + softmax runs
+ * inside stage 0's kernel (the workgroup that completes a token tile's router partials
+ * selects its tokens' experts) and stage 1 is empty; for T <= 256 the scatter runs inside
  * stage 2's kernel and stage 3 is empty, and when also top_k <= 4 and T * E <= 16384 one
  * kernel does top-k, scan and scatter in stage 1 and stages 2 and 3 are both empty.
  * `events` must point to MOE_PROFILE_EVENTS entries (NULL array: MOE_ERR_INVALID_ARG);

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(512) void moe_decode_fused_kernel(const FusedArgs f
     const int s = q % f.ksplit, rest = q / f.ksplit;
     const int ey = rest % f.ney, tx = rest / f.ney;
     uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
-    auto wp = reinterpret_cast<uint16_t(*)[kRouterTile * kRS]>(lds + kRouterTile * kRS * 2);
+    uint16_t* wp = reinterpret_cast<uint16_t*>(lds + kRouterTile * kRS * 2);
     router_tile<false, 512, true>(f.x, f.rw, f.T, f.H, f.E, f.kslice, tx, ey, s, f.partial, f.xq,
                                   f.sx, nullptr, f.sx_mx, xs, wp);
     if (publish(f.ctr + kFusedRouterDone, &word) == R - 1) {

@@ -45,6 +45,19 @@ void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E
                           int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
                           uint8_t* xq = nullptr, float* sx = nullptr, uint16_t* parts = nullptr,
                           uint8_t* sx_mx = nullptr);
+// Prefill-sized routing (T > 448): the weight split into W's three bf16 planes (which also
+// zeroes hist [nchunks][E] and tile_done [ceil(T/64)], contiguous), then one kernel that
+// computes 64-token x 128-expert router tiles over ksplit H slices of kslice columns
+// (partials [ksplit][T][E], x quantised as launch_router_logits does) and, in the workgroup
+// that completes each token tile, its tokens' top-k + softmax (ids, gates, the per-chunk
+// histogram).  route_prefill_shape gives the H split; route_prefill_prepare makes the
+// kernel's large-LDS opt-in (false if the device cannot hold it).
+void route_prefill_shape(int T, int H, int E, int* ksplit, int* kslice);
+bool route_prefill_prepare(int E, int top_k);
+void launch_route_prefill(const uint16_t* x, const float* W, const float* bias, int T, int H, int E,
+                          int top_k, int ksplit, int kslice, uint16_t* parts, float* partial,
+                          uint8_t* xq, float* sx, uint8_t* sx_mx, int32_t* ids, float* gates,
+                          int32_t* hist, int nchunks, int32_t* tile_done, hipStream_t st);
 // ids/gates, counted into the per-chunk expert histogram hist[chunk][E] (cleared before)
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
                  int32_t* ids, float* gates, int32_t* hist, hipStream_t st);

@@ -21,7 +21,8 @@ struct Plan {
   int T, H, E, k, I;
   long rows;
   int ksplit, kslice, nchunks, bm, max_tiles;
-  bool presplit;   // router weights split once per call (many token tiles)
+  bool presplit;   // prefill-sized routing: W split once per call, then the routing kernel
+                   // (route_prefill: 64-token x 128-expert router tiles, top-k fused)
   size_t partial, hist, wparts, chunk_base, tiles, num_tiles, expert_tile_off;
   size_t ids, gates, counts, offsets, perm, inv;
   size_t xq, sx, h, sh, y;
@@ -68,6 +69,8 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   p->kslice = ceil_div(ceil_div(H, ks), moe::kBlock) * moe::kBlock;   // whole quantisation groups
   p->ksplit = ceil_div(H, p->kslice);
   p->nchunks = ceil_div(T, moe::kChunk);
+  p->presplit = ceil_div(T, moe::kRouterTile) >= 8;
+  if (p->presplit) moe::route_prefill_shape(T, H, E, &p->ksplit, &p->kslice);
   // the tile list is sized for the block-scaled tile height, an upper bound for the
   // 256-row tiles of MXFP8 too, so both formats share one workspace layout
   const int bm_block = moe::gemm_tile_rows(p->rows, E);
@@ -85,8 +88,8 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
     return o;
   };
   p->partial = take(sizeof(float) * p->ksplit * static_cast<size_t>(T) * E);
-  p->hist = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
-  p->presplit = ceil_div(T, moe::kRouterTile) >= 8;
+  // the dispatch histograms, then (prefill) the routing kernel's per-token-tile counters
+  p->hist = take(sizeof(int32_t) * (p->nchunks * static_cast<size_t>(E) + ceil_div(T, 64)));
   p->wparts = take(p->presplit ? sizeof(uint16_t) * 3 * static_cast<size_t>(E) * H : 0);
   p->chunk_base = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
   p->max_tiles16 = static_cast<int>(p->rows / 16 + std::min<long>(E, p->rows));
@@ -140,6 +143,25 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
                      const Tables& tb, void* ws, hipStream_t st, hipEvent_t* ev = nullptr,
                      bool quant_x = false, bool mx = false) {
   mark(ev, 0, st);
+  if (p.presplit) {
+    // prefill: router GEMM with the top-k fused (stage 0), the scan (2) and the scatter (3)
+    moe::launch_route_prefill(x, rw, rb, p.T, p.H, p.E, p.k, p.ksplit, p.kslice,
+                              at<uint16_t>(ws, p.wparts), at<float>(ws, p.partial),
+                              quant_x ? at<uint8_t>(ws, p.xq) : nullptr,
+                              quant_x && !mx ? at<float>(ws, p.sx) : nullptr,
+                              quant_x && mx ? at<uint8_t>(ws, p.sx) : nullptr, tb.ids, tb.gates,
+                              at<int32_t>(ws, p.hist), p.nchunks,
+                              at<int32_t>(ws, p.hist) + static_cast<size_t>(p.nchunks) * p.E, st);
+    mark(ev, 1, st);
+    mark(ev, 2, st);
+    moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, tb.counts, tb.offsets,
+                              at<int32_t>(ws, p.chunk_base), at<moe::MTile>(ws, p.tiles),
+                              at<int32_t>(ws, p.num_tiles), at<int32_t>(ws, p.expert_tile_off), st);
+    mark(ev, 3, st);
+    moe::launch_dispatch_scatter(tb.ids, at<int32_t>(ws, p.chunk_base), p.T, p.E, p.k, tb.perm,
+                                 tb.inv, st);
+    return;
+  }
   // a single chunk of tokens (decode-sized T): one workgroup does the scan and the
   // scatter; with few logits the same workgroup also does top-k + softmax
   const bool one_chunk = p.nchunks == 1;
@@ -148,7 +170,7 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
                             at<int32_t>(ws, p.hist), tail ? 0 : p.nchunks * p.E, st,
                             quant_x ? at<uint8_t>(ws, p.xq) : nullptr,
                             quant_x && !mx ? at<float>(ws, p.sx) : nullptr,
-                            p.presplit ? at<uint16_t>(ws, p.wparts) : nullptr,
+                            nullptr,
                             quant_x && mx ? at<uint8_t>(ws, p.sx) : nullptr);
   mark(ev, 1, st);
   if (tail) {
@@ -210,6 +232,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   if (!moe::gemm_prepare(true, mx, fmt == kMxfp4, H, p.bm) ||
       !moe::gemm_prepare(false, mx, fmt == kMxfp4, I, p.bm))
     return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (p.presplit && !moe::route_prefill_prepare(E, top_k)) return MOE_ERR_UNSUPPORTED_SHAPE;
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   void* ws = workspace;
@@ -587,6 +610,7 @@ moe_status moe_route(const uint16_t* x, const float* router_w, const float* rout
   Plan p;
   make_plan(T, H, E, top_k, 64, &p);
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (p.presplit && !moe::route_prefill_prepare(E, top_k)) return MOE_ERR_UNSUPPORTED_SHAPE;
   (void)hipGetLastError();
   const Tables tb{out->topk_ids, out->topk_gates, out->expert_counts, out->expert_offsets,
                   out->perm, out->inv_perm};

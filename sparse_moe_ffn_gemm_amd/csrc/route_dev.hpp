@@ -56,19 +56,20 @@ __device__ __forceinline__ void split3(const float4 v, uint2& ph, uint2& pm, uin
   pl = make_uint2(l[0], l[1]);
 }
 
-// W [E, H] fp32 -> planes [3][E, H] bf16 (hi, mid, lo), once per call for layers with
-// many token tiles, so the router workgroups load the parts instead of each splitting
-// its weight tile again.
+// LDS bytes of one router tile of TT tokens x TE experts: the x rows and the three W planes,
+// rows of kRS bf16.
+template <int TT, int TE>
+constexpr int router_lds() { return (TT + 3 * TE) * kRS * 2; }
+constexpr int kRouterLds = router_lds<kRouterTile, kRouterTile>();
 
-// LDS of one router tile: the x rows and the three W planes, kRouterTile rows of kRS bf16.
-constexpr int kRouterLds = 4 * kRouterTile * kRS * 2;
-
-// One router tile (token tile tx, expert tile ey, H slice s of kslice columns) by a
-// workgroup of NTHR threads (256: four waves of 32 tokens x 32 experts; 512: eight waves
-// of 32 x 16).  Each 16 x 16 output sub-tile sees the same sequence of matrix-core steps
-// in either width, so the partials do not depend on it.  xs / wp: kRouterLds bytes of LDS.
-// COH: the partials, x codes and scales are stored device-coherently (store_c).
-template <bool PRESPLIT, int NTHR, bool COH = false>
+// One router tile (token tile tx of TT tokens, expert tile ey of TE experts, H slice s of
+// kslice columns) by a workgroup of NTHR threads: waves in a (TT / 32) x (NTHR / 64 / (TT /
+// 32)) grid, each 32 tokens x (16 NJ) experts (64 x 64 by 256 threads: 2 x 2 waves of 32 x
+// 32; by 512: 2 x 4 of 32 x 16; 128 x 128 by 512: 4 x 2 of 32 x 64).  Each 16 x 16 output
+// sub-tile sees the same sequence of matrix-core steps in every geometry, so the partials
+// do not depend on it.  xs / wp: router_lds<TT, TE>() bytes of LDS (wp: three planes of TE
+// rows).  COH: the partials, x codes and scales are stored device-coherently (store_c).
+template <bool PRESPLIT, int NTHR, bool COH = false, int TT = kRouterTile, int TE = kRouterTile>
 __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
                                             const float* __restrict__ W, int T, int H, int E,
                                             int kslice, int tx, int ey, int s,
@@ -76,17 +77,23 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
                                             float* __restrict__ sx,
                                             const uint16_t* __restrict__ parts,
                                             uint8_t* __restrict__ sx_mx, uint16_t* xs,
-                                            uint16_t (*wp)[kRouterTile * kRS]) {
+                                            uint16_t* wp) {
   static_assert(NTHR == 256 || NTHR == 512, "router workgroup width");
-  constexpr int NJ = NTHR == 256 ? 2 : 1;        // 16-expert sub-tiles per wave
-  constexpr int XL = 1024 / NTHR;                // x loads per thread (64 rows x 16 chunks)
-  constexpr int WL = 2048 / NTHR;                // W float4 loads per thread (64 rows x 32)
-  constexpr int PL = 3 * XL;                     // pre-split part loads per thread
-  const int t0 = tx * kRouterTile, e0 = ey * kRouterTile;
+  constexpr int WAVES = NTHR / 64;
+  constexpr int WMW = TT / 32;                    // waves along tokens
+  constexpr int WNW = WAVES / WMW;                // waves along experts
+  static_assert(WMW * WNW == WAVES && TE % (16 * WNW) == 0, "router tile geometry");
+  constexpr int NJ = TE / WNW / 16;               // 16-expert sub-tiles per wave
+  constexpr int XL = TT * 16 / NTHR;              // x loads per thread (TT rows x 16 chunks)
+  constexpr int WL = TE * 32 / NTHR;              // W float4 loads per thread (TE rows x 32)
+  constexpr int PX = TE * 16 / NTHR;              // pre-split part loads per thread and plane
+  constexpr int PL = 3 * PX;
+  constexpr int PLANE = TE * kRS;                 // LDS plane stride of wp
+  const int t0 = tx * TT, e0 = ey * TE;
   const int h_begin = s * kslice;
   const int h_end = min(H, h_begin + kslice);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WMW, wn = wave / WMW;
   const bool quant = xq != nullptr && ey == 0;
   const int KBH = ceil_div(H, kBlock);
   v4f acc[2][NJ], tot[2][NJ];
@@ -95,8 +102,8 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < NJ; ++j) tot[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // one step's global loads: x 64 rows x 16 chunks of 8 bf16; W 64 rows x 32 float4, or
-  // (pre-split) three planes of 64 rows x 16 chunks of 8 bf16
+  // one step's global loads: x TT rows x 16 chunks of 8 bf16; W TE rows x 32 float4, or
+  // (pre-split) three planes of TE rows x 16 chunks of 8 bf16
   uint4 xr[XL];
   float4 wr[PRESPLIT ? 1 : WL];
   uint4 pr[PRESPLIT ? PL : 1];
@@ -112,7 +119,7 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
     if constexpr (PRESPLIT) {
 #pragma unroll
       for (int i = 0; i < PL; ++i) {
-        const int q = tid + NTHR * (i % XL), pl = i / XL;
+        const int q = tid + NTHR * (i % PX), pl = i / PX;
         const int e = e0 + (q >> 4), h = h0 + (q & 15) * 8;
         pr[i] = make_uint4(0u, 0u, 0u, 0u);
         if (e < E && h < h_end)
@@ -138,8 +145,8 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
     if constexpr (PRESPLIT) {
 #pragma unroll
       for (int i = 0; i < PL; ++i) {
-        const int q = tid + NTHR * (i % XL);
-        *reinterpret_cast<uint4*>(&wp[i / XL][(q >> 4) * kRS + (q & 15) * 8]) = pr[i];
+        const int q = tid + NTHR * (i % PX);
+        *reinterpret_cast<uint4*>(wp + (i / PX) * PLANE + (q >> 4) * kRS + (q & 15) * 8) = pr[i];
       }
     } else {
 #pragma unroll
@@ -148,9 +155,9 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
         const int row = q >> 5, c = q & 31;
         uint2 ph, pm, pl;
         split3(wr[i], ph, pm, pl);
-        *reinterpret_cast<uint2*>(&wp[0][row * kRS + c * 4]) = ph;
-        *reinterpret_cast<uint2*>(&wp[1][row * kRS + c * 4]) = pm;
-        *reinterpret_cast<uint2*>(&wp[2][row * kRS + c * 4]) = pl;
+        *reinterpret_cast<uint2*>(wp + row * kRS + c * 4) = ph;
+        *reinterpret_cast<uint2*>(wp + PLANE + row * kRS + c * 4) = pm;
+        *reinterpret_cast<uint2*>(wp + 2 * PLANE + row * kRS + c * 4) = pl;
       }
     }
     __syncthreads();
@@ -158,7 +165,7 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
     if (quant) {   // 16 lanes per token group, NTHR / 16 tokens per pass
       const int g = h0 / kBlock;
 #pragma unroll
-      for (int pass = 0; pass < kRouterTile / (NTHR / 16); ++pass) {
+      for (int pass = 0; pass < TT / (NTHR / 16); ++pass) {
         const int row = pass * (NTHR / 16) + (tid >> 4), col = 8 * (tid & 15);
         const int t = t0 + row;
         const bool in = t < T && h0 + col < h_end;
@@ -188,7 +195,7 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
       for (int p = 0; p < 3; ++p)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          b[p][j] = lds_bf8(&wp[p][(wn * 16 * NJ + 16 * j + (lane & 15)) * kRS + kofs]);
+          b[p][j] = lds_bf8(wp + p * PLANE + (wn * 16 * NJ + 16 * j + (lane & 15)) * kRS + kofs);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -215,6 +222,7 @@ __device__ __forceinline__ void router_tile(const uint16_t* __restrict__ x,
         if (t < T && e < E) store_c<COH>(out + static_cast<size_t>(t) * E + e, tot[i][j][r]);
       }
 }
+
 // ------------------------------------------------------------------------------------
 // top-k + softmax: one wave per token, four tokens per workgroup.  Lane l holds experts
 // l, l+64, l+128, l+192.  Each round takes the wave-wide (largest value, lowest index)
@@ -511,25 +519,28 @@ __device__ __forceinline__ float logit_wide(const float* __restrict__ partial, i
 }
 
 // logits[t * SE + e] for every (t, e), a NaN logit stored as -inf (it never wins).
-// G logits per thread and pass, so that G x MAXS loads are in flight together.
+// Tokens [t0, t0 + nt) of T: logits[(t - t0) * SE + e].  G logits per thread and pass, so
+// that G x MAXS loads are in flight together.
 template <int MAXS, bool COH = false>
 __device__ __forceinline__ void tail_logits(const float* __restrict__ partial, int ksplit,
                                             const float* __restrict__ bias, int T, int E, int SE,
-                                            float* logits) {
+                                            float* logits, int t0 = 0, int nt = -1) {
   constexpr int G = MAXS >= 64 ? 1 : 64 / MAXS;
-  const int TE = T * E;
+  const size_t TE = static_cast<size_t>(T) * E;
+  const int n = (nt < 0 ? T : nt) * E;
+  const size_t base = static_cast<size_t>(t0) * E;
   const int step = static_cast<int>(blockDim.x);
-  for (int i0 = threadIdx.x; i0 < TE; i0 += G * step) {
+  for (int i0 = threadIdx.x; i0 < n; i0 += G * step) {
     float v[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int i = min(i0 + g * step, TE - 1);   // past the end: recompute the last logit
-      v[g] = logit_wide<MAXS, COH>(partial, ksplit, bias, TE, i, i % E);
+      const int i = min(i0 + g * step, n - 1);   // past the end: recompute the last logit
+      v[g] = logit_wide<MAXS, COH>(partial, ksplit, bias, TE, base + i, i % E);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int i = i0 + g * step;
-      if (i < TE) logits[(i / E) * SE + i % E] = v[g] == v[g] ? v[g] : -INFINITY;
+      if (i < n) logits[(i / E) * SE + i % E] = v[g] == v[g] ? v[g] : -INFINITY;
     }
   }
 }

@@ -25,6 +25,12 @@ EDGE = [
     # one-workgroup routing tail: fewer experts than list slots, uneven expert parts
     custom_shape(T=40, H=128, E=3, top_k=3, I=64, seed=29),
     custom_shape(T=64, H=128, E=70, top_k=4, I=64, seed=30),
+    # the prefill routing kernel (T > 448): a ragged last 128-token tile, several H slices,
+    # experts beyond one 128-expert tile, a single expert, top-8 of 256
+    custom_shape(T=449, H=320, E=8, top_k=2, I=64, seed=31),
+    custom_shape(T=700, H=1536, E=200, top_k=6, I=64, seed=32),
+    custom_shape(T=520, H=192, E=1, top_k=1, I=64, seed=33),
+    custom_shape(T=1000, H=576, E=256, top_k=8, I=64, seed=34, router="hot"),
 ]
 
 
@@ -70,11 +76,13 @@ def test_route_deterministic():
         assert torch.equal(a[k], c[k]), k
 
 
-@pytest.mark.parametrize("T,E,k", [(64, 32, 4), (64, 32, 8), (300, 32, 4), (7, 5, 3)])
+@pytest.mark.parametrize("T,E,k", [(64, 32, 4), (64, 32, 8), (300, 32, 4), (7, 5, 3), (600, 32, 4),
+                                   (530, 256, 8)])
 def test_route_exact_ties(T, E, k):
     """A zero router gives every logit exactly 0: each token takes experts 0 .. k-1 (ties
     to the lower index) with gates 1/k, on the one-workgroup tail (k <= 4, one chunk), the
-    single-chunk kernels (k = 8) and the multi-chunk path (T = 300)."""
+    single-chunk kernels (k = 8), the multi-chunk path (T = 300) and the prefill routing
+    kernel (T > 448, one and two 128-expert tiles)."""
     g = torch.Generator().manual_seed(T * 1000 + E * 10 + k)
     x = torch.randn(T, 128, generator=g).to(torch.bfloat16).cuda()
     W = torch.zeros(E, 128, dtype=torch.float32, device="cuda")
