@@ -259,6 +259,26 @@ def decode_layer(shape, fmt, dev, steps=40, warmup=5):
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
     cold, warm = run(True), run(False)
+    # the same layer through the one-kernel decode path (moe_forward_fused)
+    fused = None
+    try:
+        for _ in range(warmup):
+            moe.forward_fused(*fa, out=out, routing=routing, workspace=ws)
+        evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evf:
+            torch.sum(flush, dim=0, out=sink)
+            a.record()
+            moe.forward_fused(*fa, out=out, routing=routing, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        st = moe.fused_status(ws, shape.T, shape.H, shape.E, shape.top_k, shape.I)
+        tf = np.array([a.elapsed_time(b) for a, b in evf]) * 1e3
+        fused = {"cold_us_p50": round(float(np.median(tf)), 1), "waits_ok": st == 0}
+        print(f"[bench] {shape.name}: one-kernel decode path cold p50 {fused['cold_us_p50']:.1f} us",
+              file=sys.stderr, flush=True)
+    except moe.MoEError as e:             # outside the fused kernel's envelope
+        fused = {"unsupported": str(e)}
     counts = routing["expert_counts"].cpu().numpy()
     alg = algorithmic(shape, counts, fmt)
     p50 = float(np.median(cold))
@@ -272,7 +292,8 @@ def decode_layer(shape, fmt, dev, steps=40, warmup=5):
          "warm_us_p50": round(float(np.median(warm)), 1),
          "tokens_per_s": round(shape.T / (p50 * 1e-6), 1),
          "compulsory_bytes": alg["layer_bytes"], "active_experts": alg["active_experts"],
-         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "steps": steps}
+         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "steps": steps,
+         "path": "multi-kernel (moe_forward)", "fused_kernel": fused}
     del layer, ws, flush
     torch.cuda.empty_cache()
     return r
