@@ -76,9 +76,16 @@ def pmc_record(workload, kernel):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "sparse_moe_ffn_gemm_amd", "csrc", rec.get("source", "gemm.hip"))
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return rec if sha == rec.get("source_sha256") else None
+    return rec if sources_sha256(rec.get("sources", ["gemm.hip"])) == rec.get("source_sha256") else None
+
+
+def sources_sha256(names):
+    """sha256 of the named kernel sources (csrc/), concatenated in the given order."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_moe_ffn_gemm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def gpu_sysfs(torch, index=0):
@@ -219,10 +226,11 @@ def roofline(k_alg, k_s, shape, fmt, kernel):
     return roof
 
 
-def decode_layer(shape, fmt, dev, steps=40, warmup=5):
+def decode_layer(shape, fmt, dev, steps=40, warmup=5, fused_only=False):
     """A decode-sized (weight-streaming) layer timed in the same run: per-step times with
     the caches evicted before every step by reading a 1 GiB buffer (outside the events),
-    and warm; the compulsory bytes (bench.algorithmic) over the cold median against 8 TB/s."""
+    and warm; the compulsory bytes (bench.algorithmic) over the cold median against 8 TB/s.
+    Also the cold median of the one-kernel path; with fused_only, that path alone."""
     import numpy as np
     import torch
 
@@ -242,10 +250,11 @@ def decode_layer(shape, fmt, dev, steps=40, warmup=5):
     ws = layer.workspace(shape.T)
     fa = (x, layer.router_w, layer.router_b, layer.w13, layer.w13_scales, layer.b13, layer.w2,
           layer.w2_scales, layer.b2, shape.top_k)
-    for _ in range(warmup):
-        moe.forward(*fa, out=out, routing=routing, workspace=ws)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
+    if not fused_only:
+        for _ in range(warmup):
+            moe.forward(*fa, out=out, routing=routing, workspace=ws)
 
     def run(cold):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -258,7 +267,7 @@ def decode_layer(shape, fmt, dev, steps=40, warmup=5):
             b.record()
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
-    cold, warm = run(True), run(False)
+    cold, warm = (run(True), run(False)) if not fused_only else (None, None)
     # the same layer through the one-kernel decode path (moe_forward_fused)
     fused = None
     try:
@@ -279,6 +288,10 @@ def decode_layer(shape, fmt, dev, steps=40, warmup=5):
               file=sys.stderr, flush=True)
     except moe.MoEError as e:             # outside the fused kernel's envelope
         fused = {"unsupported": str(e)}
+    if fused_only:
+        del layer, ws, flush
+        torch.cuda.empty_cache()
+        return fused
     counts = routing["expert_counts"].cpu().numpy()
     alg = algorithmic(shape, counts, fmt)
     p50 = float(np.median(cold))
@@ -403,6 +416,9 @@ def main():
     ap.add_argument("--microbench", choices=["one-token-per-expert"],
                     help="instead of the layer benchmark: the decode GEMM sweep over "
                          "expert-parallel degrees, every expert given one token")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="only time the one-kernel decode path (moe_forward_fused) on --workload "
+                         "(decode-sized), caches evicted before every step; prints one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -417,6 +433,13 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.fused_only:
+        from synth import SHAPES
+        import torch
+        r = decode_layer(SHAPES[args.workload], args.format, torch.device("cuda:0"),
+                         steps=args.steps, warmup=args.warmup, fused_only=True)
+        print(json.dumps({"fused_only": args.workload, "format": args.format, **r}), flush=True)
         return
     if args.microbench:
         one_token_per_expert(args)

@@ -534,8 +534,8 @@ __device__ __forceinline__ void tail_logits(const float* __restrict__ partial, i
     float v[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int i = min(i0 + g * step, n - 1);   // past the end: recompute the last logit
-      v[g] = logit_wide<MAXS, COH>(partial, ksplit, bias, TE, base + i, i % E);
+      const int i = i0 + g * step;
+      v[g] = i < n ? logit_wide<MAXS, COH>(partial, ksplit, bias, TE, base + i, i % E) : 0.f;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
