@@ -283,13 +283,13 @@ def e2m1_encode(v) -> np.ndarray:
     if np.isnan(v).any():
         raise ValueError("NaN has no defined code here")
     table = e2m1_decode(np.arange(8))                 # the 8 magnitudes, ascending
+    mids = (table[:-1] + table[1:]) / 2               # halfway between neighbours
     a = np.minimum(np.abs(v), E2M1_MAX)
-    d = np.abs(a[..., None] - table)
-    best = d.min(axis=-1, keepdims=True)
-    cand = d == best
-    # ties: the even code among the nearest ones
-    code = np.where(cand.sum(-1) > 1, np.argmax(cand & (np.arange(8) % 2 == 0), axis=-1),
-                    np.argmax(cand, axis=-1))
+    # the nearest magnitude's index is the number of midpoints below |v|; exactly on a
+    # midpoint both neighbours are nearest and the even code is taken
+    below = np.searchsorted(mids, a, side="left")     # midpoints < |v|
+    upto = np.searchsorted(mids, a, side="right")     # midpoints <= |v|
+    code = np.where(below == upto, below, np.where(below % 2 == 0, below, upto))
     return (code | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
 
 
