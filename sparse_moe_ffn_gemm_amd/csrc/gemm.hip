@@ -447,8 +447,12 @@ constexpr int big_tile_lds() {
 // One M-tile x n-tile: WM x (8 / WM) waves, each SM 16-row sub-tiles by BN / (8 / WM)
 // columns; SA / SB ring slots.  FP4 (with MX): MXFP4 weights in the tiled storage; a
 // B-ring slot is BN / 16 weight tiles of 1 KB, each fetched whole by one load.
+// Thread 0 takes the workgroup's next ticket from `queue` as the epilogue begins and
+// stores it to *next (LDS) during the epilogue, so the atomic's round trip overlaps the
+// epilogue's arithmetic instead of following it.
 template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX, bool FP4 = false, bool RAW = false>
-__device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile mt, uint8_t* lds) {
+__device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile mt, uint8_t* lds,
+                                         int32_t* queue, int* next) {
   constexpr int WAVES = 8, NT = WAVES * 64, WN = WAVES / WM, BM = 16 * SM * WM;
   constexpr int WR = 16 * SM, WC = BN / WN;          // rows / columns of a wave
   constexpr int SN = WC / 16;                        // sub-tiles per wave along N
@@ -466,7 +470,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // per A slot and wave: lanes [0, A_ROWS) the activation scales of the wave's A rows,
   // [32, 32 + WN SN) the weight block scales of sub-tile n of column wave wn (wn SN + n)
   float (*sS)[WAVES][64] = reinterpret_cast<float (*)[WAVES][64]>(ringB + SB * B_BYTES);
-  int* rowsrc = reinterpret_cast<int*>(sS + SA);                   // [BM]
+  int* rowsrc = reinterpret_cast<int*>(sS + SA);                   // [BM] gemm1: perm entries
   float (*red)[BM] = reinterpret_cast<float (*)[BM]>(rowsrc + BM);  // [WN][BM]
   uint16_t* sbias = reinterpret_cast<uint16_t*>(red + WN);          // [BN] bias of the B rows (bf16)
 
@@ -480,14 +484,22 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * (FP4 ? KB * 64 : K);
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
 
-  for (int r = tid; r < BM; r += NT) {
+  // gemm1: the perm entries of the tile's rows go to LDS first (direct-to-LDS, so that the
+  // weight prologue issued next can stay in flight while they are waited for)
+  if constexpr (SWIGLU) {
+    if (wave * 64 < BM) {
+      const int p = mt.row_begin + tid;
+      load_lds4(p < mt.row_end ? static_cast<const void*>(a.perm + p) : static_cast<const void*>(kZeroScale),
+                rowsrc + wave * 64);
+    }
+  }
+  // source row in A of tile row r (-1: past the tile's rows; never past A)
+  auto row_src = [&](int r) {
     const int p = mt.row_begin + r;
     int src = -1;
-    if (p < mt.row_end) src = SWIGLU ? a.perm[p] / a.top_k : p;
-    if (static_cast<unsigned>(src) >= static_cast<unsigned>(a.A_rows)) src = -1;   // never read past A
-    rowsrc[r] = src;
-  }
-  __syncthreads();
+    if (p < mt.row_end) src = SWIGLU ? rowsrc[r] / a.top_k : p;
+    return static_cast<unsigned>(src) < static_cast<unsigned>(a.A_rows) ? src : -1;
+  };
 
   // global row of w13 / w2 behind B-tile row br (-1: past the matrix)
   auto b_global_row = [&](int br) {
@@ -499,17 +511,11 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     return col < N ? col : -1;
   };
 
-  // ---- fetch descriptors ----
+  // ---- fetch descriptors: the weight side first (it does not depend on the tile's rows),
+  // so the B prologue is in flight while the activation rows are located ----
   const int a_slot = lane & 7, a_r8 = lane >> 3;
-  unsigned a_off[A_INSTR], b_off[B_INSTR];
-  bool a_ok[A_INSTR], b_ok[B_INSTR];
-#pragma unroll
-  for (int i = 0; i < A_INSTR; ++i) {
-    const int row = wave * A_ROWS + i * 8 + a_r8;
-    const int src = rowsrc[row];
-    a_ok[i] = src >= 0;
-    a_off[i] = static_cast<unsigned>(src < 0 ? 0 : src) * K + ((a_slot ^ swz_key(row)) << 4);
-  }
+  unsigned b_off[B_INSTR];
+  bool b_ok[B_INSTR];
 #pragma unroll
   for (int i = 0; i < B_INSTR; ++i) {
     if constexpr (FP4) {
@@ -530,86 +536,6 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       b_off[i] = static_cast<unsigned>(g < 0 ? b_global_row(0) : g) * K + ((a_slot ^ swz_key(row)) << 4);
     }
   }
-  // A rows' scales: per token row (stride 1 per K-step), or gathered in dispatch order
-  // with the K-step major (A_sd: the tile's rows of a K-step are one contiguous run)
-  const float* s_ptr = kZeroScale;
-  bool s_live = false;
-  int s_step = 1;
-  if (lane < A_ROWS) {
-    const int src = rowsrc[wave * A_ROWS + lane];
-    s_live = src >= 0;
-    if (a.A_sd != nullptr) {
-      s_ptr = reinterpret_cast<const float*>(a.A_sd) + (s_live ? mt.row_begin + wave * A_ROWS + lane : 0);
-      s_step = a.sd_rows;
-    } else {
-      s_ptr = a.A_scale + static_cast<size_t>(src < 0 ? 0 : src) * KB;
-    }
-  } else if (lane >= 32 && lane < 32 + WN * SN) {
-    const int q = lane - 32, qw = q / SN, n = q % SN;   // column wave qw, sub-tile n
-    int row;
-    if (SWIGLU) {
-      const int j0 = nt * (BN / 2) + qw * GW + 16 * (n % NG);
-      row = j0 < I ? ((n >= NG ? I : 0) + j0) / kBlock : -1;
-    } else {
-      const int c0 = nt * BN + qw * WC + 16 * n;
-      row = c0 < N ? c0 / kBlock : -1;
-    }
-    s_live = row >= 0;
-    s_ptr = Bsc + static_cast<size_t>(row < 0 ? 0 : row) * KB;
-  }
-
-  // MXFP8: every thread stages one 4-byte E8M0 row of K-step kt (the four 32-blocks of
-  // its 128 columns): thread t < BM the A row t, BM <= t < BM + BN the B row t - BM; one
-  // load per wave and step, like the block scales above
-  // (a B row's 4 codes of step kt sit in its 16-row tile's 64-byte scale block)
-  const uint8_t* x_ptr = reinterpret_cast<const uint8_t*>(kZeroScale);
-  bool x_live = false;
-  int x_step = 4;
-  if constexpr (MX) {
-    const int RS = 4 * KB;
-    if (tid < BM) {
-      const int src = rowsrc[tid];
-      x_live = src >= 0;
-      if (a.A_sd != nullptr) {
-        x_ptr = reinterpret_cast<const uint8_t*>(a.A_sd + (x_live ? mt.row_begin + tid : 0));
-        x_step = 4 * a.sd_rows;
-      } else {
-        x_ptr = a.A_mx + static_cast<size_t>(src < 0 ? 0 : src) * RS;
-      }
-    } else if (tid < BM + BN) {
-      const int g = b_global_row(tid - BM);
-      x_live = g >= 0;
-      const int gg = g < 0 ? 0 : g;
-      x_ptr = a.B_mx + (static_cast<size_t>(e) * N + (gg & ~15)) * RS + 4 * (gg & 15);
-      x_step = 64;
-    }
-  }
-
-  auto issue_a = [&](int kt) {   // A rows and all scales of K-step kt
-    uint8_t* As = ringA + (kt % SA) * A_BYTES;
-    const int k0 = kt * kBlock;
-    if (k0 + kBlock <= K) {
-#pragma unroll
-      for (int i = 0; i < A_INSTR; ++i) load_lds16_s(a_off[i], a.A + k0, As + (wave * A_ROWS + i * 8) * 128);
-    } else {
-#pragma unroll
-      for (int i = 0; i < A_INSTR; ++i) {
-        const int row = wave * A_ROWS + i * 8 + a_r8;
-        const int kk = k0 + ((a_slot ^ swz_key(row)) << 4);
-        unsigned off = a_off[i];
-        asm volatile("" : "+v"(off));   // recompute the address here: no hoisted 64-bit copies
-        const void* src = (a_ok[i] && kk < K) ? static_cast<const void*>(a.A + off + k0) : kZeroChunk;
-        load_lds16(src, As + (wave * A_ROWS + i * 8) * 128);
-      }
-    }
-    if constexpr (MX) {
-      const void* src = x_live ? static_cast<const void*>(x_ptr + static_cast<size_t>(x_step) * kt) : kZeroScale;
-      load_lds4(src, &sS[kt % SA][wave][0]);
-    } else if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN)) {   // lanes 0.. always: one instruction
-      const void* src = s_live ? static_cast<const void*>(s_ptr + static_cast<size_t>(kt) * s_step) : kZeroScale;
-      load_lds4(src, &sS[kt % SA][wave][0]);
-    }
-  };
   auto issue_b = [&](int kt) {
     uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
     const int k0 = kt * kBlock;
@@ -652,17 +578,113 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
                           : static_cast<const void*>(kZeroChunk);
     if (lane < BN / (2 * WAVES)) load_lds4(src, &sbias[wave * (BN / WAVES)]);
   }
-  // prologue: B runs SB-1 steps ahead, A SA-1; within a step the A loads are issued
-  // before the B loads of the later step, so "A(k) and B(k) landed" is "at most the B
-  // loads issued after A(k) are outstanding"
-  for (int s = 0; s < SB - SA && s < KB; ++s) issue_b(s);
-  for (int s = 0; s < SA - 1; ++s) {
-    if (s < KB) issue_a(s);
-    if (s + SB - SA < KB) issue_b(s + SB - SA);
+  // prologue: the weight loads of steps [0, SB-1) go out first, then (gemm1) the perm
+  // entries fetched above are waited for, and the activation loads of steps [0, SA-1)
+  // follow; step 0 waits for all of them.  From then on every step issues A(kt + SA - 1)
+  // before B(kt + SB - 1).
+  for (int s = 0; s < SB - 1 && s < KB; ++s) issue_b(s);
+  if constexpr (SWIGLU) {
+    // the perm fetch is older than this wave's weight prologue and bias loads
+    if (wave * 64 < BM) {
+      if (KB >= SB - 1) wait_vmcnt<(SB - 1) * B_INSTR + 1>();
+      else wait_vmcnt<0>();
+    }
+    barrier_only();
   }
-  // "this wave's loads of step kt landed": A(j) is always followed by B(j + SB - SA), and
-  // by the time step kt is waited for, A(kt + SA - 2) and B(kt + SB - 2) are the last
-  // loads issued.  So with SB > SA the loads after A(kt) are B(kt + SB - SA) and the
+
+  unsigned a_off[A_INSTR];
+  bool a_ok[A_INSTR];
+#pragma unroll
+  for (int i = 0; i < A_INSTR; ++i) {
+    const int row = wave * A_ROWS + i * 8 + a_r8;
+    const int src = row_src(row);
+    a_ok[i] = src >= 0;
+    a_off[i] = static_cast<unsigned>(src < 0 ? 0 : src) * K + ((a_slot ^ swz_key(row)) << 4);
+  }
+  // A rows' scales: per token row (stride 1 per K-step), or gathered in dispatch order
+  // with the K-step major (A_sd: the tile's rows of a K-step are one contiguous run)
+  const float* s_ptr = kZeroScale;
+  bool s_live = false;
+  int s_step = 1;
+  if (lane < A_ROWS) {
+    const int src = row_src(wave * A_ROWS + lane);
+    s_live = src >= 0;
+    if (a.A_sd != nullptr) {
+      s_ptr = reinterpret_cast<const float*>(a.A_sd) + (s_live ? mt.row_begin + wave * A_ROWS + lane : 0);
+      s_step = a.sd_rows;
+    } else {
+      s_ptr = a.A_scale + static_cast<size_t>(src < 0 ? 0 : src) * KB;
+    }
+  } else if (lane >= 32 && lane < 32 + WN * SN) {
+    const int q = lane - 32, qw = q / SN, n = q % SN;   // column wave qw, sub-tile n
+    int row;
+    if (SWIGLU) {
+      const int j0 = nt * (BN / 2) + qw * GW + 16 * (n % NG);
+      row = j0 < I ? ((n >= NG ? I : 0) + j0) / kBlock : -1;
+    } else {
+      const int c0 = nt * BN + qw * WC + 16 * n;
+      row = c0 < N ? c0 / kBlock : -1;
+    }
+    s_live = row >= 0;
+    s_ptr = Bsc + static_cast<size_t>(row < 0 ? 0 : row) * KB;
+  }
+
+  // MXFP8: every thread stages one 4-byte E8M0 row of K-step kt (the four 32-blocks of
+  // its 128 columns): thread t < BM the A row t, BM <= t < BM + BN the B row t - BM; one
+  // load per wave and step, like the block scales above
+  // (a B row's 4 codes of step kt sit in its 16-row tile's 64-byte scale block)
+  const uint8_t* x_ptr = reinterpret_cast<const uint8_t*>(kZeroScale);
+  bool x_live = false;
+  int x_step = 4;
+  if constexpr (MX) {
+    const int RS = 4 * KB;
+    if (tid < BM) {
+      const int src = row_src(tid);
+      x_live = src >= 0;
+      if (a.A_sd != nullptr) {
+        x_ptr = reinterpret_cast<const uint8_t*>(a.A_sd + (x_live ? mt.row_begin + tid : 0));
+        x_step = 4 * a.sd_rows;
+      } else {
+        x_ptr = a.A_mx + static_cast<size_t>(src < 0 ? 0 : src) * RS;
+      }
+    } else if (tid < BM + BN) {
+      const int g = b_global_row(tid - BM);
+      x_live = g >= 0;
+      const int gg = g < 0 ? 0 : g;
+      x_ptr = a.B_mx + (static_cast<size_t>(e) * N + (gg & ~15)) * RS + 4 * (gg & 15);
+      x_step = 64;
+    }
+  }
+
+  auto issue_a = [&](int kt) {   // A rows and all scales of K-step kt
+    uint8_t* As = ringA + (kt % SA) * A_BYTES;
+    const int k0 = kt * kBlock;
+    if (k0 + kBlock <= K) {
+#pragma unroll
+      for (int i = 0; i < A_INSTR; ++i) load_lds16_s(a_off[i], a.A + k0, As + (wave * A_ROWS + i * 8) * 128);
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_INSTR; ++i) {
+        const int row = wave * A_ROWS + i * 8 + a_r8;
+        const int kk = k0 + ((a_slot ^ swz_key(row)) << 4);
+        unsigned off = a_off[i];
+        asm volatile("" : "+v"(off));   // recompute the address here: no hoisted 64-bit copies
+        const void* src = (a_ok[i] && kk < K) ? static_cast<const void*>(a.A + off + k0) : kZeroChunk;
+        load_lds16(src, As + (wave * A_ROWS + i * 8) * 128);
+      }
+    }
+    if constexpr (MX) {
+      const void* src = x_live ? static_cast<const void*>(x_ptr + static_cast<size_t>(x_step) * kt) : kZeroScale;
+      load_lds4(src, &sS[kt % SA][wave][0]);
+    } else if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN)) {   // lanes 0.. always: one instruction
+      const void* src = s_live ? static_cast<const void*>(s_ptr + static_cast<size_t>(kt) * s_step) : kZeroScale;
+      load_lds4(src, &sS[kt % SA][wave][0]);
+    }
+  };
+  for (int s = 0; s < SA - 1 && s < KB; ++s) issue_a(s);
+  // "this wave's loads of step kt landed" (kt >= 1): A(j) is always followed by
+  // B(j + SB - SA), and by the time step kt is waited for, A(kt + SA - 2) and
+  // B(kt + SB - 2) are the last loads issued.  So with SB > SA the loads after A(kt) are B(kt + SB - SA) and the
   // SA - 2 later (A, B) step pairs; with SB == SA (B(kt) right after A(kt)) just those
   // pairs.  Near the end of K, where some of them were never issued, wait for all.
   auto wait_step = [&](int kt) {
@@ -730,7 +752,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   static_assert(NP % P == 0 && LAG < P, "partials rotate across steps");
   v4f pp[P];
   float sc_tail[LAG] = {};
-  wait_step(0);
+  wait_vmcnt<0>();   // the prologue (and the bias)
   barrier_only();
   if (wave_live) read_step(0);
   for (int kt = 0; kt < KB; ++kt) {
@@ -784,11 +806,14 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     }
   }
   wait_vmcnt<0>();
+  int ticket = 0;
+  if (tid == 0) ticket = atomicAdd(queue, 1);   // lands while the epilogue computes
 
   // ---- epilogue: lane holds rows r(m) = wm*WR + 16m + (lane & 15) and, per sub-tile n,
   // the four adjacent columns 16n + 4 (lane >> 4) + i of its column range ----
   const int cq = 4 * (lane >> 4);
   if constexpr (RAW) {   // the fp32 accumulators, at the B rows' global columns of C [rows, N]
+    if (tid == 0) *next = ticket;
 #pragma unroll
     for (int n = 0; n < SN; ++n) {
       const int g = b_global_row(sub_brow(n) + cq);   // four consecutive rows: all or none
@@ -827,6 +852,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
           hv[m][n][i] = ok ? h : 0.f;
         }
     }
+    if (tid == 0) *next = ticket;
     if constexpr (MX) {
       // 1x32 MX blocks of h: the wave's gate sub-tiles 2q and 2q+1 are 32 aligned
       // columns; the block maximum of a row is the lane's 8 values and those of the row's
@@ -910,6 +936,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       }
     }
   } else {
+    if (tid == 0) *next = ticket;
 #pragma unroll
     for (int n = 0; n < SN; ++n) {
       const int c0 = nt * BN + wn * WC + 16 * n + cq;
@@ -941,13 +968,16 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
 // the workgroups of an XCD run neighbouring tiles together and share the expert's
 // activation rows and weight tiles in their L2; a workgroup whose XCD's queue is empty
 // takes from the other XCDs' queues.  Every queue head only grows, so every workgroup
-// leaves after at most total + 8 of its fetches.
+// leaves after at most total + 8 of its fetches.  A tile's successor in the same queue is
+// claimed during its epilogue (big_tile), the first ticket of each queue before its loop.
 template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN, bool MX = false, bool FP4 = false,
           bool RAW = false>
 __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int ntiles) {
   constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB, FP4>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN, FP4>();
   __shared__ __align__(16) uint8_t lds[kFull > kNarrow ? kFull : kNarrow];
   __shared__ int s_next;
+  __shared__ int32_t s_eto[257];   // expert_tile_off, read by every tile's lookup
+  for (int i = threadIdx.x; i <= a.E; i += blockDim.x) s_eto[i] = a.expert_tile_off[i];
   const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
   const int per_xcd = (total + kGemmQueues - 1) / kGemmQueues;
   const int x0 = blockIdx.x % kGemmQueues;
@@ -955,20 +985,22 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
     const int x = (x0 + d) % kGemmQueues;
     const int lo = x * per_xcd;
     const int n = total - lo < per_xcd ? total - lo : per_xcd;   // may be <= 0
-    for (;;) {
-      __syncthreads();   // the previous tile is done with LDS and with s_next
-      if (threadIdx.x == 0) s_next = n > 0 ? atomicAdd(&a.queue[x], 1) : n;
-      __syncthreads();
-      const int t = __builtin_amdgcn_readfirstlane(s_next);
-      if (t >= n) break;
+    __syncthreads();   // the previous tile is done with LDS, every thread has read s_next
+    if (threadIdx.x == 0) s_next = n > 0 ? atomicAdd(&a.queue[x], 1) : n;
+    __syncthreads();
+    int t = __builtin_amdgcn_readfirstlane(s_next);
+    while (t < n) {
       int nt;
       MTile mt;
-      tile_of(a, ntiles, lo + t, nt, mt);
+      tile_of(a, s_eto, ntiles, lo + t, nt, mt);
+      // (big_tile's first barrier precedes its write of s_next: every thread has read t)
       if (mt.row_end - mt.row_begin <= 64) {
-        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4, RAW>(a, nt, mt, lds);
+        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4, RAW>(a, nt, mt, lds, &a.queue[x], &s_next);
       } else {
-        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4, RAW>(a, nt, mt, lds);
+        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4, RAW>(a, nt, mt, lds, &a.queue[x], &s_next);
       }
+      __syncthreads();   // the tile is done with LDS; its successor's ticket is in s_next
+      t = __builtin_amdgcn_readfirstlane(s_next);
     }
   }
 }

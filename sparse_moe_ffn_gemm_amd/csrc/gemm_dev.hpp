@@ -94,20 +94,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // `ntiles` n-tiles per M-tile.  The expert e with off[e] * ntiles <= L < off[e+1] * ntiles:
 // off is non-decreasing, so e + 1 is the number of experts with off[e] * ntiles <= L,
 // counted by ballots over one round of independent loads (E <= 256).
-__device__ __forceinline__ void tile_of(const GemmArgs& a, int ntiles, int L, int& nt, MTile& mt) {
+// `eto`: the expert_tile_off table, in global memory or a workgroup's LDS copy.
+__device__ __forceinline__ void tile_of(const GemmArgs& a, const int32_t* eto, int ntiles, int L,
+                                        int& nt, MTile& mt) {
   const int lane = threadIdx.x & 63;
   int cnt = 0;
 #pragma unroll
   for (int base = 0; base < 256; base += 64) {
     if (base < a.E) {
       const int idx = base + lane;
-      const bool le = idx < a.E && a.expert_tile_off[idx] * ntiles <= L;
+      const bool le = idx < a.E && eto[idx] * ntiles <= L;
       cnt += __builtin_popcountll(__ballot(le));
     }
   }
   const int lo = __builtin_amdgcn_readfirstlane(cnt - 1);
-  const int t0 = a.expert_tile_off[lo];
-  const int mcount = a.expert_tile_off[lo + 1] - t0;
+  const int t0 = eto[lo];
+  const int mcount = eto[lo + 1] - t0;
   const int local = L - t0 * ntiles;
   nt = local / mcount;
   mt = a.tiles[t0 + local % mcount];
@@ -128,7 +130,7 @@ __device__ __forceinline__ bool pick_tile(const GemmArgs& a, int ntiles, int& nt
   if (b / 8 >= per_xcd) return false;
   const int L = (b % 8) * per_xcd + b / 8;
   if (L >= total) return false;
-  tile_of(a, ntiles, L, nt, mt);
+  tile_of(a, a.expert_tile_off, ntiles, L, nt, mt);
   return true;
 }
 
