@@ -1015,6 +1015,22 @@ __global__ __launch_bounds__(512) void grouped_gemm_rowrun_kernel(const GemmArgs
   rowrun_tile<SWIGLU, KS, MX, FP4, NW, RAW>(a, nt, mt, dyn_lds);
 }
 
+// Block-scaled gemm1 on the row-run body at three workgroups per CU: bursts of 3 K-blocks
+// keep it within 80 VGPRs (six waves per SIMD; with 4 it needs 94), so the gemm1
+// workgroups of a decode layer (an M-tile x 128 h columns each; 736 on the 64-token
+// gpt-oss-20b layer) are all resident at once instead of running in two rounds of 512
+// (GEMM1 101.5 -> 95.7 us there, same box).  gemm2 at six waves either spills (3 K-blocks)
+// or streams no faster (2), so it keeps the kernel above.
+template <bool RAW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6, 6)))
+void grouped_gemm_rowrun_g1_kernel(const GemmArgs a, int ntiles) {
+  extern __shared__ __align__(16) uint8_t dyn_lds[];
+  int nt;
+  MTile mt;
+  if (!pick_tile(a, ntiles, nt, mt)) return;
+  rowrun_tile<true, 3, false, false, 8, RAW>(a, nt, mt, dyn_lds);
+}
+
 // Large-group launch shapes (workgroup tile 256 x BN, A / B ring depths).
 constexpr int kG1BN = 256, kG1SA = 2, kG1SB = 2;
 constexpr int kG2BN = 192, kG2SA = 2, kG2SB = 3;
@@ -1050,11 +1066,19 @@ int gemm_tile_rows(long rows, int E) {
 
 // Large dynamic LDS (above 64 KB) must be opted into per kernel; the row-run kernels stage
 // up to 64 K-blocks of their 16-row activation tile.
+static bool lds_opt_in(const void* kernel, size_t lds) {
+  if (lds <= 64 * 1024) return true;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
+}
 template <bool SWIGLU, int KS, bool MX, bool FP4, int NW, bool RAW>
 static bool rowrun_lds_ok(size_t lds) {
-  if (lds <= 64 * 1024) return true;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, KS, MX, FP4, NW, RAW>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kRowrunMaxLds) == hipSuccess;
+  return lds_opt_in(reinterpret_cast<const void*>(grouped_gemm_rowrun_kernel<SWIGLU, KS, MX, FP4, NW, RAW>), lds);
+}
+// The block-scaled row-run launch of gemm1 (SWIGLU) or gemm2.
+template <bool SWIGLU, bool RAW>
+static bool rowrun_block_lds_ok(size_t lds) {
+  if constexpr (SWIGLU) return lds_opt_in(reinterpret_cast<const void*>(grouped_gemm_rowrun_g1_kernel<RAW>), lds);
+  else return rowrun_lds_ok<false, 4, false, false, 8, RAW>(lds);
 }
 
 static size_t rowrun_lds(int K) { return rowrun_lds_bytes(K); }
@@ -1083,7 +1107,7 @@ static bool prepare(bool mx, bool fp4, int K, int bm) {
     case Family::kRowrun:
       // block-scaled: without the opt-in the LDS-ring kernel takes the launch instead
       return mx ? rowrun_lds_ok<SWIGLU, KS, true, false, 8, RAW>(lds)
-                : (rowrun_lds_ok<SWIGLU, KS, false, false, 8, RAW>(lds), true);
+                : (rowrun_block_lds_ok<SWIGLU, RAW>(lds), true);
     default:
       return true;
   }
@@ -1162,8 +1186,11 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
         grouped_gemm_rowrun_kernel<SWIGLU, KS, true, false, 8, RAW><<<g, 512, lds, st>>>(a, nts);
         return;
       }
-      if (rowrun_lds_ok<SWIGLU, KS, false, false, 8, RAW>(lds)) {
-        grouped_gemm_rowrun_kernel<SWIGLU, KS, false, false, 8, RAW><<<g, 512, lds, st>>>(a, nts);
+      if (rowrun_block_lds_ok<SWIGLU, RAW>(lds)) {
+        if constexpr (SWIGLU)
+          grouped_gemm_rowrun_g1_kernel<RAW><<<g, 512, lds, st>>>(a, nts);
+        else
+          grouped_gemm_rowrun_kernel<false, KS, false, false, 8, RAW><<<g, 512, lds, st>>>(a, nts);
         return;
       }
       break;   // no large-LDS opt-in: the LDS-ring kernel

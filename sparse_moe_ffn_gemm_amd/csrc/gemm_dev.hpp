@@ -304,22 +304,26 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
       const v8i af = lds_frag(sA + jj * 2048, r, g);
       pr[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[t], af, zero, 0, 0, 0, 0, 0, 0);
     }
-    v4f part = zero;
+    // each K-block's product folded into the accumulator in K order (the sum does not
+    // depend on the burst length)
+    float sc[KS];
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
       const int j = j0 + t;
       const int jj = j < KB ? j : KB - 1;
       const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbs), jj));
-      const float sc = (bl && j < KB) ? sSa[jj * 16 + r] * sb : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] = fmaf(pr[t][i], sc, part[i]);
+      sc[t] = (bl && j < KB) ? sSa[jj * 16 + r] * sb : 0.f;
     }
     if (NSUB == 2 && s == 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[NSUB - 1][i] += part[i];
+      for (int t = 0; t < KS; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[NSUB - 1][i] = fmaf(pr[t][i], sc[t], acc[NSUB - 1][i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[0][i] += part[i];
+      for (int t = 0; t < KS; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[0][i] = fmaf(pr[t][i], sc[t], acc[0][i]);
     }
   };
 
