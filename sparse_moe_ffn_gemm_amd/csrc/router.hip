@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int word;
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
-  router_tile<true, kRouteThreads, true, kRouteTT, kRouteTE>(x, nullptr, T, H, E, kslice, blockIdx.x, blockIdx.y,
+  // (the partials pass between this launch's workgroups; x codes and scales only to GEMM1)
+  router_tile<true, kRouteThreads, true, kRouteTT, kRouteTE, false>(x, nullptr, T, H, E, kslice, blockIdx.x, blockIdx.y,
                                                    blockIdx.z, partial, xq, sx, parts, sx_mx, xs,
                                                    xs + kRouteTT * kRS);
   // every wave's partial stores acknowledged, then the token tile's counter
@@ -80,7 +81,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(
   int32_t* h = hist + static_cast<size_t>(blockIdx.x * kRouteTT / kChunk) * E;   // one chunk
   for (int t0 = blockIdx.x * kRouteTT; t0 < min(T, (blockIdx.x + 1) * kRouteTT); t0 += kTopkRows) {
     const int nt = min(kTopkRows, T - t0);
-    if (ksplit <= 8)
+    if (ksplit <= 2)
+      tail_logits<2, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
+    else if (ksplit <= 4)
+      tail_logits<4, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
+    else if (ksplit <= 8)
       tail_logits<8, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
     else if (ksplit <= 16)
       tail_logits<16, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
