@@ -365,6 +365,13 @@ __device__ __forceinline__ void rowrun_tile(const GemmArgs& a, const int nt, con
 
   wait_vmcnt<0>();   // this wave's staging fetches (and its first bursts) have landed ...
   __syncthreads();   // ... and so have every wave's
+  // the weight block scales have landed too: passing them through an empty asm makes them
+  // values the compiler no longer tracks as outstanding loads, so it does not drain every
+  // in-flight burst (vmcnt(0)) before their first use in each K-loop iteration
+  if constexpr (!MX) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) asm volatile("" : "+v"(sbg[s]));
+  }
 
   if (live) {
     for (int b0 = 0; b0 < nbp - NB; b0 += NB) {

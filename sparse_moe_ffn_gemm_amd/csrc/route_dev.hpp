@@ -521,34 +521,30 @@ __device__ __forceinline__ float logit_wide(const float* __restrict__ partial, i
 }
 
 // logits[t * SE + e] for every (t, e), a NaN logit stored as -inf (it never wins).
-// Tokens [t0, t0 + nt) of T: logits[(t - t0) * SE + e].  Thread (q, e) = (tid / E, tid % E)
-// takes expert e of tokens q, q + P, ... (P = blockDim / E tokens per pass; E <= blockDim),
-// G of them at a time so that G x MAXS loads are in flight together (G <= 8: this code runs
-// once per workgroup, from a cold instruction cache, and a longer unrolled body cost more
-// in instruction fetches than it saved in memory round trips); the thread's (q, e) is its
-// only integer division.
-template <int MAXS, bool COH = false>
+// Tokens [t0, t0 + nt) of T: logits[(t - t0) * SE + e].  G logits per thread and pass, so
+// that G x MAXS loads are in flight together; GMAX caps G (this code runs once per
+// workgroup, from a cold instruction cache: for the prefill routing kernel's few-slice sums a
+// shorter unrolled body saved more instruction fetches than it cost in memory round trips).
+template <int MAXS, bool COH = false, int GMAX = 64>
 __device__ __forceinline__ void tail_logits(const float* __restrict__ partial, int ksplit,
                                             const float* __restrict__ bias, int T, int E, int SE,
                                             float* logits, int t0 = 0, int nt = -1) {
-  constexpr int G = MAXS >= 64 ? 1 : (64 / MAXS < 8 ? 64 / MAXS : 8);
+  constexpr int G = MAXS >= 64 ? 1 : (64 / MAXS < GMAX ? 64 / MAXS : GMAX);
   const size_t TE = static_cast<size_t>(T) * E;
-  const int n = nt < 0 ? T : nt;
-  const int P = static_cast<int>(blockDim.x) / E;
-  const int q = static_cast<int>(threadIdx.x) / E, e = static_cast<int>(threadIdx.x) - q * E;
-  if (q >= P) return;
-  for (int tb = q; tb < n; tb += G * P) {
+  const int n = (nt < 0 ? T : nt) * E;
+  const size_t base = static_cast<size_t>(t0) * E;
+  const int step = static_cast<int>(blockDim.x);
+  for (int i0 = threadIdx.x; i0 < n; i0 += G * step) {
     float v[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int t = tb + g * P;
-      v[g] = t < n ? logit_wide<MAXS, COH>(partial, ksplit, bias, TE, static_cast<size_t>(t0 + t) * E + e, e)
-                   : 0.f;
+      const int i = i0 + g * step;
+      v[g] = i < n ? logit_wide<MAXS, COH>(partial, ksplit, bias, TE, base + i, i % E) : 0.f;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int t = tb + g * P;
-      if (t < n) logits[t * SE + e] = v[g] == v[g] ? v[g] : -INFINITY;
+      const int i = i0 + g * step;
+      if (i < n) logits[(i / E) * SE + i % E] = v[g] == v[g] ? v[g] : -INFINITY;
     }
   }
 }
@@ -619,13 +615,8 @@ __device__ __forceinline__ void tail_topk(const float* logits, int SE, int T, in
         lv[s] = __int_as_float(0x7FC00000);
         li[s] = 0;
       }
-      if (t < T) {
-        // P <= 4 lists of K: unrolled to the bound, so the candidates' LDS loads are issued
-        // ahead of the dependent inserts
-#pragma unroll
-        for (int c = 0; c < 4 * K; ++c)
-          if (c < P * K) list_insert<K>(lv, li, cv[c * cs + t], ci[c * cs + t]);
-      }
+      if (t < T)
+        for (int c = 0; c < P * K; ++c) list_insert<K>(lv, li, cv[c * cs + t], ci[c * cs + t]);
     }
   }
   // the finished list of token 64 g + lane is in wave 4 g (P == 1) or wave g (P > 1)
@@ -686,11 +677,7 @@ __device__ __forceinline__ void route_tail_body(const float* __restrict__ partia
   const int tid = threadIdx.x;
   const int SE = E | 1;
   if (tid < 256) L.hist[tid] = 0;
-  if (ksplit <= 2)
-    tail_logits<2, COH>(partial, ksplit, bias, T, E, SE, L.logits);
-  else if (ksplit <= 4)
-    tail_logits<4, COH>(partial, ksplit, bias, T, E, SE, L.logits);
-  else if (ksplit <= 8)
+  if (ksplit <= 8)
     tail_logits<8, COH>(partial, ksplit, bias, T, E, SE, L.logits);
   else if (ksplit <= 16)
     tail_logits<16, COH>(partial, ksplit, bias, T, E, SE, L.logits);

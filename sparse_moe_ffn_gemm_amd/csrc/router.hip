@@ -82,17 +82,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_prefill_kernel(
   for (int t0 = blockIdx.x * kRouteTT; t0 < min(T, (blockIdx.x + 1) * kRouteTT); t0 += kTopkRows) {
     const int nt = min(kTopkRows, T - t0);
     if (ksplit <= 2)
-      tail_logits<2, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
+      tail_logits<2, true, 8>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
     else if (ksplit <= 4)
-      tail_logits<4, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
+      tail_logits<4, true, 8>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
     else if (ksplit <= 8)
-      tail_logits<8, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
+      tail_logits<8, true, 8>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
     else if (ksplit <= 16)
-      tail_logits<16, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
+      tail_logits<16, true, 8>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
     else if (ksplit <= 32)
-      tail_logits<32, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
+      tail_logits<32, true, 8>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
     else
-      tail_logits<64, true>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
+      tail_logits<64, true, 8>(partial, ksplit, bias, T, E, SE, logits, t0, nt);
     __syncthreads();
     int32_t* id = ids + static_cast<size_t>(t0) * top_k;
     float* gt = gates + static_cast<size_t>(t0) * top_k;
