@@ -480,7 +480,12 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   const int K = a.K, N = a.N, I = a.I;
   const int KB = ceil_div(K, kBlock), NBs = ceil_div(N, kBlock);
   const int e = mt.expert;
-  const bool wave_live = wm * WR < mt.row_end - mt.row_begin;
+  // a wave computes only if some of its rows and some of its columns exist (the last
+  // n-tile of a gemm1 over I = 64 mod 128 h columns, or of a gemm2 over N = 64 mod BN,
+  // leaves whole column waves idle: they still fetch their share of the tile and pass the
+  // barriers, but issue no fragment reads or matrix products)
+  const int wave_col0 = SWIGLU ? nt * (BN / 2) + wn * GW : nt * BN + wn * WC;
+  const bool wave_live = wm * WR < mt.row_end - mt.row_begin && wave_col0 < (SWIGLU ? I : N);
   const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * (FP4 ? KB * 64 : K);
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
 
