@@ -151,8 +151,8 @@ moe_status moe_forward(const uint16_t* x, const float* router_w, const float* ro
  * before each stage and after the last one:
  *   0 router GEMM (with the 1x128 quantisation of x fused in)  1 top-k + softmax
  *   2 dispatch scan  3 dispatch scatter  4 x scale-word regrouping  5 GEMM1 (+ bias,
- *   SwiGLU, requantisation)  6 GEMM2 (+ bias; for 256-row tiles, the h scale-word
- *   regrouping runs first)  7 combine  8 end
+ *   SwiGLU, requantisation; for 256-row tiles it also stores h's scale words K-block
+ *   major for GEMM2)  6 GEMM2 (+ bias)  7 combine  8 end
  * so hipEventElapsedTime(events[i], events[i+1]) is stage i's device time.  Stage 4
  * regroups the x scale words into dispatch order, K-block major, for the 256-row GEMM
  * tiles, and is empty for the other tile heights; for T > 448 the top-k + softmax runs

@@ -888,7 +888,12 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
                 *reinterpret_cast<uint32_t*>(hrow + j0) =
                     encode4_mul(hv[m][n][0], hv[m][n][1], hv[m][n][2], hv[m][n][3], mul);
             }
-            if ((lane >> 4) == 0) a.h_mx[static_cast<size_t>(p) * RSI + jb / kMxBlock] = static_cast<uint8_t>(code);
+            if ((lane >> 4) == 0) {
+              a.h_mx[static_cast<size_t>(p) * RSI + jb / kMxBlock] = static_cast<uint8_t>(code);
+              if (a.h_sd != nullptr)   // byte (jb / 32) mod 4 of word [jb / 128][p]
+                reinterpret_cast<uint8_t*>(a.h_sd)[(static_cast<size_t>(jb / kBlock) * a.sd_rows + p) * 4 +
+                                                   (jb / kMxBlock) % 4] = static_cast<uint8_t>(code);
+            }
           }
         }
       }
@@ -937,7 +942,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
           const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], 0, false)) & 0xFFFFu;
           if (j0 < I) *reinterpret_cast<uint32_t*>(hrow + j0) = lo | (hi << 16);
         }
-        if (wn == 0 && lane < 16) a.h_scale[static_cast<size_t>(p) * KBI + nt] = sc;
+        if (wn == 0 && lane < 16) {
+          a.h_scale[static_cast<size_t>(p) * KBI + nt] = sc;
+          if (a.h_sd != nullptr) a.h_sd[static_cast<size_t>(nt) * a.sd_rows + p] = __float_as_uint(sc);
+        }
       }
     }
   } else {

@@ -116,6 +116,9 @@ struct GemmArgs {
   // K-step in dispatch order, [ceil(K/128)][sd_rows]; NULL: read A_scale / A_mx
   const uint32_t* A_sd;
   int sd_rows;
+  // gemm1 of the large-group kernel: also store h's scale words in that layout,
+  // [ceil(I/128)][sd_rows] (gemm2's A_sd), or NULL
+  uint32_t* h_sd;
   float* c_raw;              // launch_gemm_raw only: [rows, N] fp32 accumulators
 };
 

@@ -283,6 +283,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   if (gather_sx) {
     g1.A_sd = at<uint32_t>(ws, p.y);
     g1.sd_rows = static_cast<int>(p.rows);
+    g1.h_sd = at<uint32_t>(ws, p.shd);   // GEMM2's A_sd, written by GEMM1's epilogue
   }
   moe::launch_gemm1(g1, p.bm, p.max_tiles, st);
   mark(ev, 6, st);
@@ -312,9 +313,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.I = I;
   g2.y_out = at<uint16_t>(ws, p.y);
   g2.queue = at<int32_t>(ws, p.num_tiles) + 1 + moe::kGemmQueues;
-  if (gather_sx) {   // h's scale words K-block major
-    moe::launch_gather_row_scales(at<uint32_t>(ws, p.sh), ceil_div(I, moe::kBlock), nullptr, 1,
-                                  static_cast<int>(p.rows), at<uint32_t>(ws, p.shd), st);
+  if (gather_sx) {   // h's scale words K-block major (stored by GEMM1)
     g2.A_sd = at<uint32_t>(ws, p.shd);
     g2.sd_rows = static_cast<int>(p.rows);
   }
