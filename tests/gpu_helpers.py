@@ -18,10 +18,12 @@ other side of an e4m3 rounding boundary than the exact value):
 from __future__ import annotations
 
 import sys
+from collections import OrderedDict
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 import sparse_moe_ffn_gemm_amd as moe
 from oracle import moe_ref as R
@@ -86,6 +88,21 @@ class GpuLayer:
         return self.layer.workspace(s.T)[off:off + nbytes].view(dtype).view(*shape)
 
 
+# The host work of a check (dequantised weights, products, windows) is per expert and
+# independent: it runs on CHECK_THREADS threads with single-threaded BLAS (numpy releases
+# the GIL), and nothing of it reads the device.
+CHECK_THREADS = 16
+
+
+def par_map(fn, items):
+    """[fn(i) for i in items] on the check threads, in order."""
+    items = list(items)
+    if len(items) <= 1:
+        return [fn(i) for i in items]
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=CHECK_THREADS) as ex:
+        return list(ex.map(fn, items))
+
+
 def quantize_by_rows(quant, w: np.ndarray, rows: int = 128):
     """The oracle's weight quantiser applied to 128-row slices of w (every format's scale
     blocks lie within one slice, so the result is the whole-matrix one; the slices keep the
@@ -101,7 +118,24 @@ def _base(shape):
 
 class OracleExperts:
     """Lazily quantised experts for the oracle (from the generator's fp32 weights, by the
-    oracle's own quantiser), in the block-scaled, the MXFP8 or the MXFP4-weight format."""
+    oracle's own quantiser), in the block-scaled, the MXFP8 or the MXFP4-weight format.
+    ``OracleExperts.of`` shares them between the checks of layers drawn from the same
+    weights (a decode layer and the prefill layer whose draw it reuses, the multi-kernel
+    and the one-kernel forward)."""
+
+    _shared: "OrderedDict" = OrderedDict()
+    KEEP = 4   # weight draws x formats kept
+
+    @classmethod
+    def of(cls, shape: LayerShape, li, fmt="block"):
+        key = (_base(shape), fmt)
+        ox = cls._shared.pop(key, None)
+        if ox is None:
+            ox = cls(shape, li, fmt)
+        cls._shared[key] = ox
+        while len(cls._shared) > cls.KEEP:
+            cls._shared.popitem(last=False)
+        return ox
 
     def __init__(self, shape: LayerShape, li, fmt="block"):
         self.shape, self.li = shape, li
@@ -196,7 +230,8 @@ class LayerCheck:
         s, li = self.shape, g.li
         self.T, self.H, self.E, self.k, self.I = s.T, s.H, s.E, s.top_k, s.I
         self.rows = s.T * s.top_k
-        self.ox = OracleExperts(s, li, g.fmt)
+        self.ox = OracleExperts.of(s, li, g.fmt)
+        self.y_cache = {}
         self.q_act, self.dq_act, _ = R._quantizer(g.fmt)
         self.out_bits = bits_host(out)
         # routing (all tokens)
@@ -273,10 +308,13 @@ class LayerCheck:
         self.weights_checked.add(e)
 
     # ---- the two halves ----
-    def check_h(self, e, p, what=""):
-        """GPU h codes and scales of expert e's dispatch rows p inside the analytic window."""
-        self.ox.prepare([e])
-        self.check_weights(e)
+    # Each check reads what it needs from the device first (serially), then does its host
+    # arithmetic per expert on the check threads; the per-expert reports are printed and the
+    # assertions made afterwards, in expert order.
+    def _h_host(self, e, hq, hs):
+        """(ok, report) of GPU h codes hq and scales hs of expert e's rows against the window
+        (host arithmetic only; ``self.rows_of[e]`` names the rows)."""
+        p, what = self.rows_of[e]
         c13, s13, _, _ = self.ox.cache[e]
         W13 = self.ox.dequant_w(c13, s13)
         C, C_abs, C_gmax = W.product_sums(self.xd[self.tok[p]], W13)
@@ -284,7 +322,6 @@ class LayerCheck:
         del W13
         h, dh = W.swiglu_window(C, C_abs, self.H, self.I, C_gmax)
         del C, C_abs, C_gmax
-        hq, hs = self.gpu_h(p)
         if self.fmt == "block":
             sok, cok, diag = W.block_h_check(h, dh, hq, hs)
         else:
@@ -292,43 +329,67 @@ class LayerCheck:
         oq, osc = self.q_act(h.astype(np.float32))
         nd = int((hq != oq).sum())
         width = np.mean(_codes_between(diag["lo"], diag["hi"]))
-        say(f"  h {what}expert {e} ({len(p)} rows): scales outside the window {int((~sok).sum())} "
-            f"of {sok.size}, codes outside {int((~cok).sum())} of {cok.size}; codes unlike the "
-            f"oracle's own {nd} ({nd / max(hq.size, 1):.1e}); admissible codes per element "
-            f"{width:.2f} on average")
-        if not (sok.all() and cok.all()):
+        rep = [f"  h {what}expert {e} ({len(p)} rows): scales outside the window {int((~sok).sum())} "
+               f"of {sok.size}, codes outside {int((~cok).sum())} of {cok.size}; codes unlike the "
+               f"oracle's own {nd} ({nd / max(hq.size, 1):.1e}); admissible codes per element "
+               f"{width:.2f} on average"]
+        ok = bool(sok.all() and cok.all())
+        if not ok:
             for rr, cc in np.argwhere(~cok)[:5]:
-                say(f"    row {rr} col {cc}: gpu code {hq[rr, cc]:#04x} oracle {oq[rr, cc]:#04x} "
-                    f"h={h[rr, cc]:.6g} dh={dh[rr, cc]:.3g}")
-        assert sok.all() and cok.all()
+                rep.append(f"    row {rr} col {cc}: gpu code {hq[rr, cc]:#04x} oracle {oq[rr, cc]:#04x} "
+                           f"h={h[rr, cc]:.6g} dh={dh[rr, cc]:.3g}")
+        return ok, rep
 
-    def y_ref(self, e, p):
-        """oracle(GPU h): y_ref and its bound for expert e's dispatch rows p."""
-        self.ox.prepare([e])
-        self.check_weights(e)
+    def _y_host(self, e, hq, hs):
+        """oracle(GPU h): (y_ref, bound) for expert e's rows with GPU h codes hq, scales hs."""
         _, _, c2, s2 = self.ox.cache[e]
         W2 = self.ox.dequant_w(c2, s2)
-        y, y_abs, y_gmax = W.product_sums(self.h_dequant(*self.gpu_h(p)), W2)
+        y, y_abs, y_gmax = W.product_sums(self.h_dequant(hq, hs), W2)
         y += R.bf16_to_f64(self.g.li.b2[e])
         dy = W.y_bound(y, y_abs, self.I, y_gmax)
-        assert np.abs(y).max() < W.F16_MAX
         return y, dy
 
-    def check_y(self, e, p, what=""):
-        y, dy = self.y_ref(e, p)
-        gy = self.gpu_y(p)
-        bad = np.abs(gy - y) > dy
-        say(f"  y {what}expert {e} ({len(p)} rows): max |err| / bound {np.max(np.abs(gy - y) / dy):.3f}, "
-            f"outside {int(bad.sum())} of {bad.size}")
-        assert not bad.any()
+    def _prepare(self, rows_of):
+        """Quantised experts, their weights checked, and the GPU h of their rows."""
+        self.rows_of = rows_of
+        experts = list(rows_of)
+        self.ox.prepare(experts)
+        for e in experts:
+            self.check_weights(e)
+        return {e: self.gpu_h(rows_of[e][0]) for e in experts}
 
     def check_experts(self, experts=None):
         """h window and y bound on every dispatch row of the experts (all active ones by default)."""
         experts = [e for e in (range(self.E) if experts is None else experts) if self.counts[e] > 0]
-        for e in experts:
-            p = np.arange(self.offsets[e], self.offsets[e + 1])
-            self.check_h(e, p)
-            self.check_y(e, p)
+        rows_of = {int(e): (np.arange(self.offsets[e], self.offsets[e + 1]), "") for e in experts}
+        gh = self._prepare(rows_of)
+        gy = {e: self.gpu_y(rows_of[e][0]) for e in rows_of}
+
+        def work(e):
+            ok, rep = self._h_host(e, *gh[e])
+            y, dy = self._y_host(e, *gh[e])
+            assert np.abs(y).max() < W.F16_MAX
+            ratio = np.abs(gy[e] - y) / dy
+            bad = int((ratio > 1).sum())
+            rep.append(f"  y expert {e} ({len(rows_of[e][0])} rows): max |err| / bound {ratio.max():.3f}, "
+                       f"outside {bad} of {ratio.size}")
+            return ok and bad == 0, rep, (y, dy)
+
+        res = par_map(work, list(rows_of))
+        for e, (ok, rep, yd) in zip(rows_of, res):
+            for line in rep:
+                say(line)
+            self.y_cache[(e, np.asarray(rows_of[e][0], np.int64).tobytes())] = yd
+        for e, (ok, rep, _) in zip(rows_of, res):
+            assert ok, f"expert {e}"
+
+    def plain_oracle_out(self, toks):
+        """The plain oracle's out of the tokens: its forward's per-token steps (routing over
+        all tokens, x quantisation of the tokens, each expert's FFN on its rows, the
+        gate-weighted sum), with the experts' FFNs (``oracle.expert_ffn``) on the check
+        threads.  Equal to ``oracle.forward(..., token_subset=toks)["out"]`` bit for bit
+        (``tests/test_oracle_layer.py`` pins that on the CPU)."""
+        return oracle_forward_out(self.g.li, self.k, self.I, self.ox, toks, self.fmt)
 
     def check_tokens(self, toks=None, h_window=True):
         """out of the tokens: oracle(GPU h) at the literal bound and the combine bound; the
@@ -339,31 +400,41 @@ class LayerCheck:
         flat = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
         p_all = self.inv[flat]
         e_all = self.ids[toks].reshape(-1)
+        what = "of the sampled tokens, " if toks.size < T else ""
+        sel_of = {int(e): np.nonzero(e_all == e)[0] for e in np.unique(e_all)}
+        gh = self._prepare({e: (p_all[sel], what) for e, sel in sel_of.items()})
+
+        def work(e):
+            p = self.rows_of[e][0]
+            ok, rep = self._h_host(e, *gh[e]) if h_window else (True, [])
+            yd = self.y_cache.get((e, np.asarray(p, np.int64).tobytes()))
+            if yd is None:
+                yd = self._y_host(e, *gh[e])
+            assert np.abs(yd[0]).max() < W.F16_MAX
+            return ok, rep, yd
+
+        res = par_map(work, list(sel_of))
         yr = np.zeros((toks.size * k, H))
         dy = np.zeros((toks.size * k, H))
-        for e in np.unique(e_all):
-            sel = np.nonzero(e_all == e)[0]
-            p = p_all[sel]
-            if h_window:
-                self.check_h(int(e), p, "of the sampled tokens, " if toks.size < T else "")
-            yr[sel], dy[sel] = self.y_ref(int(e), p)
+        for e, (ok, rep, (y, d)) in zip(sel_of, res):
+            for line in rep:
+                say(line)
+            yr[sel_of[e]], dy[sel_of[e]] = y, d
+        for e, (ok, _, _) in zip(sel_of, res):
+            assert ok, f"expert {e}"
         yr = yr.reshape(toks.size, k, H)
         dy = dy.reshape(toks.size, k, H)
         out2 = np.einsum("tk,tkh->th", self.gates[toks], yr)
         got = R.bf16_to_f64(self.out_bits[toks])
         # the plain oracle (its own h) on the same tokens
-        self.ox.prepare(np.unique(e_all))
-        ox = self.ox
-        ref = R.forward(self.g.li.x, self.g.li.router_w, self.g.li.router_b, k, self.I, ox.view(0),
-                        ox.view(1), self.g.li.b13, ox.view(2), ox.view(3), self.g.li.b2,
-                        token_subset=toks, fmt=self.fmt)
-        rms = np.sqrt(np.mean(ref["out"] ** 2))
+        ref_out = self.plain_oracle_out(toks)
+        rms = np.sqrt(np.mean(ref_out ** 2))
         d2 = np.abs(got - out2)
         lit = np.maximum(MAX_ELT_TOL * rms, bf16_ulp(out2))
         cb = W.combine_bound(self.gates[toks], self.gates_dev[toks], yr, dy, out2)
         rel2 = np.linalg.norm(got - out2) / np.linalg.norm(out2)
-        rel = np.linalg.norm(got - ref["out"]) / np.linalg.norm(ref["out"])
-        lit_plain = np.abs(got - ref["out"]).max() / rms
+        rel = np.linalg.norm(got - ref_out) / np.linalg.norm(ref_out)
+        lit_plain = np.abs(got - ref_out).max() / rms
         say(f"  out ({toks.size} tokens): vs oracle(GPU h) max/RMS {d2.max() / rms:.3e}, over the literal "
             f"bound {int((d2 > lit).sum())}, over the combine bound {int((d2 > cb).sum())}, rel_fro "
             f"{rel2:.3e}; vs plain oracle rel_fro {rel:.3e} (max/RMS {lit_plain:.3e}) of {d2.size}")
@@ -371,6 +442,32 @@ class LayerCheck:
         assert not (d2 > cb).any()
         assert rel2 <= REL_FRO_TOL and rel <= REL_FRO_TOL
         return dict(rel_fro=rel, max_over_rms=d2.max() / rms, rel_fro_gpu_h=rel2)
+
+
+def oracle_forward_out(li, top_k, I, ox, toks, fmt):
+    """``oracle.forward(...)["out"]`` of the tokens ``toks``, its per-expert FFNs on the check
+    threads (``ox``: an OracleExperts holding every expert the tokens use)."""
+    q_act, dq_act, _ = R._quantizer(fmt)
+    logits = R.router_logits(li.x, li.router_w, li.router_b)
+    ids, gates = R.topk_softmax(logits, top_k)
+    x32 = R.bf16_to_f64(li.x).astype(np.float32)
+    toks = np.asarray(toks)
+    xq, sx = q_act(x32[toks])
+    xd = dq_act(xq, sx)
+    H = li.x.shape[1]
+    experts = [int(e) for e in np.unique(ids[toks])]
+    ox.prepare(experts)
+
+    def ffn(e):
+        rows_t, rows_j = np.nonzero(ids[toks] == e)
+        c13, s13, c2, s2 = ox.cache[e]
+        ye = R.expert_ffn(xd[rows_t], c13, s13, li.b13[e], c2, s2, li.b2[e], I, fmt)[0]
+        return rows_t, rows_j, ye
+
+    y = np.zeros((toks.size, top_k, H))
+    for rows_t, rows_j, ye in par_map(ffn, experts):
+        y[rows_t, rows_j] = ye
+    return np.einsum("tk,tkh->th", gates[toks], y)
 
 
 def pick_experts(counts, bm=256):
