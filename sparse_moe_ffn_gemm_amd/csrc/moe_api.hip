@@ -62,10 +62,12 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   p->rows = static_cast<long>(T) * k;
   // split H across workgroups when there are few token x expert tiles (decode)
   const int tiles2d = ceil_div(T, moe::kRouterTile) * ceil_div(E, moe::kRouterTile);
+  // (slices of one 128-column step each where the tiles are few: gpt-oss-20b decode, 64
+  // tokens x 32 experts, 23 slices instead of 12 of two steps, routing 1 us faster)
   int ks = ceil_div(1024, tiles2d);
-  ks = std::max(1, std::min(ks, H / 128 > 0 ? H / 128 : 1));
+  ks = std::max(1, std::min(ks, ceil_div(H, moe::kBlock)));
   // the one-workgroup routing tail reads every slice of every logit: keep them few
-  if (uses_route_tail(T, E, k, 0)) ks = std::min(ks, 16);
+  if (uses_route_tail(T, E, k, 0)) ks = std::min(ks, 32);
   p->kslice = ceil_div(ceil_div(H, ks), moe::kBlock) * moe::kBlock;   // whole quantisation groups
   p->ksplit = ceil_div(H, p->kslice);
   p->nchunks = ceil_div(T, moe::kChunk);
