@@ -1044,9 +1044,14 @@ void grouped_gemm_rowrun_g1_kernel(const GemmArgs a, int ntiles) {
   rowrun_tile<true, 3, false, false, 8, RAW>(a, nt, mt, dyn_lds);
 }
 
-// Large-group launch shapes (workgroup tile 256 x BN, A / B ring depths).
+// Large-group launch shapes (workgroup tile 256 x BN, A / B ring depths).  gemm2 takes the
+// same 256-column tiles as gemm1 (a 64 x 128 tile per wave: fewer LDS fragment bytes per
+// matrix product than 192 columns' 64 x 96); the waves whose columns lie past N skip their
+// work, so an N that is not a multiple of 256 costs little (gemm2 453.9 -> 446.1 us at
+// gpt-oss-120b prefill, N = 2880; 364 -> 341 us at qwen3 prefill; 3049 -> 2775 us at the
+// DeepSeek-shaped layer, against 192-column tiles with a 3-deep weight ring).
 constexpr int kG1BN = 256, kG1SA = 2, kG1SB = 2;
-constexpr int kG2BN = 192, kG2SA = 2, kG2SB = 3;
+constexpr int kG2BN = 256, kG2SA = 2, kG2SB = 2;
 // Ring depth of narrow (at most 64-row) tiles in the large-group launch.
 constexpr int kNarrowS = 3;
 // MXFP4 weights (half the B bytes per step): both GEMMs 256 wide, B rings one deeper,
