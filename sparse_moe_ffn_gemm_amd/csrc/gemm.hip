@@ -999,7 +999,8 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
     const int lo = x * per_xcd;
     const int n = total - lo < per_xcd ? total - lo : per_xcd;   // may be <= 0
     __syncthreads();   // the previous tile is done with LDS, every thread has read s_next
-    if (threadIdx.x == 0) s_next = n > 0 ? atomicAdd(&a.queue[x], 1) : n;
+    int32_t* head = a.queue + x * kQueueStride;
+    if (threadIdx.x == 0) s_next = n > 0 ? atomicAdd(head, 1) : n;
     __syncthreads();
     int t = __builtin_amdgcn_readfirstlane(s_next);
     while (t < n) {
@@ -1008,9 +1009,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
       tile_of(a, s_eto, ntiles, lo + t, nt, mt);
       // (big_tile's first barrier precedes its write of s_next: every thread has read t)
       if (mt.row_end - mt.row_begin <= 64) {
-        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4, RAW>(a, nt, mt, lds, &a.queue[x], &s_next);
+        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4, RAW>(a, nt, mt, lds, head, &s_next);
       } else {
-        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4, RAW>(a, nt, mt, lds, &a.queue[x], &s_next);
+        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4, RAW>(a, nt, mt, lds, head, &s_next);
       }
       __syncthreads();   // the tile is done with LDS; its successor's ticket is in s_next
       t = __builtin_amdgcn_readfirstlane(s_next);

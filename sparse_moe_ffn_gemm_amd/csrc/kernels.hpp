@@ -32,6 +32,12 @@ void launch_quantize_weights_mxfp4(const float* w, int E, int N, int K, uint8_t*
 constexpr int kRouterTile = 64;     // tokens / experts per router GEMM workgroup
 constexpr int kChunk = 256;         // tokens per dispatch chunk
 constexpr int kGemmQueues = 8;      // per-XCD work queues of one large-group GEMM launch
+// Ints between work-queue heads (and after the tile count): 4 KB, so that each head is an
+// address of its own memory channel.  Atomics that several XCDs issue to one address are
+// performed one after another beyond the XCDs' own L2s; with the eight heads of a launch
+// on one line, one ticket per workgroup at the start of a 1104-workgroup launch cost
+// 33 us there, which the queue heads' spacing avoids.
+constexpr int kQueueStride = 1024;
 
 // partial[s][t][e] = sum over the s-th slice of H (kslice a multiple of 128) of
 // x[t,h] * W[e,h]; also clears hist[0, hist_n) for the top-k step, and with xq != NULL
@@ -99,7 +105,7 @@ struct GemmArgs {
   const MTile* tiles;
   const int32_t* num_tiles;
   const int32_t* expert_tile_off;   // [E+1] first M-tile of each expert, [E] = num_tiles
-  int32_t* queue;            // [kGemmQueues] work-queue heads, zero at launch
+  int32_t* queue;            // kGemmQueues work-queue heads kQueueStride ints apart, zero at launch
   int E;
   int K, N, I;
   uint8_t* h_out;            // gemm1: [rows, I]

@@ -96,7 +96,8 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   p->chunk_base = take(sizeof(int32_t) * p->nchunks * static_cast<size_t>(E));
   p->max_tiles16 = static_cast<int>(p->rows / 16 + std::min<long>(E, p->rows));
   p->tiles = take(sizeof(moe::MTile) * static_cast<size_t>(p->max_tiles16));
-  p->num_tiles = take(sizeof(int32_t) * (1 + 2 * moe::kGemmQueues));   // + the GEMMs' queues
+  // the tile count, then the two GEMMs' queue heads, kQueueStride ints apart
+  p->num_tiles = take(sizeof(int32_t) * moe::kQueueStride * (1 + 2 * moe::kGemmQueues));
   p->expert_tile_off = take(sizeof(int32_t) * (E + 1));
   p->ids = take(sizeof(int32_t) * p->rows);
   p->gates = take(sizeof(float) * p->rows);
@@ -281,7 +282,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g1.N = 2 * I;
   g1.I = I;
   g1.h_out = at<uint8_t>(ws, p.h);
-  g1.queue = at<int32_t>(ws, p.num_tiles) + 1;
+  g1.queue = at<int32_t>(ws, p.num_tiles) + moe::kQueueStride;
   if (gather_sx) {
     g1.A_sd = at<uint32_t>(ws, p.y);
     g1.sd_rows = static_cast<int>(p.rows);
@@ -314,7 +315,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.N = H;
   g2.I = I;
   g2.y_out = at<uint16_t>(ws, p.y);
-  g2.queue = at<int32_t>(ws, p.num_tiles) + 1 + moe::kGemmQueues;
+  g2.queue = at<int32_t>(ws, p.num_tiles) + moe::kQueueStride * (1 + moe::kGemmQueues);
   if (gather_sx) {   // h's scale words K-block major (stored by GEMM1)
     g2.A_sd = at<uint32_t>(ws, p.shd);
     g2.sd_rows = static_cast<int>(p.rows);

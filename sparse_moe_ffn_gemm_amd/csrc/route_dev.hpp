@@ -491,7 +491,8 @@ __device__ __forceinline__ void dispatch_scan_body(const int32_t* hist, int nchu
       store_c<COH>(expert_tile_off + E, toff + ntl);
     }
   }
-  if (tid >= 1 && tid <= 2 * kGemmQueues) store_c<COH>(num_tiles + tid, 0);   // the GEMMs' work queues
+  if (tid >= 1 && tid <= 2 * kGemmQueues)   // the GEMMs' work-queue heads
+    store_c<COH>(num_tiles + kQueueStride * tid, 0);
   if (ids != nullptr) {   // a single chunk (T <= kChunk): its scatter follows in this workgroup
     __syncthreads();      // every thread is past the tile scan's use of tmp and part
     if (tid < E) tmp[tid] = off;   // the chunk's first slot of each expert = its offset

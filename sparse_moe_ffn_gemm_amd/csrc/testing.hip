@@ -30,7 +30,7 @@ RawPlan raw_plan(long rows, int E, int K) {
     return o;
   };
   p.tiles = take(sizeof(moe::MTile) * static_cast<size_t>(rows / 16 + std::min<long>(E, rows)));
-  p.num_tiles = take(sizeof(int32_t) * (1 + 2 * moe::kGemmQueues));
+  p.num_tiles = take(sizeof(int32_t) * moe::kQueueStride * (1 + 2 * moe::kGemmQueues));
   p.expert_tile_off = take(sizeof(int32_t) * (E + 1));
   p.sd = take(sizeof(uint32_t) * static_cast<size_t>(rows) * ceil_div(K, moe::kBlock));
   p.total = off;
@@ -81,7 +81,7 @@ moe_status moe_test_gemm_raw(int gemm, int format, int bm, const uint8_t* A,
 
   // the tile list: bm-row tiles per expert, expert-major; work-queue heads zero
   std::vector<moe::MTile> tiles;
-  std::vector<int32_t> tile_off(E + 1), head(1 + 2 * moe::kGemmQueues, 0);
+  std::vector<int32_t> tile_off(E + 1), head(moe::kQueueStride * (1 + 2 * moe::kGemmQueues), 0);
   int off = 0;
   for (int e = 0; e < E; ++e) {
     tile_off[e] = static_cast<int32_t>(tiles.size());
@@ -124,7 +124,7 @@ moe_status moe_test_gemm_raw(int gemm, int format, int bm, const uint8_t* A,
   g.tiles = d_tiles;
   g.num_tiles = d_num;
   g.expert_tile_off = d_off;
-  g.queue = d_num + 1;
+  g.queue = d_num + moe::kQueueStride;
   g.E = E;
   g.K = K;
   g.N = N;
