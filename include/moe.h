@@ -289,9 +289,9 @@ moe_status moe_forward_mxfp4_profiled(const uint16_t* x, const float* router_w,
  * T <= 128, T * E <= 16384, at most 24 routed rows per expert on average
  * (T * top_k / E <= 24), H, I <= 8192.
  * Every wait of a workgroup inside the kernel is on work taken from the queue before its
- * own, so it ends once that work does; each wait is nevertheless bounded (about 2^21 polls)
- * and, past the bound, the workgroup records an error in the workspace and exits, leaving
- * `out` incomplete.  moe_fused_status reports it. */
+ * own, so it ends once that work does; each wait is nevertheless bounded (about 2^17 polls,
+ * a fraction of a second) and, past the bound, the workgroup records an error in the
+ * workspace and exits, leaving `out` incomplete.  moe_fused_status reports it. */
 moe_status moe_forward_fused(const uint16_t* x, const float* router_w, const float* router_b,
                              const uint8_t* w13, const void* w13_scales, const uint16_t* b13,
                              const uint8_t* w2, const void* w2_scales, const uint16_t* b2,

@@ -57,7 +57,7 @@ moe_status moe_test_gemm_raw(int gemm, int format, int bm, const uint8_t* A,
                              size_t workspace_bytes, void* stream);
 
 /* Bound on the polls of every wait inside later moe_forward_fused launches of this process
- * (default 2097152).  A negative value makes every wait give up at once, so the error path
+ * (default 131072).  A negative value makes every wait give up at once, so the error path
  * (the status word that moe_fused_status reads, every workgroup exiting normally) can be
  * exercised without any wait actually running out.  Returns the previous bound. */
 int moe_test_set_fused_spin_limit(int polls);

@@ -41,7 +41,7 @@ namespace moe {
 
 namespace {
 
-int g_spin_limit = 1 << 21;
+int g_spin_limit = 1 << 17;   // about 0.2 s of polls (one per ~4k cycles)
 
 // Work items: workgroup b's first ticket is b (the queue head starts at the grid size, so
 // the launch does not begin with one atomic per workgroup on one address); after that,
@@ -61,9 +61,13 @@ __device__ __forceinline__ int next_item(int32_t* head, int& claimed, int* word)
   return q;
 }
 
-// Waits until *w >= target: thread 0 polls (relaxed device-scope loads), the workgroup
-// follows; the handed-off data is then read with device-coherent loads.  False (and the
-// error code recorded) after `limit` unsuccessful polls.
+// Waits until *w >= target: thread 0 polls (relaxed device-scope loads, about one per
+// 4k cycles: device-scope accesses to one address are served one after another outside the
+// XCDs' L2s, and tighter polling by the waiting workgroups delays the counter updates and
+// ticket claims of the working ones -- one poll per 128 cycles took the gpt-oss-20b decode
+// layer 227.5 us, one per 4k cycles 215.9 us), the workgroup follows; the handed-off data is
+// then read with device-coherent loads.  False (and the error code recorded) after `limit`
+// unsuccessful polls.
 __device__ __forceinline__ bool wait_at_least(int32_t* w, int target, int32_t* err, int limit,
                                               int* word) {
   __syncthreads();
@@ -78,7 +82,7 @@ __device__ __forceinline__ bool wait_at_least(int32_t* w, int target, int32_t* e
           ok = 0;
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(60);
       }
     }
     if (!ok) atomicOr(err, kFusedErrWait);

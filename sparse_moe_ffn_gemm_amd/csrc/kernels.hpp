@@ -187,7 +187,7 @@ bool fused_prepare(int fmt, size_t lds);
 // as many workgroups as the device holds at once (at most max_items).
 void launch_fused(const FusedArgs& f, int fmt, size_t lds, int max_tiles, long max_items,
                   hipStream_t st);
-// Polls per wait of later launches (test hook; default 1 << 21); returns the previous bound.
+// Polls per wait of later launches (test hook; default 1 << 17); returns the previous bound.
 int set_fused_spin_limit(int polls);
 
 // ---- combine ----
