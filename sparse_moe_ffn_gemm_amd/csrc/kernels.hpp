@@ -40,17 +40,15 @@ constexpr int kGemmQueues = 8;      // per-XCD work queues of one large-group GE
 constexpr int kQueueStride = 1024;
 
 // partial[s][t][e] = sum over the s-th slice of H (kslice a multiple of 128) of
-// x[t,h] * W[e,h]; also clears hist[0, hist_n) for the top-k step, and with xq != NULL
-// writes the 1x128 quantisation of x (codes xq [T,H], scales sx [T, ceil(H/128)]), the
-// same as launch_quantize_act.  With parts != NULL (space for 3 E H bf16) W is first
-// split once into its three bf16 planes there (worth it when many token tiles would each
-// split their weight tile again).
+// x[t,h] * W[e,h] (each tile splits its W rows into their three bf16 planes itself); also
+// clears hist[0, hist_n) for the top-k step, and with xq != NULL writes the 1x128
+// quantisation of x (codes xq [T,H], scales sx [T, ceil(H/128)]), the same as
+// launch_quantize_act.
 // With sx_mx != NULL the x quantisation is MXFP8 instead (E8M0 codes into sx_mx, rows of
 // 4 ceil(H/128) bytes).
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
                           int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
-                          uint8_t* xq = nullptr, float* sx = nullptr, uint16_t* parts = nullptr,
-                          uint8_t* sx_mx = nullptr);
+                          uint8_t* xq = nullptr, float* sx = nullptr, uint8_t* sx_mx = nullptr);
 // Prefill-sized routing (T > 448): the weight split into W's three bf16 planes (which also
 // zeroes hist [nchunks][E] and tile_done [ceil(T/64)], contiguous), then one kernel that
 // computes 64-token x 128-expert router tiles over ksplit H slices of kslice columns

@@ -173,7 +173,6 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
                             at<int32_t>(ws, p.hist), tail ? 0 : p.nchunks * p.E, st,
                             quant_x ? at<uint8_t>(ws, p.xq) : nullptr,
                             quant_x && !mx ? at<float>(ws, p.sx) : nullptr,
-                            nullptr,
                             quant_x && mx ? at<uint8_t>(ws, p.sx) : nullptr);
   mark(ev, 1, st);
   if (tail) {

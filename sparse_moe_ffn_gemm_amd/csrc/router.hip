@@ -116,7 +116,6 @@ static size_t route_prefill_lds(int E, int top_k) {
 }
 
 // One router tile per workgroup: grid (token tiles, expert tiles, H slices).
-template <bool PRESPLIT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ W, int T,
                                                             int H, int E, int kslice,
@@ -124,7 +123,6 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             int32_t* __restrict__ hist,
                                                             int hist_n, uint8_t* __restrict__ xq,
                                                             float* __restrict__ sx,
-                                                            const uint16_t* __restrict__ parts,
                                                             uint8_t* __restrict__ sx_mx) {
   __shared__ __align__(16) uint16_t xs[kRouterTile * kRS];
   __shared__ __align__(16) uint16_t wp[3][kRouterTile * kRS];   // hi, mid, lo parts of W
@@ -135,8 +133,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     const int lo = bid * per, hi = min(hist_n, lo + per);
     for (int i = lo + threadIdx.x; i < hi; i += 256) hist[i] = 0;
   }
-  router_tile<PRESPLIT, 256>(x, W, T, H, E, kslice, blockIdx.x, blockIdx.y, blockIdx.z, partial, xq,
-                             sx, parts, sx_mx, xs, &wp[0][0]);
+  router_tile<false, 256>(x, W, T, H, E, kslice, blockIdx.x, blockIdx.y, blockIdx.z, partial, xq,
+                          sx, nullptr, sx_mx, xs, &wp[0][0]);
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int ksplit,
@@ -230,18 +228,10 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
 
 void launch_router_logits(const uint16_t* x, const float* W, int T, int H, int E, int ksplit,
                           int kslice, float* partial, int32_t* hist, int hist_n, hipStream_t st,
-                          uint8_t* xq, float* sx, uint16_t* parts, uint8_t* sx_mx) {
+                          uint8_t* xq, float* sx, uint8_t* sx_mx) {
   dim3 grid(ceil_div(T, kRouterTile), ceil_div(E, kRouterTile), ksplit);
-  if (parts != nullptr) {
-    const long n4 = static_cast<long>(E) * H / 4;   // H is a multiple of 64
-    router_split_kernel<<<dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st>>>(
-        W, n4, static_cast<long>(E) * H, parts, nullptr, 0);
-    router_logits_kernel<true><<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist,
-                                                           hist_n, xq, sx, parts, sx_mx);
-  } else {
-    router_logits_kernel<false><<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist,
-                                                            hist_n, xq, sx, nullptr, sx_mx);
-  }
+  router_logits_kernel<<<grid, dim3(256), 0, st>>>(x, W, T, H, E, kslice, partial, hist, hist_n, xq,
+                                                   sx, sx_mx);
 }
 
 void route_prefill_shape(int T, int H, int E, int* ksplit, int* kslice) {
