@@ -438,11 +438,17 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
 // ------------------------------------------------------------------------------------
 // LDS bytes of one tile body: A and B rings, scale slots, row sources, row-amax exchange,
 // bias
-template <int BN, int WM, int SM, int SA, int SB, bool FP4 = false>
+template <int BN, int WM, int SM, int SA, int SB, bool FP4 = false, int XR = 0>
 constexpr int big_tile_lds() {
-  return SA * (16 * SM * WM) * 128 + SB * BN * (FP4 ? 64 : 128) + SA * 8 * 64 * 4 + (16 * SM * WM) * 4 +
-         (8 / WM) * (16 * SM * WM) * 4 + BN * 2;
+  constexpr int BM = 16 * SM * WM + 16 * XR;
+  return SA * BM * 128 + SB * BN * (FP4 ? 64 : 128) + SA * 8 * 64 * 4 + (BM + 63) / 64 * 64 * 4 +
+         (8 / WM) * BM * 4 + BN * 2;
 }
+
+// Row stride (floats) of the extra rows' sums in LDS: BN + 4, so that the 16 rows of a
+// fragment's float4 accesses fall in distinct banks.
+template <int BN>
+constexpr int big_extra_stride() { return BN + 4; }
 
 // One M-tile x n-tile: WM x (8 / WM) waves, each SM 16-row sub-tiles by BN / (8 / WM)
 // columns; SA / SB ring slots.  FP4 (with MX): MXFP4 weights in the tiled storage; a
@@ -450,28 +456,42 @@ constexpr int big_tile_lds() {
 // Thread 0 takes the workgroup's next ticket from `queue` as the epilogue begins and
 // stores it to *next (LDS) during the epilogue, so the atomic's round trip overlaps the
 // epilogue's arithmetic instead of following it.
-template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX, bool FP4 = false, bool RAW = false>
+// XR = 1 (block-scaled full tiles): the tile may hold 16 rows beyond BM (an expert's last
+// rows, kBigExtraRows).  They are staged with the A ring (2 rows per wave) and each wave
+// multiplies them with two of its 16-column weight sub-tiles per step, after its own
+// products; their sums live in LDS (accx, [16][big_extra_stride]), since the wave's
+// registers are taken by its 64 x 128 accumulators, and get their own epilogue.  The
+// arithmetic per element is the same as for every other row (the same promotion, in K
+// order), so the outputs equal those of a separate 16-row tile.
+template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX, bool FP4 = false, bool RAW = false,
+          int XR = 0>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile mt, uint8_t* lds,
-                                         int32_t* queue, int* next) {
+                                         int32_t* queue, int* next, float* accx) {
   constexpr int WAVES = 8, NT = WAVES * 64, WN = WAVES / WM, BM = 16 * SM * WM;
+  constexpr int BMX = BM + 16 * XR, XPW = 16 * XR / WAVES;   // rows with the extra ones, per wave
+  constexpr int XS = big_extra_stride<BN>();
   constexpr int WR = 16 * SM, WC = BN / WN;          // rows / columns of a wave
   constexpr int SN = WC / 16;                        // sub-tiles per wave along N
   constexpr int NG = SN / 2, GW = BN / (2 * WN);     // gemm1: gate sub-tiles / columns per wave
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * (FP4 ? 64 : 128);
+  constexpr int A_BYTES = BMX * 128, B_BYTES = BN * (FP4 ? 64 : 128);
   constexpr int A_ROWS = BM / WAVES, B_ROWS = BN / WAVES;   // rows each wave fetches per step
   constexpr int A_INSTR = A_ROWS / 8, B_INSTR = FP4 ? B_ROWS / 16 : B_ROWS / 8;
   static_assert(!FP4 || (MX && B_ROWS % 16 == 0), "MXFP4 weights: E8M0 scales, whole tiles per wave");
   static_assert(WC % 16 == 0 && BN % 64 == 0 && (!SWIGLU || SN % 2 == 0), "tile");
   static_assert(SA >= 2 && SB >= SA, "rings");
   static_assert(A_ROWS % 8 == 0 && A_ROWS <= 32 && WN * SN <= 32 && B_ROWS % 8 == 0, "scale lanes");
+  // extra rows: block scales only; two of a wave's sub-tiles each (gemm1: a gate and its up
+  // sub-tile), all of a wave's columns in one 128-row weight scale block (gemm2)
+  static_assert(XR == 0 || (XR == 1 && !MX && !FP4 && XPW == 2 && 32 + WN * SN <= 48 &&
+                            (SWIGLU ? NG == WM : SN == 2 * WM && WC == 128)), "extra rows");
 
   uint8_t* ringA = lds;
   uint8_t* ringB = ringA + SA * A_BYTES;
   // per A slot and wave: lanes [0, A_ROWS) the activation scales of the wave's A rows,
   // [32, 32 + WN SN) the weight block scales of sub-tile n of column wave wn (wn SN + n)
   float (*sS)[WAVES][64] = reinterpret_cast<float (*)[WAVES][64]>(ringB + SB * B_BYTES);
-  int* rowsrc = reinterpret_cast<int*>(sS + SA);                   // [BM] gemm1: perm entries
-  float (*red)[BM] = reinterpret_cast<float (*)[BM]>(rowsrc + BM);  // [WN][BM]
+  int* rowsrc = reinterpret_cast<int*>(sS + SA);   // [BMX rounded up to 64] gemm1: perm entries
+  float (*red)[BMX] = reinterpret_cast<float (*)[BMX]>(rowsrc + (BMX + 63) / 64 * 64);  // [WN][BMX]
   uint16_t* sbias = reinterpret_cast<uint16_t*>(red + WN);          // [BN] bias of the B rows (bf16)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -486,13 +506,14 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // barriers, but issue no fragment reads or matrix products)
   const int wave_col0 = SWIGLU ? nt * (BN / 2) + wn * GW : nt * BN + wn * WC;
   const bool wave_live = wm * WR < mt.row_end - mt.row_begin && wave_col0 < (SWIGLU ? I : N);
+  const bool has_extra = XR > 0 && mt.row_end - mt.row_begin > BM;   // uniform
   const uint8_t* Bexp = a.B + static_cast<size_t>(e) * N * (FP4 ? KB * 64 : K);
   const float* Bsc = a.B_scale + static_cast<size_t>(e) * NBs * KB;
 
   // gemm1: the perm entries of the tile's rows go to LDS first (direct-to-LDS, so that the
   // weight prologue issued next can stay in flight while they are waited for)
   if constexpr (SWIGLU) {
-    if (wave * 64 < BM) {
+    if (wave * 64 < BMX) {
       const int p = mt.row_begin + tid;
       load_lds4(p < mt.row_end ? static_cast<const void*>(a.perm + p) : static_cast<const void*>(kZeroScale),
                 rowsrc + wave * 64);
@@ -590,7 +611,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   for (int s = 0; s < SB - 1 && s < KB; ++s) issue_b(s);
   if constexpr (SWIGLU) {
     // the perm fetch is older than this wave's weight prologue and bias loads
-    if (wave * 64 < BM) {
+    if (wave * 64 < BMX) {
       if (KB >= SB - 1) wait_vmcnt<(SB - 1) * B_INSTR + 1>();
       else wait_vmcnt<0>();
     }
@@ -606,16 +627,28 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     a_ok[i] = src >= 0;
     a_off[i] = static_cast<unsigned>(src < 0 ? 0 : src) * K + ((a_slot ^ swz_key(row)) << 4);
   }
+  // XR: the wave's XPW extra rows, one load of lanes [0, 8 XPW) per step
+  unsigned xr_off = 0;
+  bool xr_ok = false;
+  if constexpr (XR > 0) {
+    const int row = BM + wave * XPW + a_r8;
+    const int src = lane < 8 * XPW ? row_src(row) : -1;
+    xr_ok = src >= 0;
+    xr_off = static_cast<unsigned>(src < 0 ? 0 : src) * K + ((a_slot ^ swz_key(row)) << 4);
+  }
   // A rows' scales: per token row (stride 1 per K-step), or gathered in dispatch order
   // with the K-step major (A_sd: the tile's rows of a K-step are one contiguous run)
   const float* s_ptr = kZeroScale;
   bool s_live = false;
   int s_step = 1;
-  if (lane < A_ROWS) {
-    const int src = row_src(wave * A_ROWS + lane);
+  // (XR: lanes [48, 48 + XPW) the scales of the wave's extra rows)
+  const bool xs_lane = XR > 0 && lane >= 48 && lane < 48 + XPW;
+  if (lane < A_ROWS || xs_lane) {
+    const int r = lane < A_ROWS ? wave * A_ROWS + lane : BM + wave * XPW + (lane - 48);
+    const int src = row_src(r);
     s_live = src >= 0;
     if (a.A_sd != nullptr) {
-      s_ptr = reinterpret_cast<const float*>(a.A_sd) + (s_live ? mt.row_begin + wave * A_ROWS + lane : 0);
+      s_ptr = reinterpret_cast<const float*>(a.A_sd) + (s_live ? mt.row_begin + r : 0);
       s_step = a.sd_rows;
     } else {
       s_ptr = a.A_scale + static_cast<size_t>(src < 0 ? 0 : src) * KB;
@@ -678,10 +711,23 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
         load_lds16(src, As + (wave * A_ROWS + i * 8) * 128);
       }
     }
+    if constexpr (XR > 0) {
+      if (lane < 8 * XPW) {
+        uint8_t* dst = As + (BM + wave * XPW) * 128;
+        if (k0 + kBlock <= K) {
+          load_lds16_s(xr_off, a.A + k0, dst);
+        } else {
+          const int kk = k0 + ((a_slot ^ swz_key(BM + wave * XPW + a_r8)) << 4);
+          unsigned off = xr_off;
+          asm volatile("" : "+v"(off));
+          load_lds16(xr_ok && kk < K ? static_cast<const void*>(a.A + off + k0) : kZeroChunk, dst);
+        }
+      }
+    }
     if constexpr (MX) {
       const void* src = x_live ? static_cast<const void*>(x_ptr + static_cast<size_t>(x_step) * kt) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
-    } else if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN)) {   // lanes 0.. always: one instruction
+    } else if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN) || xs_lane) {   // lanes 0.. always: one instruction
       const void* src = s_live ? static_cast<const void*>(s_ptr + static_cast<size_t>(kt) * s_step) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
     }
@@ -693,7 +739,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // SA - 2 later (A, B) step pairs; with SB == SA (B(kt) right after A(kt)) just those
   // pairs.  Near the end of K, where some of them were never issued, wait for all.
   auto wait_step = [&](int kt) {
-    constexpr int PAIR = A_INSTR + 1 + B_INSTR;
+    constexpr int PAIR = A_INSTR + 1 + (XR > 0 ? 1 : 0) + B_INSTR;
     constexpr int AFTER = (SB > SA ? B_INSTR : 0) + (SA - 2) * PAIR;
     if (kt + SB - 2 < KB) {
       wait_vmcnt<AFTER>();
@@ -795,6 +841,30 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       }
 #pragma unroll
       for (int j = 0; j < LAG; ++j) sc_tail[j] = sav[(NP - LAG + j) % SM] * sbv[scale_col((NP - LAG + j) / SM)];
+      if constexpr (XR > 0) {
+        {   // the extra rows x the wave's sub-tiles c0, c1: sums in accx
+          // (the lane index is produced here, in the loop, so that no address of this block
+          // stays live across the K loop: the body has no register to spare for one)
+          int ln;
+          asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+          const int xr = ln & 15, xg = ln >> 4;
+          const v8i ax = lds_frag(ringA + (kt % SA) * A_BYTES, BM + xr, xg);
+          const float sx = sS[kt % SA][xr / XPW][48 + xr % XPW];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int c = SWIGLU ? wm + u * NG : 2 * wm + u;
+            float4* d = reinterpret_cast<float4*>(accx + xr * XS + sub_brow(c) + 4 * xg);
+            float4 sm = *d;
+            const v8i bx = lds_frag(Bs, sub_brow(c) + xr, xg);
+            const v4f q = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bx, ax, zero, 0, 0, 0, 0, 0, 0);
+            const float ec = sx * sbv[SWIGLU && u == 1 ? NG : 0];
+            sm.x = fmaf(q[0], ec, sm.x); sm.y = fmaf(q[1], ec, sm.y);
+            sm.z = fmaf(q[2], ec, sm.z); sm.w = fmaf(q[3], ec, sm.w);
+            *d = sm;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
     }
     if (kt + 1 < KB) {
       wait_step(kt + 1);
@@ -814,6 +884,85 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   int ticket = 0;
   if (tid == 0) ticket = atomicAdd(queue, 1);   // lands while the epilogue computes
 
+  // The extra rows' epilogue (has_extra, uniform): thread t takes row t / 32 of them and
+  // 8 B-tile rows (gemm1: 4 h columns) of it; it clears what it read for the next tile.
+  auto extra_epilogue = [&]() {
+    __syncthreads();   // every wave's last accumulation into accx is done
+    const int xr = tid >> 5, p = mt.row_begin + BM + xr;
+    if constexpr (RAW) {
+      const int c = (tid & 31) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int g = b_global_row(c + i);
+        if (g >= 0 && p < mt.row_end) a.c_raw[static_cast<size_t>(p) * N + g] = accx[xr * XS + c + i];
+        accx[xr * XS + c + i] = 0.f;
+      }
+    } else if constexpr (SWIGLU) {
+      const int hc = (tid & 31) * 4, j0 = nt * (BN / 2) + hc;
+      const bool ok = j0 < I;
+      float4* gp = reinterpret_cast<float4*>(accx + xr * XS + hc);
+      float4* up = reinterpret_cast<float4*>(accx + xr * XS + BN / 2 + hc);
+      const float4 gs = *gp, us = *up;
+      *gp = make_float4(0.f, 0.f, 0.f, 0.f);
+      *up = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float ga[4] = {gs.x, gs.y, gs.z, gs.w}, ua[4] = {us.x, us.y, us.z, us.w};
+      const uint2 g2 = *reinterpret_cast<const uint2*>(&sbias[hc]);
+      const uint2 u2 = *reinterpret_cast<const uint2*>(&sbias[BN / 2 + hc]);
+      float bg[4], bu[4];
+      bg[0] = __uint_as_float(g2.x << 16); bg[1] = __uint_as_float(g2.x & 0xFFFF0000u);
+      bg[2] = __uint_as_float(g2.y << 16); bg[3] = __uint_as_float(g2.y & 0xFFFF0000u);
+      bu[0] = __uint_as_float(u2.x << 16); bu[1] = __uint_as_float(u2.x & 0xFFFF0000u);
+      bu[2] = __uint_as_float(u2.y << 16); bu[3] = __uint_as_float(u2.y & 0xFFFF0000u);
+      float hv[4], mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = ga[i] + bg[i];
+        const float u = ua[i] + bu[i];
+        const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+        hv[i] = ok ? h : 0.f;
+        mx = fmaxf(mx, fabsf(hv[i]));
+      }
+#pragma unroll
+      for (int w = 1; w < 32; w <<= 1) mx = fmaxf(mx, __shfl_xor(mx, w, 64));
+      const float sc = group_scale(mx);
+      const float rs = __builtin_amdgcn_rcpf(sc);
+      float q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q0 = hv[i] * rs;
+        const float q1 = fmaf(fmaf(-q0, sc, hv[i]), rs, q0);
+        q[i] = fminf(fmaxf(q1, -kFp8Max), kFp8Max);
+      }
+      if (p < mt.row_end) {
+        const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false)) & 0xFFFFu;
+        const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], 0, false)) & 0xFFFFu;
+        if (ok) *reinterpret_cast<uint32_t*>(a.h_out + static_cast<size_t>(p) * I + j0) = lo | (hi << 16);
+        if ((tid & 31) == 0) {
+          a.h_scale[static_cast<size_t>(p) * ceil_div(I, kBlock) + nt] = sc;
+          if (a.h_sd != nullptr) a.h_sd[static_cast<size_t>(nt) * a.sd_rows + p] = __float_as_uint(sc);
+        }
+      }
+    } else {
+      const int c = (tid & 31) * 8, c0 = nt * BN + c;
+      float4* sp = reinterpret_cast<float4*>(accx + xr * XS + c);
+      const float4 v0 = sp[0], v1 = sp[1];
+      sp[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      sp[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c0 < N && p < mt.row_end) {   // N is a multiple of 64: all eight or none
+        const uint4 b4 = *reinterpret_cast<const uint4*>(&sbias[c]);
+        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float blo = __uint_as_float(bw[i] << 16), bhi = __uint_as_float(bw[i] & 0xFFFF0000u);
+          o[i] = f32_to_f16_sat(v[2 * i] + blo) | (static_cast<uint32_t>(f32_to_f16_sat(v[2 * i + 1] + bhi)) << 16);
+        }
+        *reinterpret_cast<uint4*>(a.y_out + static_cast<size_t>(p) * N + c0) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  };
+
   // ---- epilogue: lane holds rows r(m) = wm*WR + 16m + (lane & 15) and, per sub-tile n,
   // the four adjacent columns 16n + 4 (lane >> 4) + i of its column range ----
   const int cq = 4 * (lane >> 4);
@@ -830,6 +979,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
           *reinterpret_cast<float4*>(a.c_raw + static_cast<size_t>(p) * N + g) =
               make_float4(acc[m][n][0], acc[m][n][1], acc[m][n][2], acc[m][n][3]);
       }
+    }
+    if constexpr (XR > 0) {
+      if (has_extra) extra_epilogue();
     }
     return;
   }
@@ -948,6 +1100,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
         }
       }
     }
+    if constexpr (XR > 0) {
+      if (has_extra) extra_epilogue();
+    }
   } else {
     if (tid == 0) *next = ticket;
 #pragma unroll
@@ -967,6 +1122,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
               f32_to_f16_sat(acc[m][n][2] + bv[2]) | (static_cast<uint32_t>(f32_to_f16_sat(acc[m][n][3] + bv[3])) << 16));
       }
     }
+    if constexpr (XR > 0) {
+      if (has_extra) extra_epilogue();
+    }
   }
 }
 
@@ -983,14 +1141,20 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
 // takes from the other XCDs' queues.  Every queue head only grows, so every workgroup
 // leaves after at most total + 8 of its fetches.  A tile's successor in the same queue is
 // claimed during its epilogue (big_tile), the first ticket of each queue before its loop.
+// XR = 1 (block scales, a.xr = kBigExtraRows): full tiles of up to 256 + 16 rows take
+// the extra-row body; a separate instantiation, so that launches without such tiles keep
+// the two-body kernel and its register allocation.
 template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN, bool MX = false, bool FP4 = false,
-          bool RAW = false>
+          bool RAW = false, int XR = 0>
 __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int ntiles) {
-  constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB, FP4>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN, FP4>();
+  static_assert(XR == 0 || (!MX && !FP4 && 16 * XR == kBigExtraRows), "extra rows of the tile list");
+  constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB, FP4, XR>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN, FP4>();
   __shared__ __align__(16) uint8_t lds[kFull > kNarrow ? kFull : kNarrow];
+  __shared__ __align__(16) float accx[XR ? 16 * big_extra_stride<BN>() : 4];
   __shared__ int s_next;
   __shared__ int32_t s_eto[257];   // expert_tile_off, read by every tile's lookup
   for (int i = threadIdx.x; i <= a.E; i += blockDim.x) s_eto[i] = a.expert_tile_off[i];
+  for (int i = threadIdx.x; i < (XR ? 16 * big_extra_stride<BN>() : 4); i += blockDim.x) accx[i] = 0.f;
   const int total = __builtin_amdgcn_readfirstlane(*a.num_tiles) * ntiles;
   const int per_xcd = (total + kGemmQueues - 1) / kGemmQueues;
   const int x0 = blockIdx.x % kGemmQueues;
@@ -1009,9 +1173,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a,
       tile_of(a, s_eto, ntiles, lo + t, nt, mt);
       // (big_tile's first barrier precedes its write of s_next: every thread has read t)
       if (mt.row_end - mt.row_begin <= 64) {
-        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4, RAW>(a, nt, mt, lds, head, &s_next);
+        big_tile<SWIGLU, BN, 2, 2, SAN, SBN, MX, FP4, RAW>(a, nt, mt, lds, head, &s_next, accx);
+      } else if (XR > 0 && mt.row_end - mt.row_begin > 256) {
+        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4, RAW, XR>(a, nt, mt, lds, head, &s_next, accx);
       } else {
-        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4, RAW>(a, nt, mt, lds, head, &s_next);
+        big_tile<SWIGLU, BN, 4, 4, SA, SB, MX, FP4, RAW>(a, nt, mt, lds, head, &s_next, accx);
       }
       __syncthreads();   // the tile is done with LDS; its successor's ticket is in s_next
       t = __builtin_amdgcn_readfirstlane(s_next);
@@ -1185,6 +1351,11 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
           grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, true, false, RAW><<<g, 512, 0, st>>>(a, nt_big);
         else
           grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS, true, false, RAW><<<g, 512, 0, st>>>(a, nt_big);
+      } else if (a.xr > 0) {   // M-tiles of up to 256 + kBigExtraRows rows
+        if constexpr (SWIGLU)
+          grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, false, false, RAW, 1><<<g, 512, 0, st>>>(a, nt_big);
+        else
+          grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS, false, false, RAW, 1><<<g, 512, 0, st>>>(a, nt_big);
       } else if constexpr (SWIGLU) {
         grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, false, false, RAW><<<g, 512, 0, st>>>(a, nt_big);
       } else {

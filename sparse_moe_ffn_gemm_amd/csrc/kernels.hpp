@@ -38,6 +38,24 @@ constexpr int kGemmQueues = 8;      // per-XCD work queues of one large-group GE
 // on one line, one ticket per workgroup at the start of a 1104-workgroup launch cost
 // 33 us there, which the queue heads' spacing avoids.
 constexpr int kQueueStride = 1024;
+// Rows that an expert's last 256-row M-tile may hold beyond 256 in the block-scaled
+// large-group GEMMs (their full tile body takes them, the sums of the extra rows kept in
+// LDS), so that an expert with up to 272 rows is one M-tile instead of a full tile and a
+// 16-row tile that streams the same weights again.
+constexpr int kBigExtraRows = 16;
+// The extra rows of a block-scaled 256-row layer of `rows` routed rows over E experts:
+// kBigExtraRows where the mean group is below 384 rows (most groups then hold just over
+// 256 rows or fewer, and many would end in a tile of a few rows), else 0 (their
+// remainders spread evenly, few end that short, and the kernel without the extra-row
+// body keeps more of its registers).
+inline int big_extra_rows(long rows, int E) { return rows < 384L * E ? kBigExtraRows : 0; }
+// M-tiles of an expert with cnt rows in tiles of bm rows whose last one may hold xr more:
+// tile i covers rows [i bm, i bm + bm), the last one [i bm, cnt).
+__host__ __device__ inline int expert_tiles(int cnt, int bm, int xr) {
+  if (cnt <= 0) return 0;
+  const int n = (cnt - xr + bm - 1) / bm;
+  return n > 1 ? n : 1;
+}
 
 // partial[s][t][e] = sum over the s-th slice of H (kslice a multiple of 128) of
 // x[t,h] * W[e,h] (each tile splits its W rows into their three bf16 planes itself); also
@@ -65,11 +83,12 @@ void launch_route_prefill(const uint16_t* x, const float* W, const float* bias, 
 // ids/gates, counted into the per-chunk expert histogram hist[chunk][E] (cleared before)
 void launch_topk(const float* partial, int ksplit, const float* bias, int T, int E, int top_k,
                  int32_t* ids, float* gates, int32_t* hist, hipStream_t st);
-// counts, offsets, per-chunk bases and the M-tile list for tiles of `bm` rows;
+// counts, offsets, per-chunk bases and the M-tile list for tiles of `bm` rows (an expert's
+// last tile up to bm + xr, expert_tiles);
 // num_tiles[0] = number of M-tiles, num_tiles[1 .. 2 kGemmQueues] (the two GEMMs' work
 // queues) are cleared.  With ids != NULL (only when nchunks == 1) the same workgroup also
 // does the scatter (perm, inv), replacing launch_dispatch_scatter.
-void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32_t* counts,
+void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int xr, int32_t* counts,
                           int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
                           int32_t* expert_tile_off, hipStream_t st, const int32_t* ids = nullptr,
                           int T = 0, int top_k = 0, int32_t* perm = nullptr, int32_t* inv = nullptr);
@@ -124,6 +143,7 @@ struct GemmArgs {
   // [ceil(I/128)][sd_rows] (gemm2's A_sd), or NULL
   uint32_t* h_sd;
   float* c_raw;              // launch_gemm_raw only: [rows, N] fp32 accumulators
+  int xr;                    // block-scaled 256-row tiles: rows an M-tile holds past 256 (0 or kBigExtraRows)
 };
 
 // Rows per M-tile chosen for a layer with `rows` routed rows over E experts.

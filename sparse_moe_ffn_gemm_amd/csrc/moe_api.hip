@@ -21,6 +21,7 @@ struct Plan {
   int T, H, E, k, I;
   long rows;
   int ksplit, kslice, nchunks, bm, max_tiles;
+  int xr;          // rows an expert's last M-tile may hold beyond bm (moe::expert_tiles)
   bool presplit;   // prefill-sized routing: W split once per call, then the routing kernel
                    // (route_prefill: 64-token x 128-expert router tiles, top-k fused)
   size_t partial, hist, wparts, chunk_base, tiles, num_tiles, expert_tile_off;
@@ -80,6 +81,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   // (H and I = 64 mod 128, the row-run kernel) keep 16-row tiles, all others 256
   const bool mx_rowrun = bm_block == 16 && H % 128 != 0 && I % 128 != 0 && H <= 8192 && I <= 8192;
   p->bm = fmt == kMxfp4 ? (bm_block == 16 ? 16 : 256) : fmt == kMxfp8 ? (mx_rowrun ? 16 : 256) : bm_block;
+  p->xr = fmt == kBlockFp8 && p->bm == 256 ? moe::big_extra_rows(p->rows, E) : 0;
   p->max_tiles = static_cast<int>(p->rows / p->bm + std::min<long>(E, p->rows));
   // the tile list is sized for 16-row tiles, the most of any format, so that every format
   // shares one workspace layout
@@ -157,7 +159,7 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
                               at<int32_t>(ws, p.hist) + static_cast<size_t>(p.nchunks) * p.E, st);
     mark(ev, 1, st);
     mark(ev, 2, st);
-    moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, tb.counts, tb.offsets,
+    moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, p.xr, tb.counts, tb.offsets,
                               at<int32_t>(ws, p.chunk_base), at<moe::MTile>(ws, p.tiles),
                               at<int32_t>(ws, p.num_tiles), at<int32_t>(ws, p.expert_tile_off), st);
     mark(ev, 3, st);
@@ -187,7 +189,7 @@ void enqueue_routing(const Plan& p, const uint16_t* x, const float* rw, const fl
   moe::launch_topk(at<float>(ws, p.partial), p.ksplit, rb, p.T, p.E, p.k, tb.ids, tb.gates,
                    at<int32_t>(ws, p.hist), st);
   mark(ev, 2, st);
-  moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, tb.counts, tb.offsets,
+  moe::launch_dispatch_scan(at<int32_t>(ws, p.hist), p.nchunks, p.E, p.bm, p.xr, tb.counts, tb.offsets,
                             at<int32_t>(ws, p.chunk_base), at<moe::MTile>(ws, p.tiles),
                             at<int32_t>(ws, p.num_tiles), at<int32_t>(ws, p.expert_tile_off), st,
                             one_chunk ? tb.ids : nullptr, p.T, p.k, tb.perm, tb.inv);
@@ -263,6 +265,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g1.B = w13;
   g1.mx = mx;
   g1.fp4 = fmt == kMxfp4;
+  g1.xr = p.xr;
   if (mx) {
     g1.A_mx = at<uint8_t>(ws, p.sx);
     g1.B_mx = static_cast<const uint8_t*>(w13_scales);
@@ -298,6 +301,7 @@ static moe_status forward_impl(const uint16_t* x, const float* router_w, const f
   g2.B = w2;
   g2.mx = mx;
   g2.fp4 = fmt == kMxfp4;
+  g2.xr = p.xr;
   if (mx) {
     g2.A_mx = at<uint8_t>(ws, p.sh);
     g2.B_mx = static_cast<const uint8_t*>(w2_scales);

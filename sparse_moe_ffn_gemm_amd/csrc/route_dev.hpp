@@ -435,6 +435,7 @@ __device__ int exclusive_scan256(int v, int* tmp) {
 // memory or to this workgroup's LDS.  COH: the tables are stored device-coherently.
 template <bool COH = false>
 __device__ __forceinline__ void dispatch_scan_body(const int32_t* hist, int nchunks, int E, int bm,
+                                                   int xr,
                                                    int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ chunk_base,
@@ -473,14 +474,14 @@ __device__ __forceinline__ void dispatch_scan_body(const int32_t* hist, int nchu
     }
   }
   __syncthreads();
-  const int ntl = (q == 0 && e < E) ? (cnt + bm - 1) / bm : 0;
+  const int ntl = (q == 0 && e < E) ? expert_tiles(cnt, bm, xr) : 0;
   const int toff = exclusive_scan256(ntl, tmp);
   if (q == 0) {
     const int base = off;
     for (int i = 0; i < ntl; ++i) {
       // (expert, row_begin) and (row_end, pad) as two 8-byte words
       const uint32_t rb = static_cast<uint32_t>(base + i * bm);
-      const uint32_t re = static_cast<uint32_t>(min(base + (i + 1) * bm, base + cnt));
+      const uint32_t re = static_cast<uint32_t>(i + 1 < ntl ? base + (i + 1) * bm : base + cnt);
       uint64_t* w = reinterpret_cast<uint64_t*>(tiles + toff + i);
       store_c<COH>(w, static_cast<uint64_t>(static_cast<uint32_t>(e)) | (static_cast<uint64_t>(rb) << 32));
       store_c<COH>(w + 1, static_cast<uint64_t>(re));
@@ -694,7 +695,7 @@ __device__ __forceinline__ void route_tail_body(const float* __restrict__ partia
   else
     tail_topk<8, COH>(L.logits, SE, T, E, top_k, L.cv, L.ci, L.cs, ids, gates, L.sids, L.hist);
   __syncthreads();
-  dispatch_scan_body<COH>(L.hist, 1, E, bm, counts, offsets, chunk_base, tiles, num_tiles,
+  dispatch_scan_body<COH>(L.hist, 1, E, bm, 0, counts, offsets, chunk_base, tiles, num_tiles,
                           expert_tile_off, L.sids, T, top_k, perm, inv, L.part, L.tmp);
 }
 

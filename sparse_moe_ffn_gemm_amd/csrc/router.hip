@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
 }
 
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ hist,
-                                                             int nchunks, int E, int bm,
+                                                             int nchunks, int E, int bm, int xr,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ chunk_base,
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
                                                              int32_t* __restrict__ inv) {
   __shared__ int part[4][256];
   __shared__ int tmp[256];
-  dispatch_scan_body(hist, nchunks, E, bm, counts, offsets, chunk_base, tiles, num_tiles,
+  dispatch_scan_body(hist, nchunks, E, bm, xr, counts, offsets, chunk_base, tiles, num_tiles,
                      expert_tile_off, ids, T, top_k, perm, inv, part, tmp);
 }
 
@@ -271,11 +271,11 @@ void launch_topk(const float* partial, int ksplit, const float* bias, int T, int
                                                         gates, hist);
 }
 
-void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int32_t* counts,
+void launch_dispatch_scan(const int32_t* hist, int nchunks, int E, int bm, int xr, int32_t* counts,
                           int32_t* offsets, int32_t* chunk_base, MTile* tiles, int32_t* num_tiles,
                           int32_t* expert_tile_off, hipStream_t st, const int32_t* ids, int T,
                           int top_k, int32_t* perm, int32_t* inv) {
-  dispatch_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(hist, nchunks, E, bm, counts, offsets,
+  dispatch_scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(hist, nchunks, E, bm, xr, counts, offsets,
                                                        chunk_base, tiles, num_tiles,
                                                        expert_tile_off, ids, T, top_k, perm, inv);
 }

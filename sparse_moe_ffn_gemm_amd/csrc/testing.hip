@@ -79,15 +79,19 @@ moe_status moe_test_gemm_raw(int gemm, int format, int bm, const uint8_t* A,
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (rows == 0) return MOE_OK;
 
-  // the tile list: bm-row tiles per expert, expert-major; work-queue heads zero
+  // the tile list: bm-row tiles per expert, expert-major, by the forward's rule (the last
+  // tile of a block-scaled 256-row launch may hold moe::kBigExtraRows more); work-queue
+  // heads zero
+  const int xr = !mx && bm == 256 ? moe::big_extra_rows(rows, E) : 0;
   std::vector<moe::MTile> tiles;
   std::vector<int32_t> tile_off(E + 1), head(moe::kQueueStride * (1 + 2 * moe::kGemmQueues), 0);
   int off = 0;
   for (int e = 0; e < E; ++e) {
     tile_off[e] = static_cast<int32_t>(tiles.size());
-    for (int r = 0; r < expert_counts[e]; r += bm)
-      tiles.push_back(moe::MTile{e, off + r, off + std::min(r + bm, expert_counts[e]), 0});
-    off += expert_counts[e];
+    const int cnt = expert_counts[e], n = moe::expert_tiles(cnt, bm, xr);
+    for (int i = 0; i < n; ++i)
+      tiles.push_back(moe::MTile{e, off + i * bm, off + (i + 1 < n ? (i + 1) * bm : cnt), 0});
+    off += cnt;
   }
   tile_off[E] = static_cast<int32_t>(tiles.size());
   head[0] = static_cast<int32_t>(tiles.size());
@@ -130,6 +134,7 @@ moe_status moe_test_gemm_raw(int gemm, int format, int bm, const uint8_t* A,
   g.N = N;
   g.I = gemm == 1 ? N / 2 : K;
   g.c_raw = C;
+  g.xr = xr;
   if (ok && bm == 256) {   // the large-group kernels read the A scale words K-block major
     moe::launch_gather_row_scales(static_cast<const uint32_t*>(A_scales), ceil_div(K, moe::kBlock),
                                   g.perm, g.top_k, static_cast<int>(rows),

@@ -470,15 +470,17 @@ def oracle_forward_out(li, top_k, I, ox, toks, fmt):
     return np.einsum("tk,tkh->th", gates[toks], y)
 
 
-def pick_experts(counts, bm=256):
-    """Experts whose every row the prefill checks cover: one with a full 256-row tile and a
-    narrow overflow tile (256 < rows <= 320) if any, the hottest, and the least busy active
-    one."""
+def pick_experts(counts, bm=256, extra=16):
+    """Experts whose every row the prefill checks cover: one whose single M-tile holds rows
+    past 256 (256 < rows <= 256 + extra: the block-scaled full tile's extra rows; other
+    formats split it), one with a full 256-row tile and a narrow overflow tile
+    (256 + extra < rows <= 320), if any, the hottest, and the least busy active one."""
     act = np.nonzero(counts > 0)[0]
     pick = [int(act[np.argmax(counts[act])]), int(act[np.argmin(counts[act])])]
-    over = np.nonzero((counts > bm) & (counts <= bm + 64))[0]
-    if over.size:
-        pick.insert(0, int(over[0]))
+    for lo, hi in ((bm + extra, bm + 64), (bm, bm + extra)):
+        over = np.nonzero((counts > lo) & (counts <= hi))[0]
+        if over.size:
+            pick.insert(0, int(over[0]))
     return list(dict.fromkeys(pick))
 
 

@@ -9,7 +9,8 @@ significand, so any correct evaluation order gives the exact result, and the GPU
 equal the float64 reference bit for bit.  A wrong fragment layout, a wrong K-tail chunk, a
 swapped gate/up pairing, a wrong scale row or block, or a tile that reads another expert's
 rows changes the exact value.  Every kernel family is covered: the persistent 256-row
-kernel (full tiles, full-body tiles of 65..255 rows, narrow tiles of at most 64 rows), the
+kernel (full tiles, block-scaled full tiles with 1..16 extra rows, full-body tiles of
+65..255 rows, narrow tiles of at most 64 rows), the
 LDS-ring kernel (16/64/128-row tiles), the row-run streaming kernel (K = 64 mod 128), in
 the block-scaled, MXFP8 and MXFP4 formats, with K tails of 64, N tails, idle experts.
 
@@ -51,11 +52,23 @@ class Case:
 
 
 CASES = [
-    # persistent 256-row kernel: full + narrow (44), idle, exact 256, narrow only (17),
-    # full + full-body 74-row tile; K tail 64; gate tile half past I
+    # persistent 256-row kernel.  Block scales: a layer whose mean group is below 384 rows
+    # takes the kernel whose full tiles may hold 16 extra rows, a layer of larger groups
+    # the one without (cases 24, 25).
+    # full + narrow (44), idle, exact 256, narrow only (17), full + full-body 74-row tile;
+    # K tail 64; gate tile half past I
     Case(1, "block", 256, [300, 0, 256, 17, 330], 320, 384, 1),
     Case(1, "block", 256, [300, 0, 256, 17, 330], 320, 384, 2, unit_scales=True),
     Case(2, "block", 256, [270, 64, 0, 500], 192, 320, 3),           # N tail (192-wide tiles)
+    # 256-row tiles holding up to 16 more rows (an expert's last rows, sums kept in LDS):
+    # 272 and 257 rows (one tile each), 528 (full + 272), 273 (full + a 17-row narrow tile)
+    Case(1, "block", 256, [272, 0, 257, 17, 528, 273], 320, 384, 21),
+    Case(1, "block", 256, [272, 0, 257, 17, 528, 273], 320, 384, 22, unit_scales=True),
+    Case(2, "block", 256, [271, 528, 0, 258], 192, 320, 23),
+    # mean group >= 384 rows: no extra rows (full tiles, full + 32- and 18-row narrow tiles,
+    # a 188-row full-body tile)
+    Case(1, "block", 256, [800, 0, 530], 320, 384, 24),
+    Case(2, "block", 256, [700, 0, 460], 192, 320, 25),
     # LDS-ring kernel: 16-row tiles (K = 0 mod 128), 64- and 128-row tiles with K tails
     Case(1, "block", 16, [5, 16, 0, 33, 1], 256, 384, 4),
     Case(2, "block", 16, [5, 16, 0, 33, 1], 256, 320, 5),
@@ -237,6 +250,7 @@ ACC_CASES = [
     (1, "block", 256, [300, 256], 2880, 512),
     (1, "block", 16, [12, 16], 2880, 512),
     (2, "block", 256, [300, 256], 2048, 384),
+    (1, "block", 256, [270, 256], 2880, 512),    # a tile with extra rows
     (2, "block", 16, [24, 30], 128, 256),
     (1, "mxfp8", 256, [300, 256], 2880, 512),
     (2, "mxfp8", 16, [24, 30], 192, 256),
@@ -244,7 +258,7 @@ ACC_CASES = [
 ]
 
 
-@pytest.mark.parametrize("gemm,fmt,bm,counts,K,N", ACC_CASES, ids=[f"g{a[0]}-{a[1]}-bm{a[2]}-K{a[4]}" for a in ACC_CASES])
+@pytest.mark.parametrize("gemm,fmt,bm,counts,K,N", ACC_CASES, ids=[f"g{a[0]}-{a[1]}-bm{a[2]}-K{a[4]}-r{a[3][0]}" for a in ACC_CASES])
 def test_raw_gemm_within_accumulation_bound(gemm, fmt, bm, counts, K, N):
     """Quantised N(0,1) activations and N(0, 0.02^2) weights (the oracle's quantisers): the
     GPU's accumulators lie within the accumulation bound of tests/windows.py (the matrix
