@@ -441,7 +441,7 @@ void grouped_gemm_kernel(const GemmArgs a, int max_tiles,
 template <int BN, int WM, int SM, int SA, int SB, bool FP4 = false, int XR = 0>
 constexpr int big_tile_lds() {
   constexpr int BM = 16 * SM * WM + 16 * XR;
-  return SA * BM * 128 + SB * BN * (FP4 ? 64 : 128) + SA * 8 * 64 * 4 + (BM + 63) / 64 * 64 * 4 +
+  return SA * BM * 128 + SB * BN * (FP4 ? 64 : 128) + SA * (8 + XR) * 64 * 4 + (BM + 63) / 64 * 64 * 4 +
          (8 / WM) * BM * 4 + BN * 2;
 }
 
@@ -456,13 +456,14 @@ constexpr int big_extra_stride() { return BN + 4; }
 // Thread 0 takes the workgroup's next ticket from `queue` as the epilogue begins and
 // stores it to *next (LDS) during the epilogue, so the atomic's round trip overlaps the
 // epilogue's arithmetic instead of following it.
-// XR = 1 (block-scaled full tiles): the tile may hold 16 rows beyond BM (an expert's last
-// rows, kBigExtraRows).  They are staged with the A ring (2 rows per wave) and each wave
-// multiplies them with two of its 16-column weight sub-tiles per step, after its own
-// products; their sums live in LDS (accx, [16][big_extra_stride]), since the wave's
-// registers are taken by its 64 x 128 accumulators, and get their own epilogue.  The
-// arithmetic per element is the same as for every other row (the same promotion, in K
-// order), so the outputs equal those of a separate 16-row tile.
+// XR = 1 (full tiles, block scales or MXFP8): the tile may hold 16 rows beyond BM (an
+// expert's last rows, kBigExtraRows).  They are staged with the A ring (2 rows per wave,
+// their scales in lanes 48.. of the wave's scale load, MX codes in a ninth row of the scale
+// slot) and each wave multiplies them with two of its 16-column weight sub-tiles per step,
+// after its own products; their sums live in LDS (accx, [16][big_extra_stride]), since the
+// wave's registers are taken by its 64 x 128 accumulators, and get their own epilogue.  The
+// arithmetic per element is the same as for every other row (the same promotion or the
+// same scaled accumulation, in K order), so the outputs equal those of a separate tile.
 template <bool SWIGLU, int BN, int WM, int SM, int SA, int SB, bool MX, bool FP4 = false, bool RAW = false,
           int XR = 0>
 __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile mt, uint8_t* lds,
@@ -482,14 +483,15 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   static_assert(A_ROWS % 8 == 0 && A_ROWS <= 32 && WN * SN <= 32 && B_ROWS % 8 == 0, "scale lanes");
   // extra rows: block scales only; two of a wave's sub-tiles each (gemm1: a gate and its up
   // sub-tile), all of a wave's columns in one 128-row weight scale block (gemm2)
-  static_assert(XR == 0 || (XR == 1 && !MX && !FP4 && XPW == 2 && 32 + WN * SN <= 48 &&
+  static_assert(XR == 0 || (XR == 1 && !FP4 && XPW == 2 && 32 + WN * SN <= 48 &&
                             (SWIGLU ? NG == WM : SN == 2 * WM && WC == 128)), "extra rows");
 
   uint8_t* ringA = lds;
   uint8_t* ringB = ringA + SA * A_BYTES;
   // per A slot and wave: lanes [0, A_ROWS) the activation scales of the wave's A rows,
   // [32, 32 + WN SN) the weight block scales of sub-tile n of column wave wn (wn SN + n)
-  float (*sS)[WAVES][64] = reinterpret_cast<float (*)[WAVES][64]>(ringB + SB * B_BYTES);
+  // (XR: a ninth row per slot, the MX codes of the extra rows: word 2 w + i = row BM + 2 w + i)
+  float (*sS)[WAVES + XR][64] = reinterpret_cast<float (*)[WAVES + XR][64]>(ringB + SB * B_BYTES);
   int* rowsrc = reinterpret_cast<int*>(sS + SA);   // [BMX rounded up to 64] gemm1: perm entries
   float (*red)[BMX] = reinterpret_cast<float (*)[BMX]>(rowsrc + (BMX + 63) / 64 * 64);  // [WN][BMX]
   uint16_t* sbias = reinterpret_cast<uint16_t*>(red + WN);          // [BN] bias of the B rows (bf16)
@@ -694,6 +696,23 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     }
   }
 
+  // XR with MX: lanes [0, XPW) fetch the E8M0 words of the wave's extra rows
+  const uint8_t* xx_ptr = reinterpret_cast<const uint8_t*>(kZeroScale);
+  bool xx_live = false;
+  int xx_step = 4;
+  if constexpr (MX && XR > 0) {
+    if (lane < XPW) {
+      const int src = row_src(BM + wave * XPW + lane);
+      xx_live = src >= 0;
+      if (a.A_sd != nullptr) {
+        xx_ptr = reinterpret_cast<const uint8_t*>(a.A_sd + (xx_live ? mt.row_begin + BM + wave * XPW + lane : 0));
+        xx_step = 4 * a.sd_rows;
+      } else {
+        xx_ptr = a.A_mx + static_cast<size_t>(src < 0 ? 0 : src) * 4 * KB;
+      }
+    }
+  }
+
   auto issue_a = [&](int kt) {   // A rows and all scales of K-step kt
     uint8_t* As = ringA + (kt % SA) * A_BYTES;
     const int k0 = kt * kBlock;
@@ -727,6 +746,11 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
     if constexpr (MX) {
       const void* src = x_live ? static_cast<const void*>(x_ptr + static_cast<size_t>(x_step) * kt) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
+      if constexpr (XR > 0) {
+        if (lane < XPW)
+          load_lds4(xx_live ? static_cast<const void*>(xx_ptr + static_cast<size_t>(xx_step) * kt) : kZeroScale,
+                    &sS[kt % SA][WAVES][wave * XPW]);
+      }
     } else if (lane < A_ROWS || (lane >= 32 && lane < 32 + WN * SN) || xs_lane) {   // lanes 0.. always: one instruction
       const void* src = s_live ? static_cast<const void*>(s_ptr + static_cast<size_t>(kt) * s_step) : kZeroScale;
       load_lds4(src, &sS[kt % SA][wave][0]);
@@ -739,7 +763,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   // SA - 2 later (A, B) step pairs; with SB == SA (B(kt) right after A(kt)) just those
   // pairs.  Near the end of K, where some of them were never issued, wait for all.
   auto wait_step = [&](int kt) {
-    constexpr int PAIR = A_INSTR + 1 + (XR > 0 ? 1 : 0) + B_INSTR;
+    constexpr int PAIR = A_INSTR + 1 + (XR > 0 ? (MX ? 2 : 1) : 0) + B_INSTR;
     constexpr int AFTER = (SB > SA ? B_INSTR : 0) + (SA - 2) * PAIR;
     if (kt + SB - 2 < KB) {
       wait_vmcnt<AFTER>();
@@ -819,6 +843,26 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
         acc[m][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[n % 3], af[m], acc[m][n], FP4 ? 4 : 0,
                                                                      0, 0, xb[n], 0, xa[m]);
       }
+      if constexpr (XR > 0) {   // the extra rows x the wave's sub-tiles c0, c1 (sums in accx)
+        int ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const int xr = ln & 15, xg = ln >> 4;
+        const uint8_t* xs = reinterpret_cast<const uint8_t*>(&sS[kt % SA][0][0]);
+        const v8i ax = lds_frag(ringA + (kt % SA) * A_BYTES, BM + xr, xg);
+        const int xax = xs[4 * (WAVES * 64 + xr) + xg];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int c = SWIGLU ? wm + u * NG : 2 * wm + u;
+          float4* d = reinterpret_cast<float4*>(accx + xr * XS + sub_brow(c) + 4 * xg);
+          const float4 sm = *d;
+          const v8i bx = bfrag(Bs, sub_brow(c) + xr, xg);
+          const int xbx = xs[4 * (BM + sub_brow(c) + xr) + xg];
+          const v4f q = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bx, ax, v4f{sm.x, sm.y, sm.z, sm.w},
+                                                                         FP4 ? 4 : 0, 0, 0, xbx, 0, xax);
+          *d = make_float4(q[0], q[1], q[2], q[3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     } else if (wave_live) {
       const uint8_t* Bs = ringB + (kt % SB) * B_BYTES;
 #pragma unroll
@@ -896,6 +940,46 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
         const int g = b_global_row(c + i);
         if (g >= 0 && p < mt.row_end) a.c_raw[static_cast<size_t>(p) * N + g] = accx[xr * XS + c + i];
         accx[xr * XS + c + i] = 0.f;
+      }
+    } else if constexpr (SWIGLU && MX) {   // 1x32 blocks: 8 threads of a row each
+      const int hc = (tid & 31) * 4, j0 = nt * (BN / 2) + hc;
+      const bool ok = j0 < I;
+      float4* gp = reinterpret_cast<float4*>(accx + xr * XS + hc);
+      float4* up = reinterpret_cast<float4*>(accx + xr * XS + BN / 2 + hc);
+      const float4 gs = *gp, us = *up;
+      *gp = make_float4(0.f, 0.f, 0.f, 0.f);
+      *up = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float ga[4] = {gs.x, gs.y, gs.z, gs.w}, ua[4] = {us.x, us.y, us.z, us.w};
+      const uint2 g2 = *reinterpret_cast<const uint2*>(&sbias[hc]);
+      const uint2 u2 = *reinterpret_cast<const uint2*>(&sbias[BN / 2 + hc]);
+      float bg[4], bu[4];
+      bg[0] = __uint_as_float(g2.x << 16); bg[1] = __uint_as_float(g2.x & 0xFFFF0000u);
+      bg[2] = __uint_as_float(g2.y << 16); bg[3] = __uint_as_float(g2.y & 0xFFFF0000u);
+      bu[0] = __uint_as_float(u2.x << 16); bu[1] = __uint_as_float(u2.x & 0xFFFF0000u);
+      bu[2] = __uint_as_float(u2.y << 16); bu[3] = __uint_as_float(u2.y & 0xFFFF0000u);
+      float hv[4], mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = ga[i] + bg[i];
+        const float u = ua[i] + bu[i];
+        const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+        hv[i] = ok ? h : 0.f;
+        mx = fmaxf(mx, fabsf(hv[i]));
+      }
+#pragma unroll
+      for (int w = 1; w < 8; w <<= 1) mx = fmaxf(mx, __shfl_xor(mx, w, 64));
+      const int code = mx_scale_code(mx);
+      const float mul = mx_inv_scale(code);
+      if (p < mt.row_end) {
+        if (ok)
+          *reinterpret_cast<uint32_t*>(a.h_out + static_cast<size_t>(p) * I + j0) =
+              encode4_mul(hv[0], hv[1], hv[2], hv[3], mul);
+        if ((tid & 7) == 0) {   // j0 starts a 32-column block
+          a.h_mx[static_cast<size_t>(p) * 4 * ceil_div(I, kBlock) + j0 / kMxBlock] = static_cast<uint8_t>(code);
+          if (a.h_sd != nullptr)
+            reinterpret_cast<uint8_t*>(a.h_sd)[(static_cast<size_t>(j0 / kBlock) * a.sd_rows + p) * 4 +
+                                               (j0 / kMxBlock) % 4] = static_cast<uint8_t>(code);
+        }
       }
     } else if constexpr (SWIGLU) {
       const int hc = (tid & 31) * 4, j0 = nt * (BN / 2) + hc;
@@ -1049,6 +1133,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
           }
         }
       }
+      if constexpr (XR > 0) {
+        if (has_extra) extra_epilogue();
+      }
       return;
     }
     // Each 1x128 group of h is a row's 128 columns [128 c, 128 c + 128); a tile holds
@@ -1141,13 +1228,13 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
 // takes from the other XCDs' queues.  Every queue head only grows, so every workgroup
 // leaves after at most total + 8 of its fetches.  A tile's successor in the same queue is
 // claimed during its epilogue (big_tile), the first ticket of each queue before its loop.
-// XR = 1 (block scales, a.xr = kBigExtraRows): full tiles of up to 256 + 16 rows take
+// XR = 1 (block scales or MXFP8, a.xr = kBigExtraRows): full tiles of up to 256 + 16 rows take
 // the extra-row body; a separate instantiation, so that launches without such tiles keep
 // the two-body kernel and its register allocation.
 template <bool SWIGLU, int BN, int SA, int SB, int SAN, int SBN, bool MX = false, bool FP4 = false,
           bool RAW = false, int XR = 0>
 __global__ __launch_bounds__(512) void grouped_gemm_big_kernel(const GemmArgs a, int ntiles) {
-  static_assert(XR == 0 || (!MX && !FP4 && 16 * XR == kBigExtraRows), "extra rows of the tile list");
+  static_assert(XR == 0 || (!FP4 && 16 * XR == kBigExtraRows), "extra rows of the tile list");
   constexpr int kFull = big_tile_lds<BN, 4, 4, SA, SB, FP4, XR>(), kNarrow = big_tile_lds<BN, 2, 2, SAN, SBN, FP4>();
   __shared__ __align__(16) uint8_t lds[kFull > kNarrow ? kFull : kNarrow];
   __shared__ __align__(16) float accx[XR ? 16 * big_extra_stride<BN>() : 4];
@@ -1346,7 +1433,12 @@ static void launch_gemm(const GemmArgs& a, int bm, int max_tiles, hipStream_t st
       const long tot = static_cast<long>(max_tiles) * nt_big;
       // persistent: one workgroup per CU (a multiple of the queue count), at most one per tile
       const int g = static_cast<int>(std::min((tot + 7) / 8 * 8, (cus + 7) / 8 * 8));
-      if (a.mx) {
+      if (a.mx && a.xr > 0) {   // M-tiles of up to 256 + kBigExtraRows rows
+        if constexpr (SWIGLU)
+          grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, true, false, RAW, 1><<<g, 512, 0, st>>>(a, nt_big);
+        else
+          grouped_gemm_big_kernel<false, kG2BN, kG2SA, kG2SB, kNarrowS, kNarrowS, true, false, RAW, 1><<<g, 512, 0, st>>>(a, nt_big);
+      } else if (a.mx) {
         if constexpr (SWIGLU)
           grouped_gemm_big_kernel<true, kG1BN, kG1SA, kG1SB, kNarrowS, kNarrowS, true, false, RAW><<<g, 512, 0, st>>>(a, nt_big);
         else

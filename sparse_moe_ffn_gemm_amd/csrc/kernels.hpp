@@ -38,12 +38,12 @@ constexpr int kGemmQueues = 8;      // per-XCD work queues of one large-group GE
 // on one line, one ticket per workgroup at the start of a 1104-workgroup launch cost
 // 33 us there, which the queue heads' spacing avoids.
 constexpr int kQueueStride = 1024;
-// Rows that an expert's last 256-row M-tile may hold beyond 256 in the block-scaled
-// large-group GEMMs (their full tile body takes them, the sums of the extra rows kept in
+// Rows that an expert's last 256-row M-tile may hold beyond 256 in the block-scaled and
+// MXFP8 large-group GEMMs (their full tile body takes them, the sums of the extra rows kept in
 // LDS), so that an expert with up to 272 rows is one M-tile instead of a full tile and a
 // 16-row tile that streams the same weights again.
 constexpr int kBigExtraRows = 16;
-// The extra rows of a block-scaled 256-row layer of `rows` routed rows over E experts:
+// The extra rows of a block-scaled or MXFP8 256-row layer of `rows` routed rows over E experts:
 // kBigExtraRows where the mean group is below 384 rows (most groups then hold just over
 // 256 rows or fewer, and many would end in a tile of a few rows), else 0 (their
 // remainders spread evenly, few end that short, and the kernel without the extra-row
@@ -143,7 +143,7 @@ struct GemmArgs {
   // [ceil(I/128)][sd_rows] (gemm2's A_sd), or NULL
   uint32_t* h_sd;
   float* c_raw;              // launch_gemm_raw only: [rows, N] fp32 accumulators
-  int xr;                    // block-scaled 256-row tiles: rows an M-tile holds past 256 (0 or kBigExtraRows)
+  int xr;                    // block-scaled / MXFP8 256-row tiles: rows an M-tile holds past 256 (0 or kBigExtraRows)
 };
 
 // Rows per M-tile chosen for a layer with `rows` routed rows over E experts.

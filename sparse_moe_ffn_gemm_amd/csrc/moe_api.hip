@@ -81,7 +81,7 @@ void make_plan(int T, int H, int E, int k, int I, Plan* p, int fmt = kBlockFp8) 
   // (H and I = 64 mod 128, the row-run kernel) keep 16-row tiles, all others 256
   const bool mx_rowrun = bm_block == 16 && H % 128 != 0 && I % 128 != 0 && H <= 8192 && I <= 8192;
   p->bm = fmt == kMxfp4 ? (bm_block == 16 ? 16 : 256) : fmt == kMxfp8 ? (mx_rowrun ? 16 : 256) : bm_block;
-  p->xr = fmt == kBlockFp8 && p->bm == 256 ? moe::big_extra_rows(p->rows, E) : 0;
+  p->xr = fmt != kMxfp4 && p->bm == 256 ? moe::big_extra_rows(p->rows, E) : 0;
   p->max_tiles = static_cast<int>(p->rows / p->bm + std::min<long>(E, p->rows));
   // the tile list is sized for 16-row tiles, the most of any format, so that every format
   // shares one workspace layout

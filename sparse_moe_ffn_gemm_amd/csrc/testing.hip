@@ -80,9 +80,9 @@ moe_status moe_test_gemm_raw(int gemm, int format, int bm, const uint8_t* A,
   if (rows == 0) return MOE_OK;
 
   // the tile list: bm-row tiles per expert, expert-major, by the forward's rule (the last
-  // tile of a block-scaled 256-row launch may hold moe::kBigExtraRows more); work-queue
-  // heads zero
-  const int xr = !mx && bm == 256 ? moe::big_extra_rows(rows, E) : 0;
+  // tile of a block-scaled or MXFP8 256-row launch may hold moe::kBigExtraRows more);
+  // work-queue heads zero
+  const int xr = !fp4 && bm == 256 ? moe::big_extra_rows(rows, E) : 0;
   std::vector<moe::MTile> tiles;
   std::vector<int32_t> tile_off(E + 1), head(moe::kQueueStride * (1 + 2 * moe::kGemmQueues), 0);
   int off = 0;

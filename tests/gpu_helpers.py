@@ -472,8 +472,7 @@ def oracle_forward_out(li, top_k, I, ox, toks, fmt):
 
 def pick_experts(counts, bm=256, extra=16):
     """Experts whose every row the prefill checks cover: one whose single M-tile holds rows
-    past 256 (256 < rows <= 256 + extra: the block-scaled full tile's extra rows; other
-    formats split it), one with a full 256-row tile and a narrow overflow tile
+    past 256 (256 < rows <= 256 + extra: the full tile's extra rows; MXFP4 splits it), one with a full 256-row tile and a narrow overflow tile
     (256 + extra < rows <= 320), if any, the hottest, and the least busy active one."""
     act = np.nonzero(counts > 0)[0]
     pick = [int(act[np.argmax(counts[act])]), int(act[np.argmin(counts[act])])]

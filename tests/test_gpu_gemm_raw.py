@@ -9,7 +9,7 @@ significand, so any correct evaluation order gives the exact result, and the GPU
 equal the float64 reference bit for bit.  A wrong fragment layout, a wrong K-tail chunk, a
 swapped gate/up pairing, a wrong scale row or block, or a tile that reads another expert's
 rows changes the exact value.  Every kernel family is covered: the persistent 256-row
-kernel (full tiles, block-scaled full tiles with 1..16 extra rows, full-body tiles of
+kernel (full tiles, block-scaled and MXFP8 full tiles with 1..16 extra rows, full-body tiles of
 65..255 rows, narrow tiles of at most 64 rows), the
 LDS-ring kernel (16/64/128-row tiles), the row-run streaming kernel (K = 64 mod 128), in
 the block-scaled, MXFP8 and MXFP4 formats, with K tails of 64, N tails, idle experts.
@@ -52,7 +52,7 @@ class Case:
 
 
 CASES = [
-    # persistent 256-row kernel.  Block scales: a layer whose mean group is below 384 rows
+    # persistent 256-row kernel.  Block scales and MXFP8: a layer whose mean group is below 384 rows
     # takes the kernel whose full tiles may hold 16 extra rows, a layer of larger groups
     # the one without (cases 24, 25).
     # full + narrow (44), idle, exact 256, narrow only (17), full + full-body 74-row tile;
@@ -81,6 +81,10 @@ CASES = [
     # MXFP8: persistent kernel and row-run kernel
     Case(1, "mxfp8", 256, [300, 0, 256, 17, 330], 320, 384, 11),
     Case(2, "mxfp8", 256, [270, 64, 0, 500], 192, 320, 12),
+    Case(1, "mxfp8", 256, [272, 0, 257, 17, 528, 273], 320, 384, 26),   # extra rows
+    Case(2, "mxfp8", 256, [271, 528, 0, 258], 192, 320, 27),
+    Case(1, "mxfp8", 256, [800, 0, 530], 320, 384, 28),                 # no extra rows
+    Case(2, "mxfp8", 256, [700, 0, 460], 192, 320, 29),
     Case(1, "mxfp8", 16, [5, 16, 0, 33, 1], 320, 640, 13),
     Case(2, "mxfp8", 16, [5, 16, 0, 33, 1], 192, 448, 14),
     # MXFP4 weights: persistent kernel; row-run with 32-column workgroups (few tiles) and
