@@ -481,8 +481,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
   static_assert(WC % 16 == 0 && BN % 64 == 0 && (!SWIGLU || SN % 2 == 0), "tile");
   static_assert(SA >= 2 && SB >= SA, "rings");
   static_assert(A_ROWS % 8 == 0 && A_ROWS <= 32 && WN * SN <= 32 && B_ROWS % 8 == 0, "scale lanes");
-  // extra rows: block scales only; two of a wave's sub-tiles each (gemm1: a gate and its up
-  // sub-tile), all of a wave's columns in one 128-row weight scale block (gemm2)
+  // extra rows: block scales or MXFP8; two of a wave's sub-tiles each (gemm1: a gate and its
+  // up sub-tile), all of a wave's columns in one 128-row weight scale block (gemm2)
   static_assert(XR == 0 || (XR == 1 && !FP4 && XPW == 2 && 32 + WN * SN <= 48 &&
                             (SWIGLU ? NG == WM : SN == 2 * WM && WC == 128)), "extra rows");
 
@@ -885,28 +885,26 @@ __device__ __forceinline__ void big_tile(const GemmArgs& a, const int nt, MTile 
       }
 #pragma unroll
       for (int j = 0; j < LAG; ++j) sc_tail[j] = sav[(NP - LAG + j) % SM] * sbv[scale_col((NP - LAG + j) / SM)];
-      if constexpr (XR > 0) {
-        {   // the extra rows x the wave's sub-tiles c0, c1: sums in accx
-          // (the lane index is produced here, in the loop, so that no address of this block
-          // stays live across the K loop: the body has no register to spare for one)
-          int ln;
-          asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-          const int xr = ln & 15, xg = ln >> 4;
-          const v8i ax = lds_frag(ringA + (kt % SA) * A_BYTES, BM + xr, xg);
-          const float sx = sS[kt % SA][xr / XPW][48 + xr % XPW];
+      if constexpr (XR > 0) {   // the extra rows x the wave's sub-tiles c0, c1: sums in accx
+        // (the lane index is produced here, in the loop, so that no address of this block
+        // stays live across the K loop: the body has no register to spare for one)
+        int ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        const int xr = ln & 15, xg = ln >> 4;
+        const v8i ax = lds_frag(ringA + (kt % SA) * A_BYTES, BM + xr, xg);
+        const float sx = sS[kt % SA][xr / XPW][48 + xr % XPW];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int c = SWIGLU ? wm + u * NG : 2 * wm + u;
-            float4* d = reinterpret_cast<float4*>(accx + xr * XS + sub_brow(c) + 4 * xg);
-            float4 sm = *d;
-            const v8i bx = lds_frag(Bs, sub_brow(c) + xr, xg);
-            const v4f q = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bx, ax, zero, 0, 0, 0, 0, 0, 0);
-            const float ec = sx * sbv[SWIGLU && u == 1 ? NG : 0];
-            sm.x = fmaf(q[0], ec, sm.x); sm.y = fmaf(q[1], ec, sm.y);
-            sm.z = fmaf(q[2], ec, sm.z); sm.w = fmaf(q[3], ec, sm.w);
-            *d = sm;
-            __builtin_amdgcn_sched_barrier(0);
-          }
+        for (int u = 0; u < 2; ++u) {
+          const int c = SWIGLU ? wm + u * NG : 2 * wm + u;
+          float4* d = reinterpret_cast<float4*>(accx + xr * XS + sub_brow(c) + 4 * xg);
+          float4 sm = *d;
+          const v8i bx = lds_frag(Bs, sub_brow(c) + xr, xg);
+          const v4f q = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bx, ax, zero, 0, 0, 0, 0, 0, 0);
+          const float ec = sx * sbv[SWIGLU && u == 1 ? NG : 0];
+          sm.x = fmaf(q[0], ec, sm.x); sm.y = fmaf(q[1], ec, sm.y);
+          sm.z = fmaf(q[2], ec, sm.z); sm.w = fmaf(q[3], ec, sm.w);
+          *d = sm;
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
