@@ -38,7 +38,9 @@ size_t moe_test_gemm_raw_workspace_bytes(int rows, int E, int K);
  *                     storage), MXFP8 A
  *   bm             M-tile rows, which selects the kernel family exactly as moe_forward's
  *                  plan does: 256 -> the persistent large-group kernel (tiles of at most
- *                  64 rows take its narrow body); 16 with K = 64 mod 128 (or MXFP4) -> the
+ *                  64 rows take its narrow body; formats 0 and 1 with a mean group below
+ *                  384 rows let an expert's last tile hold up to 16 more rows, as the
+ *                  forward's tile list does); 16 with K = 64 mod 128 (or MXFP4) -> the
  *                  row-run streaming kernel; 16, 64 or 128 otherwise -> the LDS-ring kernel
  *                  (block scales only; MX formats take 16 or 256)
  *   A [A_rows, K]  e4m3 codes;  perm [rows] (GEMM1 only) device int32
