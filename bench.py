@@ -220,9 +220,6 @@ def roofline(k_alg, k_s, shape, fmt, kernel):
         "intensity_flop_per_byte": round(flops / nbytes, 1),
         "mfma_tflops": round(mfma, 2), "mfma_frac": round(mfma / PEAK_FP8_TFLOPS, 4),
         "hbm_gbs": round(hbm, 1), "hbm_frac": round(hbm / PEAK_HBM_GBS, 4)})
-    if rec and "mfma_busy_frac" in rec:
-        # matrix-core busy cycles / (active cycles x SIMDs), from the same counter run
-        roof["mfma_busy_frac_counter"] = rec["mfma_busy_frac"]
     return roof
 
 
